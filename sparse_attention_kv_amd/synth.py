@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the lazy-update loop attention step.
+
+This module only draws random inputs and describes workload shapes and
+schedules; it holds none of the method's arithmetic.  Both the GPU library's
+tests/benchmark and the CPU oracle consume the same arrays from here.
+
+Random numbers: numpy PCG64 with a fixed seed per workload and a fixed draw
+order.  Values are drawn in fp32; bf16 workloads round each per-loop tensor to
+bf16 (round to nearest even), and both sides read the same bf16 bytes (the
+oracle reads their exact fp32 expansion).
+
+Inputs per loop r (0-based list index r-1): the hidden state entering the loop
+h_r [N][D], and the loop's query/key/value rows q_r, k_r, v_r [N][H][d].  In
+this attention-only harness the loop's projections are given; the method
+decides which rows of them it uses.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (bit manipulation of IEEE fp32; round to nearest even)
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f32(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp32 values of a stored tensor (bf16 bits or fp32)."""
+    return bf16_bits_to_f32(a) if dtype == "bf16" else np.ascontiguousarray(a, np.float32)
+
+
+# --------------------------------------------------------------------------
+# Workload table
+
+@dataclass
+class Workload:
+    name: str
+    N: int
+    H: int
+    d: int
+    R: int
+    g: int
+    n_sink: int
+    rho: list            # per loop, fraction of N kept active (rho[0] == 1)
+    kcols: list          # per loop, column budget (kcols[0] == N: dense first loop)
+    bits: list           # per loop: bits[0] base (8), later residual bits (4/2)
+    dtype: str           # "f32" or "bf16"
+    seed: int
+    kind: str = "prefill"   # "tiny", "prefill", "decode", "block"
+    sigma_mu: tuple = (-2.0, -0.5)   # log sigma mean = a + b*r
+    sigma_sd: float = 1.0
+    boost_frac: float = 0.03
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def D(self) -> int:
+        return self.H * self.d
+
+    def sched(self) -> dict:
+        return dict(N=self.N, H=self.H, d=self.d, g=self.g, R=self.R, n_sink=self.n_sink,
+                    rho=list(self.rho), kcols=list(self.kcols), bits=list(self.bits))
+
+    def scaled(self, **kw) -> "Workload":
+        """Same recipe at other sizes; column budgets scale with N unless given."""
+        w = dataclasses.replace(self, **kw)
+        if "N" in kw and "kcols" not in kw:
+            ratio = kw["N"] / self.N
+            kc = [kw["N"]] + [max(w.n_sink + 1, int(round(c * ratio))) for c in self.kcols[1:]]
+            w = dataclasses.replace(w, kcols=kc)
+        return w
+
+
+WORKLOADS = {
+    # 1 head x 64, seq 256, R=2, fp32; rho 0.25, 64 columns incl. 4 sinks;
+    # int8 base / int4 residual, group 32.
+    "tiny": Workload("tiny", N=256, H=1, d=64, R=2, g=32, n_sink=4, rho=[1.0, 0.25],
+                     kcols=[256, 64], bits=[8, 4], dtype="f32", seed=0, kind="tiny"),
+    # one looped attention layer, 16 x 128, seq 4096, R=4, bf16; rho 0.2, k 512,
+    # int8 base + int4 residuals, group 64.
+    "layer4k": Workload("layer4k", N=4096, H=16, d=128, R=4, g=64, n_sink=4,
+                        rho=[1.0, 0.2, 0.2, 0.2], kcols=[4096, 512, 512, 512],
+                        bits=[8, 4, 4, 4], dtype="bf16", seed=1, sigma_sd=1.0),
+    # long-context prefill, 16 x 128, seq 32768, R=4, bf16; active fractions
+    # 1/.4/.2/.1; 2048 columns incl. 4 sinks; int4 at loop 2, int2 at 3-4.
+    "prefill32k": Workload("prefill32k", N=32768, H=16, d=128, R=4, g=64, n_sink=4,
+                           rho=[1.0, 0.4, 0.2, 0.1], kcols=[32768, 2048, 2048, 2048],
+                           bits=[8, 4, 2, 2], dtype="bf16", seed=2, sigma_sd=1.5),
+}
+
+
+# --------------------------------------------------------------------------
+# Generators
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def gen_tiny(w: Workload) -> dict:
+    """Tiny case: h_1, K_1, V_1 ~ N(0,1); q_r is h_r (H*d == D); per-token
+    loop-2 delta scale sigma_i = exp(N(-3,1)), 25% of tokens scaled x20."""
+    rng = _rng(w.seed)
+    N, D = w.N, w.D
+    h1 = rng.standard_normal((N, D), dtype=np.float32)
+    k1 = rng.standard_normal((N, D), dtype=np.float32)
+    v1 = rng.standard_normal((N, D), dtype=np.float32)
+    sig = np.exp(rng.normal(-3.0, 1.0, N)).astype(np.float32)
+    boost = rng.choice(N, size=N // 4, replace=False)
+    sig[boost] *= np.float32(20.0)
+    hs, ks, vs = [h1], [k1], [v1]
+    for _ in range(1, w.R):
+        hs.append(hs[-1] + sig[:, None] * rng.standard_normal((N, D), dtype=np.float32))
+        ks.append(ks[-1] + sig[:, None] * rng.standard_normal((N, D), dtype=np.float32))
+        vs.append(vs[-1] + sig[:, None] * rng.standard_normal((N, D), dtype=np.float32))
+    shp = (N, w.H, w.d)
+    return dict(h=hs, q=[x.reshape(shp).copy() for x in hs], k=[x.reshape(shp) for x in ks],
+                v=[x.reshape(shp) for x in vs], dtype="f32")
+
+
+def gen_prefill(w: Workload) -> dict:
+    """Ouro-class layer: per-head mean query direction m_h ~ N(0, I_d);
+    q_1 = m_h + N(0,I); K_1, V_1 ~ N(0,I); h_1 ~ N(0, I_D).  Per head a
+    fraction boost_frac of columns (drawn from positions >= 4) get
+    K_1 += 3 m_h/|m_h| (about +3 logits).  Loop r >= 2: per-token
+    sigma = exp(N(a + b*r, sigma_sd)); h, q, K, V each get + sigma * N(0, I),
+    accumulated in fp32 and rounded to bf16 per loop."""
+    rng = _rng(w.seed)
+    N, H, d, D = w.N, w.H, w.d, w.D
+    m = rng.standard_normal((H, d), dtype=np.float32)
+    q = m[None] + rng.standard_normal((N, H, d), dtype=np.float32)
+    k = rng.standard_normal((N, H, d), dtype=np.float32)
+    v = rng.standard_normal((N, H, d), dtype=np.float32)
+    h = rng.standard_normal((N, D), dtype=np.float32)
+    nb = int(round(w.boost_frac * N))
+    unit = m / np.linalg.norm(m, axis=1, keepdims=True)
+    for hh in range(H):
+        cols = rng.choice(np.arange(4, N), size=nb, replace=False)
+        k[cols, hh, :] += np.float32(3.0) * unit[hh]
+    cast = f32_to_bf16_bits if w.dtype == "bf16" else (lambda x: x.copy())
+    hs, qs, ks, vs = [cast(h)], [cast(q)], [cast(k)], [cast(v)]
+    a, b = w.sigma_mu
+    for r in range(2, w.R + 1):
+        sig = np.exp(rng.normal(a + b * r, w.sigma_sd, N)).astype(np.float32)
+        h += sig[:, None] * rng.standard_normal((N, D), dtype=np.float32)
+        q += sig[:, None, None] * rng.standard_normal((N, H, d), dtype=np.float32)
+        k += sig[:, None, None] * rng.standard_normal((N, H, d), dtype=np.float32)
+        v += sig[:, None, None] * rng.standard_normal((N, H, d), dtype=np.float32)
+        hs.append(cast(h)); qs.append(cast(q)); ks.append(cast(k)); vs.append(cast(v))
+    return dict(h=hs, q=qs, k=ks, v=vs, dtype=w.dtype)
+
+
+def generate(w: Workload) -> dict:
+    if w.kind == "tiny":
+        return gen_tiny(w)
+    if w.kind == "prefill":
+        return gen_prefill(w)
+    raise ValueError(f"no generator for kind {w.kind}")
+
+
+def as_f32_inputs(inp: dict) -> dict:
+    """The same inputs as exact fp32 arrays (what the oracle reads)."""
+    dt = inp["dtype"]
+    return {key: [to_f32(a, dt) for a in inp[key]] for key in ("h", "q", "k", "v")}
