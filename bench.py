@@ -1,0 +1,291 @@
+#!/usr/bin/env python
+"""Benchmark of FlashLoop's lazy-update loop attention step on one MI355X.
+
+A step is one full pass of the R-loop attention step over one synthetic
+sequence: loop 1 (int8 base quantisation, dense causal attention, column
+statistics) then loops 2..R (token statistic + nested top-k, residual
+quantisation, column selection, cache rebuild when the column set shrinks,
+sparse attention, column statistics when the next loop prunes).  Inputs are
+resident in HBM before the timed region.
+
+value = active-query tokens per second over the whole step,
+        sum_r n_r / step time (n_1 = N: every token is a query in loop 1).
+
+Prints ONE JSON line.  Extra fields: per-loop times, the lazy loops' own rate,
+per-kernel times, the dominant kernel's roofline, KV bytes/token, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "active-query tokens/s of loop-r sparse attention @32K, R=4; KV bytes/token; %roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill32k")
+    ap.add_argument("--cpu-rows", type=int, default=32,
+                    help="query rows per loop in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs_per_head(torch, act, sel, N):
+    """sum over heads and active rows of |S(i)| = #selected columns <= i."""
+    a = act.to(torch.int64)
+    if sel is None:
+        return int((a + 1).sum().item()), None
+    cnt = torch.searchsorted(sel.to(torch.int64).contiguous(), a.expand(sel.shape[0], -1).contiguous(),
+                             right=True)
+    return int(cnt.sum().item()) // 1, cnt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_kv_amd import fl, synth
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.generate(w)
+    log(f"[bench] generated {w.name} inputs in {time.time() - t0:.1f}s")
+    dt = inp["dtype"]
+
+    def dev(a):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    D = {k: [dev(a) for a in inp[k]] for k in ("h", "q", "k", "v")}
+    N, H, d, R = w.N, w.H, w.d, w.R
+    n_act = [N]
+    for r in range(1, R):
+        n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
+    run = fl.LoopRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
+                        dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for r in range(1, R + 1):
+            if events is not None:
+                events[r - 1].record(stream)
+            hp = D["h"][r - 2] if r > 1 else None
+            qp = D["q"][r - 2] if r > 1 else None
+            run.step(r, D["h"][r - 1], hp, D["q"][r - 1], D["k"][r - 1], D["v"][r - 1], qp)
+        if events is not None:
+            events[R].record(stream)
+
+    log(f"[bench] inputs resident; n_active={n_act} k={w.kcols}")
+    # ---- warmup ----
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    # algorithmic work per loop from the actual index sets
+    loops = []
+    for r in range(1, R + 1):
+        act = run.active[r - 1]
+        sel = run.sel_used(r)
+        pairs, _ = pairs_per_head(torch, act, sel, N)
+        if sel is None:
+            pairs *= H
+        rebuilt = r > 1 and run.k_used(r) < run.k_used(r - 1)
+        colstat = r < R and w.kcols[r] < run.k_used(r)
+        loops.append(dict(r=r, n=n_act[r - 1], k=run.k_used(r), pairs=pairs, rebuilt=rebuilt,
+                          colstat=colstat))
+
+    log("[bench] warmup done")
+    # ---- timed region ----
+    if not args.no_kernel_timing:
+        fl.fl_timing_report()          # discard warmup records
+        fl.fl_timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ktab = {}
+    if not args.no_kernel_timing:
+        fl.fl_timing_enable(False)
+        ktab = fl.fl_timing_report()
+    loop_ms = np.array([[evs[s][r].elapsed_time(evs[s][r + 1]) for r in range(R)]
+                        for s in range(args.steps)])
+    step_ms = loop_ms.sum(axis=1)
+    ms_per_step = float(np.mean(step_ms))
+    tokens = sum(n_act)
+    value = tokens / (ms_per_step / 1e3)
+    lazy_ms = float(np.mean(loop_ms[:, 1:].sum(axis=1))) if R > 1 else 0.0
+    lazy_tokens = sum(n_act[1:])
+
+    # ---- roofline of the dominant kernel ----
+    flops_step = {"attn": sum(4.0 * d * L["pairs"] for L in loops),
+                  "attn_rebuild": sum(4.0 * d * L["pairs"] for L in loops if L["rebuilt"]),
+                  "colstat": sum(2.0 * d * L["pairs"] for L in loops if L["colstat"])}
+    kernels = {}
+    for name, (cnt, ms) in ktab.items():
+        per_step_ms = ms / args.steps
+        e = dict(launches_per_step=cnt / args.steps, ms_per_step=round(per_step_ms, 4),
+                 avg_launch_us=round(1e3 * ms / max(cnt, 1), 2))
+        if name in flops_step and ms > 0:
+            e["tflops"] = round(flops_step[name] / (per_step_ms / 1e3) / 1e12, 2)
+        kernels[name] = e
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        if dom in flops_step:
+            ach = flops_step[dom] / (kernels[dom]["ms_per_step"] / 1e3) / 1e12
+            roofline = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS,
+                            unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                            flops_per_step=flops_step[dom],
+                            avg_launch_us=kernels[dom]["avg_launch_us"])
+        else:
+            roofline = dict(kernel=dom, bound="hbm", achieved=None, peak=PEAK_HBM_GBS, unit="GB/s",
+                            frac=None, traffic=None)
+
+    # ---- KV bytes per token (codes + scales, and with index metadata) ----
+    HD = H * d
+    kv_codes = 2 * N * (HD + 4 * HD // w.g)
+    meta = 0
+    for r in range(2, R + 1):
+        kv_codes += 2 * n_act[r - 1] * (HD * w.bits[r - 1] // 8 + 4 * HD // w.g)
+        meta += 4 * n_act[r - 1] + 4 * N          # row list + slot map
+    kv = dict(codes_scales=round(kv_codes / N, 1), with_metadata=round((kv_codes + meta) / N, 1),
+              bf16_all_loops=2 * HD * 2 * R, ratio=round(2 * HD * 2 * R / (kv_codes / N), 2))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "active-query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "H": H, "d": d, "R": R, "g": w.g,
+                   "active_per_loop": n_act, "k_per_loop": [L["k"] for L in loops],
+                   "bits_per_loop": w.bits, "n_sink": w.n_sink},
+        "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.mean(loop_ms[:, i])), 4),
+                       pairs=L["pairs"], rebuilt=L["rebuilt"], colstat=L["colstat"])
+                  for i, L in enumerate(loops)],
+        "lazy_loops_tokens_per_s": round(lazy_tokens / (lazy_ms / 1e3), 1) if lazy_ms else None,
+        "wall_s_timed": round(wall, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "kv_bytes_per_token": kv,
+    }
+
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, run, n_act, loops, args.cpu_rows, torch, np)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
+    """The oracle, as is, on a bounded sample of the same workload: token
+    statistic + selection, quantisation and column selection in full; the
+    per-row work (attention, cache rebuild, column statistics) on m evenly
+    spaced active rows per loop (all heads), extrapolated to n_r rows."""
+    import oracle
+
+    t_all = time.time()
+    x = {k: [synth_f32(a, inp["dtype"], np) for a in inp[k]] for k in ("h", "q", "k", "v")}
+    N, H, d, g = w.N, w.H, w.d, w.g
+    sm = np.float32(1.0 / np.sqrt(d))
+    total_s = 0.0
+    khat = vhat = None
+    per_loop = []
+    for r in range(1, w.R + 1):
+        act = run.active[r - 1].cpu().numpy()
+        sel = run.sel_used(r)
+        sel = None if sel is None else sel.cpu().numpy()
+        samp = act[np.linspace(0, len(act) - 1, min(m, len(act))).astype(np.int64)]
+        t_full = t_rows = 0.0
+        t = time.perf_counter()
+        if r == 1:
+            _, _, _, khat_n = oracle.quantize_rows(x["k"][0], None, g, w.bits[0])
+            _, _, _, vhat_n = oracle.quantize_rows(x["v"][0], None, g, w.bits[0])
+        else:
+            prev = run.active[r - 2].cpu().numpy()
+            stat = oracle.delta_norm(x["h"][r - 1], x["h"][r - 2], prev)
+            oracle.top_select(stat, n_act[r - 1], prev)
+            _, _, _, kr = oracle.quantize_rows(x["k"][r - 1][act], khat[act], g, w.bits[r - 1])
+            _, _, _, vr = oracle.quantize_rows(x["v"][r - 1][act], vhat[act], g, w.bits[r - 1])
+            khat_n = khat.copy(); khat_n[act] = kr
+            vhat_n = vhat.copy(); vhat_n[act] = vr
+            if loops[r - 1]["rebuilt"]:
+                cs = run.col_stat[r - 2][:, : loops[r - 2]["k"]].cpu().numpy()
+                sp = run.sel_used(r - 1)
+                oracle.select_columns(cs, None if sp is None else sp.cpu().numpy(),
+                                      loops[r - 1]["k"], w.n_sink)
+        t_full = time.perf_counter() - t
+        lse_s = run.lse.cpu().numpy()[samp]
+        mu_s = run.mass_u.cpu().numpy()[samp]
+        ou_s = run.out_u.cpu().numpy()[samp]
+        t = time.perf_counter()
+        if loops[r - 1]["rebuilt"]:
+            sp = run.sel_used(r - 1)
+            oracle.unselected_cache(x["q"][r - 2], khat, vhat, samp,
+                                    None if sp is None else sp.cpu().numpy(), sel, lse_s, sm,
+                                    None if sp is None else mu_s, None if sp is None else ou_s)
+        o, l = oracle.attend(x["q"][r - 1], khat_n, vhat_n, samp, sel, sm,
+                             None if r == 1 else mu_s, None if r == 1 else ou_s)
+        if loops[r - 1]["colstat"]:
+            oracle.column_stats(x["q"][r - 1], khat_n, samp, sel, l, sm, None if r == 1 else mu_s)
+        t_rows = time.perf_counter() - t
+        t_loop = t_full + t_rows * len(act) / len(samp)
+        per_loop.append(dict(r=r, full_s=round(t_full, 3), sampled_rows=len(samp),
+                             rows_s=round(t_rows, 3), extrapolated_s=round(t_loop, 2)))
+        total_s += t_loop
+        khat, vhat = khat_n, vhat_n
+        log(f"[bench] cpu oracle loop {r}: full {t_full:.2f}s, {len(samp)} rows {t_rows:.2f}s")
+    tokens = sum(n_act)
+    return {"value": round(tokens / total_s, 1), "unit": "active-query tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"all {w.R} loops of {w.name}; token statistic/selection, quantisation and "
+                       f"column selection in full; attention, cache rebuild and column statistics "
+                       f"on {m} evenly spaced active rows per loop (all {H} heads), extrapolated "
+                       f"to n_r rows"),
+            "extrapolated_step_s": round(total_s, 2), "measured_s": round(time.time() - t_all, 1),
+            "loops": per_loop}
+
+
+def synth_f32(a, dtype, np):
+    from sparse_attention_kv_amd import synth
+    return synth.to_f32(a, dtype)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,291 @@
+/*
+ * flashloop.h -- C ABI of the MI355X (gfx950) FlashLoop lazy-update loop
+ * attention library (libflashloop.so).
+ *
+ * Method: "FlashLoop: Fast and Memory-Efficient Looped Transformers via Lazy
+ * Updates" (arXiv 2609.29812).  One call sequence per loop r of a looped
+ * (weight-shared, R-times repeated) Transformer layer:
+ *   fl_select_active      Sec. 4.1  token-change statistic + nested top-k
+ *   fl_kv_residual_quant  Sec. 3.3, 4.3, App. E  int8 base / int4,int2 residual
+ *   fl_select_columns     Sec. 4.2  column ranking from the previous loop
+ *   fl_sparse_loop_attn   Sec. 4.2  sparse attention with cached pruned mass
+ *   fl_loop_step          Sec. 4.1-4.3  one whole loop (the four above)
+ *
+ * Conventions (all entry points):
+ *  - Return FL_OK (0) or a negative FL_ERR_*; fl_last_error() gives a
+ *    thread-local message for the last failure on the calling thread.
+ *  - Arguments are validated on the host before anything is enqueued; a call
+ *    that fails validation has no side effects.
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees them and keeps no reference after the call returns.  Work is
+ *    enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream); outputs are valid in stream order.  No call synchronises the
+ *    device with the host.
+ *  - Scratch memory comes from a caller workspace sized by fl_workspace_size.
+ *  - Layouts are row-major.  Per-token tensors are [N][H][d] indexed by token
+ *    position; per-row loop state (out, lse, mass_u, out_u) is also indexed by
+ *    token position ([N][H][d] / [N][H]) so that rows that are inactive in a
+ *    loop keep the values of the last loop that computed them.
+ *  - Index lists are int32, ascending, unique.
+ *  - Supported shapes: d in {64, 128}; g in {32, 64} dividing d; H*d <= 8192.
+ */
+#ifndef FLASHLOOP_H
+#define FLASHLOOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FL_VERSION_MAJOR 0
+#define FL_VERSION_MINOR 1
+
+typedef void* fl_stream_t; /* hipStream_t */
+
+enum fl_status {
+    FL_OK = 0,
+    FL_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
+    FL_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. d = 96)   */
+    FL_ERR_WORKSPACE = -3,   /* workspace smaller than fl_workspace_size  */
+    FL_ERR_HIP = -4          /* a HIP runtime call failed                 */
+};
+
+enum fl_dtype { FL_F32 = 0, FL_BF16 = 1 };
+
+#define FL_MAX_LEVELS 16
+
+/* One level of the loop-indexed KV cache (paper Sec. 3.3 / 4.3: a quantised
+ * base state plus quantised cross-loop residuals; residuals exist only for
+ * the tokens active in that loop).
+ *   level 0 (loop 1): all N tokens, bits 8 (int8) or 32 (raw fp32).
+ *   level l >= 1 (loop l+1): the n_rows tokens active in loop l+1 (ascending
+ *   positions `rows`, and `slot` mapping position -> packed row or -1),
+ *   bits 4, 2, 8 or 32.
+ * Codes: two's complement, per (row, head) d*bits/8 bytes; int4 holds the
+ * even channel in the low nibble, int2 holds channel c at bits 2*(c mod 4);
+ * bits 32 stores the raw fp32 values (residuals) instead of codes.
+ * Scales: fp32 [n_rows][H][d/g], one per group of g contiguous channels
+ * (unused for bits 32).  The dequantised value of a token at loop r is
+ *   xhat = code_0*s_0, then xhat = xhat + code_l*s_l for l = 1..r-1 while the
+ * token is present in level l (sets are nested, so presence stops at the first
+ * absent level). */
+typedef struct fl_kv_level {
+    int bits;
+    int n_rows;
+    const int32_t* rows; /* [n_rows]; NULL for level 0 */
+    const int32_t* slot; /* [N];      NULL for level 0 */
+    void* k_codes;       /* [n_rows][H][d*bits/8] */
+    void* v_codes;
+    float* k_scale;      /* [n_rows][H][d/g] */
+    float* v_scale;
+} fl_kv_level;
+
+typedef struct fl_kv_cache {
+    int N, H, d, g;
+    int n_levels; /* levels 0..n_levels-1 hold data */
+    fl_kv_level level[FL_MAX_LEVELS];
+} fl_kv_cache;
+
+/* ------------------------------------------------------------------------
+ * Workspace sizing.  op is one of the fl_ws_op values; the remaining
+ * arguments are the sizes the call will use (unused ones are ignored).
+ * Returns the byte count, or 0 when the sizes are invalid. */
+enum fl_ws_op {
+    FL_WS_SELECT_ACTIVE = 1,  /* a = n_cand                                    */
+    FL_WS_SELECT_COLUMNS = 2, /* a = H, b = n_cand                             */
+    FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = dtype of q/k/v       */
+    FL_WS_LOOP_STEP = 4       /* a = H, b = N (largest k), c = d, e = dtype    */
+};
+size_t fl_workspace_size(int op, long a, long b, long c, long e);
+
+/* ------------------------------------------------------------------------
+ * fl_select_active -- paper Sec. 4.1 (cross-loop token-sparse updates).
+ * For each candidate token cand[t] (the tokens active in the previous loop;
+ * NULL = all positions 0..n_cand-1) computes the statistic
+ *   stat_out[t] = || h_cur[cand[t]] - h_prev[cand[t]] ||_2   (fp32)
+ * over D channels (h_* are [N][D], dtype FL_BF16 or FL_F32), then selects the
+ * n_select candidates with the largest statistic; equal statistics go to the
+ * lower position; -0 ranks as +0; statistics must be finite.
+ * If stat_in != NULL the statistic is not computed and stat_in[n_cand] is
+ * ranked instead (h_cur / h_prev may then be NULL).
+ * Outputs: active_out[n_select] ascending positions; slot_out (optional, [N])
+ * gets slot_out[active_out[s]] = s and -1 for every other position.
+ * Workspace: fl_workspace_size(FL_WS_SELECT_ACTIVE, n_cand, ...).
+ * Errors: FL_ERR_INVALID_ARG for null required pointers, n_select outside
+ * [1, n_cand], n_cand > N, D < 1. */
+int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, int D,
+                     const int32_t* cand, int n_cand, int n_select, const float* stat_in,
+                     float* stat_out, int32_t* active_out, int32_t* slot_out, void* ws,
+                     size_t ws_bytes, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_select_columns -- paper Sec. 4.2 (loop-aware sparse attention: rank the
+ * columns with the previous loop's statistics, keep the top-K under a
+ * loop-specific budget, prune progressively).
+ * Per head h: candidates cand_cols[h][0..n_cand-1] (ascending positions that
+ * include the sinks 0..n_sink-1; NULL = positions 0..n_cand-1) with
+ * statistics col_stat[h][n_cand].  Output sel_out[h][k]: the sinks plus the
+ * k - n_sink non-sink candidates with the largest statistic (ties to the
+ * lower position), ascending.  If n_cand <= k the candidates are copied
+ * (sel_out is then [H][n_cand]).
+ * Errors: FL_ERR_INVALID_ARG for null pointers, n_sink < 0, k <= n_sink,
+ * k - n_sink > n_cand - n_sink. */
+int fl_select_columns(const float* col_stat, const int32_t* cand_cols, int H, int n_cand,
+                      int n_sink, int k, int32_t* sel_out, void* ws, size_t ws_bytes,
+                      fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_kv_residual_quant -- paper Sec. 3.3, Sec. 4.3, App. E (quantised base
+ * plus low-bit cross-loop residuals; residuals only for the active tokens).
+ * Writes codes and scales of cache->level[level] (descriptor filled by the
+ * caller: bits, n_rows, rows, slot and the code/scale buffers).
+ *   level 0: quantises k_new / v_new of all N tokens (int8, or raw fp32).
+ *   level l >= 1: for each row t, token i = rows[t]:
+ *     x = new(i) - xhat_{l-1}(i)   (fp32; xhat from levels 0..l-1 of token i)
+ *     per group: s = max|x| / qmax (qmax = 2^(bits-1)-1), code =
+ *     round-half-even(x/s) clamped to [-qmax, qmax] (s = 0 -> codes 0).
+ * The arithmetic is IEEE fp32 with correctly rounded division and no fused
+ * multiply-add, so codes and scales are reproducible bit for bit.
+ * k_new / v_new: dtype FL_BF16 or FL_F32, [N][H][d] by position
+ * (new_gathered = 0) or [n_rows][H][d] aligned with rows (new_gathered = 1).
+ * Errors: FL_ERR_INVALID_ARG (null buffers, level >= FL_MAX_LEVELS, levels
+ * below `level` missing, n_rows > N), FL_ERR_UNSUPPORTED (bits not in
+ * {2,4,8,32}, d or g unsupported). */
+int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const void* k_new,
+                         const void* v_new, int new_gathered, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_sparse_loop_attn -- paper Sec. 4.2 (sparse attention over the selected
+ * columns; the softmax over the selected logits is rescaled by the cached
+ * probability mass of the selected set, and the pruned columns' cached
+ * contribution is added back):
+ *   S(i) = { j in sel[h] : j <= i }
+ *   lse(i) = log sum_{j in S(i)} exp(sm * q(i).khat(j))
+ *   o(i)   = (1 - M_U(i)) * sum_{j in S(i)} exp(sm*q(i).khat(j) - lse(i)) vhat(j)
+ *            + O_U(i)
+ * for each active row i and head h, with khat / vhat dequantised from cache
+ * levels 0..level (dequantisation happens inside the kernel's column-tile loop
+ * or once per head into a compact bf16 buffer, see `mode`).
+ * Cache build (cache_op FL_CACHE_REBUILD; needed when the column set shrank):
+ * before the
+ * attention M_U and O_U of the active rows are rebuilt under the previous
+ * loop's distribution (query q_prev, cache levels 0..level-1, the previous
+ * selection, lse and M_U as stored in the state arrays):
+ *   M_U(i) = 1 - sum_{j in S(i)} P_prev(i,j)
+ *   O_U(i) = o_prev(i) - sum_{j in S(i)} P_prev(i,j) vhat_prev(j)
+ *   P_prev(i,j) = (1 - M_U_prev(i)) exp(sm*q_prev(i).khat_prev(j) - lse_prev(i))
+ * (the difference form of the pruned columns' mass and output).
+ * Column statistics (col_stat != NULL): after the attention,
+ *   col_stat[h][p] = sum_{active i >= sel[h][p]} (1 - M_U(i)) *
+ *                    exp(sm*q(i).khat(sel[h][p]) - lse(i))
+ * (the previous-loop statistic that ranks the next loop's columns).
+ * With sel == NULL (all N columns, k == N) and M_U = O_U = 0 this is the
+ * dense first loop.
+ */
+enum fl_attn_mode {
+    FL_DEQ_AUTO = 0,    /* library choice                                      */
+    FL_DEQ_ONCE = 1,    /* dequantise the selected columns once per head into a
+                           compact bf16 buffer, then stream it per tile        */
+    FL_DEQ_IN_TILE = 2  /* gather quantised codes compactly, dequantise inside
+                           the attention kernel's column-tile loop             */
+};
+
+enum fl_cache_op {
+    FL_CACHE_CARRY = 0,   /* read M_U / O_U of the active rows as stored        */
+    FL_CACHE_ZERO = 1,    /* treat M_U = O_U = 0 (dense first loop); not read   */
+    FL_CACHE_REBUILD = 2  /* rebuild M_U / O_U from the previous loop first     */
+};
+
+typedef struct fl_attn_args {
+    int dtype;                 /* of q and q_prev: FL_BF16 or FL_F32            */
+    const void* q;             /* [N][H][d] by position, or [n][H][d] gathered  */
+    int q_gathered;            /* 1: q rows aligned with `active`               */
+    const int32_t* active;     /* [n] ascending positions                       */
+    int n;
+    const int32_t* sel;        /* [H][k] ascending, or NULL (all columns, k = N) */
+    int k;
+    float sm;                  /* softmax scale, normally 1/sqrt(d)             */
+    int level;                 /* newest cache level used (loop level+1)        */
+    int mode;                  /* fl_attn_mode                                  */
+    int cache_op;              /* fl_cache_op                                   */
+    /* loop state, fp32, indexed by token position: */
+    float* out;                /* [N][H][d]: o_prev read (rebuild), o written   */
+    float* lse;                /* [N][H]: lse_prev read (rebuild), lse written  */
+    float* mass_u;             /* [N][H]: M_U (read; written on rebuild)        */
+    float* out_u;              /* [N][H][d]: O_U (read; written on rebuild)     */
+    float* col_stat;           /* NULL or [H][k]: written                       */
+    /* rebuild input: the previous loop's queries (same layout rules as q) */
+    const void* q_prev;
+    int q_prev_gathered;
+} fl_attn_args;
+
+int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void* ws,
+                        size_t ws_bytes, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_loop_step -- one whole loop r >= 1 of the lazy-update attention step
+ * (paper Sec. 4.1-4.3) in attention-only form: the loop's hidden states and
+ * q/k/v projections are given for all N tokens; the step uses the rows it
+ * selects.
+ *   r == 1: base level, dense attention, column statistics (if r < R needs them).
+ *   r >= 2: fl_select_active over the previous active set, the residual level
+ *           r-1, fl_select_columns when the budget shrinks, cache build when the
+ *           column set changed, sparse attention, column statistics when the
+ *           next loop prunes further.
+ * All state lives in caller-owned device buffers listed in fl_loop_state.
+ */
+typedef struct fl_loop_cfg {
+    int N, H, d, g, R, n_sink;
+    int dtype;              /* of h / q / k / v                                */
+    int n_active[FL_MAX_LEVELS]; /* active rows per loop (index r-1); [0] = N   */
+    int k_cols[FL_MAX_LEVELS];   /* column budget per loop; [0] = N             */
+    int bits[FL_MAX_LEVELS];     /* [0] base bits (8/32), [r-1] residual bits   */
+    int mode;               /* fl_attn_mode                                    */
+} fl_loop_cfg;
+
+typedef struct fl_loop_state {
+    fl_kv_cache cache;      /* level buffers pre-allocated by the caller        */
+    int32_t* active[FL_MAX_LEVELS]; /* [n_active[r-1]] per loop; active[0] unused */
+    int32_t* slot[FL_MAX_LEVELS];   /* [N] per loop (r >= 2)                     */
+    float* stat;            /* [N] scratch for the token statistic              */
+    int32_t* sel[FL_MAX_LEVELS];    /* [H][k_cols[r-1]] per loop (r >= 2)        */
+    const int32_t* sel_used[FL_MAX_LEVELS]; /* filled by the step: the column set
+                                       used in each loop (NULL = all columns)   */
+    int k_cur[FL_MAX_LEVELS];       /* filled by the step: columns used per loop  */
+    float* col_stat[FL_MAX_LEVELS]; /* [H][k of loop r] when computed, per loop  */
+    float* out; float* lse; float* mass_u; float* out_u; /* position-indexed    */
+} fl_loop_state;
+
+typedef struct fl_loop_inputs {
+    const void* h_cur;      /* [N][H*d] hidden state entering loop r           */
+    const void* h_prev;     /* [N][H*d] hidden state entering loop r-1 (r >= 2) */
+    const void* q;          /* [N][H][d] loop r queries                        */
+    const void* k;          /* [N][H][d] loop r keys                           */
+    const void* v;          /* [N][H][d] loop r values                         */
+    const void* q_prev;     /* [N][H][d] loop r-1 queries (r >= 2)              */
+} fl_loop_inputs;
+
+int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* st, const fl_loop_inputs* in, int r,
+                 void* ws, size_t ws_bytes, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later
+ * launch of the library record a HIP event pair around each kernel on the
+ * launch stream.  fl_timing_report waits for those events and writes one line
+ * per kernel name, "name launches total_ms\n", into buf (NUL-terminated,
+ * truncated to len), then forgets the recorded launches.  Returns FL_OK, or
+ * FL_ERR_INVALID_ARG when the report was truncated, FL_ERR_HIP on an event
+ * error. */
+int fl_timing_enable(int on);
+int fl_timing_report(char* buf, size_t len);
+
+/* ------------------------------------------------------------------------ */
+const char* fl_last_error(void);
+const char* fl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHLOOP_H */

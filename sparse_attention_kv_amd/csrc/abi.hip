@@ -1,0 +1,395 @@
+// Host side of the C ABI declared in include/flashloop.h: argument
+// validation (before anything is enqueued), workspace carving and kernel
+// sequencing for one loop of FlashLoop's lazy-update attention step.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "fl_kernels.h"
+
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(FL_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define FL_REQUIRE(cond, ...)                                        \
+    do {                                                             \
+        if (!(cond)) return fail(FL_ERR_INVALID_ARG, __VA_ARGS__);   \
+    } while (0)
+#define FL_HIP(expr, where)                                          \
+    do {                                                             \
+        hipError_t e_ = (expr);                                      \
+        if (e_ != hipSuccess) return hip_fail(e_, where);            \
+    } while (0)
+
+constexpr long kAlign = 256;
+long align_up(long x) { return (x + kAlign - 1) / kAlign * kAlign; }
+long kpad(long k) { return (k + 63) / 64 * 64; }
+
+// workspace of fl_sparse_loop_attn: two compact bf16 copies (K, V^T) for the
+// current loop and, for a cache rebuild, two for the previous loop, plus the
+// column positions; fp32 inputs (x3) add a "lo" copy of each.
+long attn_ws_bytes(long H, long k, long d, bool x3) {
+    const long kp = kpad(k);
+    return (x3 ? 8 : 4) * align_up(H * kp * d * 2) + align_up(H * kp * 4) + kAlign;
+}
+
+// ---- optional per-kernel HIP-event timing of the library's launches ----
+struct TimedLaunch {
+    const char* name;
+    hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t ev_get() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& f) {
+    if (!g_timing) return f();
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t a = ev_get(), b = ev_get();
+    if (a) hipEventRecord(a, st);
+    const hipError_t e = f();
+    if (b) hipEventRecord(b, st);
+    if (a && b) g_recs.push_back({name, a, b});
+    return e;
+}
+
+bool dtype_ok(int dt) { return dt == FL_F32 || dt == FL_BF16; }
+
+int check_cache(const fl_kv_cache* c, int upto) {
+    FL_REQUIRE(c != nullptr, "cache is NULL");
+    FL_REQUIRE(c->N > 0 && c->H > 0, "cache: N=%d H=%d", c->N, c->H);
+    if (!(c->d == 64 || c->d == 128)) return fail(FL_ERR_UNSUPPORTED, "head dim %d (64 or 128)", c->d);
+    if (!(c->g == 32 || c->g == 64) || c->d % c->g)
+        return fail(FL_ERR_UNSUPPORTED, "group size %d (32 or 64, dividing d)", c->g);
+    FL_REQUIRE(c->H * c->d <= 8192, "H*d = %d > 8192", c->H * c->d);
+    FL_REQUIRE(upto >= 0 && upto < FL_MAX_LEVELS, "level %d out of range", upto);
+    for (int l = 0; l <= upto; ++l) {
+        const fl_kv_level& L = c->level[l];
+        if (l == 0) {
+            if (!(L.bits == 8 || L.bits == 32))
+                return fail(FL_ERR_UNSUPPORTED, "base level bits %d (8 or 32)", L.bits);
+        } else {
+            if (!(L.bits == 2 || L.bits == 4 || L.bits == 8 || L.bits == 32))
+                return fail(FL_ERR_UNSUPPORTED, "level %d bits %d", l, L.bits);
+            FL_REQUIRE(L.rows && L.slot, "level %d: rows/slot NULL", l);
+            FL_REQUIRE(L.n_rows >= 0 && L.n_rows <= c->N, "level %d: n_rows %d", l, L.n_rows);
+        }
+        FL_REQUIRE(L.k_codes && L.v_codes, "level %d: code buffers NULL", l);
+        FL_REQUIRE(L.bits == 32 || (L.k_scale && L.v_scale), "level %d: scale buffers NULL", l);
+    }
+    return FL_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* fl_last_error(void) { return g_err; }
+
+const char* fl_version(void) { return "flashloop-mi355x 0.1 (gfx950)"; }
+
+size_t fl_workspace_size(int op, long a, long b, long c, long e) {
+    switch (op) {
+    case FL_WS_SELECT_ACTIVE: return a > 0 ? (size_t)kAlign : 0;
+    case FL_WS_SELECT_COLUMNS: return (a > 0 && b > 0) ? (size_t)kAlign : 0;
+    case FL_WS_SPARSE_ATTN:
+    case FL_WS_LOOP_STEP:
+        if (a <= 0 || b <= 0 || !(c == 64 || c == 128)) return 0;
+        return (size_t)attn_ws_bytes(a, b, c, e != FL_BF16);
+    default: return 0;
+    }
+}
+
+int fl_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = on != 0;
+    return FL_OK;
+}
+
+int fl_timing_report(char* buf, size_t len) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    std::map<std::string, std::pair<long, double>> agg;
+    int rc = FL_OK;
+    for (auto& r : g_recs) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) rc = hip_fail(e, "timing");
+        auto& x = agg[r.name];
+        x.first += 1;
+        x.second += ms;
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+    std::string out;
+    char line[160];
+    for (auto& kv : agg) {
+        snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+        out += line;
+    }
+    if (buf && len) {
+        snprintf(buf, len, "%s", out.c_str());
+        if (out.size() + 1 > len) rc = fail(FL_ERR_INVALID_ARG, "timing report truncated");
+    }
+    return rc;
+}
+
+int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, int D,
+                     const int32_t* cand, int n_cand, int n_select, const float* stat_in,
+                     float* stat_out, int32_t* active_out, int32_t* slot_out, void* ws,
+                     size_t ws_bytes, fl_stream_t stream) {
+    (void)ws; (void)ws_bytes;
+    FL_REQUIRE(N > 0, "N = %d", N);
+    FL_REQUIRE(n_cand >= 1 && n_cand <= N, "n_cand %d not in [1, N=%d]", n_cand, N);
+    FL_REQUIRE(n_select >= 1 && n_select <= n_cand, "n_select %d not in [1, n_cand=%d]", n_select, n_cand);
+    FL_REQUIRE(active_out != nullptr, "active_out is NULL");
+    if (!stat_in) {
+        FL_REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+        FL_REQUIRE(h_cur && h_prev && stat_out, "h_cur/h_prev/stat_out NULL");
+        FL_REQUIRE(D >= 8 && D % 8 == 0, "D = %d (multiple of 8 required)", D);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const float* keys = stat_in;
+    if (!stat_in) {
+        FL_HIP(timed("delta_norm", st, [&] {
+                   return fl::launch_delta_norm(h_cur, h_prev, dtype, D, cand, n_cand, stat_out, st);
+               }),
+               "delta_norm");
+        keys = stat_out;
+    }
+    FL_HIP(timed("select_topk", st, [&] {
+               return fl::launch_topk(keys, 0, cand, 0, n_cand, n_select, 0, active_out, 0, slot_out,
+                                      slot_out ? N : 0, 1, st);
+           }),
+           "topk");
+    return FL_OK;
+}
+
+int fl_select_columns(const float* col_stat, const int32_t* cand_cols, int H, int n_cand,
+                      int n_sink, int k, int32_t* sel_out, void* ws, size_t ws_bytes,
+                      fl_stream_t stream) {
+    (void)ws; (void)ws_bytes;
+    FL_REQUIRE(H >= 1 && n_cand >= 1, "H=%d n_cand=%d", H, n_cand);
+    FL_REQUIRE(sel_out != nullptr, "sel_out is NULL");
+    FL_REQUIRE(n_sink >= 0, "n_sink %d", n_sink);
+    FL_REQUIRE(k > n_sink, "k=%d must exceed n_sink=%d", k, n_sink);
+    hipStream_t st = (hipStream_t)stream;
+    if (n_cand <= k) {
+        FL_HIP(fl::launch_copy_or_iota(cand_cols, sel_out, (long)H * n_cand, n_cand, st), "copy");
+        return FL_OK;
+    }
+    FL_REQUIRE(col_stat != nullptr, "col_stat is NULL");
+    FL_REQUIRE(n_sink <= n_cand, "n_sink %d > n_cand %d", n_sink, n_cand);
+    FL_HIP(timed("select_columns", st, [&] {
+               return fl::launch_topk(col_stat, n_cand, cand_cols, cand_cols ? n_cand : 0, n_cand,
+                                      k - n_sink, n_sink, sel_out, k, nullptr, 0, H, st);
+           }),
+           "topk");
+    return FL_OK;
+}
+
+int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const void* k_new,
+                         const void* v_new, int new_gathered, fl_stream_t stream) {
+    int rc = check_cache(cache, level);
+    if (rc) return rc;
+    FL_REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+    FL_REQUIRE(k_new && v_new, "k_new/v_new NULL");
+    FL_REQUIRE(!(level == 0 && new_gathered), "level 0 takes all N rows by position");
+    hipStream_t st = (hipStream_t)stream;
+    FL_HIP(timed("kv_quant", st, [&] {
+               return fl::launch_quant(*cache, level, dtype, k_new, v_new, new_gathered, st);
+           }),
+           "quant");
+    return FL_OK;
+}
+
+int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
+                        size_t ws_bytes, fl_stream_t stream) {
+    FL_REQUIRE(a != nullptr, "args NULL");
+    int rc = check_cache(cache, a->level);
+    if (rc) return rc;
+    const int H = cache->H, d = cache->d, N = cache->N;
+    FL_REQUIRE(dtype_ok(a->dtype), "dtype %d", a->dtype);
+    FL_REQUIRE(a->q && a->active && a->out && a->lse, "q/active/out/lse NULL");
+    FL_REQUIRE(a->n >= 1 && a->n <= N, "n=%d", a->n);
+    FL_REQUIRE(a->k >= 1 && a->k <= N, "k=%d", a->k);
+    FL_REQUIRE(a->sel || a->k == N, "sel NULL requires k == N");
+    FL_REQUIRE(a->cache_op >= FL_CACHE_CARRY && a->cache_op <= FL_CACHE_REBUILD, "cache_op %d", a->cache_op);
+    FL_REQUIRE(a->cache_op == FL_CACHE_ZERO || (a->mass_u && a->out_u), "mass_u/out_u NULL");
+    if (a->cache_op == FL_CACHE_REBUILD) {
+        FL_REQUIRE(a->level >= 1, "cache rebuild needs a previous loop (level >= 1)");
+        FL_REQUIRE(a->q_prev != nullptr, "q_prev NULL");
+    }
+    FL_REQUIRE(a->mode >= FL_DEQ_AUTO && a->mode <= FL_DEQ_IN_TILE, "mode %d", a->mode);
+    if (a->mode == FL_DEQ_IN_TILE) return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE not built");
+    const bool x3 = a->dtype == FL_F32;
+    const long need = attn_ws_bytes(H, a->k, d, x3);
+    if (!ws || (long)ws_bytes < need)
+        return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
+    hipStream_t st = (hipStream_t)stream;
+    const int kp = (int)kpad(a->k);
+    char* base = (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+    const long kvb = align_up((long)H * kp * d * 2);
+    __bf16* buf[8];
+    for (int i = 0; i < (x3 ? 8 : 4); ++i) buf[i] = (__bf16*)(base + i * kvb);
+    for (int i = (x3 ? 8 : 4); i < 8; ++i) buf[i] = nullptr;
+    int32_t* cpos = (int32_t*)(base + (x3 ? 8 : 4) * kvb);
+    // new side: K, V^T (+ lo parts); previous-loop side for a rebuild
+    __bf16 *Kc = buf[0], *Vt = buf[1], *Kc_old = buf[2], *Vt_old = buf[3];
+    __bf16 *Kl = buf[4], *Vl = buf[5], *Kl_old = buf[6], *Vl_old = buf[7];
+    const float c2 = a->sm * 1.4426950408889634f;
+
+    FL_HIP(timed("gather", st, [&] {
+               return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, x3, Kc, Vt, Kl, Vl,
+                                             cpos, st);
+           }),
+           "gather");
+    fl::AttnParams P{};
+    P.H = H; P.n = a->n; P.k = a->k; P.kp = kp; P.dtype = a->dtype; P.cache_op = a->cache_op;
+    P.c2 = c2; P.active = a->active; P.cpos = cpos;
+    P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u;
+    if (a->cache_op == FL_CACHE_REBUILD) {
+        FL_HIP(timed("gather", st, [&] {
+                   return fl::launch_gather_bf16(*cache, a->level - 1, a->sel, a->k, kp, x3, Kc_old,
+                                                 Vt_old, Kl_old, Vl_old, cpos, st);
+               }),
+               "gather(prev)");
+        fl::AttnParams R = P;
+        R.q = a->q_prev; R.q_gathered = a->q_prev_gathered;
+        R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
+        FL_HIP(timed("attn_rebuild", st, [&] { return fl::launch_attn(d, fl::MODE_REBUILD, x3, R, st); }),
+               "attn(rebuild)");
+    }
+    P.q = a->q; P.q_gathered = a->q_gathered; P.Kc = Kc; P.Vt = Vt; P.Kc_lo = Kl; P.Vt_lo = Vl;
+    FL_HIP(timed("attn", st, [&] { return fl::launch_attn(d, fl::MODE_ATTN, x3, P, st); }), "attn");
+    if (a->col_stat) {
+        fl::ColParams C{};
+        C.H = H; C.n = a->n; C.k = a->k; C.kp = kp; C.dtype = a->dtype; C.q_gathered = a->q_gathered;
+        C.cache_op = a->cache_op == FL_CACHE_ZERO ? FL_CACHE_ZERO : FL_CACHE_CARRY;
+        C.c2 = c2; C.q = a->q; C.active = a->active; C.Kc = Kc; C.Kc_lo = Kl; C.cpos = cpos;
+        C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat;
+        FL_HIP(timed("colstat", st, [&] { return fl::launch_colstat(d, x3, C, st); }), "colstat");
+    }
+    return FL_OK;
+}
+
+int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs* in, int r,
+                 void* ws, size_t ws_bytes, fl_stream_t stream) {
+    FL_REQUIRE(cfg && S && in, "cfg/state/inputs NULL");
+    FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
+    const int N = cfg->N, H = cfg->H, d = cfg->d;
+    fl_kv_cache& C = S->cache;
+    FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
+    FL_REQUIRE(in->q && in->k && in->v, "q/k/v NULL");
+    FL_REQUIRE(S->out && S->lse && S->mass_u && S->out_u, "state arrays NULL");
+    hipStream_t st = (hipStream_t)stream;
+    const float sm = 1.0f / sqrtf((float)d);
+    fl_attn_args A{};
+    A.dtype = cfg->dtype; A.q = in->q; A.q_gathered = 0; A.sm = sm; A.mode = cfg->mode;
+    A.out = S->out; A.lse = S->lse; A.mass_u = S->mass_u; A.out_u = S->out_u;
+    if (r == 1) {
+        FL_REQUIRE(S->active[0] != nullptr, "active[0] (iota buffer) NULL");
+        C.level[0].bits = cfg->bits[0];
+        C.level[0].n_rows = N;
+        C.level[0].rows = nullptr; C.level[0].slot = nullptr;
+        C.n_levels = 1;
+        int rc = fl_kv_residual_quant(&C, 0, cfg->dtype, in->k, in->v, 0, stream);
+        if (rc) return rc;
+        FL_HIP(fl::launch_copy_or_iota(nullptr, S->active[0], N, N, st), "iota");
+        FL_HIP(fl::launch_fill_f32(S->mass_u, (long)N * H, 0.0f, st), "fill");
+        FL_HIP(fl::launch_fill_f32(S->out_u, (long)N * H * d, 0.0f, st), "fill");
+        S->k_cur[0] = N;
+        S->sel_used[0] = nullptr;
+        A.active = S->active[0]; A.n = N; A.sel = nullptr; A.k = N; A.level = 0;
+        A.cache_op = FL_CACHE_ZERO;
+        A.col_stat = (cfg->R > 1 && cfg->k_cols[1] < N) ? S->col_stat[0] : nullptr;
+        return fl_sparse_loop_attn(&C, &A, ws, ws_bytes, stream);
+    }
+    FL_REQUIRE(in->h_cur && in->h_prev && in->q_prev, "h_cur/h_prev/q_prev NULL");
+    const int n_prev = r == 2 ? N : cfg->n_active[r - 2];
+    const int n_r = cfg->n_active[r - 1];
+    FL_REQUIRE(n_r >= 1 && n_r <= n_prev, "n_active[%d] = %d (prev %d)", r - 1, n_r, n_prev);
+    FL_REQUIRE(S->active[r - 1] && S->slot[r - 1] && S->stat, "active/slot/stat buffers NULL");
+    int rc = fl_select_active(cfg->dtype, in->h_cur, in->h_prev, N, H * d, S->active[r - 2], n_prev,
+                              n_r, nullptr, S->stat, S->active[r - 1], S->slot[r - 1], ws, ws_bytes,
+                              stream);
+    if (rc) return rc;
+    fl_kv_level& L = C.level[r - 1];
+    L.bits = cfg->bits[r - 1];
+    L.n_rows = n_r;
+    L.rows = S->active[r - 1];
+    L.slot = S->slot[r - 1];
+    C.n_levels = r;
+    rc = fl_kv_residual_quant(&C, r - 1, cfg->dtype, in->k, in->v, 0, stream);
+    if (rc) return rc;
+    const int k_prev = S->k_cur[r - 2];
+    const int k_r = cfg->k_cols[r - 1];
+    bool changed = false;
+    if (k_prev <= k_r) {
+        S->k_cur[r - 1] = k_prev;
+        S->sel_used[r - 1] = S->sel_used[r - 2];
+    } else {
+        FL_REQUIRE(S->sel[r - 1] && S->col_stat[r - 2], "sel/col_stat buffers NULL");
+        rc = fl_select_columns(S->col_stat[r - 2], S->sel_used[r - 2], H, k_prev, cfg->n_sink, k_r,
+                               S->sel[r - 1], ws, ws_bytes, stream);
+        if (rc) return rc;
+        S->k_cur[r - 1] = k_r;
+        S->sel_used[r - 1] = S->sel[r - 1];
+        changed = true;
+    }
+    A.active = S->active[r - 1]; A.n = n_r;
+    A.sel = S->sel_used[r - 1]; A.k = S->k_cur[r - 1]; A.level = r - 1;
+    A.cache_op = changed ? FL_CACHE_REBUILD : FL_CACHE_CARRY;
+    A.q_prev = in->q_prev; A.q_prev_gathered = 0;
+    const bool need_c = r < cfg->R && cfg->k_cols[r] < S->k_cur[r - 1];
+    A.col_stat = need_c ? S->col_stat[r - 1] : nullptr;
+    FL_REQUIRE(!need_c || A.col_stat, "col_stat[%d] buffer NULL", r - 1);
+    return fl_sparse_loop_attn(&C, &A, ws, ws_bytes, stream);
+}
+
+} // extern "C"
+
+namespace fl {
+__global__ void k_fill_f32(float* p, long n, float v) {
+    const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+} // namespace fl

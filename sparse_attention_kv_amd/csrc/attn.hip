@@ -1,0 +1,534 @@
+// Sparse loop attention (FlashLoop paper, Sec. 4.2 loop-aware sparse
+// attention; Sec. 4.4 compact buffers of the selected keys).
+//
+// Kernels (bf16 MFMA 32x32x16 on gfx950, fp32 softmax and accumulation):
+//   k_gather_bf16   dequantise the selected columns of every head once per
+//                   loop (base + residual chain) into a compact bf16 buffer:
+//                   K as [H][kp][d] and V transposed per 64-column tile as
+//                   [H][kp/64][d][64] (key order permuted inside each 16-key
+//                   group so one 16-byte LDS read feeds one MFMA operand).
+//   k_attn<MODE>    one workgroup = 128 gathered active query rows (4 waves x
+//                   32 rows) of one head; loops over 64-column tiles of the
+//                   head's selected columns up to the tile's causal bound.
+//                   Each wave computes S^T = K Q^T (the lane owns one query
+//                   row), masks j > i, runs the softmax in registers and
+//                   accumulates O^T = V^T P^T.
+//                   MODE_ATTN: online softmax, o = (1-M_U) o~ / l + O_U, lse.
+//                   MODE_REBUILD: the previous loop's probabilities with its
+//                   known lse: M_U = 1 - sum P_prev, O_U = o_prev - sum P_prev V.
+//   k_colstat       column statistics c(j) = sum_i (1-M_U(i)) exp(s - lse(i))
+//                   for the next loop's column ranking: one workgroup = 128
+//                   selected columns (a wave keeps its 32 columns' keys in
+//                   registers) sweeping the active query rows from the first
+//                   causal one; per-lane sequential sums (deterministic).
+#include "fl_device.h"
+#include "fl_kernels.h"
+
+namespace fl {
+
+constexpr int BM = 128; // query rows per workgroup (4 waves x 32)
+constexpr int BN = 64;  // columns per tile
+
+__host__ __device__ __forceinline__ long round_up(long x, long m) { return (x + m - 1) / m * m; }
+
+// stored offset (0..15) inside a 16-key group -> key offset
+__device__ __forceinline__ int vt_key_of_slot(int so) {
+    return (so >> 3) * 4 + ((so >> 2) & 1) * 8 + (so & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Compact gather + dequantisation of the selected columns (levels 0..upto).
+// With X3 (fp32 inputs) a second "lo" copy holds the bf16 rounding of
+// x - bf16(x), so that products can be formed as hi*hi + hi*lo + lo*hi.
+template <int D, bool X3>
+__global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
+                                                     const int32_t* __restrict__ sel, int k,
+                                                     int kp, __bf16* __restrict__ Kc,
+                                                     __bf16* __restrict__ Vt,
+                                                     __bf16* __restrict__ Kc_lo,
+                                                     __bf16* __restrict__ Vt_lo,
+                                                     int32_t* __restrict__ cpos) {
+    __shared__ __bf16 sV[X3 ? 2 : 1][BN][D + 8];
+    const int h = blockIdx.y;
+    const int p0 = blockIdx.x * BN;
+    const int tid = threadIdx.x;
+    const int col = tid >> 2;                 // 0..63
+    constexpr int CPT = D / 4;                // channels per thread
+    const int c0 = (tid & 3) * CPT;
+    const int p = p0 + col;
+    const bool live = p < k;
+    const long j = live ? (sel ? (long)sel[(long)h * k + p] : (long)p) : 0;
+    if ((tid & 3) == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
+    const int HD = c.H * D;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        float x[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) x[e] = 0.0f;
+        if (live) {
+            // base level
+            const fl_kv_level& L0 = c.level[0];
+            const long e0 = j * HD + (long)h * D + c0;
+            const void* codes = which ? L0.v_codes : L0.k_codes;
+            if (L0.bits == 32) {
+                const float* src = reinterpret_cast<const float*>(codes) + e0;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) x[e] = src[e];
+            } else {
+                const float* sc = which ? L0.v_scale : L0.k_scale;
+#pragma unroll
+                for (int e8 = 0; e8 < CPT; e8 += 8) {
+                    const float s = sc[(e0 + e8) / c.g];
+                    const uint64_t w = load_codes8(codes, e0 + e8, 8);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[e8 + i] = (float)code_at(w, 8, i) * s;
+                }
+            }
+            for (int l = 1; l <= upto; ++l) {
+                const fl_kv_level& L = c.level[l];
+                const int sl = L.slot[j];
+                if (sl < 0) break;
+                const long el = (long)sl * HD + (long)h * D + c0;
+                const void* cl = which ? L.v_codes : L.k_codes;
+                if (L.bits == 32) {
+                    const float* src = reinterpret_cast<const float*>(cl) + el;
+#pragma unroll
+                    for (int e = 0; e < CPT; ++e) x[e] += src[e];
+                } else {
+                    const float* sc = which ? L.v_scale : L.k_scale;
+#pragma unroll
+                    for (int e8 = 0; e8 < CPT; e8 += 8) {
+                        const float s = sc[(el + e8) / c.g];
+                        const uint64_t w = load_codes8(cl, el + e8, L.bits);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) x[e8 + i] += (float)code_at(w, L.bits, i) * s;
+                    }
+                }
+            }
+        }
+        if (which == 0) {
+            __bf16* dst = Kc + ((long)h * kp + p) * D + c0;
+            __bf16* dlo = X3 ? Kc_lo + ((long)h * kp + p) * D + c0 : nullptr;
+#pragma unroll
+            for (int e8 = 0; e8 < CPT; e8 += 8) {
+                bf16x8 v, vl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v[i] = (__bf16)x[e8 + i];
+                    if (X3) vl[i] = (__bf16)(x[e8 + i] - (float)v[i]);
+                }
+                *reinterpret_cast<bf16x8*>(dst + e8) = v;
+                if (X3) *reinterpret_cast<bf16x8*>(dlo + e8) = vl;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+                const __bf16 hi = (__bf16)x[e];
+                sV[0][col][c0 + e] = hi;
+                if (X3) sV[X3 ? 1 : 0][col][c0 + e] = (__bf16)(x[e] - (float)hi);
+            }
+        }
+    }
+    __syncthreads();
+    // transpose the V tile: rows d, 64 keys in permuted order, 16-byte stores
+#pragma unroll
+    for (int part = 0; part < (X3 ? 2 : 1); ++part) {
+        __bf16* vdst = (part ? Vt_lo : Vt) + ((long)h * (kp / BN) + blockIdx.x) * D * BN;
+        for (int idx = tid; idx < D * (BN / 8); idx += 256) {
+            const int dd = idx / (BN / 8);
+            const int oct = idx % (BN / 8);
+            bf16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int so = oct * 8 + i;                      // stored position in tile
+                const int key = (so & ~15) + vt_key_of_slot(so & 15);
+                v[i] = sV[part][key][dd];
+            }
+            *reinterpret_cast<bf16x8*>(vdst + (long)dd * BN + oct * 8) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void block_coords(int xcd_remap, int n_tiles, int H, int& tile, int& h) {
+    const int b = blockIdx.x;
+    if (xcd_remap) {
+        // keep every head's workgroups on one XCD (blocks are dealt to the
+        // 8 XCDs round-robin), so the head's compact K/V stays in that L2;
+        // the costliest (latest-position) tiles start first.
+        const int x = b & 7, m = b >> 3;
+        h = x + 8 * (m / n_tiles);
+        tile = n_tiles - 1 - (m % n_tiles);
+    } else {
+        h = b / n_tiles;
+        tile = n_tiles - 1 - (b % n_tiles);
+    }
+}
+
+template <int D, int MODE, bool X3>
+__global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
+    constexpr int NP = X3 ? 2 : 1; // hi (+ lo) parts
+    __shared__ __bf16 Ks[NP][BN][D + 8];
+    __shared__ __bf16 Vs[NP][D][BN + 8];
+    __shared__ int cps[BN];
+    __shared__ int s_bounds[2];
+    const int n_tiles = (P.n + BM - 1) / BM;
+    int tile, h;
+    block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 31, half = lane >> 5;
+    const int t0 = tile * BM;
+    const int t = t0 + w * 32 + r;
+    const bool valid = t < P.n;
+    const int rowpos = valid ? P.active[t] : -1;
+    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
+    if (tid == 0) {
+        const int tl = min(t0 + BM, P.n) - 1;
+        s_bounds[0] = upper_bound_i32(cpos_h, P.k, P.active[tl]); // p_end
+        s_bounds[1] = upper_bound_i32(cpos_h, P.k, P.active[t0]); // p_full
+    }
+    // query fragment: B operand of S^T = K Q^T (lane: row r, d = 16kk + 8half)
+    bf16x8 qf[D / 16], ql[X3 ? D / 16 : 1];
+    {
+        const long qrow = P.q_gathered ? (long)t : (long)rowpos;
+        const long qoff = (qrow * P.H + h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            if (X3) {
+                float f[8];
+                if (valid) load8_f32(P.q, qoff + 16 * kk, P.dtype, f);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    qf[kk][i] = (__bf16)f[i];
+                    ql[X3 ? kk : 0][i] = (__bf16)(f[i] - (float)qf[kk][i]);
+                }
+            } else if (valid) {
+                qf[kk] = load8_bf16(P.q, qoff + 16 * kk, P.dtype);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.0f;
+            }
+        }
+    }
+    const long rh = valid ? (long)rowpos * P.H + h : 0;
+    float lse_prev2 = 0.0f, wgt = 1.0f;
+    if (MODE == MODE_REBUILD && valid) {
+        lse_prev2 = P.lse[rh] * 1.4426950408889634f;
+        wgt = 1.0f - P.mass_u[rh];
+    }
+    __syncthreads();
+    const int p_end = s_bounds[0], p_full = s_bounds[1];
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const long koff = (long)h * P.kp * D;
+    const long voff = (long)h * (P.kp / BN) * D * BN;
+    for (int p0 = 0; p0 < p_end; p0 += BN) {
+        // ---- stage the K and V^T tiles in LDS ----
+#pragma unroll
+        for (int part = 0; part < NP; ++part) {
+            const __bf16* Kh = (part ? P.Kc_lo : P.Kc) + koff;
+            const __bf16* Vh = (part ? P.Vt_lo : P.Vt) + voff;
+#pragma unroll
+            for (int m = 0; m < (BN * D / 8) / 256; ++m) {
+                const int idx = tid + m * 256;
+                const int key = idx / (D / 8), c8 = idx % (D / 8);
+                *reinterpret_cast<uint4*>(&Ks[part][key][c8 * 8]) =
+                    *reinterpret_cast<const uint4*>(Kh + (long)(p0 + key) * D + c8 * 8);
+                const int dd = idx / (BN / 8), oc = idx % (BN / 8);
+                *reinterpret_cast<uint4*>(&Vs[part][dd][oc * 8]) =
+                    *reinterpret_cast<const uint4*>(Vh + ((long)(p0 / BN) * D + dd) * BN + oc * 8);
+            }
+        }
+        if (tid < BN) cps[tid] = cpos_h[p0 + tid];
+        __syncthreads();
+
+        // ---- S^T = K Q^T: two 32-key tiles ----
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[0][32 * kt + r][16 * kk + 8 * half]);
+                s[kt] = mfma32(a, qf[kk], s[kt]);
+                if (X3) {
+                    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Ks[NP - 1][32 * kt + r][16 * kk + 8 * half]);
+                    s[kt] = mfma32(a, ql[X3 ? kk : 0], s[kt]);
+                    s[kt] = mfma32(al, qf[kk], s[kt]);
+                }
+            }
+        }
+        const bool need_mask = p0 + BN > p_full;
+        bf16x8 pb[2][2], pl[X3 ? 2 : 1][2];
+        if (MODE == MODE_ATTN) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float v = s[kt][j] * P.c2;
+                    if (need_mask) {
+                        const int key = 32 * kt + (j >> 2) * 8 + half * 4 + (j & 3);
+                        if (cps[key] > rowpos) v = -INFINITY;
+                    }
+                    s[kt][j] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m_run, tmax);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float pj = __builtin_amdgcn_exp2f(s[kt][j] - m_use);
+                    l_run += pj;
+                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
+                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
+                }
+            m_run = m_new;
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float v = s[kt][j] * P.c2 - lse_prev2;
+                    if (need_mask) {
+                        const int key = 32 * kt + (j >> 2) * 8 + half * 4 + (j & 3);
+                        if (cps[key] > rowpos) v = -INFINITY;
+                    }
+                    const float pj = wgt * __builtin_amdgcn_exp2f(v);
+                    l_run += pj;
+                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
+                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
+                }
+        }
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int jh = 0; jh < 2; ++jh) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        &Vs[0][32 * dt + r][32 * kt + 16 * jh + 8 * half]);
+                    o[dt] = mfma32(a, pb[kt][jh], o[dt]);
+                    if (X3) {
+                        const bf16x8 al = *reinterpret_cast<const bf16x8*>(
+                            &Vs[NP - 1][32 * dt + r][32 * kt + 16 * jh + 8 * half]);
+                        o[dt] = mfma32(a, pl[X3 ? kt : 0][jh], o[dt]);
+                        o[dt] = mfma32(al, pb[kt][jh], o[dt]);
+                    }
+                }
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!valid) return;
+    float* orow = P.out + rh * D;
+    if (MODE == MODE_ATTN) {
+        const float mu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
+        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
+        const float* ourow = P.out_u + rh * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * dt + jq * 8 + half * 4;
+                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (P.cache_op != FL_CACHE_ZERO) u = *reinterpret_cast<const float4*>(ourow + d0);
+                float4 v;
+                v.x = o[dt][4 * jq + 0] * scale + u.x;
+                v.y = o[dt][4 * jq + 1] * scale + u.y;
+                v.z = o[dt][4 * jq + 2] * scale + u.z;
+                v.w = o[dt][4 * jq + 3] * scale + u.w;
+                *reinterpret_cast<float4*>(orow + d0) = v;
+            }
+        if (half == 0)
+            P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    } else {
+        float* ourow = P.out_u + rh * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * dt + jq * 8 + half * 4;
+                const float4 op = *reinterpret_cast<const float4*>(orow + d0);
+                float4 v;
+                v.x = op.x - o[dt][4 * jq + 0];
+                v.y = op.y - o[dt][4 * jq + 1];
+                v.z = op.z - o[dt][4 * jq + 2];
+                v.w = op.w - o[dt][4 * jq + 3];
+                *reinterpret_cast<float4*>(ourow + d0) = v;
+            }
+        if (half == 0) P.mass_u[rh] = 1.0f - l_tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int CT = 128; // columns per workgroup (4 waves x 32)
+constexpr int RT = 32;  // query rows per step
+
+template <int D, bool X3>
+__global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
+    constexpr int NP = X3 ? 2 : 1;
+    __shared__ __bf16 Qs[NP][RT][D + 8];
+    __shared__ int rpos[RT];
+    __shared__ float rlse[RT], rw[RT];
+    __shared__ int s_start;
+    const int h = blockIdx.y;
+    const int pc0 = blockIdx.x * CT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 31, half = lane >> 5;
+    const int p = pc0 + w * 32 + r; // this lane's column (slot in the selection)
+    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
+    const bool colv = p < P.k;
+    const int cp = colv ? cpos_h[p] : 0x7fffffff;
+    bf16x8 kf[D / 16], kl[X3 ? D / 16 : 1];
+    {
+        const long ko = ((long)h * P.kp + (colv ? p : 0)) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            kf[kk] = *reinterpret_cast<const bf16x8*>(P.Kc + ko + 16 * kk);
+            if (X3) kl[X3 ? kk : 0] = *reinterpret_cast<const bf16x8*>(P.Kc_lo + ko + 16 * kk);
+        }
+    }
+    if (tid == 0) s_start = lower_bound_i32(P.active, P.n, cpos_h[pc0]);
+    __syncthreads();
+    const int t_start = s_start;
+    float csum = 0.0f;
+    for (int t0 = t_start; t0 < P.n; t0 += RT) {
+        // stage 32 query rows (bf16) and their lse / weight
+        for (int idx = tid; idx < RT * (D / 8); idx += 256) {
+            const int rr = idx / (D / 8), c8 = idx % (D / 8);
+            const int t = t0 + rr;
+            float f[8];
+            if (t < P.n) {
+                const long qrow = P.q_gathered ? (long)t : (long)P.active[t];
+                load8_f32(P.q, (qrow * P.H + h) * D + c8 * 8, P.dtype, f);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+            }
+            bf16x8 v, vl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = (__bf16)f[i];
+                if (X3) vl[i] = (__bf16)(f[i] - (float)v[i]);
+            }
+            *reinterpret_cast<bf16x8*>(&Qs[0][rr][c8 * 8]) = v;
+            if (X3) *reinterpret_cast<bf16x8*>(&Qs[NP - 1][rr][c8 * 8]) = vl;
+        }
+        if (tid < RT) {
+            const int t = t0 + tid;
+            if (t < P.n) {
+                const int pos = P.active[t];
+                const long rh = (long)pos * P.H + h;
+                rpos[tid] = pos;
+                rlse[tid] = P.lse[rh] * 1.4426950408889634f;
+                rw[tid] = P.cache_op == FL_CACHE_ZERO ? 1.0f : 1.0f - P.mass_u[rh];
+            } else {
+                rpos[tid] = -1; rlse[tid] = 0.0f; rw[tid] = 0.0f;
+            }
+        }
+        __syncthreads();
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qs[0][r][16 * kk + 8 * half]);
+            s = mfma32(a, kf[kk], s);
+            if (X3) {
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Qs[NP - 1][r][16 * kk + 8 * half]);
+                s = mfma32(a, kl[X3 ? kk : 0], s);
+                s = mfma32(al, kf[kk], s);
+            }
+        }
+        // s[j]: column r of this wave, row (j/4)*8 + half*4 + j%4
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int row = (j >> 2) * 8 + half * 4 + (j & 3);
+            const float v = s[j] * P.c2 - rlse[row];
+            const float pj = rw[row] * __builtin_amdgcn_exp2f(v);
+            csum += (rpos[row] >= cp) ? pj : 0.0f;
+        }
+        __syncthreads();
+    }
+    csum += __shfl_xor(csum, 32);
+    if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
+                              bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
+                              int32_t* cpos, hipStream_t st) {
+    dim3 grid(kp / BN, c.H);
+#define FL_GATHER(D_, X_)                                                                       \
+    hipLaunchKernelGGL((k_gather_bf16<D_, X_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
+                       Vt, Kc_lo, Vt_lo, cpos)
+    if (c.d == 128) { if (x3) FL_GATHER(128, true); else FL_GATHER(128, false); }
+    else { if (x3) FL_GATHER(64, true); else FL_GATHER(64, false); }
+#undef FL_GATHER
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(int d, int mode, bool x3, const AttnParams& P, hipStream_t st) {
+    const int n_tiles = (P.n + BM - 1) / BM;
+    AttnParams Q = P;
+    Q.xcd_remap = (P.H % 8) == 0;
+    dim3 grid(n_tiles * P.H);
+#define FL_ATTN(D_, M_, X_) hipLaunchKernelGGL((k_attn<D_, M_, X_>), grid, dim3(256), 0, st, Q)
+#define FL_ATTN_D(D_)                                                    \
+    if (mode == MODE_ATTN) { if (x3) FL_ATTN(D_, MODE_ATTN, true); else FL_ATTN(D_, MODE_ATTN, false); } \
+    else { if (x3) FL_ATTN(D_, MODE_REBUILD, true); else FL_ATTN(D_, MODE_REBUILD, false); }
+    if (d == 128) { FL_ATTN_D(128) } else { FL_ATTN_D(64) }
+#undef FL_ATTN_D
+#undef FL_ATTN
+    return hipGetLastError();
+}
+
+hipError_t launch_colstat(int d, bool x3, const ColParams& P, hipStream_t st) {
+    dim3 grid((P.k + CT - 1) / CT, P.H);
+    if (d == 128) {
+        if (x3) hipLaunchKernelGGL((k_colstat<128, true>), grid, dim3(256), 0, st, P);
+        else hipLaunchKernelGGL((k_colstat<128, false>), grid, dim3(256), 0, st, P);
+    } else {
+        if (x3) hipLaunchKernelGGL((k_colstat<64, true>), grid, dim3(256), 0, st, P);
+        else hipLaunchKernelGGL((k_colstat<64, false>), grid, dim3(256), 0, st, P);
+    }
+    return hipGetLastError();
+}
+
+} // namespace fl

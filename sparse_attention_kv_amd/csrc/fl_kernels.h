@@ -1,0 +1,61 @@
+// Launch interface between the host ABI (abi.hip) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flashloop.h"
+
+namespace fl {
+
+struct AttnParams {
+    int H, n, k, kp, dtype, q_gathered, cache_op;
+    float c2;        // softmax scale * log2(e)
+    const void* q;
+    const int32_t* active;
+    const __bf16* Kc;      // [H][kp][d] compact bf16 keys
+    const __bf16* Vt;      // [H][kp/64][d][64] compact bf16 values, transposed tiles
+    const __bf16* Kc_lo;   // fp32 inputs: bf16 rounding of the residual x - bf16(x)
+    const __bf16* Vt_lo;
+    const int32_t* cpos;   // [H][kp] column positions (INT32_MAX for padding)
+    float* out;
+    float* lse;
+    float* mass_u;
+    float* out_u;
+    int xcd_remap;
+};
+
+struct ColParams {
+    int H, n, k, kp, dtype, q_gathered, cache_op;
+    float c2;
+    const void* q;
+    const int32_t* active;
+    const __bf16* Kc;
+    const __bf16* Kc_lo;
+    const int32_t* cpos;
+    const float* lse;
+    const float* mass_u;
+    float* col_stat;
+};
+
+enum { MODE_ATTN = 0, MODE_REBUILD = 1 };
+
+// select.hip
+hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, int D,
+                             const int32_t* cand, int n_cand, float* stat, hipStream_t st);
+hipError_t launch_topk(const float* keys, long key_stride, const int32_t* pos, long pos_stride,
+                       int n, int n_sel, int n_prefix, int32_t* out, long out_stride,
+                       int32_t* slot, int n_slot, int n_seg, hipStream_t st);
+hipError_t launch_copy_or_iota(const int32_t* src, int32_t* dst, long n, long row, hipStream_t st);
+// quant.hip
+hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
+                        const void* v_new, int gathered, hipStream_t st);
+// attn.hip
+hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
+                              bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
+                              int32_t* cpos, hipStream_t st);
+hipError_t launch_attn(int d, int mode, bool x3, const AttnParams& P, hipStream_t st);
+hipError_t launch_colstat(int d, bool x3, const ColParams& P, hipStream_t st);
+// abi.hip
+hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
+
+} // namespace fl

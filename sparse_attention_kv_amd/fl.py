@@ -1,0 +1,288 @@
+"""ctypes binding of libflashloop.so (C ABI in include/flashloop.h).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  PyTorch provides device memory (tensors' data pointers) and the
+stream (torch's current HIP stream).  The library must be built
+(``python -m sparse_attention_kv_amd.build``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int, c_long, c_size_t, c_void_p
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflashloop.so")
+
+FL_F32, FL_BF16 = 0, 1
+FL_DEQ_AUTO, FL_DEQ_ONCE, FL_DEQ_IN_TILE = 0, 1, 2
+FL_CACHE_CARRY, FL_CACHE_ZERO, FL_CACHE_REBUILD = 0, 1, 2
+FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 1, 2, 3, 4
+MAX_LEVELS = 16
+
+EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
+           "fl_sparse_loop_attn", "fl_loop_step", "fl_workspace_size", "fl_last_error",
+           "fl_version", "fl_timing_enable", "fl_timing_report"]
+
+
+class FlError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} -> {code}: {msg}")
+        self.code = code
+
+
+class FlKvLevel(ctypes.Structure):
+    _fields_ = [("bits", c_int), ("n_rows", c_int), ("rows", c_void_p), ("slot", c_void_p),
+                ("k_codes", c_void_p), ("v_codes", c_void_p), ("k_scale", c_void_p),
+                ("v_scale", c_void_p)]
+
+
+class FlKvCache(ctypes.Structure):
+    _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("n_levels", c_int),
+                ("level", FlKvLevel * MAX_LEVELS)]
+
+
+class FlAttnArgs(ctypes.Structure):
+    _fields_ = [("dtype", c_int), ("q", c_void_p), ("q_gathered", c_int), ("active", c_void_p),
+                ("n", c_int), ("sel", c_void_p), ("k", c_int), ("sm", c_float),
+                ("level", c_int), ("mode", c_int), ("cache_op", c_int), ("out", c_void_p),
+                ("lse", c_void_p), ("mass_u", c_void_p), ("out_u", c_void_p),
+                ("col_stat", c_void_p), ("q_prev", c_void_p), ("q_prev_gathered", c_int)]
+
+
+class FlLoopCfg(ctypes.Structure):
+    _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
+                ("n_sink", c_int), ("dtype", c_int), ("n_active", c_int * MAX_LEVELS),
+                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int)]
+
+
+class FlLoopState(ctypes.Structure):
+    _fields_ = [("cache", FlKvCache), ("active", c_void_p * MAX_LEVELS),
+                ("slot", c_void_p * MAX_LEVELS), ("stat", c_void_p),
+                ("sel", c_void_p * MAX_LEVELS), ("sel_used", c_void_p * MAX_LEVELS),
+                ("k_cur", c_int * MAX_LEVELS), ("col_stat", c_void_p * MAX_LEVELS),
+                ("out", c_void_p), ("lse", c_void_p), ("mass_u", c_void_p), ("out_u", c_void_p)]
+
+
+class FlLoopInputs(ctypes.Structure):
+    _fields_ = [("h_cur", c_void_p), ("h_prev", c_void_p), ("q", c_void_p), ("k", c_void_p),
+                ("v", c_void_p), ("q_prev", c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_attention_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fl_last_error.restype = ctypes.c_char_p
+        L.fl_version.restype = ctypes.c_char_p
+        L.fl_workspace_size.restype = c_size_t
+        L.fl_workspace_size.argtypes = [c_int, c_long, c_long, c_long, c_long]
+        L.fl_select_active.argtypes = [c_int, c_void_p, c_void_p, c_int, c_int, c_void_p, c_int,
+                                       c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_size_t, c_void_p]
+        L.fl_select_columns.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p,
+                                        c_void_p, c_size_t, c_void_p]
+        L.fl_kv_residual_quant.argtypes = [POINTER(FlKvCache), c_int, c_int, c_void_p, c_void_p,
+                                           c_int, c_void_p]
+        L.fl_sparse_loop_attn.argtypes = [POINTER(FlKvCache), POINTER(FlAttnArgs), c_void_p,
+                                          c_size_t, c_void_p]
+        L.fl_loop_step.argtypes = [POINTER(FlLoopCfg), POINTER(FlLoopState), POINTER(FlLoopInputs),
+                                   c_int, c_void_p, c_size_t, c_void_p]
+        L.fl_timing_enable.argtypes = [c_int]
+        L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
+        for name in EXPORTS:
+            if name not in ("fl_last_error", "fl_version", "fl_workspace_size"):
+                getattr(L, name).restype = c_int
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    """Device pointer of a tensor (or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise FlError(fn, rc, lib().fl_last_error().decode())
+
+
+def _dtype_code(t):
+    return FL_BF16 if t.dtype == torch.bfloat16 else FL_F32
+
+
+def fl_version():
+    return lib().fl_version().decode()
+
+
+def fl_workspace_size(op, a, b=0, c=0, e=0):
+    return int(lib().fl_workspace_size(op, a, b, c, e))
+
+
+def fl_timing_enable(on=True):
+    _check("fl_timing_enable", lib().fl_timing_enable(int(bool(on))))
+
+
+def fl_timing_report():
+    """{kernel name: (launches, total ms)} of the launches recorded since the
+    last report (waits for their events)."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check("fl_timing_report", lib().fl_timing_report(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
+def fl_select_active(h_cur, h_prev, cand, n_select, stat_out, active_out, slot_out=None,
+                     stat_in=None, N=None, stream=None):
+    """Sec. 4.1: token statistic over candidates and nested top-k (see header)."""
+    if stat_in is not None:
+        n_cand = stat_in.numel()
+        dt, D = FL_F32, 0
+        N = N if N is not None else (slot_out.numel() if slot_out is not None else n_cand)
+    else:
+        N, D = h_cur.shape
+        dt = _dtype_code(h_cur)
+        n_cand = N if cand is None else cand.numel()
+    rc = lib().fl_select_active(dt, _p(h_cur), _p(h_prev), N, D, _p(cand), n_cand, n_select,
+                                _p(stat_in), _p(stat_out), _p(active_out), _p(slot_out), None, 0,
+                                _stream(stream))
+    _check("fl_select_active", rc)
+
+
+def fl_select_columns(col_stat, cand_cols, n_sink, k, sel_out, stream=None):
+    """Sec. 4.2: per-head nested column selection with sinks (see header)."""
+    H, n_cand = col_stat.shape
+    rc = lib().fl_select_columns(_p(col_stat), _p(cand_cols), H, n_cand, n_sink, k, _p(sel_out),
+                                 None, 0, _stream(stream))
+    _check("fl_select_columns", rc)
+
+
+def fl_kv_residual_quant(cache: FlKvCache, level, k_new, v_new, gathered=False, stream=None):
+    """Sec. 3.3/4.3: writes codes and scales of cache.level[level]."""
+    rc = lib().fl_kv_residual_quant(ctypes.byref(cache), level, _dtype_code(k_new), _p(k_new),
+                                    _p(v_new), int(gathered), _stream(stream))
+    _check("fl_kv_residual_quant", rc)
+
+
+def fl_sparse_loop_attn(cache: FlKvCache, args: FlAttnArgs, ws, stream=None):
+    """Sec. 4.2: sparse attention (+ cache rebuild, + column statistics)."""
+    rc = lib().fl_sparse_loop_attn(ctypes.byref(cache), ctypes.byref(args), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _check("fl_sparse_loop_attn", rc)
+
+
+def fl_loop_step(cfg: FlLoopCfg, state: FlLoopState, inputs: FlLoopInputs, r, ws, stream=None):
+    """Sec. 4.1-4.3: one whole loop r."""
+    rc = lib().fl_loop_step(ctypes.byref(cfg), ctypes.byref(state), ctypes.byref(inputs), r,
+                            _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("fl_loop_step", rc)
+
+
+# --------------------------------------------------------------------------
+# Device-memory holder for a whole R-loop run (buffers only; no arithmetic).
+
+def level_code_bytes(bits, H, d):
+    return H * d * bits // 8
+
+
+class LoopRunner:
+    """Allocates the cache levels and loop state for one attention layer of
+    N tokens and runs ``fl_loop_step`` for r = 1..R."""
+
+    def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, dtype=torch.bfloat16,
+                 mode=FL_DEQ_AUTO, device="cuda"):
+        self.N, self.H, self.d, self.g, self.R = N, H, d, g, R
+        dev = torch.device(device)
+        self.dev = dev
+        cfg = FlLoopCfg()
+        cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = N, H, d, g, R, n_sink
+        cfg.dtype = FL_BF16 if dtype == torch.bfloat16 else FL_F32
+        cfg.mode = mode
+        for r in range(R):
+            cfg.n_active[r] = n_active[r]
+            cfg.k_cols[r] = k_cols[r]
+            cfg.bits[r] = bits[r]
+        self.cfg = cfg
+        st = FlLoopState()
+        self._keep = []
+
+        def buf(shape, dt):
+            t = torch.empty(shape, dtype=dt, device=dev)
+            self._keep.append(t)
+            return t
+
+        st.cache.N, st.cache.H, st.cache.d, st.cache.g = N, H, d, g
+        self.codes = []
+        for r in range(R):
+            rows = N if r == 0 else n_active[r]
+            b = bits[r]
+            kc = buf((rows, H, d * b // 8), torch.uint8)
+            vc = buf((rows, H, d * b // 8), torch.uint8)
+            ks = buf((rows, H, d // g), torch.float32)
+            vs = buf((rows, H, d // g), torch.float32)
+            L = st.cache.level[r]
+            L.bits, L.n_rows = b, rows
+            L.k_codes, L.v_codes, L.k_scale, L.v_scale = _p(kc), _p(vc), _p(ks), _p(vs)
+            self.codes.append(dict(k=kc, v=vc, ks=ks, vs=vs))
+        self.active, self.slot, self.sel, self.col_stat = [], [], [], []
+        for r in range(R):
+            a = buf((n_active[r],), torch.int32)
+            s = buf((N,), torch.int32) if r > 0 else None
+            sl = buf((H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < N else None
+            k_here = min(k_cols[: r + 1])
+            cs = buf((H, k_here), torch.float32)
+            st.active[r] = _p(a)
+            st.slot[r] = _p(s)
+            st.sel[r] = _p(sl)
+            st.col_stat[r] = _p(cs)
+            self.active.append(a); self.slot.append(s); self.sel.append(sl); self.col_stat.append(cs)
+        self.stat = buf((N,), torch.float32)
+        self.out = buf((N, H, d), torch.float32)
+        self.lse = buf((N, H), torch.float32)
+        self.mass_u = buf((N, H), torch.float32)
+        self.out_u = buf((N, H, d), torch.float32)
+        st.stat, st.out, st.lse = _p(self.stat), _p(self.out), _p(self.lse)
+        st.mass_u, st.out_u = _p(self.mass_u), _p(self.out_u)
+        self.state = st
+        ws_bytes = fl_workspace_size(FL_WS_LOOP_STEP, H, N, d, cfg.dtype)
+        self.ws = buf((ws_bytes,), torch.uint8)
+        self.inputs = FlLoopInputs()
+
+    def step(self, r, h_cur, h_prev, q, k, v, q_prev, stream=None):
+        inp = self.inputs
+        inp.h_cur, inp.h_prev = _p(h_cur), _p(h_prev)
+        inp.q, inp.k, inp.v, inp.q_prev = _p(q), _p(k), _p(v), _p(q_prev)
+        fl_loop_step(self.cfg, self.state, inp, r, self.ws, stream)
+
+    def sel_used(self, r):
+        """Column set used at loop r (None = all columns)."""
+        p = self.state.sel_used[r - 1]
+        if not p:
+            return None
+        for t in self.sel:
+            if t is not None and t.data_ptr() == p:
+                return t
+        raise RuntimeError("unknown selection buffer")
+
+    def k_used(self, r):
+        return self.state.k_cur[r - 1]

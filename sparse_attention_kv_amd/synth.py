@@ -27,8 +27,9 @@ import numpy as np
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # finite inputs only: u + 0x7fff + lsb cannot wrap below the NaN range
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 

@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: run the whole R-loop step through the
+C ABI (``fl_loop_step``) and read back every loop's results, then run the
+oracle on the same inputs, feeding it the GPU's own fp32 statistic buffers
+for its selections (index sets are then unique and compared exactly)."""
+import numpy as np
+import torch
+
+import oracle
+from oracle.loop import run_prefill
+from sparse_attention_kv_amd import fl, synth
+
+
+def to_dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def counts(w):
+    n = [w.N]
+    for r in range(1, w.R):
+        n.append(oracle.active_count(w.rho[r], w.N, n[-1]))
+    return n
+
+
+def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None):
+    bits = bits or w.bits
+    dt = inp["dtype"]
+    dev = {key: [to_dev(a, dt) for a in inp[key]] for key in ("h", "q", "k", "v")}
+    n_act = counts(w)
+    runner = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, bits,
+                           dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode)
+    res = []
+    for r in range(1, w.R + 1):
+        hp = dev["h"][r - 2] if r > 1 else None
+        qp = dev["q"][r - 2] if r > 1 else None
+        runner.step(r, dev["h"][r - 1], hp, dev["q"][r - 1], dev["k"][r - 1], dev["v"][r - 1], qp)
+        torch.cuda.synchronize()
+        rec = dict(r=r)
+        act = runner.active[r - 1].cpu().numpy()
+        rec["active"] = act
+        if r > 1:
+            rec["stat"] = runner.stat[: n_act[r - 2]].cpu().numpy().copy()
+            rec["slot"] = runner.slot[r - 1].cpu().numpy()
+        cb = runner.codes[r - 1]
+        rec["k_codes"] = cb["k"].cpu().numpy()
+        rec["v_codes"] = cb["v"].cpu().numpy()
+        rec["k_scale"] = cb["ks"].cpu().numpy()
+        rec["v_scale"] = cb["vs"].cpu().numpy()
+        sel = runner.sel_used(r)
+        rec["sel"] = None if sel is None else sel.cpu().numpy()
+        rec["k"] = runner.k_used(r)
+        need_c = r < w.R and w.kcols[r] < rec["k"]
+        rec["cstat"] = runner.col_stat[r - 1][:, : rec["k"]].cpu().numpy().copy() if need_c else None
+        rec["out"] = runner.out.cpu().numpy()[act]
+        rec["lse"] = runner.lse.cpu().numpy()[act]
+        rec["mass_u"] = runner.mass_u.cpu().numpy()[act]
+        rec["out_u"] = runner.out_u.cpu().numpy()[act]
+        res.append(rec)
+    return res, runner
+
+
+def run_oracle_lockstep(w, inp, gres, bits=None):
+    x = synth.as_f32_inputs(inp)
+    sched = w.sched()
+    if bits:
+        sched["bits"] = list(bits)
+    ov = {}
+    for r in range(2, w.R + 1):
+        ov[("stat", r)] = gres[r - 1]["stat"]
+        if gres[r - 2]["cstat"] is not None:
+            ov[("cstat", r)] = gres[r - 2]["cstat"]
+    return run_prefill(x["h"], x["q"], x["k"], x["v"], sched, override=ov)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def assert_close(got, want, what, rel=1e-2, mabs=3e-2):
+    got = np.asarray(got, np.float64); want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    e = rel_l2(got, want)
+    m = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert e <= rel and m <= mabs, f"{what}: rel-L2 {e:.3e} (<= {rel}), max-abs {m:.3e} (<= {mabs})"
+    return e, m
+
+
+def assert_close_scaled(got, want, what, rel=1e-2, mabs=3e-2):
+    """Column statistics are sums of up to N probabilities (values up to
+    ~N at sink columns): rel-L2 <= rel and |got - want| <= mabs * max(1, |want|)
+    elementwise (the absolute bound in units of one row's probability mass)."""
+    got = np.asarray(got, np.float64); want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    e = rel_l2(got, want)
+    lim = mabs * np.maximum(1.0, np.abs(want))
+    worst = float(np.max(np.abs(got - want) / lim)) if got.size else 0.0
+    assert e <= rel and worst <= 1.0, f"{what}: rel-L2 {e:.3e} (<= {rel}), scaled max {worst:.3f} (<= 1)"
+    return e, worst
+
+
+def compare_chain(w, gres, ores, bits=None, check_codes=True):
+    bits = bits or w.bits
+    report = []
+    for r in range(1, w.R + 1):
+        g, o = gres[r - 1], ores[r - 1]
+        np.testing.assert_array_equal(g["active"], o["active"], err_msg=f"loop {r} active set")
+        if r > 1:
+            np.testing.assert_allclose(g["stat"], o["stat"], rtol=1e-5, err_msg=f"loop {r} stat")
+            slot = np.full(w.N, -1, np.int32)
+            slot[o["active"]] = np.arange(len(o["active"]))
+            np.testing.assert_array_equal(g["slot"], slot, err_msg=f"loop {r} slot map")
+        if check_codes:
+            for kv in ("k", "v"):
+                lvl = o["level_" + kv]
+                if bits[r - 1] == 32:
+                    raw = g[kv + "_codes"].view(np.float32).reshape(lvl["raw"].shape)
+                    np.testing.assert_array_equal(raw, lvl["raw"], err_msg=f"loop {r} raw {kv}")
+                else:
+                    packed = oracle.pack_codes(lvl["codes"], bits[r - 1])
+                    np.testing.assert_array_equal(g[kv + "_codes"], packed,
+                                                  err_msg=f"loop {r} {kv} codes")
+                    np.testing.assert_array_equal(g[kv + "_scale"].view(np.uint32),
+                                                  lvl["scales"].view(np.uint32),
+                                                  err_msg=f"loop {r} {kv} scales")
+        if o["sel"] is None:
+            assert g["sel"] is None and g["k"] == w.N
+        else:
+            np.testing.assert_array_equal(g["sel"], o["sel"], err_msg=f"loop {r} columns")
+        e_o = assert_close(g["out"], o["out"], f"loop {r} out")
+        e_l = assert_close(g["lse"], o["lse"], f"loop {r} lse")
+        assert_close(g["mass_u"], o["mass_u"], f"loop {r} mass_u", mabs=3e-2)
+        if o["out_u"] is not None:
+            assert_close(g["out_u"], o["out_u"], f"loop {r} out_u")
+        if o["cstat"] is not None:
+            assert g["cstat"] is not None
+            assert_close_scaled(g["cstat"], o["cstat"], f"loop {r} cstat")
+        report.append((r, e_o, e_l))
+    return report

@@ -1,0 +1,134 @@
+"""The C-ABI library loads without a GPU, exports every entry point that
+include/flashloop.h declares, and rejects invalid arguments on the host
+before enqueuing anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_kv_amd import fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashloop.h")
+
+FAKE = 0x10000  # a non-null pointer value; never dereferenced by host validation
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fl_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fl.LIB_PATH):
+        from sparse_attention_kv_amd import build
+        build.build()
+    return fl.lib()
+
+
+def test_exports_match_header(L):
+    declared = _declared()
+    assert set(fl.EXPORTS) == set(declared), declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_workspace(L):
+    assert "gfx950" in fl.fl_version()
+    assert fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, 16, 2048, 128, 4) >= 4 * 16 * 2048 * 128 * 2
+    assert fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, 16, 2048, 96, 4) == 0
+    assert fl.fl_workspace_size(99, 1, 1, 1, 1) == 0
+
+
+def _err(L):
+    return L.fl_last_error().decode()
+
+
+def test_select_active_rejects(L):
+    rc = L.fl_select_active(1, FAKE, FAKE, 100, 64, None, 100, 0, None, FAKE, FAKE, None, None, 0, None)
+    assert rc == -1 and "n_select" in _err(L)
+    rc = L.fl_select_active(1, FAKE, FAKE, 100, 64, None, 101, 5, None, FAKE, FAKE, None, None, 0, None)
+    assert rc == -1 and "n_cand" in _err(L)
+    rc = L.fl_select_active(1, FAKE, FAKE, 100, 60, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
+    assert rc == -1 and "multiple of 8" in _err(L)
+    rc = L.fl_select_active(1, None, FAKE, 100, 64, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
+    assert rc == -1
+
+
+def test_select_columns_rejects(L):
+    assert L.fl_select_columns(FAKE, None, 2, 100, 4, 4, FAKE, None, 0, None) == -1
+    assert L.fl_select_columns(FAKE, None, 2, 100, -1, 10, FAKE, None, 0, None) == -1
+    assert L.fl_select_columns(None, None, 2, 100, 4, 10, FAKE, None, 0, None) == -1
+    assert L.fl_select_columns(FAKE, None, 0, 100, 4, 10, FAKE, None, 0, None) == -1
+
+
+def _cache(N=64, H=2, d=128, g=64, bits=(8, 4)):
+    c = fl.FlKvCache()
+    c.N, c.H, c.d, c.g, c.n_levels = N, H, d, g, len(bits)
+    for l, b in enumerate(bits):
+        L = c.level[l]
+        L.bits, L.n_rows = b, N if l == 0 else N // 2
+        L.rows = None if l == 0 else FAKE
+        L.slot = None if l == 0 else FAKE
+        L.k_codes = L.v_codes = L.k_scale = L.v_scale = FAKE
+    return c
+
+
+def test_quant_rejects(L):
+    c = _cache(d=96)
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 0, None) == -2
+    c = _cache(bits=(8, 3))
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 1, 1, FAKE, FAKE, 0, None) == -2
+    c = _cache(bits=(4,))
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 0, None) == -2
+    c = _cache()
+    c.level[1].slot = None
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 1, 1, FAKE, FAKE, 0, None) == -1
+    c = _cache(g=48)
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 0, None) == -2
+    assert L.fl_kv_residual_quant(None, 0, 1, FAKE, FAKE, 0, None) == -1
+    c = _cache()
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 1, None) == -1
+
+
+def _args(**kw):
+    a = fl.FlAttnArgs()
+    a.dtype, a.q, a.active, a.n, a.sel, a.k = 1, FAKE, FAKE, 10, FAKE, 8
+    a.sm, a.level, a.mode, a.cache_op = 0.125, 1, 0, 0
+    a.out = a.lse = a.mass_u = a.out_u = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_attn_rejects(L):
+    c = _cache()
+    a = _args()
+    ws = ctypes.create_string_buffer(64)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), ctypes.addressof(ws), 64, None) == -3
+    assert "workspace" in _err(L)
+    a = _args(sel=None)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+    a = _args(cache_op=2, q_prev=None)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+    a = _args(cache_op=2, level=0, q_prev=FAKE)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+    a = _args(mode=2)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) in (-2, -3)
+    a = _args(n=0)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+
+
+def test_loop_step_rejects(L):
+    cfg = fl.FlLoopCfg()
+    cfg.N, cfg.H, cfg.d, cfg.g, cfg.R = 64, 2, 128, 64, 2
+    st = fl.FlLoopState()
+    inp = fl.FlLoopInputs()
+    assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 3, None, 0, None) == -1
+    assert L.fl_loop_step(None, ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
+    st.cache.N, st.cache.H, st.cache.d, st.cache.g = 64, 2, 128, 64
+    assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
+    assert "q/k/v" in _err(L)
