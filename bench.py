@@ -42,6 +42,8 @@ def parse():
                     help="query rows per loop in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--mode", default="auto", choices=["auto", "once", "in_tile"],
+                    help="where the cache is dequantised (library default: auto)")
     return ap.parse_args()
 
 
@@ -88,8 +90,9 @@ def main():
     n_act = [N]
     for r in range(1, R):
         n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
+    mode = {"auto": fl.FL_DEQ_AUTO, "once": fl.FL_DEQ_ONCE, "in_tile": fl.FL_DEQ_IN_TILE}[args.mode]
     run = fl.LoopRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
-                        dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+                        dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -196,7 +199,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "R": R, "g": w.g,
                    "active_per_loop": n_act, "k_per_loop": [L["k"] for L in loops],
-                   "bits_per_loop": w.bits, "n_sink": w.n_sink},
+                   "bits_per_loop": w.bits, "n_sink": w.n_sink, "dequant": args.mode},
         "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.mean(loop_ms[:, i])), 4),
                        pairs=L["pairs"], rebuilt=L["rebuilt"], colstat=L["colstat"])
                   for i, L in enumerate(loops)],

@@ -95,8 +95,8 @@ typedef struct fl_kv_cache {
 enum fl_ws_op {
     FL_WS_SELECT_ACTIVE = 1,  /* a = n_cand                                    */
     FL_WS_SELECT_COLUMNS = 2, /* a = H, b = n_cand                             */
-    FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = dtype of q/k/v       */
-    FL_WS_LOOP_STEP = 4       /* a = H, b = N (largest k), c = d, e = dtype    */
+    FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = cache levels used (level+1; <= 0: max) */
+    FL_WS_LOOP_STEP = 4       /* a = H, b = N (largest k), c = d, e = R        */
 };
 size_t fl_workspace_size(int op, long a, long b, long c, long e);
 

@@ -45,12 +45,26 @@ long align_up(long x) { return (x + kAlign - 1) / kAlign * kAlign; }
 long kpad(long k) { return (k + 63) / 64 * 64; }
 
 // workspace of fl_sparse_loop_attn: two compact bf16 copies (K, V^T) for the
-// current loop and, for a cache rebuild, two for the previous loop, plus the
-// column positions; fp32 inputs (x3) add a "lo" copy of each.
-long attn_ws_bytes(long H, long k, long d, bool x3) {
-    const long kp = kpad(k);
-    return (x3 ? 8 : 4) * align_up(H * kp * d * 2) + align_up(H * kp * 4) + kAlign;
+// current loop and, for a cache rebuild, two for the previous loop, each with
+// a "lo" copy (used when the cache has residual levels or inputs are fp32),
+// plus the column positions.
+// The in-tile path adds per-level quantised planes (codes <= 8 bits, fp32
+// scales per group of >= 32 channels) for K and V.
+long quant_plane_bytes(long H, long kp, long d) {
+    return 2 * (align_up(H * kp * d) + align_up(H * kp * (d / 32) * 4));
 }
+long attn_ws_bytes(long H, long k, long d, long levels) {
+    const long kp = kpad(k);
+    if (levels <= 0 || levels > FL_MAX_LEVELS) levels = FL_MAX_LEVELS;
+    return 8 * align_up(H * kp * d * 2) + align_up(H * kp * 4) + levels * quant_plane_bytes(H, kp, d) +
+           kAlign;
+}
+
+// Operand precision of the attention products: residual levels hold the
+// cross-loop updates, which sit below bf16's resolution of the summed value,
+// so a cache with residual levels feeds K, V and P as hi + lo bf16 pairs;
+// fp32 inputs split q as well.
+int attn_prec(int dtype, int level) { return dtype == FL_F32 ? 2 : (level >= 1 ? 1 : 0); }
 
 // ---- optional per-kernel HIP-event timing of the library's launches ----
 struct TimedLaunch {
@@ -127,7 +141,7 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     case FL_WS_SPARSE_ATTN:
     case FL_WS_LOOP_STEP:
         if (a <= 0 || b <= 0 || !(c == 64 || c == 128)) return 0;
-        return (size_t)attn_ws_bytes(a, b, c, e != FL_BF16);
+        return (size_t)attn_ws_bytes(a, b, c, e);
     default: return 0;
     }
 }
@@ -254,9 +268,14 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
         FL_REQUIRE(a->q_prev != nullptr, "q_prev NULL");
     }
     FL_REQUIRE(a->mode >= FL_DEQ_AUTO && a->mode <= FL_DEQ_IN_TILE, "mode %d", a->mode);
-    if (a->mode == FL_DEQ_IN_TILE) return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE not built");
-    const bool x3 = a->dtype == FL_F32;
-    const long need = attn_ws_bytes(H, a->k, d, x3);
+    const int prec = attn_prec(a->dtype, a->level);
+    const int prec_old = attn_prec(a->dtype, a->level - 1);
+    const bool in_tile = a->mode == FL_DEQ_IN_TILE;
+    if (in_tile)
+        for (int l = 0; l <= a->level; ++l)
+            if (cache->level[l].bits == 32)
+                return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE needs quantised levels (level %d is raw)", l);
+    const long need = attn_ws_bytes(H, a->k, d, a->level + 1);
     if (!ws || (long)ws_bytes < need)
         return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
     hipStream_t st = (hipStream_t)stream;
@@ -264,44 +283,78 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     char* base = (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
     const long kvb = align_up((long)H * kp * d * 2);
     __bf16* buf[8];
-    for (int i = 0; i < (x3 ? 8 : 4); ++i) buf[i] = (__bf16*)(base + i * kvb);
-    for (int i = (x3 ? 8 : 4); i < 8; ++i) buf[i] = nullptr;
-    int32_t* cpos = (int32_t*)(base + (x3 ? 8 : 4) * kvb);
+    for (int i = 0; i < 8; ++i) buf[i] = (__bf16*)(base + i * kvb);
+    int32_t* cpos = (int32_t*)(base + 8 * kvb);
+    char* qbase = base + 8 * kvb + align_up((long)H * kp * 4);
     // new side: K, V^T (+ lo parts); previous-loop side for a rebuild
     __bf16 *Kc = buf[0], *Vt = buf[1], *Kc_old = buf[2], *Vt_old = buf[3];
     __bf16 *Kl = buf[4], *Vl = buf[5], *Kl_old = buf[6], *Vl_old = buf[7];
     const float c2 = a->sm * 1.4426950408889634f;
 
-    FL_HIP(timed("gather", st, [&] {
-               return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, x3, Kc, Vt, Kl, Vl,
-                                             cpos, st);
-           }),
-           "gather");
     fl::AttnParams P{};
     P.H = H; P.n = a->n; P.k = a->k; P.kp = kp; P.dtype = a->dtype; P.cache_op = a->cache_op;
     P.c2 = c2; P.active = a->active; P.cpos = cpos;
     P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u;
-    if (a->cache_op == FL_CACHE_REBUILD) {
-        FL_HIP(timed("gather", st, [&] {
-                   return fl::launch_gather_bf16(*cache, a->level - 1, a->sel, a->k, kp, x3, Kc_old,
-                                                 Vt_old, Kl_old, Vl_old, cpos, st);
+    if (in_tile) {
+        fl::QTiles& qt = P.qt;
+        qt.n_levels = a->level + 1;
+        qt.g = cache->g;
+        char* q = qbase;
+        const int G = d / cache->g;
+        for (int l = 0; l <= a->level; ++l) {
+            const int b = cache->level[l].bits;
+            qt.bits[l] = b;
+            qt.kq[l] = (uint8_t*)q; q += align_up((long)H * kp * d * b / 8);
+            qt.ks[l] = (float*)q;   q += align_up((long)H * kp * G * 4);
+            qt.vq[l] = (uint8_t*)q; q += align_up((long)H * kp * d * b / 8);
+            qt.vs[l] = (float*)q;   q += align_up((long)H * kp * G * 4);
+        }
+        FL_HIP(timed("gather_q", st, [&] {
+                   return fl::launch_gather_q(*cache, a->level, a->sel, a->k, kp, qt, cpos, st);
                }),
-               "gather(prev)");
+               "gather_q");
+    } else {
+        FL_HIP(timed("gather", st, [&] {
+                   return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc, Vt,
+                                                 Kl, Vl, cpos, st);
+               }),
+               "gather");
+    }
+    if (a->cache_op == FL_CACHE_REBUILD) {
         fl::AttnParams R = P;
+        if (in_tile) {
+            R.deq_levels = a->level; // the previous loop's cache: levels 0..level-1
+        } else {
+            FL_HIP(timed("gather", st, [&] {
+                       return fl::launch_gather_bf16(*cache, a->level - 1, a->sel, a->k, kp,
+                                                     prec_old >= 1, Kc_old, Vt_old, Kl_old, Vl_old,
+                                                     cpos, st);
+                   }),
+                   "gather(prev)");
+            R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
+        }
         R.q = a->q_prev; R.q_gathered = a->q_prev_gathered;
-        R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
-        FL_HIP(timed("attn_rebuild", st, [&] { return fl::launch_attn(d, fl::MODE_REBUILD, x3, R, st); }),
+        FL_HIP(timed("attn_rebuild", st,
+                     [&] { return fl::launch_attn(d, fl::MODE_REBUILD, prec_old, in_tile, R, st); }),
                "attn(rebuild)");
     }
     P.q = a->q; P.q_gathered = a->q_gathered; P.Kc = Kc; P.Vt = Vt; P.Kc_lo = Kl; P.Vt_lo = Vl;
-    FL_HIP(timed("attn", st, [&] { return fl::launch_attn(d, fl::MODE_ATTN, x3, P, st); }), "attn");
+    P.deq_levels = a->level + 1;
+    FL_HIP(timed("attn", st, [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),
+           "attn");
     if (a->col_stat) {
+        if (in_tile) // the statistics sweep reads the keys as compact bf16
+            FL_HIP(timed("gather", st, [&] {
+                       return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc,
+                                                     Vt, Kl, Vl, cpos, st);
+                   }),
+                   "gather");
         fl::ColParams C{};
         C.H = H; C.n = a->n; C.k = a->k; C.kp = kp; C.dtype = a->dtype; C.q_gathered = a->q_gathered;
         C.cache_op = a->cache_op == FL_CACHE_ZERO ? FL_CACHE_ZERO : FL_CACHE_CARRY;
         C.c2 = c2; C.q = a->q; C.active = a->active; C.Kc = Kc; C.Kc_lo = Kl; C.cpos = cpos;
         C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat;
-        FL_HIP(timed("colstat", st, [&] { return fl::launch_colstat(d, x3, C, st); }), "colstat");
+        FL_HIP(timed("colstat", st, [&] { return fl::launch_colstat(d, prec, C, st); }), "colstat");
     }
     return FL_OK;
 }

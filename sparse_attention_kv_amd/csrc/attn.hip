@@ -150,6 +150,80 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
 }
 
 // ---------------------------------------------------------------------------
+// Compact gather of the quantised levels of the selected columns (for the
+// in-tile dequantisation path): K code rows are copied as stored, V codes are
+// transposed per 64-column tile into the key order of the MFMA operand, and
+// scales follow their codes.  Absent levels are written as zeros.
+template <int D>
+__global__ __launch_bounds__(256) void k_gather_q(fl_kv_cache c, int upto,
+                                                  const int32_t* __restrict__ sel, int k, int kp,
+                                                  QTiles out, int32_t* __restrict__ cpos) {
+    constexpr int G_MAX = D / 32;
+    __shared__ int8_t sV[BN][D + 4];
+    __shared__ float sVs[BN][G_MAX];
+    const int h = blockIdx.y, tile = blockIdx.x, p0 = tile * BN;
+    const int tid = threadIdx.x, col = tid >> 2;
+    constexpr int CPT = D / 4;
+    const int c0 = (tid & 3) * CPT;
+    const int p = p0 + col;
+    const bool live = p < k;
+    const long j = live ? (sel ? (long)sel[(long)h * k + p] : (long)p) : 0;
+    if ((tid & 3) == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
+    const int g = c.g, G = D / g, HD = c.H * D;
+    const long prow = (long)h * kp + p;
+    const int nt = kp / BN;
+    for (int l = 0; l <= upto; ++l) {
+        const fl_kv_level& L = c.level[l];
+        const int b = L.bits;
+        long row = -1;
+        if (live) row = l == 0 ? j : (long)L.slot[j];
+        const bool present = row >= 0;
+        // K: copy this thread's CPT codes and (once per group) the scale
+        {
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(L.k_codes) + ((row * HD + (long)h * D + c0) * b) / 8);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(out.kq[l] + ((prow * D + c0) * b) / 8);
+            for (int wi = 0; wi < CPT * b / 32; ++wi) dst[wi] = present ? src[wi] : 0u;
+            if (c0 % g == 0)
+                out.ks[l][prow * G + c0 / g] = present ? L.k_scale[(row * HD + (long)h * D + c0) / g] : 0.0f;
+        }
+        // V: unpack this thread's codes into LDS
+        {
+            const long e0 = row * HD + (long)h * D + c0;
+#pragma unroll
+            for (int e8 = 0; e8 < CPT; e8 += 8) {
+                const uint64_t w = present ? load_codes8(L.v_codes, e0 + e8, b) : 0ull;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sV[col][c0 + e8 + i] = (int8_t)code_at(w, b, i);
+            }
+            if (c0 % g == 0) sVs[col][c0 / g] = present ? L.v_scale[e0 / g] : 0.0f;
+        }
+        __syncthreads();
+        // V codes: [d][64 keys in operand order], bits per code, 8 keys per step
+        for (int idx = tid; idx < D * (BN / 8); idx += 256) {
+            const int dd = idx / (BN / 8), oct = idx % (BN / 8);
+            uint64_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int so = oct * 8 + i;
+                const int key = (so & ~15) + vt_key_of_slot(so & 15);
+                w |= (uint64_t)((uint32_t)(int)sV[key][dd] & ((1u << b) - 1u)) << (b * i);
+            }
+            uint8_t* dst = out.vq[l] + ((((long)h * nt + tile) * D + dd) * BN + oct * 8) * b / 8;
+            if (b == 8) *reinterpret_cast<uint64_t*>(dst) = w;
+            else if (b == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)w;
+            else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+        }
+        for (int idx = tid; idx < G * BN; idx += 256) {
+            const int gg = idx / BN, so = idx % BN;
+            const int key = (so & ~15) + vt_key_of_slot(so & 15);
+            out.vs[l][(((long)h * nt + tile) * G + gg) * BN + so] = sVs[key][gg];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
     int lo = 0, hi = n;
@@ -175,8 +249,13 @@ __device__ __forceinline__ void block_coords(int xcd_remap, int n_tiles, int H, 
     }
 }
 
-template <int D, int MODE, bool X3>
+// PREC 0: bf16 operands (a cache without residual levels); 1: K, V and P as
+// hi + lo bf16 pairs (residual levels carry information below bf16's
+// resolution of the summed value); 2: q split as well (fp32 inputs).
+template <int D, int MODE, int PREC, bool DEQ>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
+    constexpr bool X3 = PREC >= 1;
+    constexpr bool QS = PREC == 2;
     constexpr int NP = X3 ? 2 : 1; // hi (+ lo) parts
     __shared__ __bf16 Ks[NP][BN][D + 8];
     __shared__ __bf16 Vs[NP][D][BN + 8];
@@ -198,13 +277,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
         s_bounds[1] = upper_bound_i32(cpos_h, P.k, P.active[t0]); // p_full
     }
     // query fragment: B operand of S^T = K Q^T (lane: row r, d = 16kk + 8half)
-    bf16x8 qf[D / 16], ql[X3 ? D / 16 : 1];
+    bf16x8 qf[D / 16], ql[QS ? D / 16 : 1];
     {
         const long qrow = P.q_gathered ? (long)t : (long)rowpos;
         const long qoff = (qrow * P.H + h) * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            if (X3) {
+            if (QS) {
                 float f[8];
                 if (valid) load8_f32(P.q, qoff + 16 * kk, P.dtype, f);
                 else {
@@ -214,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     qf[kk][i] = (__bf16)f[i];
-                    ql[X3 ? kk : 0][i] = (__bf16)(f[i] - (float)qf[kk][i]);
+                    ql[QS ? kk : 0][i] = (__bf16)(f[i] - (float)qf[kk][i]);
                 }
             } else if (valid) {
                 qf[kk] = load8_bf16(P.q, qoff + 16 * kk, P.dtype);
@@ -242,19 +321,79 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
     const long voff = (long)h * (P.kp / BN) * D * BN;
     for (int p0 = 0; p0 < p_end; p0 += BN) {
         // ---- stage the K and V^T tiles in LDS ----
+        if (DEQ) {
+            // dequantise the tile's levels straight into the LDS operand tiles
+            const int g = P.qt.g, G = D / g;
+            {
+                const int col = tid >> 2, c0 = (tid & 3) * (D / 4);
+                const long prow = (long)h * P.kp + p0 + col;
+                float x[D / 4];
 #pragma unroll
-        for (int part = 0; part < NP; ++part) {
-            const __bf16* Kh = (part ? P.Kc_lo : P.Kc) + koff;
-            const __bf16* Vh = (part ? P.Vt_lo : P.Vt) + voff;
+                for (int e = 0; e < D / 4; ++e) x[e] = 0.0f;
+                for (int l = 0; l < P.deq_levels; ++l) {
+                    const int b = P.qt.bits[l];
+                    const float sc = P.qt.ks[l][prow * G + c0 / g];
 #pragma unroll
-            for (int m = 0; m < (BN * D / 8) / 256; ++m) {
+                    for (int e8 = 0; e8 < D / 4; e8 += 8) {
+                        const uint64_t w = load_codes8(P.qt.kq[l], prow * D + c0 + e8, b);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) x[e8 + i] += (float)code_at(w, b, i) * sc;
+                    }
+                }
+#pragma unroll
+                for (int e8 = 0; e8 < D / 4; e8 += 8) {
+                    bf16x8 v, vl;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        v[i] = (__bf16)x[e8 + i];
+                        if (X3) vl[i] = (__bf16)(x[e8 + i] - (float)v[i]);
+                    }
+                    *reinterpret_cast<bf16x8*>(&Ks[0][col][c0 + e8]) = v;
+                    if (X3) *reinterpret_cast<bf16x8*>(&Ks[NP - 1][col][c0 + e8]) = vl;
+                }
+            }
+            const long tbase = (long)h * (P.kp / BN) + p0 / BN;
+#pragma unroll
+            for (int m = 0; m < (D * (BN / 8)) / 256; ++m) {
                 const int idx = tid + m * 256;
-                const int key = idx / (D / 8), c8 = idx % (D / 8);
-                *reinterpret_cast<uint4*>(&Ks[part][key][c8 * 8]) =
-                    *reinterpret_cast<const uint4*>(Kh + (long)(p0 + key) * D + c8 * 8);
                 const int dd = idx / (BN / 8), oc = idx % (BN / 8);
-                *reinterpret_cast<uint4*>(&Vs[part][dd][oc * 8]) =
-                    *reinterpret_cast<const uint4*>(Vh + ((long)(p0 / BN) * D + dd) * BN + oc * 8);
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = 0.0f;
+                for (int l = 0; l < P.deq_levels; ++l) {
+                    const int b = P.qt.bits[l];
+                    const uint64_t w = load_codes8(P.qt.vq[l], (tbase * D + dd) * BN + oc * 8, b);
+                    const float4* sp = reinterpret_cast<const float4*>(
+                        P.qt.vs[l] + (tbase * G + dd / g) * BN + oc * 8);
+                    const float4 s0 = sp[0], s1 = sp[1];
+                    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) y[i] += (float)code_at(w, b, i) * sc[i];
+                }
+                bf16x8 v, vl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v[i] = (__bf16)y[i];
+                    if (X3) vl[i] = (__bf16)(y[i] - (float)v[i]);
+                }
+                *reinterpret_cast<bf16x8*>(&Vs[0][dd][oc * 8]) = v;
+                if (X3) *reinterpret_cast<bf16x8*>(&Vs[NP - 1][dd][oc * 8]) = vl;
+            }
+        } else {
+    #pragma unroll
+            for (int part = 0; part < NP; ++part) {
+                const __bf16* Kh = (part ? P.Kc_lo : P.Kc) + koff;
+                const __bf16* Vh = (part ? P.Vt_lo : P.Vt) + voff;
+    #pragma unroll
+                for (int m = 0; m < (BN * D / 8) / 256; ++m) {
+                    const int idx = tid + m * 256;
+                    const int key = idx / (D / 8), c8 = idx % (D / 8);
+                    *reinterpret_cast<uint4*>(&Ks[part][key][c8 * 8]) =
+                        *reinterpret_cast<const uint4*>(Kh + (long)(p0 + key) * D + c8 * 8);
+                    const int dd = idx / (BN / 8), oc = idx % (BN / 8);
+                    *reinterpret_cast<uint4*>(&Vs[part][dd][oc * 8]) =
+                        *reinterpret_cast<const uint4*>(Vh + ((long)(p0 / BN) * D + dd) * BN + oc * 8);
+                }
             }
         }
         if (tid < BN) cps[tid] = cpos_h[p0 + tid];
@@ -271,9 +410,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
                 s[kt] = mfma32(a, qf[kk], s[kt]);
                 if (X3) {
                     const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Ks[NP - 1][32 * kt + r][16 * kk + 8 * half]);
-                    s[kt] = mfma32(a, ql[X3 ? kk : 0], s[kt]);
                     s[kt] = mfma32(al, qf[kk], s[kt]);
                 }
+                if (QS) s[kt] = mfma32(a, ql[QS ? kk : 0], s[kt]);
             }
         }
         const bool need_mask = p0 + BN > p_full;
@@ -401,9 +540,11 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
 constexpr int CT = 128; // columns per workgroup (4 waves x 32)
 constexpr int RT = 32;  // query rows per step
 
-template <int D, bool X3>
+template <int D, int PREC>
 __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
-    constexpr int NP = X3 ? 2 : 1;
+    constexpr bool X3 = PREC >= 1;  // keys as hi + lo
+    constexpr bool QS = PREC == 2;  // queries as hi + lo
+    constexpr int NP = QS ? 2 : 1;
     __shared__ __bf16 Qs[NP][RT][D + 8];
     __shared__ int rpos[RT];
     __shared__ float rlse[RT], rw[RT];
@@ -446,10 +587,10 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v[i] = (__bf16)f[i];
-                if (X3) vl[i] = (__bf16)(f[i] - (float)v[i]);
+                if (QS) vl[i] = (__bf16)(f[i] - (float)v[i]);
             }
             *reinterpret_cast<bf16x8*>(&Qs[0][rr][c8 * 8]) = v;
-            if (X3) *reinterpret_cast<bf16x8*>(&Qs[NP - 1][rr][c8 * 8]) = vl;
+            if (QS) *reinterpret_cast<bf16x8*>(&Qs[NP - 1][rr][c8 * 8]) = vl;
         }
         if (tid < RT) {
             const int t = t0 + tid;
@@ -469,9 +610,9 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
         for (int kk = 0; kk < D / 16; ++kk) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qs[0][r][16 * kk + 8 * half]);
             s = mfma32(a, kf[kk], s);
-            if (X3) {
+            if (X3) s = mfma32(a, kl[X3 ? kk : 0], s);
+            if (QS) {
                 const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Qs[NP - 1][r][16 * kk + 8 * half]);
-                s = mfma32(a, kl[X3 ? kk : 0], s);
                 s = mfma32(al, kf[kk], s);
             }
         }
@@ -504,30 +645,44 @@ hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel
     return hipGetLastError();
 }
 
-hipError_t launch_attn(int d, int mode, bool x3, const AttnParams& P, hipStream_t st) {
+hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
+                           const QTiles& out, int32_t* cpos, hipStream_t st) {
+    dim3 grid(kp / BN, c.H);
+    if (c.d == 128)
+        hipLaunchKernelGGL(k_gather_q<128>, grid, dim3(256), 0, st, c, upto, sel, k, kp, out, cpos);
+    else
+        hipLaunchKernelGGL(k_gather_q<64>, grid, dim3(256), 0, st, c, upto, sel, k, kp, out, cpos);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st) {
     const int n_tiles = (P.n + BM - 1) / BM;
     AttnParams Q = P;
     Q.xcd_remap = (P.H % 8) == 0;
     dim3 grid(n_tiles * P.H);
-#define FL_ATTN(D_, M_, X_) hipLaunchKernelGGL((k_attn<D_, M_, X_>), grid, dim3(256), 0, st, Q)
-#define FL_ATTN_D(D_)                                                    \
-    if (mode == MODE_ATTN) { if (x3) FL_ATTN(D_, MODE_ATTN, true); else FL_ATTN(D_, MODE_ATTN, false); } \
-    else { if (x3) FL_ATTN(D_, MODE_REBUILD, true); else FL_ATTN(D_, MODE_REBUILD, false); }
+#define FL_ATTN(D_, M_, P_, Q_) hipLaunchKernelGGL((k_attn<D_, M_, P_, Q_>), grid, dim3(256), 0, st, Q)
+#define FL_ATTN_Q(D_, M_, P_) \
+    if (in_tile) FL_ATTN(D_, M_, P_, true); else FL_ATTN(D_, M_, P_, false);
+#define FL_ATTN_M(D_, M_) \
+    if (prec == 0) { FL_ATTN_Q(D_, M_, 0) } else if (prec == 1) { FL_ATTN_Q(D_, M_, 1) } else { FL_ATTN_Q(D_, M_, 2) }
+#define FL_ATTN_D(D_) \
+    if (mode == MODE_ATTN) { FL_ATTN_M(D_, MODE_ATTN) } else { FL_ATTN_M(D_, MODE_REBUILD) }
     if (d == 128) { FL_ATTN_D(128) } else { FL_ATTN_D(64) }
 #undef FL_ATTN_D
+#undef FL_ATTN_M
+#undef FL_ATTN_Q
 #undef FL_ATTN
     return hipGetLastError();
 }
 
-hipError_t launch_colstat(int d, bool x3, const ColParams& P, hipStream_t st) {
+hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
     dim3 grid((P.k + CT - 1) / CT, P.H);
-    if (d == 128) {
-        if (x3) hipLaunchKernelGGL((k_colstat<128, true>), grid, dim3(256), 0, st, P);
-        else hipLaunchKernelGGL((k_colstat<128, false>), grid, dim3(256), 0, st, P);
-    } else {
-        if (x3) hipLaunchKernelGGL((k_colstat<64, true>), grid, dim3(256), 0, st, P);
-        else hipLaunchKernelGGL((k_colstat<64, false>), grid, dim3(256), 0, st, P);
-    }
+#define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
+#define FL_COL_D(D_) \
+    if (prec == 0) FL_COL(D_, 0); else if (prec == 1) FL_COL(D_, 1); else FL_COL(D_, 2);
+    if (d == 128) { FL_COL_D(128) } else { FL_COL_D(64) }
+#undef FL_COL_D
+#undef FL_COL
     return hipGetLastError();
 }
 

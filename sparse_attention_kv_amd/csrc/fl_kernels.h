@@ -7,6 +7,23 @@
 
 namespace fl {
 
+// Compact quantised copies of the selected columns, one plane per cache level
+// (absent levels hold zero codes and scales):
+//   kq[l] [H][kp][d*bits/8]  codes, column-major rows as stored
+//   ks[l] [H][kp][d/g]       scales
+//   vq[l] [H][kp/64][d][64*bits/8]  codes transposed per 64-column tile, keys
+//                                    in the MFMA-operand order
+//   vs[l] [H][kp/64][d/g][64]        scales, same key order
+struct QTiles {
+    int n_levels;
+    int g;
+    int bits[FL_MAX_LEVELS];
+    uint8_t* kq[FL_MAX_LEVELS];
+    float* ks[FL_MAX_LEVELS];
+    uint8_t* vq[FL_MAX_LEVELS];
+    float* vs[FL_MAX_LEVELS];
+};
+
 struct AttnParams {
     int H, n, k, kp, dtype, q_gathered, cache_op;
     float c2;        // softmax scale * log2(e)
@@ -22,6 +39,8 @@ struct AttnParams {
     float* mass_u;
     float* out_u;
     int xcd_remap;
+    int deq_levels;        // in-tile dequantisation: levels 0..deq_levels-1 of q
+    QTiles qt;
 };
 
 struct ColParams {
@@ -51,10 +70,13 @@ hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const vo
                         const void* v_new, int gathered, hipStream_t st);
 // attn.hip
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
-                              bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
+                              bool split, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
                               int32_t* cpos, hipStream_t st);
-hipError_t launch_attn(int d, int mode, bool x3, const AttnParams& P, hipStream_t st);
-hipError_t launch_colstat(int d, bool x3, const ColParams& P, hipStream_t st);
+// prec: 0 bf16 operands, 1 K/V/P as hi+lo bf16 pairs, 2 also q (fp32 inputs)
+hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
+                           const QTiles& out, int32_t* cpos, hipStream_t st);
+hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st);
+hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st);
 // abi.hip
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
 

@@ -264,7 +264,7 @@ class LoopRunner:
         st.stat, st.out, st.lse = _p(self.stat), _p(self.out), _p(self.lse)
         st.mass_u, st.out_u = _p(self.mass_u), _p(self.out_u)
         self.state = st
-        ws_bytes = fl_workspace_size(FL_WS_LOOP_STEP, H, N, d, cfg.dtype)
+        ws_bytes = fl_workspace_size(FL_WS_LOOP_STEP, H, N, d, R)
         self.ws = buf((ws_bytes,), torch.uint8)
         self.inputs = FlLoopInputs()
 

@@ -78,11 +78,19 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def assert_close(got, want, what, rel=1e-2, mabs=3e-2):
+def assert_close(got, want, what, rel=1e-2, mabs=3e-2, ref_norm=None):
+    """rel-L2 (against ref_norm when given) and max-abs bounds."""
     got = np.asarray(got, np.float64); want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
-    e = rel_l2(got, want)
+    if ref_norm is None:
+        e = rel_l2(got, want)
+    else:
+        e = float(np.linalg.norm(got - want) / max(ref_norm, 1e-30))
     m = float(np.max(np.abs(got - want))) if got.size else 0.0
+    if not (e <= rel and m <= mabs):
+        idx = np.unravel_index(np.argmax(np.abs(got - want)), got.shape)
+        print(f"  {what}: worst at {idx}: got {got[idx]:.5f} want {want[idx]:.5f}; "
+              f"max |want| {np.abs(want).max():.3f}", flush=True)
     assert e <= rel and m <= mabs, f"{what}: rel-L2 {e:.3e} (<= {rel}), max-abs {m:.3e} (<= {mabs})"
     return e, m
 
@@ -132,7 +140,10 @@ def compare_chain(w, gres, ores, bits=None, check_codes=True):
         e_l = assert_close(g["lse"], o["lse"], f"loop {r} lse")
         assert_close(g["mass_u"], o["mass_u"], f"loop {r} mass_u", mabs=3e-2)
         if o["out_u"] is not None:
-            assert_close(g["out_u"], o["out_u"], f"loop {r} out_u")
+            # O_U adds straight into the output: bounded like the output
+            # (max-abs, and L2 error relative to the output's norm)
+            assert_close(g["out_u"], o["out_u"], f"loop {r} out_u",
+                         ref_norm=float(np.linalg.norm(o["out"])))
         if o["cstat"] is not None:
             assert g["cstat"] is not None
             assert_close_scaled(g["cstat"], o["cstat"], f"loop {r} cstat")

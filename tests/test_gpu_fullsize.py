@@ -1,0 +1,147 @@
+"""Full-size parity at the measured workload (prefill32k: N=32768, 16x128,
+R=4, fractions 1/.4/.2/.1, k=2048, int8/int4/int2), in the launch
+configuration bench.py times.
+
+The oracle cannot run the whole step at this size, so it checks:
+  * every index set and code in full (statistic, top-k from the GPU's own
+    statistic, quantised codes and scales of every level, column sets from
+    the GPU's own column statistics);
+  * loop-1 column statistics at sampled columns (summed over all rows with
+    the GPU's lse, whose rows are themselves checked);
+  * attention outputs, lse and the pruned-column caches at sampled rows,
+    recomputed by the oracle along each row's own recursion (dense loop 1,
+    cache rebuild at loop 2, carried caches at loops 3-4);
+  * properties at every row: conservation 0 <= M_U <= 1, lse finite.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_kv_amd import fl, synth
+
+from gpu_chain import assert_close, assert_close_scaled, counts, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.timeout(900)
+def test_prefill32k_sampled():
+    w = synth.WORKLOADS["prefill32k"]
+    _say("full-size", w.name, "N", w.N)
+    inp = synth.generate(w)
+    x = synth.as_f32_inputs(inp)
+    dev = {k: [to_dev(a, "bf16") for a in inp[k]] for k in ("h", "q", "k", "v")}
+    n_act = counts(w)
+    run = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, w.bits)
+    N, H, d, g = w.N, w.H, w.d, w.g
+    sm = np.float32(1 / np.sqrt(d))
+    G = {}
+    for r in range(1, w.R + 1):
+        run.step(r, dev["h"][r - 1], dev["h"][r - 2] if r > 1 else None, dev["q"][r - 1],
+                 dev["k"][r - 1], dev["v"][r - 1], dev["q"][r - 2] if r > 1 else None)
+        torch.cuda.synchronize()
+        rec = dict(active=run.active[r - 1].cpu().numpy(), kcols=run.k_used(r))
+        sel = run.sel_used(r)
+        rec["sel"] = None if sel is None else sel.cpu().numpy()
+        if r > 1:
+            rec["stat"] = run.stat[: n_act[r - 2]].cpu().numpy().copy()
+            rec["slot"] = run.slot[r - 1].cpu().numpy()
+        if r < w.R and w.kcols[r] < rec["kcols"]:
+            rec["cstat"] = run.col_stat[r - 1][:, : rec["kcols"]].cpu().numpy().copy()
+        cb = run.codes[r - 1]
+        for key in ("k", "v", "ks", "vs"):
+            rec["codes_" + key] = cb[key].cpu().numpy()
+        rec["out"] = run.out.cpu().numpy()
+        rec["lse"] = run.lse.cpu().numpy()
+        rec["mass_u"] = run.mass_u.cpu().numpy()
+        rec["out_u"] = run.out_u.cpu().numpy()
+        G[r] = rec
+        _say(f"  gpu loop {r} done: n={len(rec['active'])} k={rec['kcols']}")
+
+    # ---- index sets and codes, in full ----
+    khat = vhat = None
+    A_prev = np.arange(N, dtype=np.int32)
+    K = {}
+    for r in range(1, w.R + 1):
+        g_ = G[r]
+        if r == 1:
+            np.testing.assert_array_equal(g_["active"], A_prev)
+            ck, sk, _, khat = oracle.quantize_rows(x["k"][0], None, g, w.bits[0])
+            cv, sv, _, vhat = oracle.quantize_rows(x["v"][0], None, g, w.bits[0])
+        else:
+            stat = oracle.delta_norm(x["h"][r - 1], x["h"][r - 2], A_prev)
+            np.testing.assert_allclose(g_["stat"], stat, rtol=1e-5)
+            A = oracle.top_select(g_["stat"], n_act[r - 1], A_prev)
+            np.testing.assert_array_equal(g_["active"], A, err_msg=f"loop {r} active")
+            ck, sk, _, kr = oracle.quantize_rows(x["k"][r - 1][A], khat[A], g, w.bits[r - 1])
+            cv, sv, _, vr = oracle.quantize_rows(x["v"][r - 1][A], vhat[A], g, w.bits[r - 1])
+            khat = khat.copy(); khat[A] = kr
+            vhat = vhat.copy(); vhat[A] = vr
+            if "cstat" in G[r - 1]:
+                S = oracle.select_columns(G[r - 1]["cstat"], G[r - 1]["sel"], w.kcols[r - 1], w.n_sink)
+                np.testing.assert_array_equal(g_["sel"], S, err_msg=f"loop {r} columns")
+            A_prev = A
+        np.testing.assert_array_equal(g_["codes_k"], oracle.pack_codes(ck, w.bits[r - 1]))
+        np.testing.assert_array_equal(g_["codes_v"], oracle.pack_codes(cv, w.bits[r - 1]))
+        np.testing.assert_array_equal(g_["codes_ks"].view(np.uint32), sk.view(np.uint32))
+        np.testing.assert_array_equal(g_["codes_vs"].view(np.uint32), sv.view(np.uint32))
+        K[r] = (khat, vhat)
+        _say(f"  loop {r}: index sets and codes bit-exact")
+
+    # ---- sampled rows, each along its own recursion ----
+    rng = np.random.default_rng(0)
+    A4 = G[4]["active"]
+    rows = {1: np.sort(np.concatenate([rng.choice(A4, 24, replace=False),
+                                       rng.choice(N, 24, replace=False), [0, 1, 2, 5, N - 1]]))}
+    rows[1] = np.unique(rows[1]).astype(np.int32)
+    for r in range(2, w.R + 1):
+        rows[r] = rows[1][np.isin(rows[1], G[r]["active"])]
+    assert len(rows[4]) >= 24
+    mu = ou = None
+    lse_prev = None
+    for r in range(1, w.R + 1):
+        kh, vh = K[r]
+        rr = rows[r]
+        sel = G[r]["sel"]
+        if r == 1:
+            o, l = oracle.attend(x["q"][0], kh, vh, rr, None, sm)
+            mu_r = np.zeros((len(rr), H), np.float32); ou_r = np.zeros((len(rr), H, d), np.float32)
+        else:
+            keep = np.isin(rows[r - 1], rr)
+            if G[r]["kcols"] < G[r - 1]["kcols"]:
+                khp, vhp = K[r - 1]
+                mu_r, ou_r = oracle.unselected_cache(
+                    x["q"][r - 2], khp, vhp, rr, G[r - 1]["sel"], sel, lse_prev[keep], sm,
+                    None if r == 2 else mu[keep], None if r == 2 else ou[keep])
+            else:
+                mu_r, ou_r = mu[keep], ou[keep]
+            o, l = oracle.attend(x["q"][r - 1], kh, vh, rr, sel, sm, mu_r, ou_r)
+        e = assert_close(G[r]["out"][rr], o, f"loop {r} out (sampled {len(rr)} rows)")
+        assert_close(G[r]["lse"][rr], l, f"loop {r} lse")
+        if r > 1:
+            assert_close(G[r]["mass_u"][rr], mu_r, f"loop {r} mass_u")
+            assert_close(G[r]["out_u"][rr], ou_r, f"loop {r} out_u", ref_norm=float(np.linalg.norm(o)))
+        # properties at every active row
+        act = G[r]["active"]
+        assert np.all(np.isfinite(G[r]["lse"][act]))
+        m_all = G[r]["mass_u"][act]
+        assert np.all((m_all >= -1e-4) & (m_all <= 1 + 1e-4))
+        _say(f"  loop {r}: sampled out rel-L2 {e[0]:.2e} max-abs {e[1]:.2e} "
+             f"(max |o| {np.abs(o).max():.2f})")
+        mu, ou, lse_prev = mu_r, ou_r, l
+
+    # ---- loop-1 column statistics at sampled columns (all rows, GPU lse) ----
+    cols = np.stack([np.sort(np.concatenate([np.arange(4), rng.choice(np.arange(4, N), 12, replace=False),
+                                             [N - 1]])) for _ in range(H)]).astype(np.int32)
+    c = oracle.column_stats(x["q"][0], K[1][0], None, cols, G[1]["lse"], sm)
+    got = np.take_along_axis(G[1]["cstat"], cols, axis=1)
+    assert_close_scaled(got, c, "loop 1 column statistics (sampled columns)")
+    _say("  loop 1 column statistics ok")

@@ -162,25 +162,32 @@ def test_tiny_workload_full():
     _chain(synth.WORKLOADS["tiny"])
 
 
-def test_layer_recipe_pruning_ragged():
+@pytest.mark.parametrize("mode", [fl.FL_DEQ_ONCE, fl.FL_DEQ_IN_TILE])
+def test_layer_recipe_pruning_ragged(mode):
     """Ouro-class layer recipe at N=1000 (ragged tiles), 8 heads (XCD-mapped
     grid), decreasing column budgets: cache rebuild at loops 2, 3 and 4 and
     column statistics at loops 1-3."""
     w = synth.WORKLOADS["layer4k"].scaled(N=1000, H=8, kcols=[1000, 300, 150, 100])
-    _chain(w)
+    _chain(w, mode=mode)
 
 
-def test_prefill_recipe_small():
+@pytest.mark.parametrize("mode", [fl.FL_DEQ_ONCE, fl.FL_DEQ_IN_TILE])
+def test_prefill_recipe_small(mode):
     """32K-prefill recipe (fractions 1/.4/.2/.1, int4 then int2 residuals) at
-    N=2048, 8 heads, 256 columns."""
+    N=2048, 8 heads, 256 columns; both dequantisation placements."""
     w = synth.WORKLOADS["prefill32k"].scaled(N=2048, H=8, kcols=[2048, 256, 256, 256])
-    _chain(w)
+    _chain(w, mode=mode)
 
 
-def test_head_dim_64_group_32():
+@pytest.mark.parametrize("mode", [fl.FL_DEQ_ONCE, fl.FL_DEQ_IN_TILE])
+def test_head_dim_64_group_32(mode):
     w = synth.WORKLOADS["layer4k"].scaled(N=640, H=3, d=64, g=32, kcols=[640, 200, 120, 120],
                                           bits=[8, 4, 2, 4])
-    _chain(w)
+    _chain(w, mode=mode)
+
+
+def test_tiny_in_tile():
+    _chain(synth.WORKLOADS["tiny"], mode=fl.FL_DEQ_IN_TILE)
 
 
 def test_dense_reduction_raw():
