@@ -185,7 +185,7 @@ int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const v
  * dense first loop.
  */
 enum fl_attn_mode {
-    FL_DEQ_AUTO = 0,    /* library choice                                      */
+    FL_DEQ_AUTO = 0,    /* library choice (currently FL_DEQ_ONCE, the faster)  */
     FL_DEQ_ONCE = 1,    /* dequantise the selected columns once per head into a
                            compact bf16 buffer, then stream it per tile        */
     FL_DEQ_IN_TILE = 2  /* gather quantised codes compactly, dequantise inside
