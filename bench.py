@@ -150,15 +150,22 @@ def main():
     lazy_tokens = sum(n_act[1:])
 
     # ---- roofline of the dominant kernel ----
-    flops_step = {"attn": sum(4.0 * d * L["pairs"] for L in loops),
-                  "attn_rebuild": sum(4.0 * d * L["pairs"] for L in loops if L["rebuilt"]),
-                  "colstat": sum(2.0 * d * L["pairs"] for L in loops if L["colstat"])}
+    # kernel instantiations: plain bf16 operands at loop 1 (no residual
+    # levels), hi/lo split operands at loops >= 2 ("_split")
+    def fl_sum(pred, per_pair):
+        return sum(per_pair * d * L["pairs"] for L in loops if pred(L))
+    flops_step = {"attn": fl_sum(lambda L: L["r"] == 1, 4.0),
+                  "attn_split": fl_sum(lambda L: L["r"] > 1, 4.0),
+                  "attn_rebuild": fl_sum(lambda L: L["rebuilt"] and L["r"] == 2, 4.0),
+                  "attn_rebuild_split": fl_sum(lambda L: L["rebuilt"] and L["r"] > 2, 4.0),
+                  "colstat": fl_sum(lambda L: L["colstat"] and L["r"] == 1, 2.0),
+                  "colstat_split": fl_sum(lambda L: L["colstat"] and L["r"] > 1, 2.0)}
     kernels = {}
     for name, (cnt, ms) in ktab.items():
         per_step_ms = ms / args.steps
         e = dict(launches_per_step=cnt / args.steps, ms_per_step=round(per_step_ms, 4),
                  avg_launch_us=round(1e3 * ms / max(cnt, 1), 2))
-        if name in flops_step and ms > 0:
+        if name in flops_step and ms > 0 and flops_step[name] > 0:
             e["tflops"] = round(flops_step[name] / (per_step_ms / 1e3) / 1e12, 2)
         kernels[name] = e
     roofline = None

@@ -92,9 +92,9 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
     if (!g_timing) return f();
     std::lock_guard<std::mutex> lk(g_tmu);
     hipEvent_t a = ev_get(), b = ev_get();
-    if (a) hipEventRecord(a, st);
+    if (a) (void)hipEventRecord(a, st);
     const hipError_t e = f();
-    if (b) hipEventRecord(b, st);
+    if (b) (void)hipEventRecord(b, st);
     if (a && b) g_recs.push_back({name, a, b});
     return e;
 }
@@ -338,13 +338,16 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
             R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
         }
         R.q = a->q_prev; R.q_gathered = a->q_prev_gathered;
-        FL_HIP(timed("attn_rebuild", st,
+        FL_HIP(timed(prec_old ? "attn_rebuild_split" : "attn_rebuild", st,
                      [&] { return fl::launch_attn(d, fl::MODE_REBUILD, prec_old, in_tile, R, st); }),
                "attn(rebuild)");
     }
     P.q = a->q; P.q_gathered = a->q_gathered; P.Kc = Kc; P.Vt = Vt; P.Kc_lo = Kl; P.Vt_lo = Vl;
     P.deq_levels = a->level + 1;
-    FL_HIP(timed("attn", st, [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),
+    // timing names follow the kernel instantiation: bf16 operands ("attn",
+    // the dense first loop) and hi/lo split operands ("attn_split")
+    FL_HIP(timed(prec ? "attn_split" : "attn", st,
+                 [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),
            "attn");
     if (a->col_stat) {
         if (in_tile) // the statistics sweep reads the keys as compact bf16
@@ -358,7 +361,9 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
         C.cache_op = a->cache_op == FL_CACHE_ZERO ? FL_CACHE_ZERO : FL_CACHE_CARRY;
         C.c2 = c2; C.q = a->q; C.active = a->active; C.Kc = Kc; C.Kc_lo = Kl; C.cpos = cpos;
         C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat;
-        FL_HIP(timed("colstat", st, [&] { return fl::launch_colstat(d, prec, C, st); }), "colstat");
+        FL_HIP(timed(prec ? "colstat_split" : "colstat", st,
+                     [&] { return fl::launch_colstat(d, prec, C, st); }),
+               "colstat");
     }
     return FL_OK;
 }
