@@ -96,7 +96,8 @@ enum fl_ws_op {
     FL_WS_SELECT_ACTIVE = 1,  /* a = n_cand                                    */
     FL_WS_SELECT_COLUMNS = 2, /* a = H, b = n_cand                             */
     FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = cache levels used (level+1; <= 0: max) */
-    FL_WS_LOOP_STEP = 4       /* a = H, b = N (largest k), c = d, e = R        */
+    FL_WS_LOOP_STEP = 4,      /* a = H, b = N (largest k), c = d, e = R        */
+    FL_WS_BLOCK_STEP = 5      /* a = N, b = H, c = d, e = ffn width            */
 };
 size_t fl_workspace_size(int op, long a, long b, long c, long e);
 
@@ -269,6 +270,69 @@ typedef struct fl_loop_inputs {
 
 int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* st, const fl_loop_inputs* in, int r,
                  void* ws, size_t ws_bytes, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_block_step -- one loop r of a whole looped block of n_layers
+ * pre-norm Transformer layers (paper Sec. 4.1: the block computes only the
+ * active tokens, inactive tokens keep their states and reuse their K/V;
+ * Sec. 4.4: active tokens are gathered into compact buffers so the
+ * projections stay regular GEMMs).  Per loop r: (r >= 2) the token statistic
+ * ||h - h_entry|| over the previous active set and the nested top-n_active[r-1]
+ * selection; then for every layer, on the active rows only:
+ *   a = RMSNorm(h) * norm1;  [q k v] = a W_qkv^T;  RoPE(q, k) at the token
+ *   positions (theta = rope_theta, rotate-half);  residual level r-1 of the
+ *   layer's K/V cache (keys after RoPE);  column selection, cache rebuild and
+ *   sparse attention exactly as fl_loop_step;  h += attn W_o^T;
+ *   b = RMSNorm(h) * norm2;  h += (silu(b W_g^T) * (b W_u^T)) W_down^T.
+ * RMSNorm(x) = x / sqrt(mean(x^2) + norm_eps).  GEMMs are bf16 MFMA with fp32
+ * accumulation; the residual stream h is fp32.  Loop 1 runs every token and
+ * dense attention.  h_entry receives a copy of h at the start of every loop.
+ * Weights (bf16, output-major [out][in]): w_qkv [3D][D] (q rows, then k, then
+ * v), w_o [D][D], w_gu [2F][D] with row 2j the gate and row 2j+1 the up
+ * projection of hidden unit j, w_down [D][F]; norm1/norm2 [D].
+ * Requirements: D = H*d a multiple of 128, F a multiple of 128 (and of 32).
+ * Workspace: fl_workspace_size(FL_WS_BLOCK_STEP, N, H, d, F).
+ */
+typedef struct fl_block_cfg {
+    int N, H, d, g, R, n_sink;
+    int n_layers, ffn;
+    float rope_theta, norm_eps;
+    int n_active[FL_MAX_LEVELS];
+    int k_cols[FL_MAX_LEVELS];
+    int bits[FL_MAX_LEVELS];
+    int mode;               /* fl_attn_mode */
+} fl_block_cfg;
+
+typedef struct fl_layer_weights {
+    const void* w_qkv;
+    const void* w_o;
+    const void* w_gu;
+    const void* w_down;
+    const void* norm1;
+    const void* norm2;
+} fl_layer_weights;
+
+typedef struct fl_layer_state {
+    fl_kv_cache cache;      /* level buffers pre-allocated by the caller        */
+    void* q_state;          /* bf16 [N][H][d]: latest queries per token         */
+    float* out; float* lse; float* mass_u; float* out_u; /* as fl_loop_state   */
+    int32_t* sel[FL_MAX_LEVELS];
+    const int32_t* sel_used[FL_MAX_LEVELS];
+    int k_cur[FL_MAX_LEVELS];
+    float* col_stat[FL_MAX_LEVELS];
+} fl_layer_state;
+
+typedef struct fl_block_state {
+    float* h;               /* fp32 [N][D] residual stream                      */
+    float* h_entry;         /* fp32 [N][D] h at the entry of the previous loop   */
+    int32_t* active[FL_MAX_LEVELS]; /* [n_active[r-1]] per loop (active[0]: iota) */
+    int32_t* slot[FL_MAX_LEVELS];   /* [N] per loop r >= 2                      */
+    float* stat;            /* [N]                                              */
+    fl_layer_state* layers; /* host array [n_layers]                            */
+} fl_block_state;
+
+int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_state* st, int r,
+                  void* ws, size_t ws_bytes, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later

@@ -60,6 +60,15 @@ long attn_ws_bytes(long H, long k, long d, long levels) {
            kAlign;
 }
 
+// workspace of fl_block_step: compact bf16 activations of the active rows
+// (normed input, qkv, q/k/v, attention output, SwiGLU output) followed by the
+// attention workspace.
+long block_ws_bytes(long N, long H, long d, long F) {
+    const long D = H * d;
+    return align_up(N * D * 2) * 5 + align_up(N * 3 * D * 2) + align_up(N * F * 2) +
+           attn_ws_bytes(H, N, d, FL_MAX_LEVELS) + kAlign;
+}
+
 // Operand precision of the attention products: residual levels hold the
 // cross-loop updates, which sit below bf16's resolution of the summed value,
 // so a cache with residual levels feeds K, V and P as hi + lo bf16 pairs;
@@ -138,6 +147,9 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     switch (op) {
     case FL_WS_SELECT_ACTIVE: return a > 0 ? (size_t)kAlign : 0;
     case FL_WS_SELECT_COLUMNS: return (a > 0 && b > 0) ? (size_t)kAlign : 0;
+    case FL_WS_BLOCK_STEP:
+        if (a <= 0 || b <= 0 || !(c == 64 || c == 128) || e <= 0) return 0;
+        return (size_t)block_ws_bytes(a, b, c, e);
     case FL_WS_SPARSE_ATTN:
     case FL_WS_LOOP_STEP:
         if (a <= 0 || b <= 0 || !(c == 64 || c == 128)) return 0;
@@ -241,7 +253,6 @@ int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const v
     if (rc) return rc;
     FL_REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
     FL_REQUIRE(k_new && v_new, "k_new/v_new NULL");
-    FL_REQUIRE(!(level == 0 && new_gathered), "level 0 takes all N rows by position");
     hipStream_t st = (hipStream_t)stream;
     FL_HIP(timed("kv_quant", st, [&] {
                return fl::launch_quant(*cache, level, dtype, k_new, v_new, new_gathered, st);
@@ -440,6 +451,144 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
     A.col_stat = need_c ? S->col_stat[r - 1] : nullptr;
     FL_REQUIRE(!need_c || A.col_stat, "col_stat[%d] buffer NULL", r - 1);
     return fl_sparse_loop_attn(&C, &A, ws, ws_bytes, stream);
+}
+
+int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_state* S, int r,
+                  void* ws, size_t ws_bytes, fl_stream_t stream) {
+    FL_REQUIRE(cfg && W && S && S->layers, "cfg/weights/state NULL");
+    FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
+    const int N = cfg->N, H = cfg->H, d = cfg->d, D = H * d, F = cfg->ffn, L = cfg->n_layers;
+    FL_REQUIRE(N > 0 && L >= 1, "N=%d layers=%d", N, L);
+    if (!(d == 64 || d == 128)) return fail(FL_ERR_UNSUPPORTED, "head dim %d", d);
+    if (D % 128 || F % 128) return fail(FL_ERR_UNSUPPORTED, "D=%d and ffn=%d must be multiples of 128", D, F);
+    FL_REQUIRE(S->h && S->h_entry && S->stat, "h/h_entry/stat NULL");
+    const long need = block_ws_bytes(N, H, d, F);
+    if (!ws || (long)ws_bytes < need)
+        return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
+    hipStream_t st = (hipStream_t)stream;
+    char* p = (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+    auto take = [&](long bytes) { char* q = p; p += align_up(bytes); return q; };
+    __bf16* a_buf = (__bf16*)take((long)N * D * 2);
+    __bf16* qc = (__bf16*)take((long)N * D * 2);
+    __bf16* kc = (__bf16*)take((long)N * D * 2);
+    __bf16* vc = (__bf16*)take((long)N * D * 2);
+    __bf16* attn_in = (__bf16*)take((long)N * D * 2);
+    __bf16* qkv = (__bf16*)take((long)N * 3 * D * 2);
+    __bf16* act_buf = (__bf16*)take((long)N * F * 2);
+    void* aws = p;
+    const size_t aws_bytes = (size_t)attn_ws_bytes(H, N, d, FL_MAX_LEVELS);
+
+    // ---- the loop's active tokens (Sec. 4.1) ----
+    int n;
+    if (r == 1) {
+        FL_REQUIRE(S->active[0] != nullptr, "active[0] (iota buffer) NULL");
+        FL_HIP(fl::launch_copy_or_iota(nullptr, S->active[0], N, N, st), "iota");
+        n = N;
+    } else {
+        const int n_prev = r == 2 ? N : cfg->n_active[r - 2];
+        n = cfg->n_active[r - 1];
+        FL_REQUIRE(n >= 1 && n <= n_prev, "n_active[%d] = %d (prev %d)", r - 1, n, n_prev);
+        FL_REQUIRE(S->active[r - 1] && S->slot[r - 1], "active/slot buffers NULL");
+        int rc = fl_select_active(FL_F32, S->h, S->h_entry, N, D, S->active[r - 2], n_prev, n, nullptr,
+                                  S->stat, S->active[r - 1], S->slot[r - 1], nullptr, 0, stream);
+        if (rc) return rc;
+    }
+    const int32_t* act = S->active[r - 1];
+    FL_HIP(hipMemcpyAsync(S->h_entry, S->h, (size_t)N * D * 4, hipMemcpyDeviceToDevice, st), "copy");
+
+    const float sm = 1.0f / sqrtf((float)d);
+    for (int l = 0; l < L; ++l) {
+        const fl_layer_weights& w = W[l];
+        fl_layer_state& Ls = S->layers[l];
+        FL_REQUIRE(w.w_qkv && w.w_o && w.w_gu && w.w_down && w.norm1 && w.norm2, "layer %d weights NULL", l);
+        FL_REQUIRE(Ls.q_state && Ls.out && Ls.lse && Ls.mass_u && Ls.out_u, "layer %d state NULL", l);
+        fl_kv_cache& C = Ls.cache;
+        FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "layer %d cache dims", l);
+        // attention sub-block on the active rows
+        FL_HIP(timed("rmsnorm", st, [&] {
+                   return fl::launch_rmsnorm_gather(S->h, act, n, D, (const __bf16*)w.norm1,
+                                                    cfg->norm_eps, a_buf, st);
+               }), "rmsnorm");
+        fl::GemmParams G{};
+        G.M = n; G.N = 3 * D; G.K = D; G.A = a_buf; G.lda = D; G.B = (const __bf16*)w.w_qkv;
+        G.Cb = qkv; G.ldc = 3 * D;
+        FL_HIP(timed("gemm_qkv", st, [&] { return fl::launch_gemm(fl::EPI_STORE, G, st); }), "gemm");
+        FL_HIP(timed("rope", st, [&] {
+                   return fl::launch_rope_split(qkv, act, n, H, d, cfg->rope_theta, qc, kc, vc, st);
+               }), "rope");
+        // K/V cache level of this loop (keys after RoPE)
+        if (r == 1) {
+            C.level[0].bits = cfg->bits[0];
+            C.level[0].n_rows = N;
+            C.level[0].rows = nullptr;
+            C.level[0].slot = nullptr;
+            C.n_levels = 1;
+            FL_HIP(fl::launch_fill_f32(Ls.mass_u, (long)N * H, 0.0f, st), "fill");
+            FL_HIP(fl::launch_fill_f32(Ls.out_u, (long)N * H * d, 0.0f, st), "fill");
+        } else {
+            fl_kv_level& Lv = C.level[r - 1];
+            Lv.bits = cfg->bits[r - 1];
+            Lv.n_rows = n;
+            Lv.rows = act;
+            Lv.slot = S->slot[r - 1];
+            C.n_levels = r;
+        }
+        int rc = fl_kv_residual_quant(&C, r - 1, FL_BF16, kc, vc, 1, stream);
+        if (rc) return rc;
+        fl_attn_args A{};
+        A.dtype = FL_BF16; A.q = qc; A.q_gathered = 1; A.active = act; A.n = n; A.sm = sm;
+        A.level = r - 1; A.mode = cfg->mode;
+        A.out = Ls.out; A.lse = Ls.lse; A.mass_u = Ls.mass_u; A.out_u = Ls.out_u;
+        A.q_prev = Ls.q_state; A.q_prev_gathered = 0;
+        if (r == 1) {
+            Ls.k_cur[0] = N;
+            Ls.sel_used[0] = nullptr;
+            A.sel = nullptr; A.k = N; A.cache_op = FL_CACHE_ZERO;
+            A.col_stat = (cfg->R > 1 && cfg->k_cols[1] < N) ? Ls.col_stat[0] : nullptr;
+        } else {
+            const int k_prev = Ls.k_cur[r - 2], k_r = cfg->k_cols[r - 1];
+            bool changed = false;
+            if (k_prev <= k_r) {
+                Ls.k_cur[r - 1] = k_prev;
+                Ls.sel_used[r - 1] = Ls.sel_used[r - 2];
+            } else {
+                FL_REQUIRE(Ls.sel[r - 1] && Ls.col_stat[r - 2], "layer %d sel/col_stat buffers NULL", l);
+                rc = fl_select_columns(Ls.col_stat[r - 2], Ls.sel_used[r - 2], H, k_prev, cfg->n_sink,
+                                       k_r, Ls.sel[r - 1], nullptr, 0, stream);
+                if (rc) return rc;
+                Ls.k_cur[r - 1] = k_r;
+                Ls.sel_used[r - 1] = Ls.sel[r - 1];
+                changed = true;
+            }
+            A.sel = Ls.sel_used[r - 1]; A.k = Ls.k_cur[r - 1];
+            A.cache_op = changed ? FL_CACHE_REBUILD : FL_CACHE_CARRY;
+            const bool need_c = r < cfg->R && cfg->k_cols[r] < Ls.k_cur[r - 1];
+            A.col_stat = need_c ? Ls.col_stat[r - 1] : nullptr;
+            FL_REQUIRE(!need_c || A.col_stat, "layer %d col_stat[%d] NULL", l, r - 1);
+        }
+        rc = fl_sparse_loop_attn(&C, &A, aws, aws_bytes, stream);
+        if (rc) return rc;
+        FL_HIP(fl::launch_scatter_rows_bf16(qc, act, n, D, (__bf16*)Ls.q_state, st), "scatter");
+        FL_HIP(fl::launch_rows_f32_to_bf16(Ls.out, act, n, D, attn_in, st), "gather");
+        G = fl::GemmParams{};
+        G.M = n; G.N = D; G.K = D; G.A = attn_in; G.lda = D; G.B = (const __bf16*)w.w_o;
+        G.Cf = S->h; G.ldc = D; G.rows = act;
+        FL_HIP(timed("gemm_o", st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
+        // MLP sub-block
+        FL_HIP(timed("rmsnorm", st, [&] {
+                   return fl::launch_rmsnorm_gather(S->h, act, n, D, (const __bf16*)w.norm2,
+                                                    cfg->norm_eps, a_buf, st);
+               }), "rmsnorm");
+        G = fl::GemmParams{};
+        G.M = n; G.N = 2 * F; G.K = D; G.A = a_buf; G.lda = D; G.B = (const __bf16*)w.w_gu;
+        G.Cb = act_buf; G.ldc = F;
+        FL_HIP(timed("gemm_gate_up", st, [&] { return fl::launch_gemm(fl::EPI_SWIGLU, G, st); }), "gemm");
+        G = fl::GemmParams{};
+        G.M = n; G.N = D; G.K = F; G.A = act_buf; G.lda = F; G.B = (const __bf16*)w.w_down;
+        G.Cf = S->h; G.ldc = D; G.rows = act;
+        FL_HIP(timed("gemm_down", st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
+    }
+    return FL_OK;
 }
 
 } // extern "C"

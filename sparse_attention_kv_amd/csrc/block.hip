@@ -1,0 +1,236 @@
+// Token-sparse looped block (FlashLoop paper, Sec. 4.1 "the looped
+// Transformer block performs computation only on the selected active
+// tokens"; Sec. 4.4 "gathering selected tokens ... into compact,
+// compute-friendly buffers to preserve regular GEMM execution").
+//
+//   k_rmsnorm_gather  active rows of the fp32 residual stream -> RMSNorm ->
+//                     compact bf16 [n][D] (the gather is fused into the norm)
+//   k_gemm<EPI>       C = A[M][K] . W[N][K]^T, bf16 MFMA 32x32x16 with fp32
+//                     accumulation; 128x128 output tile per workgroup (4 waves
+//                     of 64x64), 32-deep K tiles in a two-buffer LDS pipeline.
+//                     Epilogues: bf16 store; residual scatter-add into the fp32
+//                     stream at the active rows; SwiGLU on interleaved
+//                     (gate, up) column pairs.
+//   k_rope_split      [n][3D] bf16 -> q, k, v [n][H][d] bf16 with rotary
+//                     position embedding (rotate-half) on q and k at the rows'
+//                     token positions (keys are quantised after RoPE).
+//   k_rows_f32_to_bf16, k_scatter_rows_bf16: row gather / scatter helpers.
+#include "fl_device.h"
+#include "fl_kernels.h"
+
+namespace fl {
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm_gather(const float* __restrict__ x,
+                                                        const int32_t* __restrict__ rows, int D,
+                                                        const __bf16* __restrict__ w, float eps,
+                                                        __bf16* __restrict__ out) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const long row = rows ? rows[m] : m;
+    const float* xr = x + row * D;
+    float ss = 0.0f;
+    for (int c = threadIdx.x * 4; c < D; c += 256 * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + c);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float inv = rsqrtf(tot / (float)D + eps);
+    __bf16* o = out + (long)m * D;
+    for (int c = threadIdx.x * 4; c < D; c += 256 * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + c);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[c + i] = (__bf16)(vv[i] * inv * (float)w[c + i]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int GBM = 128, GBN = 128, GBK = 32;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmParams G) {
+    __shared__ __bf16 As[2][GBM][GBK + 8];
+    __shared__ __bf16 Bs[2][GBN][GBK + 8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 31, half = lane >> 5;
+    const int wm = w >> 1, wn = w & 1;
+    const int n0 = blockIdx.x * GBN;
+    const int m0 = blockIdx.y * GBM;
+    // 16-byte chunks: 128 rows x 4 chunks per tile for A and for B
+    uint4 ar[2], br[2];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int idx = tid + c * 256;
+            const int row = idx >> 2, ch = (idx & 3) * 8;
+            const int m = m0 + row;
+            ar[c] = m < G.M ? *reinterpret_cast<const uint4*>(G.A + (long)m * G.lda + k0 + ch)
+                            : make_uint4(0u, 0u, 0u, 0u);
+            br[c] = *reinterpret_cast<const uint4*>(G.B + (long)(n0 + row) * G.K + k0 + ch);
+        }
+    };
+    auto lstore = [&](int b) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int idx = tid + c * 256;
+            const int row = idx >> 2, ch = (idx & 3) * 8;
+            *reinterpret_cast<uint4*>(&As[b][row][ch]) = ar[c];
+            *reinterpret_cast<uint4*>(&Bs[b][row][ch]) = br[c];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int nk = G.K / GBK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int b = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) gload((kt + 1) * GBK);
+#pragma unroll
+        for (int ks = 0; ks < GBK / 16; ++ks) {
+            bf16x8 a[2], bb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(&As[b][wm * 64 + 32 * i + r][ks * 16 + 8 * half]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *reinterpret_cast<const bf16x8*>(&Bs[b][wn * 64 + 32 * j + r][ks * 16 + 8 * half]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
+        }
+        if (more) lstore(b ^ 1);
+        __syncthreads();
+    }
+    // acc[i][j][e]: row m0 + wm*64 + 32i + (e/4)*8 + half*4 + e%4, col n0 + wn*64 + 32j + r
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + 32 * j + r;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm * 64 + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
+                const float v = acc[i][j][e];
+                if (EPI == EPI_SWIGLU) {
+                    const float u = __shfl_xor(v, 1); // (gate, up) column pair
+                    if (m < G.M && (r & 1) == 0) {
+                        const float sg = v / (1.0f + __expf(-v));
+                        G.Cb[(long)m * G.ldc + (n >> 1)] = (__bf16)(sg * u);
+                    }
+                } else if (m < G.M) {
+                    if (EPI == EPI_STORE) {
+                        G.Cb[(long)m * G.ldc + n] = (__bf16)v;
+                    } else { // EPI_RESID: residual stream += C at the active row
+                        const long row = G.rows ? G.rows[m] : m;
+                        G.Cf[row * G.ldc + n] += v;
+                    }
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rope_split(const __bf16* __restrict__ qkv,
+                                                    const int32_t* __restrict__ rows, int n, int H,
+                                                    int d, float log2_theta, __bf16* __restrict__ q,
+                                                    __bf16* __restrict__ k, __bf16* __restrict__ v) {
+    const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    const int halfd = d / 2;
+    const long per_row = (long)H * halfd;
+    if (gid >= (long)n * per_row) return;
+    const int m = (int)(gid / per_row);
+    const int rem = (int)(gid % per_row);
+    const int h = rem / halfd, i = rem % halfd;
+    const float pos = (float)(rows ? rows[m] : m);
+    // inverse frequency theta^(-2i/d), angle = pos * inv_freq (fp32)
+    const float inv_freq = exp2f(-(float)(2 * i) / (float)d * log2_theta);
+    float sn, cs;
+    sincosf(pos * inv_freq, &sn, &cs);
+    const long D = (long)H * d;
+    const __bf16* src = qkv + (long)m * 3 * D + (long)h * d;
+    const long o = ((long)m * H + h) * d;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) { // q, k
+        const float x1 = (float)src[part * D + i], x2 = (float)src[part * D + i + halfd];
+        __bf16* dst = part ? k : q;
+        dst[o + i] = (__bf16)(x1 * cs - x2 * sn);
+        dst[o + i + halfd] = (__bf16)(x2 * cs + x1 * sn);
+    }
+    v[o + i] = src[2 * D + i];
+    v[o + i + halfd] = src[2 * D + i + halfd];
+}
+
+__global__ void k_rows_f32_to_bf16(const float* __restrict__ src, const int32_t* __restrict__ rows,
+                                   long n, int D, __bf16* __restrict__ dst) {
+    const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    if (gid >= n * D) return;
+    const long m = gid / D;
+    const int c = (int)(gid % D);
+    const long row = rows ? rows[m] : m;
+    dst[gid] = (__bf16)src[row * D + c];
+}
+
+__global__ void k_scatter_rows_bf16(const __bf16* __restrict__ src, const int32_t* __restrict__ rows,
+                                    long n, int D, __bf16* __restrict__ dst) {
+    const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    if (gid >= n * D) return;
+    const long m = gid / D;
+    const int c = (int)(gid % D);
+    const long row = rows ? rows[m] : m;
+    dst[row * D + c] = src[gid];
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int D,
+                                 const __bf16* w, float eps, __bf16* out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rmsnorm_gather, dim3(n), dim3(256), 0, st, x, rows, D, w, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st) {
+    if (G.M <= 0) return hipSuccess;
+    dim3 grid(G.N / GBN, (G.M + GBM - 1) / GBM);
+    if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, G);
+    else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, G);
+    else hipLaunchKernelGGL(k_gemm<EPI_SWIGLU>, grid, dim3(256), 0, st, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_split(const __bf16* qkv, const int32_t* rows, int n, int H, int d,
+                             float theta, __bf16* q, __bf16* k, __bf16* v, hipStream_t st) {
+    const long total = (long)n * H * (d / 2);
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rope_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, qkv,
+                       rows, n, H, d, log2f(theta), q, k, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_rows_f32_to_bf16(const float* src, const int32_t* rows, long n, int D,
+                                   __bf16* dst, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rows_f32_to_bf16, dim3((unsigned)((n * D + 255) / 256)), dim3(256), 0, st,
+                       src, rows, n, D, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows_bf16(const __bf16* src, const int32_t* rows, long n, int D,
+                                    __bf16* dst, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_scatter_rows_bf16, dim3((unsigned)((n * D + 255) / 256)), dim3(256), 0, st,
+                       src, rows, n, D, dst);
+    return hipGetLastError();
+}
+
+} // namespace fl

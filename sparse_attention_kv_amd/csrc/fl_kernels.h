@@ -58,6 +58,19 @@ struct ColParams {
 
 enum { MODE_ATTN = 0, MODE_REBUILD = 1 };
 
+// C = A[M][K] . B[N][K]^T (bf16 in, fp32 accumulate); N % 128 == 0, K % 32 == 0
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+struct GemmParams {
+    int M, N, K;
+    const __bf16* A;       // [M][lda]
+    long lda;
+    const __bf16* B;       // [N][K] (weights, output-major)
+    __bf16* Cb;            // EPI_STORE: [M][ldc]; EPI_SWIGLU: [M][ldc] with ldc >= N/2
+    float* Cf;             // EPI_RESID: fp32 [*][ldc], rows selected by `rows`
+    long ldc;
+    const int32_t* rows;   // EPI_RESID: destination row of each of the M rows
+};
+
 // select.hip
 hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, int D,
                              const int32_t* cand, int n_cand, float* stat, hipStream_t st);
@@ -77,6 +90,16 @@ hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, i
                            const QTiles& out, int32_t* cpos, hipStream_t st);
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st);
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st);
+// block.hip
+hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int D,
+                                 const __bf16* w, float eps, __bf16* out, hipStream_t st);
+hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st);
+hipError_t launch_rope_split(const __bf16* qkv, const int32_t* rows, int n, int H, int d,
+                             float theta, __bf16* q, __bf16* k, __bf16* v, hipStream_t st);
+hipError_t launch_rows_f32_to_bf16(const float* src, const int32_t* rows, long n, int D,
+                                   __bf16* dst, hipStream_t st);
+hipError_t launch_scatter_rows_bf16(const __bf16* src, const int32_t* rows, long n, int D,
+                                    __bf16* dst, hipStream_t st);
 // abi.hip
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
 

@@ -23,8 +23,9 @@ FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 
 MAX_LEVELS = 16
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
-           "fl_sparse_loop_attn", "fl_loop_step", "fl_workspace_size", "fl_last_error",
-           "fl_version", "fl_timing_enable", "fl_timing_report"]
+           "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_workspace_size",
+           "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
+FL_WS_BLOCK_STEP = 5
 
 
 class FlError(RuntimeError):
@@ -71,6 +72,31 @@ class FlLoopInputs(ctypes.Structure):
                 ("v", c_void_p), ("q_prev", c_void_p)]
 
 
+class FlBlockCfg(ctypes.Structure):
+    _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
+                ("n_sink", c_int), ("n_layers", c_int), ("ffn", c_int), ("rope_theta", c_float),
+                ("norm_eps", c_float), ("n_active", c_int * MAX_LEVELS),
+                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int)]
+
+
+class FlLayerWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("w_gu", c_void_p), ("w_down", c_void_p),
+                ("norm1", c_void_p), ("norm2", c_void_p)]
+
+
+class FlLayerState(ctypes.Structure):
+    _fields_ = [("cache", FlKvCache), ("q_state", c_void_p), ("out", c_void_p), ("lse", c_void_p),
+                ("mass_u", c_void_p), ("out_u", c_void_p), ("sel", c_void_p * MAX_LEVELS),
+                ("sel_used", c_void_p * MAX_LEVELS), ("k_cur", c_int * MAX_LEVELS),
+                ("col_stat", c_void_p * MAX_LEVELS)]
+
+
+class FlBlockState(ctypes.Structure):
+    _fields_ = [("h", c_void_p), ("h_entry", c_void_p), ("active", c_void_p * MAX_LEVELS),
+                ("slot", c_void_p * MAX_LEVELS), ("stat", c_void_p),
+                ("layers", POINTER(FlLayerState))]
+
+
 _lib = None
 
 
@@ -95,6 +121,8 @@ def lib():
                                           c_size_t, c_void_p]
         L.fl_loop_step.argtypes = [POINTER(FlLoopCfg), POINTER(FlLoopState), POINTER(FlLoopInputs),
                                    c_int, c_void_p, c_size_t, c_void_p]
+        L.fl_block_step.argtypes = [POINTER(FlBlockCfg), POINTER(FlLayerWeights),
+                                    POINTER(FlBlockState), c_int, c_void_p, c_size_t, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
         for name in EXPORTS:
@@ -198,6 +226,13 @@ def fl_loop_step(cfg: FlLoopCfg, state: FlLoopState, inputs: FlLoopInputs, r, ws
     _check("fl_loop_step", rc)
 
 
+def fl_block_step(cfg: FlBlockCfg, weights, state: FlBlockState, r, ws, stream=None):
+    """Sec. 4.1/4.4: one loop r of the whole looped block (all layers)."""
+    rc = lib().fl_block_step(ctypes.byref(cfg), weights, ctypes.byref(state), r, _p(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+    _check("fl_block_step", rc)
+
+
 # --------------------------------------------------------------------------
 # Device-memory holder for a whole R-loop run (buffers only; no arithmetic).
 
@@ -286,3 +321,86 @@ class LoopRunner:
 
     def k_used(self, r):
         return self.state.k_cur[r - 1]
+
+
+class BlockRunner:
+    """Allocates per-layer caches and state for the looped block and runs
+    ``fl_block_step`` for r = 1..R.  ``weights`` is a list (one per layer) of
+    dicts of bf16 device tensors: w_qkv [3D][D], w_o [D][D], w_gu [2F][D]
+    (rows 2j gate, 2j+1 up), w_down [D][F], norm1 [D], norm2 [D]."""
+
+    def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, weights, ffn,
+                 rope_theta=10000.0, norm_eps=1e-6, mode=FL_DEQ_AUTO, device="cuda"):
+        dev = torch.device(device)
+        self.N, self.H, self.d, self.R = N, H, d, R
+        self.L = len(weights)
+        D = H * d
+        self._keep = []
+
+        def buf(shape, dt):
+            t = torch.empty(shape, dtype=dt, device=dev)
+            self._keep.append(t)
+            return t
+
+        cfg = FlBlockCfg()
+        cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = N, H, d, g, R, n_sink
+        cfg.n_layers, cfg.ffn, cfg.rope_theta, cfg.norm_eps, cfg.mode = self.L, ffn, rope_theta, norm_eps, mode
+        for r in range(R):
+            cfg.n_active[r], cfg.k_cols[r], cfg.bits[r] = n_active[r], k_cols[r], bits[r]
+        self.cfg = cfg
+        W = (FlLayerWeights * self.L)()
+        for l, wd in enumerate(weights):
+            for key in ("w_qkv", "w_o", "w_gu", "w_down", "norm1", "norm2"):
+                setattr(W[l], key, _p(wd[key]))
+        self.W = W
+        self.weights = weights
+        layers = (FlLayerState * self.L)()
+        self.layer_bufs = []
+        for l in range(self.L):
+            Ls = layers[l]
+            Ls.cache.N, Ls.cache.H, Ls.cache.d, Ls.cache.g = N, H, d, g
+            lb = dict(codes=[])
+            for r in range(R):
+                rows = N if r == 0 else n_active[r]
+                b = bits[r]
+                kc = buf((rows, H, d * b // 8), torch.uint8)
+                vc = buf((rows, H, d * b // 8), torch.uint8)
+                ks = buf((rows, H, d // g), torch.float32)
+                vs = buf((rows, H, d // g), torch.float32)
+                Lv = Ls.cache.level[r]
+                Lv.bits, Lv.n_rows = b, rows
+                Lv.k_codes, Lv.v_codes, Lv.k_scale, Lv.v_scale = _p(kc), _p(vc), _p(ks), _p(vs)
+                lb["codes"].append(dict(k=kc, v=vc, ks=ks, vs=vs))
+            lb["q_state"] = buf((N, H, d), torch.bfloat16)
+            lb["out"] = buf((N, H, d), torch.float32)
+            lb["lse"] = buf((N, H), torch.float32)
+            lb["mass_u"] = buf((N, H), torch.float32)
+            lb["out_u"] = buf((N, H, d), torch.float32)
+            Ls.q_state, Ls.out, Ls.lse = _p(lb["q_state"]), _p(lb["out"]), _p(lb["lse"])
+            Ls.mass_u, Ls.out_u = _p(lb["mass_u"]), _p(lb["out_u"])
+            lb["sel"], lb["col_stat"] = [], []
+            for r in range(R):
+                sl = buf((H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < N else None
+                cs = buf((H, min(k_cols[: r + 1])), torch.float32)
+                Ls.sel[r] = _p(sl)
+                Ls.col_stat[r] = _p(cs)
+                lb["sel"].append(sl); lb["col_stat"].append(cs)
+            self.layer_bufs.append(lb)
+        self.layers = layers
+        st = FlBlockState()
+        self.h = buf((N, D), torch.float32)
+        self.h_entry = buf((N, D), torch.float32)
+        self.stat = buf((N,), torch.float32)
+        self.active, self.slot = [], []
+        for r in range(R):
+            a = buf((n_active[r],), torch.int32)
+            s_ = buf((N,), torch.int32) if r > 0 else None
+            st.active[r], st.slot[r] = _p(a), _p(s_)
+            self.active.append(a); self.slot.append(s_)
+        st.h, st.h_entry, st.stat = _p(self.h), _p(self.h_entry), _p(self.stat)
+        st.layers = ctypes.cast(layers, POINTER(FlLayerState))
+        self.state = st
+        self.ws = buf((fl_workspace_size(FL_WS_BLOCK_STEP, N, H, d, ffn),), torch.uint8)
+
+    def step(self, r, stream=None):
+        fl_block_step(self.cfg, self.W, self.state, r, self.ws, stream)

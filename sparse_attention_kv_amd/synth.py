@@ -99,6 +99,14 @@ WORKLOADS = {
     "prefill32k": Workload("prefill32k", N=32768, H=16, d=128, R=4, g=64, n_sink=4,
                            rho=[1.0, 0.4, 0.2, 0.1], kcols=[32768, 2048, 2048, 2048],
                            bits=[8, 4, 2, 2], dtype="bf16", seed=2, sigma_sd=1.5),
+    # full looped block: 24 layers of shared random-init weights, hidden 2048
+    # (16 x 128), SwiGLU 5632, RMSNorm (eps 1e-6), RoPE (theta 1e4), R=4,
+    # seq 8192; fractions 1/.4/.2/.1, 1024 columns incl. 4 sinks, int8 base,
+    # int4 at loop 2 and int2 at loops 3-4, group 64.
+    "block8k": Workload("block8k", N=8192, H=16, d=128, R=4, g=64, n_sink=4,
+                        rho=[1.0, 0.4, 0.2, 0.1], kcols=[8192, 1024, 1024, 1024],
+                        bits=[8, 4, 2, 2], dtype="bf16", seed=4, kind="block",
+                        extra=dict(layers=24, ffn=5632, theta=10000.0, eps=1e-6, wstd=0.02)),
 }
 
 
@@ -162,7 +170,30 @@ def gen_prefill(w: Workload) -> dict:
     return dict(h=hs, q=qs, k=ks, v=vs, dtype=w.dtype)
 
 
+def gen_block(w: Workload) -> dict:
+    """Looped block: embeddings h_1 ~ N(0,1) [N][D]; per layer weights
+    ~ N(0, wstd^2), output-major: w_qkv [3D][D], w_o [D][D], w_gu [2F][D]
+    (row 2j gate, row 2j+1 up of hidden unit j), w_down [D][F]; RMSNorm
+    weights 1.  All stored as bf16 (round to nearest even)."""
+    rng = _rng(w.seed)
+    N, D = w.N, w.D
+    F, L, sd = w.extra["ffn"], w.extra["layers"], np.float32(w.extra["wstd"])
+    h1 = rng.standard_normal((N, D), dtype=np.float32)
+    layers = []
+    for _ in range(L):
+        lw = {}
+        for name, shape in (("w_qkv", (3 * D, D)), ("w_o", (D, D)), ("w_gu", (2 * F, D)),
+                            ("w_down", (D, F))):
+            lw[name] = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * sd)
+        lw["norm1"] = f32_to_bf16_bits(np.ones(D, np.float32))
+        lw["norm2"] = f32_to_bf16_bits(np.ones(D, np.float32))
+        layers.append(lw)
+    return dict(h1=h1, layers=layers, dtype="bf16")
+
+
 def generate(w: Workload) -> dict:
+    if w.kind == "block":
+        return gen_block(w)
     if w.kind == "tiny":
         return gen_tiny(w)
     if w.kind == "prefill":

@@ -91,7 +91,7 @@ def test_quant_rejects(L):
     assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 0, None) == -2
     assert L.fl_kv_residual_quant(None, 0, 1, FAKE, FAKE, 0, None) == -1
     c = _cache()
-    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 1, FAKE, FAKE, 1, None) == -1
+    assert L.fl_kv_residual_quant(ctypes.byref(c), 0, 7, FAKE, FAKE, 0, None) == -1   # dtype
 
 
 def _args(**kw):
@@ -120,6 +120,24 @@ def test_attn_rejects(L):
     assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) in (-2, -3)
     a = _args(n=0)
     assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+
+
+def test_block_step_rejects(L):
+    cfg = fl.FlBlockCfg()
+    cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_layers, cfg.ffn = 64, 2, 128, 64, 2, 1, 512
+    st = fl.FlBlockState()
+    W = (fl.FlLayerWeights * 1)()
+    layers = (fl.FlLayerState * 1)()
+    st.layers = ctypes.cast(layers, ctypes.POINTER(fl.FlLayerState))
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 3, None, 0, None) == -1
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -1  # h NULL
+    st.h = st.h_entry = st.stat = FAKE
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -3  # workspace
+    cfg.ffn = 500
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -2
+    cfg.ffn, cfg.d = 512, 96
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -2
+    assert fl.fl_workspace_size(fl.FL_WS_BLOCK_STEP, 8192, 16, 128, 5632) > 8192 * 2048 * 2 * 5
 
 
 def test_loop_step_rejects(L):
