@@ -75,6 +75,10 @@ def main():
 
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if w.kind == "block":
+        return bench_block(args, w, np, torch, fl, synth)
+    if w.kind == "decode":
+        return bench_decode(args, w, np, torch, fl, synth)
     t0 = time.time()
     inp = synth.generate(w)
     log(f"[bench] generated {w.name} inputs in {time.time() - t0:.1f}s")
@@ -290,6 +294,227 @@ def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
                        f"to n_r rows"),
             "extrapolated_step_s": round(total_s, 2), "measured_s": round(time.time() - t_all, 1),
             "loops": per_loop}
+
+
+def bench_block(args, w, np, torch, fl, synth):
+    """The full looped block: R loops of n_layers layers on each loop's active
+    tokens.  value = active tokens pushed through the whole block per second,
+    sum_r n_r / step time.  Roofline of the dominant kernel family (the
+    gathered-row GEMMs: 2*(D*3D + D*D + D*2F + F*D) flops per active token and
+    layer)."""
+    t0 = time.time()
+    inp = synth.generate(w)
+    log(f"[bench] generated {w.name} weights/inputs in {time.time() - t0:.1f}s")
+    N, H, d, R = w.N, w.H, w.d, w.R
+    D, F, L = H * d, w.extra["ffn"], w.extra["layers"]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    wdev = [{k: dev(v) for k, v in lw.items()} for lw in inp["layers"]]
+    h1 = torch.from_numpy(inp["h1"]).cuda()
+    n_act = [N]
+    for r in range(1, R):
+        n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
+    run = fl.BlockRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, wdev, F,
+                         rope_theta=w.extra["theta"], norm_eps=w.extra["eps"])
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        run.h.copy_(h1)
+        for r in range(1, R + 1):
+            if events is not None:
+                events[r - 1].record(stream)
+            run.step(r)
+        if events is not None:
+            events[R].record(stream)
+
+    log(f"[bench] block resident: {L} layers, n_active={n_act}, k={w.kcols}")
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    fl.fl_timing_report()
+    fl.fl_timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    fl.fl_timing_enable(False)
+    ktab = fl.fl_timing_report()
+    loop_ms = np.array([[evs[s_][r].elapsed_time(evs[s_][r + 1]) for r in range(R)]
+                        for s_ in range(args.steps)])
+    ms_per_step = float(np.mean(loop_ms.sum(axis=1)))
+    tokens = sum(n_act)
+    per_tok = {"gemm_qkv": 2.0 * D * 3 * D, "gemm_o": 2.0 * D * D, "gemm_gate_up": 2.0 * D * 2 * F,
+               "gemm_down": 2.0 * F * D}
+    kernels = {}
+    for name, (cnt, ms) in ktab.items():
+        e = dict(launches_per_step=cnt / args.steps, ms_per_step=round(ms / args.steps, 4),
+                 avg_launch_us=round(1e3 * ms / max(cnt, 1), 2))
+        if name in per_tok and ms > 0:
+            e["tflops"] = round(per_tok[name] * tokens * L / (ms / args.steps / 1e3) / 1e12, 2)
+        kernels[name] = e
+    gemm_ms = sum(kernels[k]["ms_per_step"] for k in per_tok if k in kernels)
+    gemm_flops = sum(per_tok.values()) * tokens * L
+    ach = gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms else None
+    out = {
+        "metric": "active tokens/s through the token-sparse looped block (24 layers, R=4, 8K)",
+        "value": round(tokens / (ms_per_step / 1e3), 1), "unit": "active tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init shared weights)",
+        "config": {"workload": w.name, "N": N, "layers": L, "hidden": D, "heads": H, "head_dim": d,
+                   "ffn": F, "R": R, "active_per_loop": n_act, "k_per_loop": w.kcols,
+                   "bits_per_loop": w.bits},
+        "loops": [dict(r=r + 1, n=n_act[r], ms=round(float(np.mean(loop_ms[:, r])), 3))
+                  for r in range(R)],
+        "kernels": kernels,
+        "roofline": dict(kernel="gemm (qkv+o+gate_up+down)", bound="mfma",
+                         achieved=round(ach, 2) if ach else None, peak=PEAK_BF16_TFLOPS,
+                         unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
+                         traffic=None, flops_per_step=gemm_flops),
+        "gemm_flops_dense_equivalent": sum(per_tok.values()) * N * R * L,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, w, np, torch, fl, synth):
+    """Batched decode: B sequences with resident loop-indexed prefix caches;
+    a step decodes one new token per sequence through all R loops (loop 1
+    dense over the prefix, later loops on the selected columns, the cached
+    mass / partial output rebuilt when the column set shrinks).
+    value = decoded tokens per second, B / step time.  The dominant kernel
+    (the dense first loop) is bounded by HBM: its algorithmic bytes are the
+    prefix's int8 K/V codes and fp32 group scales, the column statistic it
+    writes, and the token's q/k/v in and output out."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, N, H, d, R, g = w.extra["B"], w.N, w.H, w.d, w.R, w.g
+    n_act = [N]
+    for r in range(1, R):
+        n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
+    run = fl.DecodeRunner(B, N, H, d, g, R, w.n_sink, n_act, w.kcols, w.bits)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    t0 = time.time()
+    tok = {key: np.empty((R, B, H, d), np.uint16) for key in ("q_new", "k_new", "v_new")}
+    nthr = min(16, os.cpu_count() or 1)
+    sample_inputs = {}
+    n_cpu = 0 if args.no_cpu_baseline else 2
+    with ThreadPoolExecutor(nthr) as ex:
+        for b0 in range(0, B, nthr):
+            futs = [ex.submit(synth.gen_decode_seq, w, b) for b in range(b0, min(B, b0 + nthr))]
+            for i, f in enumerate(futs):
+                b, x = b0 + i, f.result()
+                st = [None] + [torch.from_numpy(a).cuda() for a in x["stat"][1:]]
+                run.load_sequence(b, [dev(a) for a in x["k"]], [dev(a) for a in x["v"]], st)
+                for key in tok:
+                    for r in range(R):
+                        tok[key][r, b] = x[key][r]
+                if b < n_cpu:
+                    sample_inputs[b] = x
+            torch.cuda.synchronize()
+    log(f"[bench] {B} sequences x {N} tokens drawn and cached in {time.time() - t0:.1f}s")
+    T = {key: [dev(tok[key][r]) for r in range(R)] for key in tok}
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for r in range(1, R + 1):
+            if events is not None:
+                events[r - 1].record(stream)
+            prev = [T[key][r - 2] if r > 1 else None for key in ("q_new", "k_new", "v_new")]
+            run.step(r, T["q_new"][r - 1], T["k_new"][r - 1], T["v_new"][r - 1], *prev)
+        if events is not None:
+            events[R].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    fl.fl_timing_report()
+    fl.fl_timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    fl.fl_timing_enable(False)
+    ktab = fl.fl_timing_report()
+    loop_ms = np.array([[evs[s_][r].elapsed_time(evs[s_][r + 1]) for r in range(R)]
+                        for s_ in range(args.steps)])
+    ms_per_step = float(np.mean(loop_ms.sum(axis=1)))
+
+    # algorithmic bytes per launch
+    G = d // g
+    col_b = [2 * d * b_ // 8 + 2 * G * 4 for b_ in w.bits]       # K+V codes + scales of one row
+    tok_io = 3 * d * 2 + d * 4 + 4                               # q,k,v in; out, lse out
+    need_c1 = R > 1 and w.kcols[1] < N
+    dense_bytes = B * H * (N * col_b[0] + (N * 4 if need_c1 else 0) + tok_io)
+    # sparse loops: selected columns' present levels (from the GPU's sets)
+    sparse_bytes = {}
+    for r in range(2, R + 1):
+        sel = run.sel_used(r)
+        if sel is None:
+            continue
+        kk = sel.shape[-1]
+        j = sel.to(torch.int64).reshape(B, -1)
+        present = torch.ones_like(j, dtype=torch.bool)
+        tot = col_b[0] * j.numel()
+        for l in range(1, r):
+            present &= torch.gather(run.slot[l].to(torch.int64), 1, j) >= 0
+            tot += (col_b[l] + 4) * int(present.sum().item())   # + the slot lookup
+        io = B * H * (kk * 4 + tok_io + d * 4 + 4)               # sel, token io, O_U / M_U in
+        sparse_bytes[r] = tot + io
+    kernels = {}
+    for name, (cnt, ms) in ktab.items():
+        kernels[name] = dict(launches_per_step=cnt / args.steps, ms_per_step=round(ms / args.steps, 4),
+                             avg_launch_us=round(1e3 * ms / max(cnt, 1), 2))
+    roof = None
+    if "decode_dense" in kernels:
+        kd = kernels["decode_dense"]
+        per_launch = dense_bytes
+        ach = per_launch / (kd["avg_launch_us"] / 1e6) / 1e9
+        kd["gbs"] = round(ach, 1)
+        roof = dict(kernel="k_decode<128,MODE_ATTN,dense> (loop 1)", bound="hbm", achieved=round(ach, 1),
+                    peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
+                    bytes_per_launch=per_launch)
+    if "decode" in kernels and sparse_bytes:
+        kd = kernels["decode"]
+        avg_b = sum(sparse_bytes.values()) / len(sparse_bytes)
+        kd["gbs"] = round(avg_b / (kd["avg_launch_us"] / 1e6) / 1e9, 1)
+        kd["bytes_per_launch_avg"] = int(avg_b)
+    cpu = None
+    if n_cpu:
+        from oracle import decode as od
+        import oracle
+        f = synth.bf16_bits_to_f32
+        sched = w.sched()
+        t_or = 0.0
+        for b, x in sample_inputs.items():
+            cache = od.build_cache([f(a) for a in x["k"]], [f(a) for a in x["v"]], x["stat"], sched)
+            t1 = time.time()
+            od.run_decode(cache, [f(a) for a in x["q_new"]], [f(a) for a in x["k_new"]],
+                          [f(a) for a in x["v_new"]], sched)
+            t_or += time.time() - t1
+        cpu = dict(value=round(len(sample_inputs) / t_or, 3), unit="decoded tokens/s",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{len(sample_inputs)} of the {B} sequences, all R={R} loops of the new "
+                          f"token (cache already built, as on the GPU)")
+    out = {
+        "metric": f"decoded tokens/s, {B} sequences x {N} cached tokens, R={R}",
+        "value": round(B / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8/int4 codes, f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "N": N, "H": H, "d": d, "R": R, "g": g,
+                   "active_per_loop": n_act, "k_per_loop": w.kcols, "bits_per_loop": w.bits},
+        "loops": [dict(r=r + 1, ms=round(float(np.mean(loop_ms[:, r])), 4)) for r in range(R)],
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def synth_f32(a, dtype, np):

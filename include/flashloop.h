@@ -335,6 +335,52 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
                   void* ws, size_t ws_bytes, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fl_decode_step -- one loop r of batched decode (paper Sec. 4.2; Sec. 5.3.1
+ * reports decode as bound by KV traffic): B sequences, each with a cached
+ * prefix of N tokens stored as the loop-indexed quantised cache (base level
+ * plus residual levels for the prefix tokens active in each loop), and one
+ * new query token per sequence.  For each sequence and head the key columns
+ * are the selected prefix columns S_r (all N at r = 1) plus the token's own
+ * fresh bf16 key/value (the self column, always included):
+ *   P(j) = (1 - M_U) softmax over S_r and self of sm * q.khat_r(j)
+ *   o = sum_j P(j) vhat_r(j) + O_U,  khat_r/vhat_r from cache levels 0..r-1.
+ * r >= 2: columns are re-selected (sinks + top by the previous loop's P over
+ * the prefix) when the budget shrinks, and M_U / O_U are rebuilt under the
+ * previous loop's distribution (its query and self column) as in
+ * fl_sparse_loop_attn.  The previous loop's P over the kept prefix columns
+ * is the column statistic (col_stat).
+ * Cache layout: cache.level[l] describes sequence 0 with the usual fields;
+ * sequence b's rows/slot/codes/scales follow at b * (n_rows, N, n_rows*H*
+ * d*bits/8 bytes, n_rows*H*d/g floats) -- B sequences of equal geometry.
+ * Requirements: N + 1 <= 12288 (the probabilities stay in LDS).
+ */
+typedef struct fl_decode_cfg {
+    int B, N, H, d, g, R, n_sink;
+    int k_cols[FL_MAX_LEVELS];  /* [0] = N */
+} fl_decode_cfg;
+
+typedef struct fl_decode_state {
+    fl_kv_cache cache;
+    float* out; float* lse; float* mass_u; float* out_u; /* [B][H][d], [B][H] */
+    int32_t* sel[FL_MAX_LEVELS];            /* [B][H][k_cols[r-1]] (r >= 2)     */
+    const int32_t* sel_used[FL_MAX_LEVELS]; /* filled by the step                */
+    int k_cur[FL_MAX_LEVELS];               /* filled by the step                */
+    float* col_stat[FL_MAX_LEVELS];         /* [B][H][k of loop r]               */
+} fl_decode_state;
+
+typedef struct fl_decode_inputs {
+    const void* q;       /* bf16 [B][H][d] loop r query of the new token        */
+    const void* k_self;  /* bf16 [B][H][d] loop r key / value of the new token  */
+    const void* v_self;
+    const void* q_prev;  /* loop r-1 values (r >= 2)                            */
+    const void* k_self_prev;
+    const void* v_self_prev;
+} fl_decode_inputs;
+
+int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* st, const fl_decode_inputs* in,
+                   int r, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later
  * launch of the library record a HIP event pair around each kernel on the
  * launch stream.  fl_timing_report waits for those events and writes one line

@@ -1,0 +1,125 @@
+"""Oracle of batched decode with the lazy-update loop attention.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__.py``).
+
+FlashLoop paper, Sec. 4.2-4.3 applied to one new token per sequence (Sec.
+5.3.1 evaluates decode).  A sequence has a prefix of N cached tokens whose
+cache was built loop by loop as in prefill: loop 1 stores every token's K/V
+as the base level; loop r >= 2 keeps the top n_r of the previous loop's
+active tokens by their statistic (nested) and stores their residual level
+r-1 against the dequantised previous value; the other tokens keep theirs.
+
+The new token at position N runs R loops.  At loop r its query attends
+causally to the prefix's loop-r dequantised keys/values on the selected
+columns S_r plus its own fresh key/value (column N, always selected):
+
+  loop 1   dense over all N + 1 columns; M_U = O_U = 0; the column
+           statistic is the token's probability of every prefix column.
+  loop r   S_r = sinks + top (k_r - sinks) of S_{r-1} by the previous
+           statistic (kept when it already fits k_r); when it changes,
+           M_U / O_U of the pruned columns under loop r-1's distribution
+           (its query, cache and self column); sparse attention
+           o = (1 - M_U) softmax_{S_r + self} + O_U; the statistic is the
+           probability of each kept prefix column.
+
+Every step is a call of the pinned C oracle on an (N + 1)-position problem
+with one query row at position N.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (active_count, attend, column_stats, quantize_rows, select_columns, top_select,
+               unselected_cache)
+
+F32 = np.float32
+
+
+def build_cache(k, v, stat, sched):
+    """Per-loop prefix cache of one sequence.
+
+    k, v: lists of R fp32 arrays [N][H][d] (the prefix tokens' loop-r K/V);
+    stat: list of R entries, stat[r-1] [N] the loop-r selection statistic
+    (stat[0] unused).  Returns a list of per-loop dicts with the active set,
+    the level's codes/scales and the dequantised cache khat/vhat [N][H][d]."""
+    N, g = sched["N"], sched["g"]
+    A = np.arange(N, dtype=np.int32)
+    khat = vhat = None
+    out = []
+    for r in range(1, sched["R"] + 1):
+        if r > 1:
+            n_r = active_count(sched["rho"][r - 1], N, len(A))
+            A = top_select(np.asarray(stat[r - 1], F32)[A], n_r, A)
+        bits = sched["bits"][r - 1]
+        kc, ks, _, kx = quantize_rows(np.asarray(k[r - 1], F32)[A], None if r == 1 else khat[A], g, bits)
+        vc, vs, _, vx = quantize_rows(np.asarray(v[r - 1], F32)[A], None if r == 1 else vhat[A], g, bits)
+        if r == 1:
+            khat, vhat = kx, vx
+        else:
+            khat = khat.copy(); khat[A] = kx
+            vhat = vhat.copy(); vhat[A] = vx
+        out.append(dict(active=A, k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs,
+                        khat=khat, vhat=vhat))
+    return out
+
+
+def _extend(x_prefix, x_self):
+    """[N][H][d] prefix rows + the new token's [H][d] row at position N."""
+    return np.concatenate([np.asarray(x_prefix, F32), np.asarray(x_self, F32)[None]], axis=0)
+
+
+def _with_self(sel, N):
+    return np.concatenate([sel, np.full((sel.shape[0], 1), N, np.int32)], axis=1)
+
+
+def run_decode(cache, q, k_self, v_self, sched, override=None):
+    """Loops 1..R of one sequence's new token.
+
+    cache: output of ``build_cache``; q, k_self, v_self: lists of R fp32
+    arrays [H][d].  override: {('cstat', r): [H][k_{r-1}]} -- the GPU's own
+    statistic for the column selection made at loop r.
+    Returns per-loop dicts: sel [H][k] prefix columns (None when dense), k,
+    out [H][d], lse [H], mass_u [H], out_u [H][d], cstat [H][k] or None."""
+    override = override or {}
+    N, H, d, R = (sched[x] for x in ("N", "H", "d", "R"))
+    sm = F32(1.0 / np.sqrt(d))
+    rows = np.array([N], np.int32)
+    S, k_cur, cstat = None, N, None
+    prev = None   # (Q, K, V, lse, mu, ou) of the previous loop
+    recs = []
+    for r in range(1, R + 1):
+        Q = np.zeros((N + 1, H, d), F32)
+        Q[N] = np.asarray(q[r - 1], F32)
+        K = _extend(cache[r - 1]["khat"], k_self[r - 1])
+        V = _extend(cache[r - 1]["vhat"], v_self[r - 1])
+        if r == 1:
+            o, lse = attend(Q, K, V, rows, None, sm)
+            mu = np.zeros((1, H), F32); ou = np.zeros((1, H, d), F32)
+            need_c = R > 1 and sched["kcols"][1] < N
+            c = column_stats(Q, K, rows, None, lse, sm)[:, :N] if need_c else None
+            S_new, k_new = None, N
+        else:
+            k_r = sched["kcols"][r - 1]
+            if k_cur <= k_r:
+                S_new, k_new, changed = S, k_cur, False
+            else:
+                S_new = select_columns(override.get(("cstat", r), cstat), S, k_r, sched["n_sink"])
+                k_new, changed = k_r, True
+            Qp, Kp, Vp, lse_p, mu_p, ou_p = prev
+            if changed:
+                mu, ou = unselected_cache(Qp, Kp, Vp, rows,
+                                          None if S is None else _with_self(S, N),
+                                          _with_self(S_new, N), lse_p, sm,
+                                          None if S is None else mu_p,
+                                          None if S is None else ou_p)
+            else:
+                mu, ou = mu_p, ou_p
+            ext = None if S_new is None else _with_self(S_new, N)
+            o, lse = attend(Q, K, V, rows, ext, sm, mu, ou)
+            need_c = r < R and sched["kcols"][r] < k_new
+            c = column_stats(Q, K, rows, ext, lse, sm, mu)[:, :k_new] if need_c else None
+        recs.append(dict(r=r, sel=S_new, k=k_new, out=o[0], lse=lse[0], mass_u=mu[0],
+                         out_u=ou[0], cstat=c))
+        prev = (Q, K, V, lse, mu, ou)
+        S, k_cur, cstat = S_new, k_new, c
+    return recs

@@ -591,6 +591,69 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
     return FL_OK;
 }
 
+int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode_inputs* in,
+                   int r, fl_stream_t stream) {
+    FL_REQUIRE(cfg && S && in, "cfg/state/inputs NULL");
+    FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
+    const int B = cfg->B, N = cfg->N, H = cfg->H, d = cfg->d;
+    FL_REQUIRE(B >= 1 && N >= 1 && H >= 1, "B=%d N=%d H=%d", B, N, H);
+    FL_REQUIRE(N + 1 <= 12288, "N=%d: decode keeps N+1 probabilities in LDS (<= 12288)", N);
+    fl_kv_cache& C = S->cache;
+    FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
+    int rc = check_cache(&C, r - 1);
+    if (rc) return rc;
+    FL_REQUIRE(in->q && in->k_self && in->v_self, "q/k_self/v_self NULL");
+    FL_REQUIRE(S->out && S->lse && S->mass_u && S->out_u, "state arrays NULL");
+    hipStream_t st = (hipStream_t)stream;
+    fl::DecodeParams P{};
+    P.B = B; P.H = H; P.sm = 1.0f / sqrtf((float)d); P.cache = C;
+    P.out = S->out; P.lse = S->lse; P.mass_u = S->mass_u; P.out_u = S->out_u;
+    if (r == 1) {
+        S->k_cur[0] = N;
+        S->sel_used[0] = nullptr;
+        P.k = N; P.sel = nullptr; P.level = 0; P.cache_op = FL_CACHE_ZERO;
+        P.q = in->q; P.kself = in->k_self; P.vself = in->v_self;
+        P.col_stat = (cfg->R > 1 && cfg->k_cols[1] < N) ? S->col_stat[0] : nullptr;
+        FL_HIP(fl::launch_fill_f32(S->mass_u, (long)B * H, 0.0f, st), "fill");
+        FL_HIP(fl::launch_fill_f32(S->out_u, (long)B * H * d, 0.0f, st), "fill");
+        FL_HIP(timed("decode_dense", st, [&] { return fl::launch_decode(d, fl::MODE_ATTN, P, st); }),
+               "decode");
+        return FL_OK;
+    }
+    FL_REQUIRE(in->q_prev && in->k_self_prev && in->v_self_prev, "previous-loop inputs NULL");
+    const int k_prev = S->k_cur[r - 2], k_r = cfg->k_cols[r - 1];
+    bool changed = false;
+    if (k_prev <= k_r) {
+        S->k_cur[r - 1] = k_prev;
+        S->sel_used[r - 1] = S->sel_used[r - 2];
+    } else {
+        FL_REQUIRE(S->sel[r - 1] && S->col_stat[r - 2], "sel/col_stat buffers NULL");
+        rc = fl_select_columns(S->col_stat[r - 2], S->sel_used[r - 2], B * H, k_prev, cfg->n_sink, k_r,
+                               S->sel[r - 1], nullptr, 0, stream);
+        if (rc) return rc;
+        S->k_cur[r - 1] = k_r;
+        S->sel_used[r - 1] = S->sel[r - 1];
+        changed = true;
+    }
+    P.k = S->k_cur[r - 1];
+    P.sel = S->sel_used[r - 1];
+    if (changed) {
+        fl::DecodeParams R = P;
+        R.level = r - 2; R.cache_op = FL_CACHE_REBUILD;
+        R.q = in->q_prev; R.kself = in->k_self_prev; R.vself = in->v_self_prev; R.col_stat = nullptr;
+        FL_HIP(timed("decode_rebuild", st, [&] { return fl::launch_decode(d, fl::MODE_REBUILD, R, st); }),
+               "decode(rebuild)");
+    }
+    P.level = r - 1; P.cache_op = FL_CACHE_CARRY;
+    P.q = in->q; P.kself = in->k_self; P.vself = in->v_self;
+    const bool need_c = r < cfg->R && cfg->k_cols[r] < S->k_cur[r - 1];
+    P.col_stat = need_c ? S->col_stat[r - 1] : nullptr;
+    FL_REQUIRE(!need_c || P.col_stat, "col_stat[%d] NULL", r - 1);
+    FL_HIP(timed(P.sel ? "decode" : "decode_dense", st,
+                 [&] { return fl::launch_decode(d, fl::MODE_ATTN, P, st); }), "decode");
+    return FL_OK;
+}
+
 } // extern "C"
 
 namespace fl {

@@ -58,6 +58,18 @@ struct ColParams {
 
 enum { MODE_ATTN = 0, MODE_REBUILD = 1 };
 
+// Batched decode: B sequences x H heads, one new query token each.
+struct DecodeParams {
+    int B, H, k, level, cache_op;
+    float sm;
+    fl_kv_cache cache;      // one sequence's geometry; level buffers hold B sequences
+    const int32_t* sel;     // [B*H][k] selected prefix columns, or NULL (all N)
+    const void* q;          // bf16 [B][H][d]
+    const void* kself;      // bf16 [B][H][d] the token's own key / value
+    const void* vself;
+    float* out; float* lse; float* mass_u; float* out_u; float* col_stat;
+};
+
 // C = A[M][K] . B[N][K]^T (bf16 in, fp32 accumulate); N % 128 == 0, K % 32 == 0
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 struct GemmParams {
@@ -100,6 +112,8 @@ hipError_t launch_rows_f32_to_bf16(const float* src, const int32_t* rows, long n
                                    __bf16* dst, hipStream_t st);
 hipError_t launch_scatter_rows_bf16(const __bf16* src, const int32_t* rows, long n, int D,
                                     __bf16* dst, hipStream_t st);
+// decode.hip
+hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st);
 // abi.hip
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
 

@@ -23,7 +23,8 @@ FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 
 MAX_LEVELS = 16
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
-           "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_workspace_size",
+           "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
+           "fl_workspace_size",
            "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
 FL_WS_BLOCK_STEP = 5
 
@@ -97,6 +98,23 @@ class FlBlockState(ctypes.Structure):
                 ("layers", POINTER(FlLayerState))]
 
 
+class FlDecodeCfg(ctypes.Structure):
+    _fields_ = [("B", c_int), ("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
+                ("n_sink", c_int), ("k_cols", c_int * MAX_LEVELS)]
+
+
+class FlDecodeState(ctypes.Structure):
+    _fields_ = [("cache", FlKvCache), ("out", c_void_p), ("lse", c_void_p), ("mass_u", c_void_p),
+                ("out_u", c_void_p), ("sel", c_void_p * MAX_LEVELS),
+                ("sel_used", c_void_p * MAX_LEVELS), ("k_cur", c_int * MAX_LEVELS),
+                ("col_stat", c_void_p * MAX_LEVELS)]
+
+
+class FlDecodeInputs(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("k_self", c_void_p), ("v_self", c_void_p), ("q_prev", c_void_p),
+                ("k_self_prev", c_void_p), ("v_self_prev", c_void_p)]
+
+
 _lib = None
 
 
@@ -123,6 +141,8 @@ def lib():
                                    c_int, c_void_p, c_size_t, c_void_p]
         L.fl_block_step.argtypes = [POINTER(FlBlockCfg), POINTER(FlLayerWeights),
                                     POINTER(FlBlockState), c_int, c_void_p, c_size_t, c_void_p]
+        L.fl_decode_step.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
+                                     POINTER(FlDecodeInputs), c_int, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
         for name in EXPORTS:
@@ -231,6 +251,13 @@ def fl_block_step(cfg: FlBlockCfg, weights, state: FlBlockState, r, ws, stream=N
     rc = lib().fl_block_step(ctypes.byref(cfg), weights, ctypes.byref(state), r, _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream))
     _check("fl_block_step", rc)
+
+
+def fl_decode_step(cfg: FlDecodeCfg, state: FlDecodeState, inputs: FlDecodeInputs, r, stream=None):
+    """Sec. 4.2 for one new token per sequence: loop r of batched decode."""
+    rc = lib().fl_decode_step(ctypes.byref(cfg), ctypes.byref(state), ctypes.byref(inputs), r,
+                              _stream(stream))
+    _check("fl_decode_step", rc)
 
 
 # --------------------------------------------------------------------------
@@ -404,3 +431,100 @@ class BlockRunner:
 
     def step(self, r, stream=None):
         fl_block_step(self.cfg, self.W, self.state, r, self.ws, stream)
+
+
+class DecodeRunner:
+    """Batched-decode buffers: B sequences' loop-indexed prefix caches (one
+    allocation per level, sequences back to back as ``fl_decode_step``
+    expects) and the new tokens' per-loop state.  ``load_sequence`` fills
+    sequence b's cache through the library (``fl_select_active`` on the given
+    statistic, ``fl_kv_residual_quant`` per level); ``step`` runs loop r."""
+
+    def __init__(self, B, N, H, d, g, R, n_sink, n_active, k_cols, bits, device="cuda"):
+        dev = torch.device(device)
+        self.B, self.N, self.H, self.d, self.g, self.R = B, N, H, d, g, R
+        self.n_active, self.k_cols, self.bits = list(n_active), list(k_cols), list(bits)
+        self._keep = []
+
+        def buf(shape, dt):
+            t = torch.empty(shape, dtype=dt, device=dev)
+            self._keep.append(t)
+            return t
+
+        cfg = FlDecodeCfg()
+        cfg.B, cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = B, N, H, d, g, R, n_sink
+        for r in range(R):
+            cfg.k_cols[r] = k_cols[r]
+        self.cfg = cfg
+        st = FlDecodeState()
+        C = st.cache
+        C.N, C.H, C.d, C.g, C.n_levels = N, H, d, g, R
+        self.codes, self.rows, self.slot = [], [], []
+        for r in range(R):
+            n = N if r == 0 else n_active[r]
+            cb = dict(k=buf((B, n, H, d * bits[r] // 8), torch.uint8),
+                      v=buf((B, n, H, d * bits[r] // 8), torch.uint8),
+                      ks=buf((B, n, H, d // g), torch.float32),
+                      vs=buf((B, n, H, d // g), torch.float32))
+            rows = buf((B, n), torch.int32) if r > 0 else None
+            slot = buf((B, N), torch.int32) if r > 0 else None
+            Lv = C.level[r]
+            Lv.bits, Lv.n_rows = bits[r], n
+            Lv.rows, Lv.slot = _p(rows), _p(slot)
+            Lv.k_codes, Lv.v_codes, Lv.k_scale, Lv.v_scale = _p(cb["k"]), _p(cb["v"]), _p(cb["ks"]), _p(cb["vs"])
+            self.codes.append(cb); self.rows.append(rows); self.slot.append(slot)
+        self.out = buf((B, H, d), torch.float32)
+        self.lse = buf((B, H), torch.float32)
+        self.mass_u = buf((B, H), torch.float32)
+        self.out_u = buf((B, H, d), torch.float32)
+        st.out, st.lse, st.mass_u, st.out_u = _p(self.out), _p(self.lse), _p(self.mass_u), _p(self.out_u)
+        self.sel, self.col_stat = [], []
+        for r in range(R):
+            sl = buf((B, H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < min(k_cols[:r]) else None
+            cs = buf((B, H, min(k_cols[: r + 1])), torch.float32)
+            st.sel[r], st.col_stat[r] = _p(sl), _p(cs)
+            self.sel.append(sl); self.col_stat.append(cs)
+        self.state = st
+
+    def seq_cache(self, b):
+        """FlKvCache of sequence b alone (pointers into the batched buffers)."""
+        c = FlKvCache()
+        c.N, c.H, c.d, c.g, c.n_levels = self.N, self.H, self.d, self.g, self.R
+        for r in range(self.R):
+            Lv = c.level[r]
+            cb = self.codes[r]
+            Lv.bits, Lv.n_rows = self.bits[r], cb["k"].shape[1]
+            Lv.rows = None if r == 0 else _p(self.rows[r][b])
+            Lv.slot = None if r == 0 else _p(self.slot[r][b])
+            Lv.k_codes, Lv.v_codes = _p(cb["k"][b]), _p(cb["v"][b])
+            Lv.k_scale, Lv.v_scale = _p(cb["ks"][b]), _p(cb["vs"][b])
+        return c
+
+    def load_sequence(self, b, k, v, stat, stream=None):
+        """k, v: per-loop bf16 device tensors [N][H][d] of the prefix tokens;
+        stat: per-loop fp32 device tensors [N] (stat[0] unused)."""
+        c = self.seq_cache(b)
+        for r in range(self.R):
+            if r > 0:
+                cand = None if r == 1 else self.rows[r - 1][b]
+                key = stat[r] if cand is None else stat[r].index_select(0, cand.long())
+                fl_select_active(None, None, cand, self.n_active[r], None, self.rows[r][b],
+                                 self.slot[r][b], stat_in=key, N=self.N, stream=stream)
+            fl_kv_residual_quant(c, r, k[r], v[r], gathered=False, stream=stream)
+        self._cache_views = c
+
+    def step(self, r, q, k_self, v_self, q_prev=None, k_prev=None, v_prev=None, stream=None):
+        inp = FlDecodeInputs()
+        inp.q, inp.k_self, inp.v_self = _p(q), _p(k_self), _p(v_self)
+        inp.q_prev, inp.k_self_prev, inp.v_self_prev = _p(q_prev), _p(k_prev), _p(v_prev)
+        fl_decode_step(self.cfg, self.state, inp, r, stream)
+
+    def k_used(self, r):
+        return self.state.k_cur[r - 1]
+
+    def sel_used(self, r):
+        """Selected prefix columns of loop r ([B][H][k]) or None (dense)."""
+        for j in range(r, 0, -1):
+            if self.sel[j - 1] is not None and self.k_cols[j - 1] < min(self.k_cols[: j - 1] or [self.N]):
+                return self.sel[j - 1]
+        return None

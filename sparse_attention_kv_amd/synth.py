@@ -103,6 +103,15 @@ WORKLOADS = {
     # (16 x 128), SwiGLU 5632, RMSNorm (eps 1e-6), RoPE (theta 1e4), R=4,
     # seq 8192; fractions 1/.4/.2/.1, 1024 columns incl. 4 sinks, int8 base,
     # int4 at loop 2 and int2 at loops 3-4, group 64.
+    # batched decode: 64 sequences x 8192 cached tokens (each cache built as
+    # the prefill recipe at N=8192, fractions 1/.4/.2/.1, int8 base + int4
+    # residuals at every loop), one new query per sequence per loop, R=4,
+    # 16 x 128; loop 1 dense over the prefix, loops 2-4 on 256 columns
+    # (4 sinks), plus the token's own column.
+    "decode64x8k": Workload("decode64x8k", N=8192, H=16, d=128, R=4, g=64, n_sink=4,
+                            rho=[1.0, 0.4, 0.2, 0.1], kcols=[8192, 256, 256, 256],
+                            bits=[8, 4, 4, 4], dtype="bf16", seed=3, kind="decode",
+                            sigma_sd=1.5, extra=dict(B=64)),
     "block8k": Workload("block8k", N=8192, H=16, d=128, R=4, g=64, n_sink=4,
                         rho=[1.0, 0.4, 0.2, 0.1], kcols=[8192, 1024, 1024, 1024],
                         bits=[8, 4, 2, 2], dtype="bf16", seed=4, kind="block",
@@ -191,7 +200,61 @@ def gen_block(w: Workload) -> dict:
     return dict(h1=h1, layers=layers, dtype="bf16")
 
 
+def decode_seeds(w: Workload):
+    """Independent seed sequences of the decode batch's sequences."""
+    return np.random.SeedSequence(w.seed).spawn(w.extra["B"])
+
+
+def gen_decode_seq(w: Workload, b: int) -> dict:
+    """Sequence b of the decode batch.
+
+    Prefix of N cached tokens, drawn with the prefill recipe: per-head mean
+    query direction m_h ~ N(0, I_d); K_1, V_1 ~ N(0, I) with boost_frac of
+    the columns (positions >= 4) given K_1 += 3 m_h/|m_h|; loop r >= 2 moves
+    every token by sigma_r(i) * N(0, I) with sigma_r(i) = exp(N(a + b*r,
+    sigma_sd)).  The prefix's hidden states only enter through the selection
+    statistic ||h_r(i) - h_{r-1}(i)||_2, which under this recipe is
+    sigma_r(i) * chi_D (D = H*d), so it is drawn directly as stat[r-1] [N]
+    (None at r = 1).  K and V are given for every position at every loop
+    (the method decides which rows it stores).
+
+    The new token: q_1 = m_h + N(0, I), k_1, v_1 ~ N(0, I) [H][d]; loop
+    r >= 2 adds s_r * N(0, I) to each, s_r = exp(N(a + b*r, sigma_sd)).
+    All K/V/q tensors are bf16 bits."""
+    rng = np.random.Generator(np.random.PCG64(decode_seeds(w)[b]))
+    N, H, d, D = w.N, w.H, w.d, w.D
+    m = rng.standard_normal((H, d), dtype=np.float32)
+    k = rng.standard_normal((N, H, d), dtype=np.float32)
+    v = rng.standard_normal((N, H, d), dtype=np.float32)
+    nb = int(round(w.boost_frac * N))
+    unit = m / np.linalg.norm(m, axis=1, keepdims=True)
+    for hh in range(H):
+        cols = rng.choice(np.arange(4, N), size=nb, replace=False)
+        k[cols, hh, :] += np.float32(3.0) * unit[hh]
+    qn = m + rng.standard_normal((H, d), dtype=np.float32)
+    kn = rng.standard_normal((H, d), dtype=np.float32)
+    vn = rng.standard_normal((H, d), dtype=np.float32)
+    cast = f32_to_bf16_bits
+    ks, vs, stats = [cast(k)], [cast(v)], [None]
+    qs, kns, vns = [cast(qn)], [cast(kn)], [cast(vn)]
+    a, bb = w.sigma_mu
+    for r in range(2, w.R + 1):
+        sig = np.exp(rng.normal(a + bb * r, w.sigma_sd, N)).astype(np.float32)
+        stats.append((sig * np.sqrt(rng.chisquare(D, N)).astype(np.float32)).astype(np.float32))
+        k += sig[:, None, None] * rng.standard_normal((N, H, d), dtype=np.float32)
+        v += sig[:, None, None] * rng.standard_normal((N, H, d), dtype=np.float32)
+        s1 = np.float32(np.exp(rng.normal(a + bb * r, w.sigma_sd)))
+        qn = qn + s1 * rng.standard_normal((H, d), dtype=np.float32)
+        kn = kn + s1 * rng.standard_normal((H, d), dtype=np.float32)
+        vn = vn + s1 * rng.standard_normal((H, d), dtype=np.float32)
+        ks.append(cast(k)); vs.append(cast(v))
+        qs.append(cast(qn)); kns.append(cast(kn)); vns.append(cast(vn))
+    return dict(stat=stats, k=ks, v=vs, q_new=qs, k_new=kns, v_new=vns, dtype="bf16")
+
+
 def generate(w: Workload) -> dict:
+    if w.kind == "decode":
+        raise ValueError("decode inputs are drawn per sequence: gen_decode_seq(w, b)")
     if w.kind == "block":
         return gen_block(w)
     if w.kind == "tiny":

@@ -150,3 +150,21 @@ def test_loop_step_rejects(L):
     st.cache.N, st.cache.H, st.cache.d, st.cache.g = 64, 2, 128, 64
     assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
     assert "q/k/v" in _err(L)
+
+
+def test_decode_step_rejects(L):
+    cfg = fl.FlDecodeCfg()
+    cfg.B, cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = 2, 64, 2, 128, 64, 2, 4
+    st = fl.FlDecodeState()
+    inp = fl.FlDecodeInputs()
+    assert L.fl_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 3, None) == -1
+    assert L.fl_decode_step(None, ctypes.byref(st), ctypes.byref(inp), 1, None) == -1
+    assert L.fl_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None) == -1
+    assert "cache dims" in _err(L)
+    cfg.N = 20000
+    assert L.fl_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None) == -1
+    assert "LDS" in _err(L)
+    cfg.N = 64
+    st.cache = _cache(N=64, H=2, d=128, g=64, bits=(8, 4))
+    assert L.fl_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None) == -1
+    assert "q/k_self/v_self" in _err(L)

@@ -1,0 +1,127 @@
+"""Pins of the decode oracle (oracle/decode.py) against closed forms written
+here in float64 numpy, independent of the C oracle's arithmetic:
+
+* loop 1 and every loop with an unpruned budget equal plain softmax
+  attention of the token's query over the prefix's loop-r dequantised keys
+  plus its own key (FlashLoop paper, Sec. 4.2 with S = all columns);
+* the pruned-column mass at the first pruning loop is one minus the previous
+  loop's probability of the kept columns and the self column (Sec. 4.2);
+* a loop whose query, self key/value and (unquantised) cache are those of
+  the previous loop reproduces the previous dense output exactly (up to rounding): the
+  cached mass and partial output restore the full softmax (Sec. 4.2);
+* the cache keeps nested active sets of the scheduled sizes and carries the
+  inactive tokens' values (Sec. 4.1, 4.3)."""
+import numpy as np
+
+import oracle
+from oracle import decode as od
+from sparse_attention_kv_amd import synth
+
+
+def _sched(N=300, H=2, d=64, R=3, kcols=(300, 40, 20), rho=(1.0, 0.5, 0.25), bits=(8, 4, 2)):
+    return dict(N=N, H=H, d=d, g=32, R=R, n_sink=4, rho=list(rho), kcols=list(kcols),
+                bits=list(bits))
+
+
+def _inputs(sched, seed=5, frozen=False):
+    w = synth.WORKLOADS["decode64x8k"].scaled(N=sched["N"], H=sched["H"], d=sched["d"],
+                                              R=sched["R"], g=sched["g"], rho=sched["rho"],
+                                              kcols=sched["kcols"], bits=sched["bits"], seed=seed)
+    w.extra = dict(B=1)
+    x = synth.gen_decode_seq(w, 0)
+    f = synth.bf16_bits_to_f32
+    k = [f(a) for a in x["k"]]; v = [f(a) for a in x["v"]]
+    q = [f(a) for a in x["q_new"]]; ks = [f(a) for a in x["k_new"]]; vs = [f(a) for a in x["v_new"]]
+    if frozen:   # nothing moves after loop 1
+        k = [k[0]] * sched["R"]; v = [v[0]] * sched["R"]
+        q = [q[0]] * sched["R"]; ks = [ks[0]] * sched["R"]; vs = [vs[0]] * sched["R"]
+    return k, v, x["stat"], q, ks, vs
+
+
+def _dense64(q, K, V, sm):
+    """[H][d] query, [n][H][d] keys/values -> out [H][d], lse [H], P [H][n]."""
+    s = np.einsum("hd,nhd->hn", q.astype(np.float64), K.astype(np.float64)) * float(sm)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    P = e / z
+    return np.einsum("hn,nhd->hd", P, V.astype(np.float64)), (m + np.log(z))[:, 0], P
+
+
+def test_cache_nested_and_carried():
+    sc = _sched()
+    k, v, stat, *_ = _inputs(sc)
+    cache = od.build_cache(k, v, stat, sc)
+    n_prev, A_prev = sc["N"], np.arange(sc["N"])
+    for r, lv in enumerate(cache, start=1):
+        A = lv["active"]
+        assert len(A) == oracle.active_count(sc["rho"][r - 1], sc["N"], n_prev)
+        assert np.all(np.diff(A) > 0) and np.isin(A, A_prev).all()
+        if r > 1:
+            # top by statistic among the previous active set
+            key = stat[r - 1][A_prev]
+            thr = np.sort(key)[::-1][len(A) - 1]
+            assert np.all(stat[r - 1][A] >= thr)
+            rest = np.setdiff1d(np.arange(sc["N"]), A)
+            np.testing.assert_array_equal(lv["khat"][rest], cache[r - 2]["khat"][rest])
+            np.testing.assert_array_equal(lv["vhat"][rest], cache[r - 2]["vhat"][rest])
+            # the stored level moves the active rows towards this loop's values
+            e_new = np.abs(lv["khat"][A] - k[r - 1][A]).mean()
+            e_old = np.abs(cache[r - 2]["khat"][A] - k[r - 1][A]).mean()
+            assert e_new < e_old
+        n_prev, A_prev = len(A), A
+
+
+def test_unpruned_loops_are_dense_softmax():
+    sc = _sched(kcols=(300, 300, 300))
+    k, v, stat, q, ks, vs = _inputs(sc)
+    cache = od.build_cache(k, v, stat, sc)
+    recs = od.run_decode(cache, q, ks, vs, sc)
+    sm = 1.0 / np.sqrt(sc["d"])
+    for r, rec in enumerate(recs, start=1):
+        K = np.concatenate([cache[r - 1]["khat"], ks[r - 1][None]])
+        V = np.concatenate([cache[r - 1]["vhat"], vs[r - 1][None]])
+        o, lse, _ = _dense64(q[r - 1], K, V, sm)
+        np.testing.assert_allclose(rec["out"], o, rtol=0, atol=2e-5)
+        np.testing.assert_allclose(rec["lse"], lse, rtol=0, atol=2e-5)
+        assert np.all(rec["mass_u"] == 0)
+
+
+def test_first_pruning_mass_and_statistic():
+    sc = _sched()
+    k, v, stat, q, ks, vs = _inputs(sc)
+    cache = od.build_cache(k, v, stat, sc)
+    recs = od.run_decode(cache, q, ks, vs, sc)
+    sm = 1.0 / np.sqrt(sc["d"])
+    K = np.concatenate([cache[0]["khat"], ks[0][None]])
+    V = np.concatenate([cache[0]["vhat"], vs[0][None]])
+    _, _, P1 = _dense64(q[0], K, V, sm)
+    # loop-1 statistic: the probability of every prefix column
+    np.testing.assert_allclose(recs[0]["cstat"], P1[:, :sc["N"]], rtol=1e-4, atol=1e-7)
+    S2 = recs[1]["sel"]
+    assert S2.shape == (sc["H"], sc["kcols"][1])
+    for h in range(sc["H"]):
+        assert set(range(sc["n_sink"])) <= set(S2[h].tolist())
+        kept = P1[h, S2[h]].sum() + P1[h, sc["N"]]
+        assert abs(recs[1]["mass_u"][h] - (1.0 - kept)) < 2e-6
+        # the kept non-sink columns are the most probable ones
+        rest = np.setdiff1d(np.arange(sc["n_sink"], sc["N"]), S2[h])
+        kept_ns = np.setdiff1d(S2[h], np.arange(sc["n_sink"]))
+        assert P1[h, kept_ns].min() >= P1[h, rest].max()
+        # O_U: the pruned columns' share of the loop-1 output
+        pruned = np.setdiff1d(np.arange(sc["N"]), S2[h])
+        ou = (P1[h, pruned][:, None] * V[pruned, h].astype(np.float64)).sum(0)
+        np.testing.assert_allclose(recs[1]["out_u"][h], ou, rtol=0, atol=2e-5)
+
+
+def test_frozen_loops_restore_dense_output():
+    # raw (unquantised) levels: an unchanged value then stores a zero residual
+    sc = _sched(bits=(32, 32, 32))
+    k, v, stat, q, ks, vs = _inputs(sc, frozen=True)
+    cache = od.build_cache(k, v, stat, sc)
+    recs = od.run_decode(cache, q, ks, vs, sc)
+    for r in (2, 3):
+        assert recs[r - 1]["sel"] is not None
+        np.testing.assert_allclose(recs[r - 1]["out"], recs[0]["out"], rtol=0, atol=3e-5)
+        np.testing.assert_allclose(recs[r - 1]["lse"] - np.log1p(-recs[r - 1]["mass_u"].astype(np.float64)),
+                                   recs[0]["lse"], rtol=0, atol=3e-5)
