@@ -30,6 +30,11 @@ if ROOT not in sys.path:
 METRIC = "active-query tokens/s of loop-r sparse attention @32K, R=4; KV bytes/token; %roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
+KERNEL_SYMBOL = {"attn": "k_attn<128, 0, 0, false>", "attn_split": "k_attn<128, 0, 1, false>",
+                 "attn_rebuild": "k_attn<128, 1, 0, false>", "colstat": "k_colstat_pipe<128, 0>",
+                 "colstat_split": "k_colstat_pipe<128, 1>", "decode_dense": "k_decode<128, 0, false>",
+                 "decode": "k_decode<128, 0, true>", "decode_rebuild": "k_decode<128, 1, true>"}
 
 
 def parse():
@@ -42,6 +47,9 @@ def parse():
                     help="query rows per loop in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     ap.add_argument("--mode", default="auto", choices=["auto", "once", "in_tile"],
                     help="where the cache is dequantised (library default: auto)")
     return ap.parse_args()
@@ -49,6 +57,29 @@ def parse():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_traffic(workload, kernel):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 PMC
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a reference copy), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.rstrip("\n").split("\t")
+        if f[0] != kernel:
+            continue
+        src, digest = f[1].split(":")
+        h = hashlib.sha256()
+        for p in (src, "fl_device.h", "fl_kernels.h"):
+            with open(os.path.join(ROOT, "sparse_attention_kv_amd", "csrc", p), "rb") as fh:
+                h.update(fh.read())
+        return int(f[5]) if h.hexdigest()[:16] == digest else None
+    return None
 
 
 def pairs_per_head(torch, act, sel, N):
@@ -75,6 +106,13 @@ def main():
 
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] reference copy of {args.calib_copy_mib} MiB done")
     if w.kind == "block":
         return bench_block(args, w, np, torch, fl, synth)
     if w.kind == "decode":
@@ -178,7 +216,9 @@ def main():
         if dom in flops_step:
             ach = flops_step[dom] / (kernels[dom]["ms_per_step"] / 1e3) / 1e12
             roofline = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS,
-                            unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                            unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4),
+                            traffic=kernel_traffic(w.name, KERNEL_SYMBOL.get(dom, dom)),
+                            kernel_symbol=KERNEL_SYMBOL.get(dom, dom),
                             flops_per_step=flops_step[dom],
                             avg_launch_us=kernels[dom]["avg_launch_us"])
         else:
@@ -476,9 +516,10 @@ def bench_decode(args, w, np, torch, fl, synth):
         per_launch = dense_bytes
         ach = per_launch / (kd["avg_launch_us"] / 1e6) / 1e9
         kd["gbs"] = round(ach, 1)
-        roof = dict(kernel="k_decode<128,MODE_ATTN,dense> (loop 1)", bound="hbm", achieved=round(ach, 1),
-                    peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
-                    bytes_per_launch=per_launch)
+        sym = KERNEL_SYMBOL["decode_dense"]
+        roof = dict(kernel="decode_dense", kernel_symbol=sym, bound="hbm", achieved=round(ach, 1),
+                    peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
+                    traffic=kernel_traffic(w.name, sym), bytes_per_launch=per_launch)
     if "decode" in kernels and sparse_bytes:
         kd = kernels["decode"]
         avg_b = sum(sparse_bytes.values()) / len(sparse_bytes)

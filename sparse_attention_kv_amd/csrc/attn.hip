@@ -539,6 +539,243 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Attention over compact bf16 tiles with an asynchronous two-buffer LDS
+// pipeline: the next K / V^T tile is copied straight from global memory into
+// the other LDS buffer (gfx950 LDS-DMA loads, 16 bytes per lane, no register
+// staging) while the current tile is computed, so one barrier per tile and
+// no exposed load latency.  A wave's LDS-DMA copy lands 64 consecutive
+// 16-byte chunks, so the tiles are stored XOR-swizzled (chunk c of row x at
+// c ^ (x & 7)): the lanes' global addresses apply the swizzle, and the
+// MFMA operand reads (eight rows at one logical chunk per LDS cycle) stay
+// free of bank conflicts.  The two buffers are distinct LDS objects so the
+// compiler's wait-count analysis sees that reads of one do not wait for
+// copies into the other.  Arithmetic as k_attn (PREC 0/1, DEQ off).
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+template <int D, int MODE, int PREC>
+__global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams P) {
+    static_assert(PREC == 0 || PREC == 1, "bf16 queries only");
+    constexpr bool X3 = PREC >= 1;
+    constexpr int NP = X3 ? 2 : 1;
+    constexpr int TB = BN * D * 2;          // bytes of one operand tile
+    constexpr int MPW = TB / 1024 / 4;      // LDS-DMA instructions per wave per operand tile
+    __shared__ __attribute__((aligned(1024))) __bf16 sK0[NP][BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV0[NP][D * BN];
+    __shared__ __attribute__((aligned(1024))) __bf16 sK1[NP][BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[NP][D * BN];
+    __shared__ __attribute__((aligned(256))) int sC0[BN];
+    __shared__ __attribute__((aligned(256))) int sC1[BN];
+    __shared__ int s_bounds[2];
+    const int n_tiles = (P.n + BM - 1) / BM;
+    int tile, h;
+    block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 31, half = lane >> 5;
+    const int t0 = tile * BM;
+    const int t = t0 + w * 32 + r;
+    const bool valid = t < P.n;
+    const int rowpos = valid ? P.active[t] : -1;
+    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
+    if (tid == 0) {
+        const int tl = min(t0 + BM, P.n) - 1;
+        s_bounds[0] = upper_bound_i32(cpos_h, P.k, P.active[tl]); // p_end
+        s_bounds[1] = upper_bound_i32(cpos_h, P.k, P.active[t0]); // p_full
+    }
+    bf16x8 qf[D / 16];
+    {
+        const long qrow = P.q_gathered ? (long)t : (long)rowpos;
+        const long qoff = (qrow * P.H + h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            if (valid) qf[kk] = load8_bf16(P.q, qoff + 16 * kk, P.dtype);
+            else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.0f;
+            }
+        }
+    }
+    const long rh = valid ? (long)rowpos * P.H + h : 0;
+    float lse_prev2 = 0.0f, wgt = 1.0f;
+    if (MODE == MODE_REBUILD && valid) {
+        lse_prev2 = P.lse[rh] * 1.4426950408889634f;
+        wgt = 1.0f - P.mass_u[rh];
+    }
+    __syncthreads();
+    const int p_end = __builtin_amdgcn_readfirstlane(s_bounds[0]);
+    const int p_full = __builtin_amdgcn_readfirstlane(s_bounds[1]);
+
+    const long koff = (long)h * P.kp * D;
+    const long voff = (long)h * (P.kp / BN) * D * BN;
+    // copy the tile at column p0 into one LDS buffer (swizzled, see above)
+    auto issue = [&](int p0, __bf16 (*sK)[BN * D], __bf16 (*sV)[BN * D], int* sC) {
+#pragma unroll
+        for (int part = 0; part < NP; ++part) {
+            const char* kg = reinterpret_cast<const char*>((part ? P.Kc_lo : P.Kc) + koff + (long)p0 * D);
+            const char* vg = reinterpret_cast<const char*>((part ? P.Vt_lo : P.Vt) + voff +
+                                                           (long)(p0 / BN) * D * BN);
+#pragma unroll
+            for (int i = 0; i < MPW; ++i) {
+                const int m = w * MPW + i;
+                const int off = m * 1024 + lane * 16;
+                const int kr = off / (D * 2), kc = ((off % (D * 2)) >> 4) ^ (kr & 7);
+                lds_dma16(kg + kr * (D * 2) + kc * 16, reinterpret_cast<char*>(sK[part]) + m * 1024);
+                const int vr = off >> 7, vc = ((off & 127) >> 4) ^ (vr & 7);
+                lds_dma16(vg + vr * 128 + vc * 16, reinterpret_cast<char*>(sV[part]) + m * 1024);
+            }
+        }
+        if (w == 0) lds_dma4(cpos_h + p0 + lane, sC);
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    auto compute = [&](int p0, const __bf16 (*sK)[BN * D], const __bf16 (*sV)[BN * D], const int* sC) {
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
+            const int key = 32 * kt + r;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int e = key * D + (((2 * kk + half) ^ (key & 7)) << 3);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[0][e]);
+                s[kt] = mfma32(a, qf[kk], s[kt]);
+                if (X3) {
+                    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sK[NP - 1][e]);
+                    s[kt] = mfma32(al, qf[kk], s[kt]);
+                }
+            }
+        }
+        if (p0 + BN > p_full) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = 32 * kt + (j >> 2) * 8 + half * 4 + (j & 3);
+                    if (sC[key] > rowpos) s[kt][j] = -INFINITY;
+                }
+        }
+        bf16x8 pb[2][2], pl[X3 ? 2 : 1][2];
+        if (MODE == MODE_ATTN) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m_run, tmax * P.c2);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            if (__ballot(m_new > m_run)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+            }
+            m_run = m_new;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
+                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
+                    l_run += pj;
+                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float pj = wgt * __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -lse_prev2));
+                    l_run += pj;
+                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
+                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
+                }
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int row = 32 * dt + r;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int jh = 0; jh < 2; ++jh) {
+                    const int e = row * BN + (((4 * kt + 2 * jh + half) ^ (row & 7)) << 3);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[0][e]);
+                    o[dt] = mfma32(a, pb[kt][jh], o[dt]);
+                    if (X3) {
+                        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sV[NP - 1][e]);
+                        o[dt] = mfma32(a, pl[X3 ? kt : 0][jh], o[dt]);
+                        o[dt] = mfma32(al, pb[kt][jh], o[dt]);
+                    }
+                }
+        }
+    };
+
+    if (p_end > 0) issue(0, sK0, sV0, sC0);
+    for (int p0 = 0; p0 < p_end;) {
+        __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the current tile landed
+        __syncthreads();               // ... every lane's; the other buffer is free
+        if (p0 + BN < p_end) issue(p0 + BN, sK1, sV1, sC1);
+        compute(p0, sK0, sV0, sC0);
+        p0 += BN;
+        if (p0 >= p_end) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (p0 + BN < p_end) issue(p0 + BN, sK0, sV0, sC0);
+        compute(p0, sK1, sV1, sC1);
+        p0 += BN;
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!valid) return;
+    float* orow = P.out + rh * D;
+    if (MODE == MODE_ATTN) {
+        const float mu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
+        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
+        const float* ourow = P.out_u + rh * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * dt + jq * 8 + half * 4;
+                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (P.cache_op != FL_CACHE_ZERO) u = *reinterpret_cast<const float4*>(ourow + d0);
+                float4 v;
+                v.x = o[dt][4 * jq + 0] * scale + u.x;
+                v.y = o[dt][4 * jq + 1] * scale + u.y;
+                v.z = o[dt][4 * jq + 2] * scale + u.z;
+                v.w = o[dt][4 * jq + 3] * scale + u.w;
+                *reinterpret_cast<float4*>(orow + d0) = v;
+            }
+        if (half == 0)
+            P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    } else {
+        float* ourow = P.out_u + rh * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+                const int d0 = 32 * dt + jq * 8 + half * 4;
+                const float4 op = *reinterpret_cast<const float4*>(orow + d0);
+                float4 v;
+                v.x = op.x - o[dt][4 * jq + 0];
+                v.y = op.y - o[dt][4 * jq + 1];
+                v.z = op.z - o[dt][4 * jq + 2];
+                v.w = op.w - o[dt][4 * jq + 3];
+                *reinterpret_cast<float4*>(ourow + d0) = v;
+            }
+        if (half == 0) P.mass_u[rh] = 1.0f - l_tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
     int lo = 0, hi = n;
@@ -645,7 +882,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
 // Column statistics for bf16 queries (PREC 0/1): 64-row steps through a
 // two-buffer LDS pipeline (the next rows are loaded into registers while the
 // current ones are used), each wave covering its 32 columns for both 32-row
-// halves of a step.  The weight 1 - M_U is folded into a per-row exponent
+// halves of a step; steps run from the last row down to the diagonal.  The weight 1 - M_U is folded into a per-row exponent
 // offset (off = lse*log2(e) - log2(1 - M_U)), so a pair costs one fma, one
 // exp2 and one add; the causal mask is only applied on diagonal steps.
 constexpr int RT2 = 64;
@@ -721,17 +958,22 @@ __global__ __launch_bounds__(256, 2) void k_colstat_pipe(ColParams P) {
         }
         if (tid < RT2) { rpos[bb][tid] = pr; roff[bb][tid] = orr; }
     };
-    if (t_start < P.n) {
-        gload(t_start);
+    // the steps are taken from the last one down to the block's diagonal, so
+    // every block of a head starts on the same rows: blocks resident together
+    // on one XCD then read each query step once through its L2
+    const int nsteps = t_start < P.n ? (P.n - t_start + RT2 - 1) / RT2 : 0;
+    const int t_last = t_start + (nsteps - 1) * RT2;
+    if (nsteps > 0) {
+        gload(t_last);
         lstore(0);
     }
     __syncthreads();
     float csum = 0.0f;
-    int it = 0;
-    for (int t0 = t_start; t0 < P.n; t0 += RT2, ++it) {
+    for (int it = 0; it < nsteps; ++it) {
+        const int t0 = t_last - it * RT2;
         const int b = it & 1;
-        const bool more = t0 + RT2 < P.n;
-        if (more) gload(t0 + RT2);
+        const bool more = it + 1 < nsteps;
+        if (more) gload(t0 - RT2);
         // every row of the step at or after every column of the block?
         const bool full = rpos[b][0] >= cmax && t0 + RT2 <= P.n;
 #pragma unroll
@@ -765,6 +1007,167 @@ __global__ __launch_bounds__(256, 2) void k_colstat_pipe(ColParams P) {
     if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
 }
 
+// Column statistics with the Q steps copied by LDS-DMA into two distinct LDS
+// buffers (swizzled as in k_attn_lds): one barrier per 64-row step, the next
+// step's rows land while the current one is computed.  The per-row exponent
+// offsets and positions are prefetched through registers by one wave.
+// Arithmetic as k_colstat_pipe.
+template <int D, int PREC>
+__global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
+    constexpr bool X3 = PREC >= 1;
+    constexpr int QB = RT2 * D * 2;         // bytes of one step's query rows
+    constexpr int MPW = QB / 1024 / 4;      // LDS-DMA instructions per wave per step
+    __shared__ __attribute__((aligned(1024))) __bf16 sQ0[RT2 * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sQ1[RT2 * D];
+    __shared__ int rp0[RT2], rp1[RT2];
+    __shared__ float ro0[RT2], ro1[RT2];
+    __shared__ int s_start, s_cmax;
+    const int h = blockIdx.y;
+    const int pc0 = blockIdx.x * CT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 31, half = lane >> 5;
+    const int p = pc0 + w * 32 + r;
+    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
+    const bool colv = p < P.k;
+    const int cp = colv ? cpos_h[p] : 0x7fffffff;
+    bf16x8 kf[D / 16], kl[X3 ? D / 16 : 1];
+    {
+        const long ko = ((long)h * P.kp + (colv ? p : 0)) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            kf[kk] = *reinterpret_cast<const bf16x8*>(P.Kc + ko + 16 * kk);
+            if (X3) kl[X3 ? kk : 0] = *reinterpret_cast<const bf16x8*>(P.Kc_lo + ko + 16 * kk);
+        }
+    }
+    if (tid == 0) {
+        s_start = lower_bound_i32(P.active, P.n, cpos_h[pc0]);
+        s_cmax = cpos_h[min(pc0 + CT, P.k) - 1];
+    }
+    __syncthreads();
+    const int t_start = __builtin_amdgcn_readfirstlane(s_start);
+    const int cmax = __builtin_amdgcn_readfirstlane(s_cmax);
+    const int nsteps = t_start < P.n ? (P.n - t_start + RT2 - 1) / RT2 : 0;
+    const int t_last = t_start + (nsteps - 1) * RT2;
+    // this thread's LDS-DMA rows inside a step and their logical chunk
+    int drow[MPW], dchunk[MPW];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int off = (w * MPW + i) * 1024 + lane * 16;
+        drow[i] = off / (D * 2);
+        dchunk[i] = ((off % (D * 2)) >> 4) ^ (drow[i] & 7);
+    }
+    // Query rows of a step are addressed through their positions, which are
+    // loaded one step ahead of the copy (two ahead of the compute), so no
+    // copy waits on a dependent load.  Rows past n repeat row n-1; their
+    // offset is +inf and position -1, so they add nothing.
+    // (kept as int until used: widening a just-loaded value would wait for it)
+    int qr_next[MPW];
+    auto load_rows = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const int tt = min(t0 + drow[i], P.n - 1);
+            qr_next[i] = P.q_gathered ? tt : P.active[tt];
+        }
+    };
+    auto issue = [&](__bf16* sQ) {
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            const char* src = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.q) +
+                                                            ((long)qr_next[i] * P.H + h) * D) + dchunk[i] * 16;
+            lds_dma16(src, reinterpret_cast<char*>(sQ) + (w * MPW + i) * 1024);
+        }
+    };
+    // wave 0: lane l's row position (loaded a step ahead) and its exponent
+    // offset lse*log2(e) - log2(1 - M_U)
+    int mpos_next = -1, mpos = -1;
+    float mlse = 0.0f, mmu = 0.0f;
+    auto meta_pos = [&](int t0) {
+        const int tt = t0 + lane;
+        mpos_next = tt < P.n ? P.active[tt] : -1;
+    };
+    auto meta_vals = [&]() {
+        mpos = mpos_next;
+        if (mpos >= 0) {
+            const long rh = (long)mpos * P.H + h;
+            mlse = P.lse[rh];
+            mmu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
+        }
+    };
+    auto meta_store = [&](int* rp, float* ro) {
+        const float wgt = fmaxf(1.0f - mmu, 0.0f);
+        rp[lane] = mpos;
+        ro[lane] = mpos >= 0 ? mlse * 1.4426950408889634f - __log2f(wgt) : INFINITY;
+    };
+    float csum = 0.0f;
+    auto compute = [&](int t0, const __bf16* sQ, const int* rpos, const float* roff) {
+        const bool full = rpos[0] >= cmax && t0 + RT2 <= P.n;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            f32x16 s = f32x16{};
+            const int row = 32 * sub + r;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int e = row * D + (((2 * kk + half) ^ (row & 7)) << 3);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[e]);
+                s = mfma32(a, kf[kk], s);
+                if (X3) s = mfma32(a, kl[X3 ? kk : 0], s);
+            }
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
+                    csum += __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[rw]));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
+                    const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[rw]));
+                    csum += (rpos[rw] >= cp) ? pj : 0.0f;
+                }
+            }
+        }
+    };
+    // prologue: step 0 copied and its metadata stored; positions of step 1
+    if (nsteps > 0) {
+        load_rows(t_last);
+        issue(sQ0);
+        if (w == 0) {
+            meta_pos(t_last);
+            meta_vals();
+            meta_store(rp0, ro0);
+        }
+        if (nsteps > 1) {
+            load_rows(t_last - RT2);
+            if (w == 0) meta_pos(t_last - RT2);
+        }
+    }
+    // steps from the last one down to the block's diagonal (see k_colstat_pipe);
+    // iteration it computes step it, copies step it+1, loads positions of it+2
+    for (int it = 0; it < nsteps;) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int t0 = t_last - it * RT2;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const bool more = it + 1 < nsteps;
+            if (more) {
+                issue(b ? sQ0 : sQ1);
+                if (w == 0) meta_vals();
+                if (it + 2 < nsteps) {
+                    load_rows(t0 - 2 * RT2);
+                    if (w == 0) meta_pos(t0 - 2 * RT2);
+                }
+            }
+            compute(t0, b ? sQ1 : sQ0, b ? rp1 : rp0, b ? ro1 : ro0);
+            if (more && w == 0) meta_store(b ? rp0 : rp1, b ? ro0 : ro1);
+            if (++it >= nsteps) break;
+        }
+    }
+    csum += __shfl_xor(csum, 32);
+    if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
@@ -790,14 +1193,23 @@ hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, i
     return hipGetLastError();
 }
 
+// the LDS-DMA pipelined kernels for bf16 queries; with hi/lo operand pairs
+// (PREC 1) the doubled tiles leave one workgroup per CU and the register-
+// staged kernel measured faster (0.87 vs 1.11 ms for the 32K sparse loops)
+static bool lds_path(int prec) { return prec == 0; }
+
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st) {
     const int n_tiles = (P.n + BM - 1) / BM;
     AttnParams Q = P;
     Q.xcd_remap = (P.H % 8) == 0;
     dim3 grid(n_tiles * P.H);
 #define FL_ATTN(D_, M_, P_, Q_) hipLaunchKernelGGL((k_attn<D_, M_, P_, Q_>), grid, dim3(256), 0, st, Q)
-#define FL_ATTN_Q(D_, M_, P_) \
-    if (in_tile) FL_ATTN(D_, M_, P_, true); else FL_ATTN(D_, M_, P_, false);
+#define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_>), grid, dim3(256), 0, st, Q)
+    // bf16 queries over compact bf16 tiles: the LDS-DMA pipelined kernel
+#define FL_ATTN_Q(D_, M_, P_)                                   \
+    if (in_tile) FL_ATTN(D_, M_, P_, true);                    \
+    else if (P_ <= 1 && lds_path(P_)) FL_ATTN_LDS(D_, M_, (P_ <= 1 ? P_ : 0)); \
+    else FL_ATTN(D_, M_, P_, false);
 #define FL_ATTN_M(D_, M_) \
     if (prec == 0) { FL_ATTN_Q(D_, M_, 0) } else if (prec == 1) { FL_ATTN_Q(D_, M_, 1) } else { FL_ATTN_Q(D_, M_, 2) }
 #define FL_ATTN_D(D_) \
@@ -806,6 +1218,7 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
 #undef FL_ATTN_D
 #undef FL_ATTN_M
 #undef FL_ATTN_Q
+#undef FL_ATTN_LDS
 #undef FL_ATTN
     return hipGetLastError();
 }
@@ -814,10 +1227,12 @@ hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
     dim3 grid((P.k + CT - 1) / CT, P.H);
 #define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
 #define FL_COLP(D_, P_) hipLaunchKernelGGL((k_colstat_pipe<D_, P_>), grid, dim3(256), 0, st, P)
+#define FL_COLL(D_, P_) hipLaunchKernelGGL((k_colstat_lds<D_, P_>), grid, dim3(256), 0, st, P)
 #define FL_COL_D(D_) \
-    if (prec == 0) FL_COLP(D_, 0); else if (prec == 1) FL_COLP(D_, 1); else FL_COL(D_, 2);
+    if (prec == 0) FL_COLL(D_, 0); else if (prec == 1) FL_COLL(D_, 1); else FL_COL(D_, 2);
     if (d == 128) { FL_COL_D(128) } else { FL_COL_D(64) }
 #undef FL_COL_D
+#undef FL_COLL
 #undef FL_COLP
 #undef FL_COL
     return hipGetLastError();
