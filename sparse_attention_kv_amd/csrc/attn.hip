@@ -543,13 +543,39 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 // pipeline: the next K / V^T tile is copied straight from global memory into
 // the other LDS buffer (gfx950 LDS-DMA loads, 16 bytes per lane, no register
 // staging) while the current tile is computed, so one barrier per tile and
-// no exposed load latency.  A wave's LDS-DMA copy lands 64 consecutive
+// no exposed load latency.  (Running keys one tile ahead of values, to
+// overlap the next tile's QK^T with this tile's softmax inside a wave, needs
+// more than the 256 registers per lane of two waves per SIMD: it spilled.)
+// A wave's LDS-DMA copy lands 64 consecutive
 // 16-byte chunks, so the tiles are stored XOR-swizzled (chunk c of row x at
-// c ^ (x & 7)): the lanes' global addresses apply the swizzle, and the
-// MFMA operand reads (eight rows at one logical chunk per LDS cycle) stay
-// free of bank conflicts.  The two buffers are distinct LDS objects so the
+// c ^ swz(x)): the lanes' global addresses apply the swizzle, and the MFMA
+// operand reads (sixteen rows at one logical chunk per LDS cycle) stay free
+// of bank conflicts.  The two buffers are distinct LDS objects so the
 // compiler's wait-count analysis sees that reads of one do not wait for
 // copies into the other.  Arithmetic as k_attn (PREC 0/1, DEQ off).
+// 16-byte-chunk swizzle of a tile row with CPR chunks: the 16 lanes that one
+// 128-bit LDS read serves per cycle (16 consecutive rows at one logical
+// chunk) land on 16 distinct chunk slots of a 256-byte bank window.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "rows of 64, 128 or 256 bytes");
+    return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 data-format word); a
+// copy through it takes a scalar base, a per-lane 32-bit offset and a
+// scalar offset, so issuing it costs no vector instructions, and offsets
+// past `bytes` read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
@@ -557,24 +583,27 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
 
-template <int D, int MODE, int PREC>
-__global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams P) {
+template <int D, int MODE, int PREC, int BT>
+__global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_attn_lds(AttnParams P) {
     static_assert(PREC == 0 || PREC == 1, "bf16 queries only");
     constexpr bool X3 = PREC >= 1;
     constexpr int NP = X3 ? 2 : 1;
-    constexpr int TB = BN * D * 2;          // bytes of one operand tile
+    static_assert(BT == 32 || BT == 64, "32- or 64-column tiles");
+    constexpr int KT = BT / 32;             // 32-column MFMA blocks per tile
+    constexpr int TB = BT * D * 2;          // bytes of one operand tile
     constexpr int MPW = TB / 1024 / 4;      // LDS-DMA instructions per wave per operand tile
-    __shared__ __attribute__((aligned(1024))) __bf16 sK0[NP][BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV0[NP][D * BN];
-    __shared__ __attribute__((aligned(1024))) __bf16 sK1[NP][BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV1[NP][D * BN];
-    __shared__ __attribute__((aligned(256))) int sC0[BN];
-    __shared__ __attribute__((aligned(256))) int sC1[BN];
+    __shared__ __attribute__((aligned(1024))) __bf16 sK0[NP][BT * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV0[NP][D * BT];
+    __shared__ __attribute__((aligned(1024))) __bf16 sK1[NP][BT * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[NP][D * BT];
+    __shared__ __attribute__((aligned(256))) int sC0[64];
+    __shared__ __attribute__((aligned(256))) int sC1[64];
     __shared__ int s_bounds[2];
     const int n_tiles = (P.n + BM - 1) / BM;
     int tile, h;
     block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
     const int t0 = tile * BM;
     const int t = t0 + w * 32 + r;
@@ -611,24 +640,37 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
 
     const long koff = (long)h * P.kp * D;
     const long voff = (long)h * (P.kp / BN) * D * BN;
-    // copy the tile at column p0 into one LDS buffer (swizzled, see above)
-    auto issue = [&](int p0, __bf16 (*sK)[BN * D], __bf16 (*sV)[BN * D], int* sC) {
+    constexpr int KCPR = D * 2 / 16, VCPR = BT * 2 / 16;
+    // copy the tile at column p0 into one LDS buffer (swizzled, see above);
+    // a 32-column tile is one half of the stored 64-column V^T tile
+    const uint32_t kbytes = (uint32_t)P.kp * D * 2, vbytes = kbytes;
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(P.Kc + koff, kbytes), rV = make_rsrc(P.Vt + voff, vbytes);
+    const __amdgpu_buffer_rsrc_t rKl = make_rsrc(X3 ? P.Kc_lo + koff : P.Kc, kbytes);
+    const __amdgpu_buffer_rsrc_t rVl = make_rsrc(X3 ? P.Vt_lo + voff : P.Vt, vbytes);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(cpos_h, (uint32_t)P.kp * 4);
+    // per-lane byte offsets of this wave's copies inside a tile
+    uint32_t kvo[MPW], vvo[MPW];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int off = (w * MPW + i) * 1024 + lane * 16;
+        const int kr = off / (D * 2), kc = ((off % (D * 2)) >> 4) ^ swz<KCPR>(kr);
+        kvo[i] = kr * (D * 2) + kc * 16;
+        const int vr = off / (BT * 2), vc = ((off % (BT * 2)) >> 4) ^ swz<VCPR>(vr);
+        vvo[i] = vr * (BN * 2) + vc * 16;
+    }
+    auto issue = [&](int p0, __bf16 (*sK)[BT * D], __bf16 (*sV)[BT * D], int* sC) {
+        const uint32_t ks = (uint32_t)p0 * D * 2;
+        const uint32_t vs = ((uint32_t)(p0 / BN) * D * BN + p0 % BN) * 2;
 #pragma unroll
         for (int part = 0; part < NP; ++part) {
-            const char* kg = reinterpret_cast<const char*>((part ? P.Kc_lo : P.Kc) + koff + (long)p0 * D);
-            const char* vg = reinterpret_cast<const char*>((part ? P.Vt_lo : P.Vt) + voff +
-                                                           (long)(p0 / BN) * D * BN);
 #pragma unroll
             for (int i = 0; i < MPW; ++i) {
                 const int m = w * MPW + i;
-                const int off = m * 1024 + lane * 16;
-                const int kr = off / (D * 2), kc = ((off % (D * 2)) >> 4) ^ (kr & 7);
-                lds_dma16(kg + kr * (D * 2) + kc * 16, reinterpret_cast<char*>(sK[part]) + m * 1024);
-                const int vr = off >> 7, vc = ((off & 127) >> 4) ^ (vr & 7);
-                lds_dma16(vg + vr * 128 + vc * 16, reinterpret_cast<char*>(sV[part]) + m * 1024);
+                buf_dma16(part ? rKl : rK, reinterpret_cast<char*>(sK[part]) + m * 1024, kvo[i], ks);
+                buf_dma16(part ? rVl : rV, reinterpret_cast<char*>(sV[part]) + m * 1024, vvo[i], vs);
             }
         }
-        if (w == 0) lds_dma4(cpos_h + p0 + lane, sC);
+        if (w == 0 && lane < BT) buf_dma4(rC, sC, lane * 4, p0 * 4);
     };
 
     f32x16 o[D / 32];
@@ -636,15 +678,15 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    auto compute = [&](int p0, const __bf16 (*sK)[BN * D], const __bf16 (*sV)[BN * D], const int* sC) {
-        f32x16 s[2];
+    auto compute = [&](int p0, const __bf16 (*sK)[BT * D], const __bf16 (*sV)[BT * D], const int* sC) {
+        f32x16 s[KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16{};
             const int key = 32 * kt + r;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const int e = key * D + (((2 * kk + half) ^ (key & 7)) << 3);
+                const int e = key * D + (((2 * kk + half) ^ swz<KCPR>(key)) << 3);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[0][e]);
                 s[kt] = mfma32(a, qf[kk], s[kt]);
                 if (X3) {
@@ -653,20 +695,20 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
                 }
             }
         }
-        if (p0 + BN > p_full) {
+        if (p0 + BT > p_full) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = 32 * kt + (j >> 2) * 8 + half * 4 + (j & 3);
                     if (sC[key] > rowpos) s[kt][j] = -INFINITY;
                 }
         }
-        bf16x8 pb[2][2], pl[X3 ? 2 : 1][2];
+        bf16x8 pb[KT][2], pl[X3 ? KT : 1][2];
         if (MODE == MODE_ATTN) {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -680,7 +722,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
             }
             m_run = m_new;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
@@ -690,7 +732,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
                 }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float pj = wgt * __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -lse_prev2));
@@ -703,10 +745,10 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
         for (int dt = 0; dt < D / 32; ++dt) {
             const int row = 32 * dt + r;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int jh = 0; jh < 2; ++jh) {
-                    const int e = row * BN + (((4 * kt + 2 * jh + half) ^ (row & 7)) << 3);
+                    const int e = row * BT + (((4 * kt + 2 * jh + half) ^ swz<VCPR>(row)) << 3);
                     const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[0][e]);
                     o[dt] = mfma32(a, pb[kt][jh], o[dt]);
                     if (X3) {
@@ -722,15 +764,15 @@ __global__ __launch_bounds__(256, PREC == 0 ? 2 : 1) void k_attn_lds(AttnParams 
     for (int p0 = 0; p0 < p_end;) {
         __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the current tile landed
         __syncthreads();               // ... every lane's; the other buffer is free
-        if (p0 + BN < p_end) issue(p0 + BN, sK1, sV1, sC1);
+        if (p0 + BT < p_end) issue(p0 + BT, sK1, sV1, sC1);
         compute(p0, sK0, sV0, sC0);
-        p0 += BN;
+        p0 += BT;
         if (p0 >= p_end) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (p0 + BN < p_end) issue(p0 + BN, sK0, sV0, sC0);
+        if (p0 + BT < p_end) issue(p0 + BT, sK0, sV0, sC0);
         compute(p0, sK1, sV1, sC1);
-        p0 += BN;
+        p0 += BT;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -1024,7 +1066,8 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
     __shared__ int s_start, s_cmax;
     const int h = blockIdx.y;
     const int pc0 = blockIdx.x * CT;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
     const int p = pc0 + w * 32 + r;
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
@@ -1054,7 +1097,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
     for (int i = 0; i < MPW; ++i) {
         const int off = (w * MPW + i) * 1024 + lane * 16;
         drow[i] = off / (D * 2);
-        dchunk[i] = ((off % (D * 2)) >> 4) ^ (drow[i] & 7);
+        dchunk[i] = ((off % (D * 2)) >> 4) ^ swz<D * 2 / 16>(drow[i]);
     }
     // Query rows of a step are addressed through their positions, which are
     // loaded one step ahead of the copy (two ahead of the compute), so no
@@ -1069,13 +1112,16 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
             qr_next[i] = P.q_gathered ? tt : P.active[tt];
         }
     };
+    // query rows of head h: row x at byte x * H * D * 2 from the head's base
+    const uint32_t qstride = (uint32_t)P.H * D * 2;
+    const __amdgpu_buffer_rsrc_t rQ =
+        make_rsrc(reinterpret_cast<const uint16_t*>(P.q) + (long)h * D,
+                  (uint32_t)(P.q_gathered ? P.n : P.active[P.n - 1] + 1) * qstride);
     auto issue = [&](__bf16* sQ) {
 #pragma unroll
-        for (int i = 0; i < MPW; ++i) {
-            const char* src = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.q) +
-                                                            ((long)qr_next[i] * P.H + h) * D) + dchunk[i] * 16;
-            lds_dma16(src, reinterpret_cast<char*>(sQ) + (w * MPW + i) * 1024);
-        }
+        for (int i = 0; i < MPW; ++i)
+            buf_dma16(rQ, reinterpret_cast<char*>(sQ) + (w * MPW + i) * 1024,
+                      (uint32_t)qr_next[i] * qstride + dchunk[i] * 16, 0);
     };
     // wave 0: lane l's row position (loaded a step ahead) and its exponent
     // offset lse*log2(e) - log2(1 - M_U)
@@ -1107,7 +1153,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
             const int row = 32 * sub + r;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const int e = row * D + (((2 * kk + half) ^ (row & 7)) << 3);
+                const int e = row * D + (((2 * kk + half) ^ swz<D * 2 / 16>(row)) << 3);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[e]);
                 s = mfma32(a, kf[kk], s);
                 if (X3) s = mfma32(a, kl[X3 ? kk : 0], s);
@@ -1197,6 +1243,7 @@ hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, i
 // (PREC 1) the doubled tiles leave one workgroup per CU and the register-
 // staged kernel measured faster (0.87 vs 1.11 ms for the 32K sparse loops)
 static bool lds_path(int prec) { return prec == 0; }
+constexpr int kAttnTile = 64;   // columns per LDS tile of the pipelined kernel
 
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st) {
     const int n_tiles = (P.n + BM - 1) / BM;
@@ -1204,7 +1251,7 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
     Q.xcd_remap = (P.H % 8) == 0;
     dim3 grid(n_tiles * P.H);
 #define FL_ATTN(D_, M_, P_, Q_) hipLaunchKernelGGL((k_attn<D_, M_, P_, Q_>), grid, dim3(256), 0, st, Q)
-#define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_>), grid, dim3(256), 0, st, Q)
+#define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_, kAttnTile>), grid, dim3(256), 0, st, Q)
     // bf16 queries over compact bf16 tiles: the LDS-DMA pipelined kernel
 #define FL_ATTN_Q(D_, M_, P_)                                   \
     if (in_tile) FL_ATTN(D_, M_, P_, true);                    \
