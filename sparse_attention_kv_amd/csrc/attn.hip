@@ -255,7 +255,7 @@ __device__ __forceinline__ void block_coords(int xcd_remap, int n_tiles, int H, 
 // DEQ: the tiles are dequantised from compact quantised planes while staged.
 // The running max is tracked on raw scores (the scale is folded into the
 // exponent's fma) and the accumulators are rescaled only when some row's max
-// moved.  (A register-prefetch, two-buffer LDS variant of the tile loop
+// passes the exponent reference by more than 8 (log2 units).  (A register-prefetch, two-buffer LDS variant of the tile loop
 // measured slower on gfx950 -- 10.6 vs 8.6 ms for the 32K dense + sparse
 // loop pair -- and is not used.)
 template <int D, int MODE, int PREC, bool DEQ>
@@ -447,15 +447,19 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
                 for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float m_new = fmaxf(m_run, tmax * P.c2);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            // rescale only when some row's running max moved (wave-uniform)
-            if (__ballot(m_new > m_run)) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            // The exponent reference m_run follows the running max lazily:
+            // it moves (with a rescale of l and O) only when some row's max
+            // exceeds it by more than 8, so probabilities stay <= 2^8 and
+            // most tiles skip the rescale (the result does not depend on
+            // the reference).
+            if (__ballot(m_new > m_run + 8.0f)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
                 l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+                m_run = m_new;
             }
-            m_run = m_new;
+            const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -680,6 +684,10 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_att
 
     auto compute = [&](int p0, const __bf16 (*sK)[BT * D], const __bf16 (*sV)[BT * D], const int* sC) {
         f32x16 s[KT];
+        // raised issue priority while this wave feeds its QK^T MFMAs: the
+        // two waves sharing a SIMD then drift apart, one on the matrix
+        // cores while the other runs its softmax (measured 4.15 -> 3.98 ms)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16{};
@@ -695,6 +703,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_att
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (p0 + BT > p_full) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
@@ -705,6 +714,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_att
                 }
         }
         bf16x8 pb[KT][2], pl[X3 ? KT : 1][2];
+        float m_use = lse_prev2;
         if (MODE == MODE_ATTN) {
             float tmax = -INFINITY;
 #pragma unroll
@@ -713,39 +723,31 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_att
                 for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float m_new = fmaxf(m_run, tmax * P.c2);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            if (__ballot(m_new > m_run)) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            // lazy exponent reference, as in k_attn
+            if (__ballot(m_new > m_run + 8.0f)) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
                 l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+                m_run = m_new;
             }
-            m_run = m_new;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
-                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
-                    l_run += pj;
-                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
-                }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pj = wgt * __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -lse_prev2));
-                    l_run += pj;
-                    pb[kt][j >> 3][j & 7] = (__bf16)pj;
-                    if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
-                }
+            m_use = m_run == -INFINITY ? 0.0f : m_run;
         }
+        // probabilities of 32-column block kt, and O^T += V^T P^T over it
+        auto expb = [&](int kt) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int row = 32 * dt + r;
+            for (int j = 0; j < 16; ++j) {
+                float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
+                if (MODE == MODE_REBUILD) pj *= wgt;
+                pb[kt][j >> 3][j & 7] = (__bf16)pj;
+                l_run += pj;
+                if (X3) pl[X3 ? kt : 0][j >> 3][j & 7] = (__bf16)(pj - (float)pb[kt][j >> 3][j & 7]);
+            }
+        };
+        auto pvb = [&](int kt) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int row = 32 * dt + r;
 #pragma unroll
                 for (int jh = 0; jh < 2; ++jh) {
                     const int e = row * BT + (((4 * kt + 2 * jh + half) ^ swz<VCPR>(row)) << 3);
@@ -757,7 +759,12 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_att
                         o[dt] = mfma32(al, pb[kt][jh], o[dt]);
                     }
                 }
-        }
+            }
+        };
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) expb(kt);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) pvb(kt);
     };
 
     if (p_end > 0) issue(0, sK0, sV0, sC0);
@@ -1147,6 +1154,9 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
     float csum = 0.0f;
     auto compute = [&](int t0, const __bf16* sQ, const int* rpos, const float* roff) {
         const bool full = rpos[0] >= cmax && t0 + RT2 <= P.n;
+        // (computing both halves' S^T before their exponentials, with or
+        // without raised issue priority, measured slower: 3.08 / 3.12 vs
+        // 3.01 ms at 32K)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             f32x16 s = f32x16{};
