@@ -31,10 +31,10 @@ METRIC = "active-query tokens/s of loop-r sparse attention @32K, R=4; KV bytes/t
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
-KERNEL_SYMBOL = {"attn": "k_attn<128, 0, 0, false>", "attn_split": "k_attn<128, 0, 1, false>",
-                 "attn_rebuild": "k_attn<128, 1, 0, false>", "colstat": "k_colstat_pipe<128, 0>",
-                 "colstat_split": "k_colstat_pipe<128, 1>", "decode_dense": "k_decode<128, 0, false>",
-                 "decode": "k_decode<128, 0, true>", "decode_rebuild": "k_decode<128, 1, true>"}
+KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn<128, 0, 1, false>",
+                 "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0>",
+                 "colstat_split": "k_colstat_lds<128, 1>", "decode_dense": "k_decode<128, 0, false, true>",
+                 "decode": "k_decode<128, 0, true, false>", "decode_rebuild": "k_decode<128, 1, true, true>"}
 
 
 def parse():

@@ -352,7 +352,9 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
  * Cache layout: cache.level[l] describes sequence 0 with the usual fields;
  * sequence b's rows/slot/codes/scales follow at b * (n_rows, N, n_rows*H*
  * d*bits/8 bytes, n_rows*H*d/g floats) -- B sequences of equal geometry.
- * Requirements: N + 1 <= 12288 (the probabilities stay in LDS).
+ * Requirements: N + 1 <= 12288 (the probabilities stay in LDS); base level
+ * int8 and quantised residual levels (FL_ERR_UNSUPPORTED otherwise); a
+ * sparse loop r keeps 4 * ((k + 1) + r * k) bytes in LDS, at most 48 KiB.
  */
 typedef struct fl_decode_cfg {
     int B, N, H, d, g, R, n_sink;

@@ -602,6 +602,10 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, r - 1);
     if (rc) return rc;
+    if (C.level[0].bits != 8) return fail(FL_ERR_UNSUPPORTED, "decode: base level bits %d (8)", C.level[0].bits);
+    for (int l = 1; l < r; ++l)
+        if (C.level[l].bits == 32)
+            return fail(FL_ERR_UNSUPPORTED, "decode: level %d is raw (quantised levels only)", l);
     FL_REQUIRE(in->q && in->k_self && in->v_self, "q/k_self/v_self NULL");
     FL_REQUIRE(S->out && S->lse && S->mass_u && S->out_u, "state arrays NULL");
     hipStream_t st = (hipStream_t)stream;
@@ -637,6 +641,10 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     }
     P.k = S->k_cur[r - 1];
     P.sel = S->sel_used[r - 1];
+    // a sparse loop keeps the probabilities and every level's row of each
+    // selected column in LDS
+    if (P.sel && (size_t)(P.k + 1) * 4 + (size_t)r * P.k * 4 > 48 * 1024)
+        return fail(FL_ERR_UNSUPPORTED, "decode: %d columns x %d levels exceed the LDS budget", P.k, r);
     if (changed) {
         fl::DecodeParams R = P;
         R.level = r - 2; R.cache_op = FL_CACHE_REBUILD;

@@ -6,14 +6,19 @@
 // One workgroup per (sequence, head) and one new query token.  The key
 // columns are the selected prefix columns (all of them in the dense first
 // loop) plus the token's own fresh bf16 key/value ("self" column).
-//   phase 1  score of every column, one column per thread: the quantised
-//            base + residual chain of the key is read straight from the cache
-//            (int8 row of d bytes, then the present residual levels) and
-//            dotted with q in fp32, scale applied per group;
+// A column's row of d codes is read by d/16 neighbouring lanes, 16 codes
+// each, so every wave load covers whole 2^k-byte code rows (coalesced), and
+// several column groups are in flight per wave.
+//   rows     (sparse) every level's cache row of every selected column is
+//            looked up once, all levels in parallel, into LDS;
+//   phase 1  scores: per lane a 16-channel dot product with the dequantised
+//            chain (codes x group scale, levels summed; a level absent from
+//            the nested sets has row -1 and is predicated off), reduced
+//            across the column's lanes;
 //   phase 2  block max / sum -> lse, probabilities kept in LDS;
-//   phase 3  P.V with d/8 channel groups x 2048/d column slices per
-//            workgroup (a wavefront reads 64*8/d value rows of d bytes per
-//            load), slices reduced through LDS.
+//   phase 3  P.V: per lane 16 channels accumulated over its columns with
+//            p x scale folded into one factor per (column, level, group),
+//            reduced across lanes and waves.
 // MODE_ATTN writes o = sum P V + O_U (P carries 1 - M_U), lse and the column
 // probabilities (the next loop's column statistic).  MODE_REBUILD recomputes
 // the previous loop's probabilities on the kept columns and its self column
@@ -23,63 +28,127 @@
 
 namespace fl {
 
-constexpr int DT = 256; // threads per workgroup
+constexpr int DT = 256;      // threads per workgroup
+constexpr int DNW = DT / 64; // waves
 
+struct SeqLevel {
+    const uint8_t* codes;
+    const float* scales;
+    const int32_t* slot;
+    int bits;
+};
+
+// level l of sequence b: rows of the B sequences are stored back to back
 template <int D>
-__device__ __forceinline__ void seq_level_ptrs(const fl_kv_cache& c, int l, int b, int which,
-                                               const uint8_t*& codes, const float*& scales,
-                                               const int32_t*& slot, long& rows) {
+__device__ __forceinline__ SeqLevel seq_level(const fl_kv_cache& c, int l, int b, int which) {
     const fl_kv_level& L = c.level[l];
-    rows = l == 0 ? c.N : L.n_rows;
-    const long cb = (long)rows * c.H * D * L.bits / 8;
-    const long sb = (long)rows * c.H * (D / c.g);
-    codes = reinterpret_cast<const uint8_t*>(which ? L.v_codes : L.k_codes) + b * cb;
-    scales = (which ? L.v_scale : L.k_scale) + b * sb;
-    slot = l == 0 ? nullptr : L.slot + (long)b * c.N;
+    const long rows = l == 0 ? c.N : L.n_rows;
+    SeqLevel s;
+    s.bits = L.bits;
+    s.codes = reinterpret_cast<const uint8_t*>(which ? L.v_codes : L.k_codes) +
+              b * (rows * c.H * D * L.bits / 8);
+    s.scales = (which ? L.v_scale : L.k_scale) + b * (rows * c.H * (D / c.g));
+    s.slot = l == 0 ? nullptr : L.slot + (long)b * c.N;
+    return s;
 }
 
-template <int D, int MODE, bool SPARSE>
+// 16 consecutive codes starting at code index e (16-aligned)
+__device__ __forceinline__ void load_codes16(const uint8_t* base, long e, int bits, float (&x)[16]) {
+    if (bits == 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(base + e);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)(int8_t)(wd[i >> 2] >> (8 * (i & 3)));
+    } else if (bits == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(base + e / 2);
+        const uint64_t wd = ((uint64_t)u.y << 32) | u.x;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((int)((int64_t)(wd << (60 - 4 * i)) >> 60));
+    } else { // bits == 2
+        const uint32_t wd = *reinterpret_cast<const uint32_t*>(base + e / 4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((int)((int32_t)(wd << (30 - 2 * i)) >> 30));
+    }
+}
+
+template <int D, int MODE, bool SPARSE, bool L0>
 __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
-    extern __shared__ float sc[]; // [k + 1] scores / probabilities
+    constexpr int LPC = D / 16;     // lanes per column
+    constexpr int CPW = 64 / LPC;   // columns per wave per load
+    constexpr int CPI = CPW * DNW;  // columns per workgroup pass
+    constexpr int U = 4;            // passes in flight
+    extern __shared__ float dyn[];  // sc[k + 1], then (sparse) rows[level + 1][k]
     __shared__ float qs[D];
-    __shared__ float red[DT / 64];
-    constexpr int CG = D / 8, CS = DT / CG; // channel groups of 8 x column slices
-    __shared__ float ored[CS][D + 4];
+    __shared__ float red[DNW];
+    __shared__ float ored[DNW][D];
     const int bh = blockIdx.x;
     const int b = bh / P.H, h = bh % P.H;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cl = lane / LPC, cs = lane % LPC;
     const fl_kv_cache& C = P.cache;
-    const int G = D / C.g;
+    const int H = C.H, G = D / C.g;
     const int k = P.k;
+    const int nlev = L0 ? 1 : P.level + 1;
     const long qo = (long)bh * D;
+    float* sc = dyn;
+    int* rowtab = reinterpret_cast<int*>(dyn + k + 1);
     for (int c = tid; c < D; c += DT)
         qs[c] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.q)[qo + c]);
+    if (SPARSE) {
+        const int32_t* sel = P.sel + (long)bh * k;
+        for (int c = tid; c < k; c += DT) {
+            const int j = sel[c];
+            rowtab[c] = j;
+            for (int l = 1; l < nlev; ++l) rowtab[l * k + c] = seq_level<D>(C, l, b, 0).slot[j];
+        }
+    }
     __syncthreads();
-    const int32_t* sel = SPARSE ? P.sel + (long)bh * k : nullptr;
+    float qv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = qs[cs * 16 + i];
     const float c2 = P.sm * 1.4426950408889634f;
+    const int grp = cs * 16 / C.g;  // this lane's scale group
+
+    auto row_of = [&](int l, int c) -> int {
+        if (SPARSE) return rowtab[l * k + c];
+        if (l == 0) return c;
+        return seq_level<D>(C, l, b, 0).slot[c];
+    };
 
     // ---- phase 1: scores (log2 units) ----
-    for (int c = tid; c < k; c += DT) {
-        const long j = SPARSE ? sel[c] : c;
-        float s = 0.0f;
-        for (int l = 0; l <= P.level; ++l) {
-            const uint8_t* codes; const float* scales; const int32_t* slot; long rows;
-            seq_level_ptrs<D>(C, l, b, 0, codes, scales, slot, rows);
-            const long row = l == 0 ? j : (long)slot[j];
-            if (row < 0) break; // nested sets: absent here means absent later
-            const int bits = C.level[l].bits;
-            const long e0 = (row * C.H + h) * D;
-            for (int gi = 0; gi < G; ++gi) {
-                float acc = 0.0f;
-                for (int e8 = 0; e8 < C.g; e8 += 8) {
-                    const uint64_t w = load_codes8(codes, e0 + gi * C.g + e8, bits);
+    for (int c0 = 0; c0 < k; c0 += CPI * U) {
+        float part[U];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc += qs[gi * C.g + e8 + i] * (float)code_at(w, bits, i);
+        for (int u = 0; u < U; ++u) {
+            part[u] = 0.0f;
+            const int c = c0 + u * CPI + w * CPW + cl;
+            if (c < k) {
+                // absent levels are predicated off (not a break), so the
+                // loads of a column's levels are issued together
+#pragma unroll 4
+                for (int l = 0; l < nlev; ++l) {
+                    const int row = row_of(l, c);
+                    if (row >= 0) {
+                        const SeqLevel L = seq_level<D>(C, l, b, 0);
+                        const long rr = (long)row * H + h;
+                        float x[16];
+                        load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                        float dot = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
+                        part[u] = fmaf(dot, L.scales[rr * G + grp], part[u]);
+                    }
                 }
-                s += acc * scales[(row * C.H + h) * G + gi];
             }
         }
-        sc[c] = s * c2;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v = part[u];
+#pragma unroll
+            for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
+            const int c = c0 + u * CPI + w * CPW + cl;
+            if (cs == 0 && c < k) sc[c] = v * c2;
+        }
     }
     if (tid < 64) { // self column: the token's own bf16 key
         float s = 0.0f;
@@ -96,14 +165,14 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         float m = -INFINITY;
         for (int c = tid; c <= k; c += DT) m = fmaxf(m, sc[c]);
         m = wave_max(m);
-        if ((tid & 63) == 0) red[tid >> 6] = m;
+        if (lane == 0) red[w] = m;
         __syncthreads();
         m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         __syncthreads();
         float z = 0.0f;
         for (int c = tid; c <= k; c += DT) z += __builtin_amdgcn_exp2f(sc[c] - m);
         z = wave_sum(z);
-        if ((tid & 63) == 0) red[tid >> 6] = z;
+        if (lane == 0) red[w] = z;
         __syncthreads();
         z = red[0] + red[1] + red[2] + red[3];
         lse2 = m + __log2f(z);
@@ -121,47 +190,49 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     __syncthreads();
 
     // ---- phase 3: P.V ----
-    const int cg = tid % CG, cs = tid / CG;
-    float acc[8];
+    float acc[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int c = cs; c < k; c += CS) {
-        const long j = SPARSE ? sel[c] : c;
-        const float p = sc[c];
-        float v[8];
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int c0 = 0; c0 < k; c0 += CPI * U) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-        for (int l = 0; l <= P.level; ++l) {
-            const uint8_t* codes; const float* scales; const int32_t* slot; long rows;
-            seq_level_ptrs<D>(C, l, b, 1, codes, scales, slot, rows);
-            const long row = l == 0 ? j : (long)slot[j];
-            if (row < 0) break;
-            const int bits = C.level[l].bits;
-            const long e = (row * C.H + h) * D + cg * 8;
-            const float s = scales[e / C.g];
-            const uint64_t w = load_codes8(codes, e, bits);
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * CPI + w * CPW + cl;
+            if (c < k) {
+                const float p = sc[c];
+#pragma unroll 4
+                for (int l = 0; l < nlev; ++l) {
+                    const int row = row_of(l, c);
+                    if (row >= 0) {
+                        const SeqLevel L = seq_level<D>(C, l, b, 1);
+                        const long rr = (long)row * H + h;
+                        float x[16];
+                        load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                        const float ps = p * L.scales[rr * G + grp];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] += (float)code_at(w, bits, i) * s;
+                        for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                    }
+                }
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += p * v[i];
     }
-    if (cs == 0) {
-        const float p = sc[k];
+    // lanes with the same channel slice hold partial sums over different columns
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] += p * bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.vself)[qo + cg * 8 + i]);
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int o = LPC; o < 64; o <<= 1) acc[i] += __shfl_xor(acc[i], o);
     }
+    if (cl == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ored[cs][cg * 8 + i] = acc[i];
+        for (int i = 0; i < 16; ++i) ored[w][cs * 16 + i] = acc[i];
+    }
     psum = wave_sum(psum);
-    if ((tid & 63) == 0) red[tid >> 6] = psum;
+    if (lane == 0) red[w] = psum;
     __syncthreads();
     const float ptot = red[0] + red[1] + red[2] + red[3];
+    const float pself = sc[k];
     for (int c = tid; c < D; c += DT) {
-        float o = 0.0f;
-#pragma unroll
-        for (int s = 0; s < CS; ++s) o += ored[s][c];
+        float o = ored[0][c] + ored[1][c] + ored[2][c] + ored[3][c];
+        o = fmaf(pself, bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.vself)[qo + c]), o);
         if (MODE == MODE_ATTN) {
             const float u = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.out_u[qo + c];
             P.out[qo + c] = o + u;
@@ -178,14 +249,15 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
 }
 
 hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st) {
-    const size_t shm = (size_t)(P.k + 1) * sizeof(float);
-    dim3 grid(P.B * P.H);
     const bool sp = P.sel != nullptr;
-#define FL_DEC(D_, M_, S_) hipLaunchKernelGGL((k_decode<D_, M_, S_>), grid, dim3(DT), shm, st, P)
+    const size_t shm = (size_t)(P.k + 1) * sizeof(float) + (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
+    dim3 grid(P.B * P.H);
+    const bool l0 = P.level == 0;
+#define FL_DEC(D_, M_, S_, L_) hipLaunchKernelGGL((k_decode<D_, M_, S_, L_>), grid, dim3(DT), shm, st, P)
 #define FL_DEC_D(D_)                                                                     \
-    if (mode == MODE_REBUILD) FL_DEC(D_, MODE_REBUILD, true);                           \
-    else if (sp) FL_DEC(D_, MODE_ATTN, true);                                           \
-    else FL_DEC(D_, MODE_ATTN, false);
+    if (mode == MODE_REBUILD) { if (l0) FL_DEC(D_, MODE_REBUILD, true, true); else FL_DEC(D_, MODE_REBUILD, true, false); } \
+    else if (sp) { if (l0) FL_DEC(D_, MODE_ATTN, true, true); else FL_DEC(D_, MODE_ATTN, true, false); } \
+    else { if (l0) FL_DEC(D_, MODE_ATTN, false, true); else FL_DEC(D_, MODE_ATTN, false, false); }
     if (d == 128) { FL_DEC_D(128) } else { FL_DEC_D(64) }
 #undef FL_DEC_D
 #undef FL_DEC
