@@ -557,36 +557,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 // of bank conflicts.  The two buffers are distinct LDS objects so the
 // compiler's wait-count analysis sees that reads of one do not wait for
 // copies into the other.  Arithmetic as k_attn (PREC 0/1, DEQ off).
-// 16-byte-chunk swizzle of a tile row with CPR chunks: the 16 lanes that one
-// 128-bit LDS read serves per cycle (16 consecutive rows at one logical
-// chunk) land on 16 distinct chunk slots of a 256-byte bank window.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "rows of 64, 128 or 256 bytes");
-    return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-
-// Raw buffer resource over [base, base + bytes) (gfx9 data-format word); a
-// copy through it takes a scalar base, a per-lane 32-bit offset and a
-// scalar offset, so issuing it costs no vector instructions, and offsets
-// past `bytes` read zeros instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
-}
-
 template <int D, int MODE, int PREC, int BT>
 __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_attn_lds(AttnParams P) {
     static_assert(PREC == 0 || PREC == 1, "bf16 queries only");

@@ -141,6 +141,115 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmParams G) {
 }
 
 // ---------------------------------------------------------------------------
+// The same GEMM with 64-deep K tiles copied by LDS-DMA (buffer loads with a
+// scalar base and constant per-lane offsets; rows past M read zeros) into two
+// distinct LDS buffers, XOR-swizzled as the attention tiles (16 rows at one
+// logical chunk hit 16 distinct slots of a 256-byte bank window): one barrier
+// per K tile, the next tile lands while the current one is multiplied.
+constexpr int LBK = 64;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_lds(GemmParams G) {
+    constexpr int TB = GBM * LBK * 2;        // bytes of one operand tile (A and B alike)
+    constexpr int MPW = TB / 1024 / 4;       // LDS-DMA instructions per wave per operand
+    constexpr int CPR = LBK * 2 / 16;        // 16-byte chunks per tile row
+    __shared__ __attribute__((aligned(1024))) __bf16 sA0[GBM * LBK];
+    __shared__ __attribute__((aligned(1024))) __bf16 sB0[GBN * LBK];
+    __shared__ __attribute__((aligned(1024))) __bf16 sA1[GBM * LBK];
+    __shared__ __attribute__((aligned(1024))) __bf16 sB1[GBN * LBK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, half = lane >> 5;
+    const int wm = w >> 1, wn = w & 1;
+    const int n0 = blockIdx.x * GBN;
+    const int m0 = blockIdx.y * GBM;
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(G.A + (long)m0 * G.lda, (uint32_t)((long)(G.M - m0) * G.lda * 2));
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(G.B + (long)n0 * G.K, (uint32_t)((long)GBN * G.K * 2));
+    uint32_t ao[MPW], bo[MPW];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+        const int off = (w * MPW + i) * 1024 + lane * 16;
+        const int row = off / (LBK * 2), ch = ((off % (LBK * 2)) >> 4) ^ swz<CPR>(row);
+        ao[i] = (uint32_t)(row * G.lda * 2 + ch * 16);
+        bo[i] = (uint32_t)(row * G.K * 2 + ch * 16);
+    }
+    auto issue = [&](int kt, __bf16* sA, __bf16* sB) {
+        const uint32_t so = (uint32_t)kt * LBK * 2;
+#pragma unroll
+        for (int i = 0; i < MPW; ++i) {
+            buf_dma16(rA, reinterpret_cast<char*>(sA) + (w * MPW + i) * 1024, ao[i], so);
+            buf_dma16(rB, reinterpret_cast<char*>(sB) + (w * MPW + i) * 1024, bo[i], so);
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto compute = [&](const __bf16* sA, const __bf16* sB) {
+#pragma unroll
+        for (int ks = 0; ks < LBK / 16; ++ks) {
+            bf16x8 a[2], bb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + 32 * i + r;
+                a[i] = *reinterpret_cast<const bf16x8*>(&sA[row * LBK + (((2 * ks + half) ^ swz<CPR>(row)) << 3)]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = wn * 64 + 32 * j + r;
+                bb[j] = *reinterpret_cast<const bf16x8*>(&sB[row * LBK + (((2 * ks + half) ^ swz<CPR>(row)) << 3)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
+        }
+    };
+    const int nk = G.K / LBK;
+    issue(0, sA0, sB0);
+    for (int kt = 0; kt < nk;) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nk) issue(kt + 1, sA1, sB1);
+        compute(sA0, sB0);
+        if (++kt >= nk) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nk) issue(kt + 1, sA0, sB0);
+        compute(sA1, sB1);
+        ++kt;
+    }
+    // acc[i][j][e]: row m0 + wm*64 + 32i + (e/4)*8 + half*4 + e%4, col n0 + wn*64 + 32j + r
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + 32 * j + r;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm * 64 + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
+                const float v = acc[i][j][e];
+                if (EPI == EPI_SWIGLU) {
+                    const float u = __shfl_xor(v, 1); // (gate, up) column pair
+                    if (m < G.M && (r & 1) == 0) {
+                        const float sg = v / (1.0f + __expf(-v));
+                        G.Cb[(long)m * G.ldc + (n >> 1)] = (__bf16)(sg * u);
+                    }
+                } else if (m < G.M) {
+                    if (EPI == EPI_STORE) {
+                        G.Cb[(long)m * G.ldc + n] = (__bf16)v;
+                    } else { // EPI_RESID: residual stream += C at the active row
+                        const long row = G.rows ? G.rows[m] : m;
+                        G.Cf[row * G.ldc + n] += v;
+                    }
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rope_split(const __bf16* __restrict__ qkv,
                                                     const int32_t* __restrict__ rows, int n, int H,
                                                     int d, float log2_theta, __bf16* __restrict__ q,
@@ -199,9 +308,17 @@ hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int
     return hipGetLastError();
 }
 
+constexpr bool kGemmLds = true;
+
 hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st) {
     if (G.M <= 0) return hipSuccess;
     dim3 grid(G.N / GBN, (G.M + GBM - 1) / GBM);
+    if (kGemmLds && G.K % LBK == 0) {
+        if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm_lds<EPI_STORE>, grid, dim3(256), 0, st, G);
+        else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm_lds<EPI_RESID>, grid, dim3(256), 0, st, G);
+        else hipLaunchKernelGGL(k_gemm_lds<EPI_SWIGLU>, grid, dim3(256), 0, st, G);
+        return hipGetLastError();
+    }
     if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, G);
     else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, G);
     else hipLaunchKernelGGL(k_gemm<EPI_SWIGLU>, grid, dim3(256), 0, st, G);

@@ -84,4 +84,29 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- LDS-DMA tiles (gfx950) ----
+
+// 16-byte-chunk swizzle of a tile row with CPR chunks: the 16 lanes that one
+// 128-bit LDS read serves per cycle (16 consecutive rows at one logical
+// chunk) land on 16 distinct chunk slots of a 256-byte bank window.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "rows of 64, 128 or 256 bytes");
+    return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 data-format word); a
+// copy through it takes a scalar base, a per-lane 32-bit offset and a
+// scalar offset, so issuing it costs no vector instructions, and offsets
+// past `bytes` read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, voff, soff, 0, 0);
+}
+
 } // namespace fl
