@@ -35,6 +35,10 @@ KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn<128,
                  "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0>",
                  "colstat_split": "k_colstat_lds<128, 1>", "decode_dense": "k_decode<128, 0, false, true>",
                  "decode": "k_decode<128, 0, true, false>", "decode_rebuild": "k_decode<128, 1, true, true>"}
+# projections of the 2048-hidden block: epilogue (0 store, 1 residual, 2 SwiGLU)
+# and tile width; o and down share one instantiation, so only the others are
+# separable in a trace
+BLOCK_GEMM_SYMBOL = {"gemm_qkv": "k_gemm_lds<0, 128>", "gemm_gate_up": "k_gemm_lds<2, 128>"}
 
 
 def parse():
@@ -339,9 +343,9 @@ def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
 def bench_block(args, w, np, torch, fl, synth):
     """The full looped block: R loops of n_layers layers on each loop's active
     tokens.  value = active tokens pushed through the whole block per second,
-    sum_r n_r / step time.  Roofline of the dominant kernel family (the
-    gathered-row GEMMs: 2*(D*3D + D*D + D*2F + F*D) flops per active token and
-    layer)."""
+    sum_r n_r / step time.  Roofline of the dominant kernel (the costliest
+    gathered-row projection; the four take 2*(D*3D + D*D + D*2F + F*D) flops
+    per active token and layer), and of the four together."""
     t0 = time.time()
     inp = synth.generate(w)
     log(f"[bench] generated {w.name} weights/inputs in {time.time() - t0:.1f}s")
@@ -395,6 +399,17 @@ def bench_block(args, w, np, torch, fl, synth):
         if name in per_tok and ms > 0:
             e["tflops"] = round(per_tok[name] * tokens * L / (ms / args.steps / 1e3) / 1e12, 2)
         kernels[name] = e
+    # dominant kernel: the costliest of the projections (a kernel of its own)
+    dom = max((k for k in per_tok if k in kernels), key=lambda k: kernels[k]["ms_per_step"], default=None)
+    roof = None
+    if dom:
+        fl_dom = per_tok[dom] * tokens * L
+        a_dom = fl_dom / (kernels[dom]["ms_per_step"] / 1e3) / 1e12
+        sym = BLOCK_GEMM_SYMBOL.get(dom)
+        roof = dict(kernel=dom, kernel_symbol=sym, bound="mfma", achieved=round(a_dom, 2),
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(a_dom / PEAK_BF16_TFLOPS, 4),
+                    traffic=kernel_traffic(w.name, sym) if sym else None, flops_per_step=fl_dom,
+                    avg_launch_us=kernels[dom]["avg_launch_us"])
     gemm_ms = sum(kernels[k]["ms_per_step"] for k in per_tok if k in kernels)
     gemm_flops = sum(per_tok.values()) * tokens * L
     ach = gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms else None
@@ -410,13 +425,95 @@ def bench_block(args, w, np, torch, fl, synth):
         "loops": [dict(r=r + 1, n=n_act[r], ms=round(float(np.mean(loop_ms[:, r])), 3))
                   for r in range(R)],
         "kernels": kernels,
-        "roofline": dict(kernel="gemm (qkv+o+gate_up+down)", bound="mfma",
-                         achieved=round(ach, 2) if ach else None, peak=PEAK_BF16_TFLOPS,
-                         unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
-                         traffic=None, flops_per_step=gemm_flops),
+        "roofline": roof,
+        "gemms_all": dict(achieved=round(ach, 2) if ach else None, unit="TFLOP/s",
+                          frac=round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
+                          flops_per_step=gemm_flops),
         "gemm_flops_dense_equivalent": sum(per_tok.values()) * N * R * L,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(w, inp, n_act, np)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_block(w, inp, n_act, np, m=32):
+    """The block oracle's step functions, as they are, on a bounded sample of
+    the same workload: the first layer through all R loops.  Token
+    selection, RMSNorm, the four projections, RoPE, quantisation and column
+    selection run in full; attention, cache rebuild and column statistics run
+    on m evenly spaced active rows per loop (all heads) and are extrapolated
+    to n_r rows; the layer is extrapolated to the workload's layer count."""
+    import oracle
+    from oracle import block as ob
+    from sparse_attention_kv_amd import synth
+    F32 = np.float32
+    N, H, d, g, R = w.N, w.H, w.d, w.g, w.R
+    D, L = H * d, w.extra["layers"]
+    sm = F32(1.0 / np.sqrt(d))
+    lw = {k: synth.bf16_bits_to_f32(v) for k, v in inp["layers"][0].items()}
+    h = np.array(inp["h1"], F32, copy=True)
+    h_entry = h.copy()
+    A = np.arange(N, dtype=np.int32)
+    khat = vhat = S = cstat = lse = None
+    qd = np.zeros((N, H, d), F32)
+    total = 0.0
+    for r in range(1, R + 1):
+        t_full = t_rows = 0.0
+        t = time.perf_counter()
+        if r > 1:
+            stat = oracle.delta_norm(h, h_entry, A)
+            A = oracle.top_select(stat, n_act[r - 1], A)
+        h_entry = h.copy()
+        a = ob.bf16(ob.rmsnorm(h[A], lw["norm1"], w.extra["eps"]))
+        qkv = ob.bf16(a @ lw["w_qkv"].T)
+        q = ob.bf16(ob.rope(qkv[:, :D].reshape(-1, H, d), A, w.extra["theta"]))
+        k = ob.bf16(ob.rope(qkv[:, D:2 * D].reshape(-1, H, d), A, w.extra["theta"]))
+        v = np.ascontiguousarray(qkv[:, 2 * D:].reshape(-1, H, d))
+        _, _, _, kx = oracle.quantize_rows(k, None if r == 1 else khat[A], g, w.bits[r - 1])
+        _, _, _, vx = oracle.quantize_rows(v, None if r == 1 else vhat[A], g, w.bits[r - 1])
+        kh = kx if r == 1 else khat.copy()
+        vh = vx if r == 1 else vhat.copy()
+        if r > 1:
+            kh[A] = kx; vh[A] = vx
+        qn = qd.copy(); qn[A] = q
+        S_new = S
+        if r > 1 and w.kcols[r - 1] < (N if S is None else S.shape[1]):
+            S_new = oracle.select_columns(cstat, S, w.kcols[r - 1], w.n_sink)
+        t_full += time.perf_counter() - t
+        samp = A[np.linspace(0, len(A) - 1, min(m, len(A))).astype(np.int64)]
+        t = time.perf_counter()
+        if r > 1 and S_new is not S:
+            oracle.unselected_cache(qd, khat, vhat, samp, S, S_new, lse[samp], sm)
+        o, l_s = oracle.attend(qn, kh, vh, samp, S_new, sm)
+        if r < R:
+            cstat_s = oracle.column_stats(qn, kh, samp, S_new, l_s, sm)
+        t_rows = time.perf_counter() - t
+        t = time.perf_counter()
+        # the rest of the layer on the active rows (outputs of the rows not
+        # sampled are zeros here: the projections' cost does not depend on them)
+        att = np.zeros((len(A), D), F32)
+        h[A] += (ob.bf16(att) @ lw["w_o"].T).astype(F32)
+        b = ob.bf16(ob.rmsnorm(h[A], lw["norm2"], w.extra["eps"]))
+        gu = (b @ lw["w_gu"].T).astype(F32)
+        h[A] += (ob.bf16(ob.silu(gu[:, 0::2]) * gu[:, 1::2]) @ lw["w_down"].T).astype(F32)
+        t_full += time.perf_counter() - t
+        total += t_full + t_rows * len(A) / len(samp)
+        log(f"[bench] cpu oracle block loop {r}: full {t_full:.2f}s, {len(samp)} rows {t_rows:.2f}s")
+        # state for the next loop (column statistic from the sampled rows,
+        # full-size so the selection runs at its real size)
+        khat, vhat, qd, S = kh, vh, qn, S_new
+        lse = np.zeros((N, H), F32)
+        if r < R:
+            cstat = np.zeros((H, N if S is None else S.shape[1]), F32)
+            cstat[:, :cstat_s.shape[1]] = cstat_s
+    step_s = total * L
+    return {"value": round(sum(n_act) / step_s, 2), "unit": "active tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"layer 1 of {L} through all {R} loops: selection, norms, projections, RoPE, "
+                       f"quantisation and column selection in full; attention, cache rebuild and column "
+                       f"statistics on {m} evenly spaced active rows per loop (all {H} heads), "
+                       f"extrapolated to n_r rows, then x{L} layers"),
+            "extrapolated_step_s": round(step_s, 1)}
 
 
 def bench_decode(args, w, np, torch, fl, synth):
