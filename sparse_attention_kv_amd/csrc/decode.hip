@@ -76,13 +76,24 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     constexpr int LPC = D / 16;     // lanes per column
     constexpr int CPW = 64 / LPC;   // columns per wave per load
     constexpr int CPI = CPW * DNW;  // columns per workgroup pass
-    constexpr int U = 4;            // passes in flight
+    constexpr int U = 4;            // passes in flight (8 measured no faster)
     extern __shared__ float dyn[];  // sc[k + 1], then (sparse) rows[level + 1][k]
     __shared__ float qs[D];
     __shared__ float red[DNW];
     __shared__ float ored[DNW][D];
-    const int bh = blockIdx.x;
-    const int b = bh / P.H, h = bh % P.H;
+    // blocks are dealt to the 8 XCDs round-robin; with B a multiple of 8 all
+    // heads of a sequence run on one XCD, so a token's scale line (all heads'
+    // group scales are adjacent) is fetched into one L2 only
+    int b, h;
+    if (P.B % 8 == 0) {
+        const int x = blockIdx.x & 7, m = blockIdx.x >> 3;
+        b = 8 * (m / P.H) + x;
+        h = m % P.H;
+    } else {
+        b = blockIdx.x / P.H;
+        h = blockIdx.x % P.H;
+    }
+    const int bh = b * P.H + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int cl = lane / LPC, cs = lane % LPC;
     const fl_kv_cache& C = P.cache;
