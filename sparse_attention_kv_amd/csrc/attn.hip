@@ -557,8 +557,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 // of bank conflicts.  The two buffers are distinct LDS objects so the
 // compiler's wait-count analysis sees that reads of one do not wait for
 // copies into the other.  Arithmetic as k_attn (PREC 0/1, DEQ off).
+constexpr int kAttnLdsSplit = 1;  // PREC value routed to the LDS-DMA kernel besides 0
+
 template <int D, int MODE, int PREC, int BT>
-__global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : 1) void k_attn_lds(AttnParams P) {
+__global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2 : 1)) void k_attn_lds(AttnParams P) {
     static_assert(PREC == 0 || PREC == 1, "bf16 queries only");
     constexpr bool X3 = PREC >= 1;
     constexpr int NP = X3 ? 2 : 1;
@@ -1219,11 +1221,12 @@ hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, i
     return hipGetLastError();
 }
 
-// the LDS-DMA pipelined kernels for bf16 queries; with hi/lo operand pairs
-// (PREC 1) the doubled tiles leave one workgroup per CU and the register-
-// staged kernel measured faster (0.87 vs 1.11 ms for the 32K sparse loops)
-static bool lds_path(int prec) { return prec == 0; }
-constexpr int kAttnTile = 64;   // columns per LDS tile of the pipelined kernel
+// the LDS-DMA pipelined kernels for bf16 queries: 64-column tiles for plain
+// bf16 operands; with hi/lo operand pairs (PREC 1) 32-column tiles, so the
+// doubled tiles still leave two workgroups per CU (64-column hi/lo tiles
+// allow one and measured slower than the register-staged kernel: 1.11 vs
+// 0.87 ms for the 32K sparse loops)
+static bool lds_path(int prec) { return prec == 0 || prec == kAttnLdsSplit; }
 
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st) {
     const int n_tiles = (P.n + BM - 1) / BM;
@@ -1231,7 +1234,7 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
     Q.xcd_remap = (P.H % 8) == 0;
     dim3 grid(n_tiles * P.H);
 #define FL_ATTN(D_, M_, P_, Q_) hipLaunchKernelGGL((k_attn<D_, M_, P_, Q_>), grid, dim3(256), 0, st, Q)
-#define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_, kAttnTile>), grid, dim3(256), 0, st, Q)
+#define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_, P_ == 0 ? 64 : 32>), grid, dim3(256), 0, st, Q)
     // bf16 queries over compact bf16 tiles: the LDS-DMA pipelined kernel
 #define FL_ATTN_Q(D_, M_, P_)                                   \
     if (in_tile) FL_ATTN(D_, M_, P_, true);                    \
