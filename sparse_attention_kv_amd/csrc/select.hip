@@ -11,6 +11,8 @@
 //                ordered block-scan compaction walks the candidates in position
 //                order.  The result is unique given the keys, so it matches any
 //                correct selector bit for bit.
+//  k_topk_res    the same for segments of up to 32K candidates, held in
+//                registers (contiguous runs per thread).
 #include "fl_device.h"
 #include "fl_kernels.h"
 
@@ -200,6 +202,127 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(
     }
 }
 
+// The same selection with every thread holding a contiguous run of at most
+// kRes candidates in registers (segments of up to kRes * 1024 candidates):
+// the radix passes read no memory, and the ordered compaction takes two
+// block scans in all (tied keys before each run, then output offsets)
+// instead of two per 1024 candidates.
+constexpr int kRes = 32;
+
+__global__ __launch_bounds__(kSelThreads) void k_topk_res(
+    const float* __restrict__ keys, long key_stride, const int32_t* __restrict__ pos,
+    long pos_stride, int n, int n_sel, int n_prefix, int32_t* __restrict__ out,
+    long out_stride, int32_t* __restrict__ slot, int n_slot) {
+    __shared__ int s_hist[256];
+    __shared__ int s_wave[2 * kSelWaves + 1];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_need;
+    const int seg = blockIdx.x;
+    keys += seg * key_stride;
+    if (pos) pos += seg * pos_stride;
+    out += seg * out_stride;
+    const int tid = threadIdx.x;
+    const int C = (n + kSelThreads - 1) / kSelThreads;  // <= kRes
+    const int t0 = min(tid * C, n), t1 = min(t0 + C, n);
+
+    if (slot) {
+        for (int i = tid; i < n_slot; i += kSelThreads) slot[i] = -1;
+    }
+    for (int q = tid; q < n_prefix; q += kSelThreads) {
+        out[q] = q;
+        if (slot && q < n_slot) slot[q] = q;
+    }
+    // this thread's run: ordered keys and positions; unranked entries
+    // (sinks, padding) get rank flag 0
+    uint32_t u[kRes];
+    int pp[kRes];
+    uint32_t ranked = 0;   // bit e: entry e takes part in the ranking
+#pragma unroll
+    for (int e = 0; e < kRes; ++e) {
+        const int t = t0 + e;
+        u[e] = 0;
+        pp[e] = -1;
+        if (t < t1) {
+            const int p = pos ? pos[t] : t;
+            pp[e] = p;
+            if (p >= n_prefix) {
+                u[e] = order_key(keys[t]);
+                ranked |= 1u << e;
+            }
+        }
+    }
+
+    // ---- radix select of the n_sel-th largest ranked key ----
+    uint32_t prefix = 0, pmask = 0;
+    int need = n_sel;
+    if (n_sel > 0) {
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int b = tid; b < 256; b += kSelThreads) s_hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kRes; ++e)
+                if (((ranked >> e) & 1u) && (u[e] & pmask) == prefix)
+                    atomicAdd(&s_hist[(u[e] >> shift) & 255], 1);
+            __syncthreads();
+            if (tid < 64) {
+                int c[4], lsum = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { c[e] = s_hist[255 - 4 * tid - e]; lsum += c[e]; }
+                int incl = lsum;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (tid >= o) incl += y;
+                }
+                int above = incl - lsum;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (above < need && need <= above + c[e]) {
+                        s_prefix = prefix | ((uint32_t)(255 - 4 * tid - e) << shift);
+                        s_need = need - above;
+                    }
+                    above += c[e];
+                }
+            }
+            __syncthreads();
+            prefix = s_prefix;
+            need = s_need;
+            pmask |= 255u << shift;
+            __syncthreads();
+        }
+    }
+    if (n_sel <= 0) return;
+    const uint32_t T = prefix;
+
+    // ---- ordered compaction: runs are in position order ----
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < kRes; ++e) {
+        const bool r = (ranked >> e) & 1u;
+        n_gt += r && u[e] > T;
+        n_eq += r && u[e] == T;
+    }
+    int eq_tot;
+    const int eq_before = block_excl_scan(n_eq, s_wave, &eq_tot);
+    const int eq_take = min(max(need - eq_before, 0), n_eq);  // this run's first eq_take ties
+    int take_tot;
+    int o = n_prefix + block_excl_scan(n_gt + eq_take, s_wave, &take_tot);
+    int eq_seen = 0;
+#pragma unroll
+    for (int e = 0; e < kRes; ++e) {
+        const bool r = (ranked >> e) & 1u;
+        const bool eq = r && u[e] == T;
+        const bool take = r && (u[e] > T || (eq && eq_seen < eq_take));
+        eq_seen += eq;
+        if (take && o < n_prefix + n_sel) { // (the bound holds for finite keys)
+            out[o] = pp[e];
+            if (slot && pp[e] < n_slot) slot[pp[e]] = o;
+        }
+        o += take;
+    }
+}
+
 __global__ void k_copy_or_iota(const int32_t* __restrict__ src, int32_t* __restrict__ dst, long n,
                                long row) {
     const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
@@ -218,8 +341,12 @@ hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, i
 hipError_t launch_topk(const float* keys, long key_stride, const int32_t* pos, long pos_stride,
                        int n, int n_sel, int n_prefix, int32_t* out, long out_stride,
                        int32_t* slot, int n_slot, int n_seg, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
-                       pos_stride, n, n_sel, n_prefix, out, out_stride, slot, n_slot);
+    if (n <= kRes * kSelThreads)
+        hipLaunchKernelGGL(k_topk_res, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
+                           pos_stride, n, n_sel, n_prefix, out, out_stride, slot, n_slot);
+    else
+        hipLaunchKernelGGL(k_topk, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
+                           pos_stride, n, n_sel, n_prefix, out, out_stride, slot, n_slot);
     return hipGetLastError();
 }
 
