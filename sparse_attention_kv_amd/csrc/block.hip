@@ -341,15 +341,16 @@ hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int
 }
 
 constexpr bool kGemmLds = true;
+constexpr long kNarrowTiles = 1024; // 128-wide tiles per two workgroup slots (512 and 2048 measured no better)
 
 hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st) {
     if (G.M <= 0) return hipSuccess;
     dim3 grid(G.N / GBN, (G.M + GBM - 1) / GBM);
     if (kGemmLds && G.K % LBK == 0) {
-        // narrow outputs with few tiles (fewer than ~4 per workgroup slot)
-        // take 64-wide tiles: twice the workgroups (measured on the 2048-wide
-        // o projection: 9.7 -> 8.6 ms per 24-layer step)
-        const bool narrow = G.N <= 2048 && (long)(G.N / GBN) * ((G.M + GBM - 1) / GBM) < 4L * 512;
+        // narrow outputs with few tiles take 64-wide tiles: twice the
+        // workgroups (2048-wide o / down projections of the 24-layer step:
+        // 9.7 -> 6.4 ms and 13.6 -> 12.5 ms)
+        const bool narrow = G.N <= 2048 && (long)(G.N / GBN) * ((G.M + GBM - 1) / GBM) < kNarrowTiles;
         if (narrow) {
             dim3 g2(G.N / 64, (G.M + GBM - 1) / GBM);
             if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemm_lds<EPI_STORE, 64>), g2, dim3(256), 0, st, G);
