@@ -28,7 +28,7 @@
 
 namespace fl {
 
-constexpr int DT = 256;      // threads per workgroup
+constexpr int DT = 256;      // threads per workgroup (512 measured slower)
 constexpr int DNW = DT / 64; // waves
 
 struct SeqLevel {
@@ -178,14 +178,18 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         m = wave_max(m);
         if (lane == 0) red[w] = m;
         __syncthreads();
-        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        m = red[0];
+#pragma unroll
+        for (int i = 1; i < DNW; ++i) m = fmaxf(m, red[i]);
         __syncthreads();
         float z = 0.0f;
         for (int c = tid; c <= k; c += DT) z += __builtin_amdgcn_exp2f(sc[c] - m);
         z = wave_sum(z);
         if (lane == 0) red[w] = z;
         __syncthreads();
-        z = red[0] + red[1] + red[2] + red[3];
+        z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DNW; ++i) z += red[i];
         lse2 = m + __log2f(z);
         wgt = P.cache_op == FL_CACHE_ZERO ? 1.0f : 1.0f - P.mass_u[bh];
     } else {
@@ -239,10 +243,14 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     psum = wave_sum(psum);
     if (lane == 0) red[w] = psum;
     __syncthreads();
-    const float ptot = red[0] + red[1] + red[2] + red[3];
+    float ptot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DNW; ++i) ptot += red[i];
     const float pself = sc[k];
     for (int c = tid; c < D; c += DT) {
-        float o = ored[0][c] + ored[1][c] + ored[2][c] + ored[3][c];
+        float o = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DNW; ++i) o += ored[i][c];
         o = fmaf(pself, bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.vself)[qo + c]), o);
         if (MODE == MODE_ATTN) {
             const float u = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.out_u[qo + c];
