@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="prefill32k")
-    ap.add_argument("--cpu-rows", type=int, default=320,
+    ap.add_argument("--cpu-rows", type=int, default=480,
                     help="query rows per loop in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
