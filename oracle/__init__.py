@@ -63,6 +63,7 @@ def lib():
         L.flo_active_count.argtypes = [ctypes.c_double, _int, _int]
         L.flo_active_count.restype = _int
         L.flo_delta_norm.argtypes = [_f32p, _f32p, _int, _vp, _int, _f32p]
+        L.flo_delta_norm_rel.argtypes = [_f32p, _f32p, _int, _vp, _int, _f32p]
         L.flo_top_select.argtypes = [_f32p, _vp, _int, _int, _i32p]
         L.flo_top_select.restype = _int
         L.flo_select_columns.argtypes = [_f32p, _vp, _int, _int, _int, _int, _i32p]
@@ -77,7 +78,7 @@ def lib():
                                            _i32p, _int, _vp, _int, _i32p, _int, _f32p,
                                            _vp, _vp, _f32p, _f32p]
         L.flo_column_stats.argtypes = [_int, _int, _int, _flt, _f32p, _f32p, _vp, _int,
-                                       _vp, _int, _f32p, _vp, _f32p]
+                                       _vp, _int, _f32p, _vp, _vp, _f32p]
         _lib = L
     return _lib
 
@@ -99,15 +100,18 @@ def active_count(rho: float, N: int, n_prev: int) -> int:
     return lib().flo_active_count(float(rho), int(N), int(n_prev))
 
 
-def delta_norm(h_cur, h_prev, cand=None):
-    """Sec. 4.1: ||h_r(i) - h_{r-1}(i)||_2 over candidate rows (fp32)."""
+def delta_norm(h_cur, h_prev, cand=None, relative=False):
+    """Sec. 4.1: ||h_r(i) - h_{r-1}(i)||_2 over candidate rows (fp32); with
+    relative=True the normalised change ||h_r(i) - h_{r-1}(i)|| / ||h_{r-1}(i)||
+    (0 for an unchanged zero state, +inf for a changed one)."""
     h_cur = _c(h_cur, np.float32)
     h_prev = _c(h_prev, np.float32)
     N, D = h_cur.shape
     cand_a = None if cand is None else _c(cand, np.int32)
     n = N if cand is None else len(cand_a)
     out = np.empty(n, np.float32)
-    lib().flo_delta_norm(h_cur, h_prev, D, _ptr(cand_a), n, out)
+    fn = lib().flo_delta_norm_rel if relative else lib().flo_delta_norm
+    fn(h_cur, h_prev, D, _ptr(cand_a), n, out)
     return out
 
 
@@ -213,8 +217,9 @@ def unselected_cache(q_prev, khat_prev, vhat_prev, rows, sel_prev, sel_new, lse_
     return mass_u, out_u
 
 
-def column_stats(q, khat, rows, sel, lse, sm, mass_u=None):
-    """Sec. 4.2: per-head column mass summed over this loop's rows -> [H][k]."""
+def column_stats(q, khat, rows, sel, lse, sm, mass_u=None, vhat=None):
+    """Sec. 4.2: per-head column mass summed over this loop's rows -> [H][k];
+    with vhat ([N][H][d]) each column's mass is weighted by ||vhat(j)||."""
     q = _c(q, np.float32); khat = _c(khat, np.float32)
     N, H, d = q.shape
     rows_a = None if rows is None else _c(rows, np.int32)
@@ -222,7 +227,8 @@ def column_stats(q, khat, rows, sel, lse, sm, mass_u=None):
     sel_a = None if sel is None else _c(sel, np.int32)
     k = N if sel is None else sel_a.shape[1]
     mu = None if mass_u is None else _c(mass_u, np.float32)
+    vh = None if vhat is None else _c(vhat, np.float32)
     out = np.empty((H, k), np.float32)
     lib().flo_column_stats(N, H, d, float(sm), q, khat, _ptr(rows_a), n, _ptr(sel_a), k,
-                           _c(lse, np.float32), _ptr(mu), out)
+                           _c(lse, np.float32), _ptr(mu), _ptr(vh), out)
     return out

@@ -115,11 +115,13 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
                mu=np.zeros((N, H), F32), ou=np.zeros((N, H, d), F32), S=None, k=N, cstat=None)
           for _ in range(L)]
     A = np.arange(N, dtype=np.int32)
+    rel = sched.get("token_stat", "abs") == "rel"
+    vw = sched.get("col_stat", "mass") == "vnorm"
     out = []
     for r in range(1, R + 1):
         rec = dict(r=r)
         if r > 1:
-            stat = delta_norm(h, h_entry, A)
+            stat = delta_norm(h, h_entry, A, relative=rel)
             n_r = active_count(sched["rho"][r - 1], N, len(A))
             A = top_select(override.get(("stat", r), stat), n_r, A)
             rec["stat"] = stat
@@ -154,7 +156,8 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
                 mu = np.zeros((N, H), F32); ou = np.zeros((N, H, d), F32)
                 S_new, k_new = None, N
                 need_c = R > 1 and sched["kcols"][1] < N
-                c = column_stats(qd, khat, None, None, lse, sm) if need_c else None
+                c = column_stats(qd, khat, None, None, lse, sm,
+                                 vhat=vhat if vw else None) if need_c else None
             else:
                 k_r = sched["kcols"][r - 1]
                 if s["k"] <= k_r:
@@ -172,7 +175,8 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
                     mu, ou = s["mu"][A].copy(), s["ou"][A].copy()
                 o, lse = attend(qd, khat, vhat, A, S_new, sm, mu, ou)
                 need_c = r < R and sched["kcols"][r] < k_new
-                c = column_stats(qd, khat, A, S_new, lse, sm, mu) if need_c else None
+                c = column_stats(qd, khat, A, S_new, lse, sm, mu,
+                                 vhat=vhat if vw else None) if need_c else None
             lrec.update(sel=S_new, k=k_new, out=o, lse=lse, mass_u=mu, cstat=c)
             rec["layers"].append(lrec)
             # carry the layer's state

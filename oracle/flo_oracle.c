@@ -77,6 +77,35 @@ void flo_delta_norm(const float* h_cur, const float* h_prev, int D,
     }
 }
 
+/* Sec. 4.1 ranks tokens by their *normalized* hidden-state change.  Read as
+ * the change relative to the previous loop's state:
+ *   stat(i) = ||h_r(i) - h_{r-1}(i)||_2 / ||h_{r-1}(i)||_2
+ * (both norms fp32, then one division).  A token whose previous state is the
+ * zero vector has no scale to normalise by: its statistic is 0 if it did not
+ * change and +infinity otherwise (any change of a zero state is unbounded
+ * relative to it). */
+void flo_delta_norm_rel(const float* h_cur, const float* h_prev, int D,
+                        const int* cand, int n_cand, float* stat) {
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < n_cand; ++t) {
+        long i = cand ? cand[t] : t;
+        const float* a = h_cur + i * (long)D;
+        const float* b = h_prev + i * (long)D;
+        float num = 0.0f, den = 0.0f;
+        for (int c = 0; c < D; ++c) {
+            float e = a[c] - b[c];
+            float e2 = e * e;
+            num = num + e2;
+            float p2 = b[c] * b[c];
+            den = den + p2;
+        }
+        float dn = sqrtf(num);
+        float pn = sqrtf(den);
+        if (pn > 0.0f) stat[t] = dn / pn;
+        else stat[t] = dn > 0.0f ? INFINITY : 0.0f;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Top-k selection used for both active tokens (Sec. 4.1) and columns
  * (Sec. 4.2): keep the n_sel candidates with the largest key; equal keys go to
@@ -359,10 +388,14 @@ void flo_unselected_cache(int N, int H, int d, float sm, const float* q_prev,
  * loop"): the attention-contribution statistic of each selected column, read
  * as its probability mass summed over the rows computed in this loop:
  *   c(j) = sum_{i in rows, i >= j} (1 - M_U(i)) * exp(sm*q(i).khat(j) - lse(i)).
- * sel == NULL means all columns (k == N).  cstat is [H][k]. */
+ * sel == NULL means all columns (k == N).  cstat is [H][k].
+ * With vhat != NULL ([N][H][d], the dequantised values the loop attended to)
+ * each column's mass is weighted by the norm of its value vector, which reads
+ * the statistic as the size of the column's contribution to the loop's
+ * outputs: sum_i (1 - M_U(i)) P(i,j) ||vhat(j)||_2 = sum_i ||(1 - M_U(i)) P(i,j) vhat(j)||_2. */
 void flo_column_stats(int N, int H, int d, float sm, const float* q, const float* khat,
                       const int* rows, int n_rows, const int* sel, int k, const float* lse,
-                      const float* mass_u, float* cstat) {
+                      const float* mass_u, const float* vhat, float* cstat) {
     (void)N;
     #pragma omp parallel for schedule(dynamic, 16)
     for (long hp = 0; hp < (long)H * k; ++hp) {
@@ -382,6 +415,13 @@ void flo_column_stats(int N, int H, int d, float sm, const float* q, const float
             float u = mass_u ? mass_u[th] : 0.0f;
             float P = (1.0f - u) * expf(s - lse[th]);
             c = c + P;
+        }
+        if (vhat) {
+            /* value-weighted variant: the column's mass times ||vhat(j)||_2 */
+            const float* vj = vhat + (j * H + h) * d;
+            float v2 = 0.0f;
+            for (int e = 0; e < d; ++e) { float sq = vj[e] * vj[e]; v2 = v2 + sq; }
+            c = c * sqrtf(v2);
         }
         cstat[hp] = c;
     }

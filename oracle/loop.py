@@ -9,7 +9,8 @@ dense early loops"):
   loop 1   base-quantise K_1, V_1; dense causal attention on the dequantised
            cache; column statistics of every column; A_1 = all tokens,
            S_1 = all columns, M_U = O_U = 0.
-  loop r   (1) token statistic ||h_r - h_{r-1}|| over A_{r-1};
+  loop r   (1) token statistic ||h_r - h_{r-1}|| (or its ratio to
+               ||h_{r-1}||) over A_{r-1};
            (2) A_r = top n_r of A_{r-1};
            (3) residual level r-1 for rows A_r against the dequantised
                previous loop; other rows keep their previous K/V;
@@ -44,7 +45,9 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
     h: list of R arrays [N][D]; q, k, v: lists of R arrays [N][H][d] (fp32
     values; bf16 inputs are passed as their exact fp32 expansion).
     sched: dict with N, H, d, g, R, n_sink, rho[R], kcols[R], bits[R]
-    (bits[0] is the base level: 8 or 32).
+    (bits[0] is the base level: 8 or 32); optional token_stat "abs" (default)
+    or "rel" (normalised change, Sec. 4.1) and col_stat "mass" (default) or
+    "vnorm" (mass weighted by the column's value norm, Sec. 4.2).
     override: optional dict {('stat', r): array, ('cstat', r): array} used in
     place of the oracle's own statistic for the selection made at loop r.
     Returns a list of per-loop dicts.
@@ -60,7 +63,10 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
     lv, vhat = _level(v[0], None, g, sched["bits"][0])
     o1, lse1 = attend(q[0], khat, vhat, None, None, sm)
     need_c = R > 1 and (stats_every_loop or sched["kcols"][1] < N)
-    c1 = column_stats(q[0], khat, None, None, lse1, sm) if need_c else None
+    vw = sched.get("col_stat", "mass") == "vnorm"
+    rel = sched.get("token_stat", "abs") == "rel"
+    c1 = column_stats(q[0], khat, None, None, lse1, sm, vhat=vhat if vw else None) \
+        if need_c else None
     A = np.arange(N, dtype=np.int32)
     S = None
     k_cur = N
@@ -75,7 +81,7 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
 
     for r in range(2, R + 1):
         # (1)-(2) token selection, nested in A_{r-1}
-        stat = delta_norm(h[r - 1], h[r - 2], cand=A)
+        stat = delta_norm(h[r - 1], h[r - 2], cand=A, relative=rel)
         stat_sel = override.get(("stat", r), stat)
         n_r = active_count(sched["rho"][r - 1], N, len(A))
         A_new = top_select(stat_sel, n_r, pos=A)
@@ -103,7 +109,8 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
         o_r, lse_r = attend(q[r - 1], khat_new, vhat_new, A_new, S_new, sm, mu, ou)
         # (7) column statistics for the next selection
         need_c = stats_every_loop or (r < R and sched["kcols"][r] < k_new)
-        c_r = column_stats(q[r - 1], khat_new, A_new, S_new, lse_r, sm, mu) if need_c else None
+        c_r = column_stats(q[r - 1], khat_new, A_new, S_new, lse_r, sm, mu,
+                           vhat=vhat_new if vw else None) if need_c else None
         rec = dict(r=r, stat=stat, active=A_new, n=n_r, level_k=lk, level_v=lv, sel=S_new,
                    k=k_new, sel_changed=changed, mass_u=mu, out_u=ou, out=o_r, lse=lse_r,
                    cstat=c_r)
