@@ -54,6 +54,12 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
+    ap.add_argument("--token-stat", default="abs", choices=["abs", "rel"],
+                    help="token ranking: absolute or normalised hidden-state change")
+    ap.add_argument("--col-stat", default="mass", choices=["mass", "vnorm"],
+                    help="column ranking: probability mass, or mass x value norm")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="block workloads: time the retention calibration instead of the step")
     ap.add_argument("--mode", default="auto", choices=["auto", "once", "in_tile"],
                     help="where the cache is dequantised (library default: auto)")
     return ap.parse_args()
@@ -137,8 +143,10 @@ def main():
     for r in range(1, R):
         n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
     mode = {"auto": fl.FL_DEQ_AUTO, "once": fl.FL_DEQ_ONCE, "in_tile": fl.FL_DEQ_IN_TILE}[args.mode]
+    ts, cs = stat_kinds(args, fl)
     run = fl.LoopRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
-                        dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode)
+                        dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode,
+                        token_stat=ts, col_stat=cs)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -254,7 +262,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "R": R, "g": w.g,
                    "active_per_loop": n_act, "k_per_loop": [L["k"] for L in loops],
-                   "bits_per_loop": w.bits, "n_sink": w.n_sink, "dequant": args.mode},
+                   "bits_per_loop": w.bits, "n_sink": w.n_sink, "dequant": args.mode,
+                   "token_stat": args.token_stat, "col_stat": args.col_stat},
         "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.mean(loop_ms[:, i])), 4),
                        pairs=L["pairs"], rebuilt=L["rebuilt"], colstat=L["colstat"])
                   for i, L in enumerate(loops)],
@@ -267,11 +276,19 @@ def main():
 
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, run, n_act, loops, args.cpu_rows, torch, np)
+        out["cpu_baseline"] = cpu_baseline(w, inp, run, n_act, loops, args.cpu_rows, torch, np,
+                                           rel=args.token_stat == "rel",
+                                           vw=args.col_stat == "vnorm")
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
+def stat_kinds(args, fl):
+    ts = fl.FL_TOKEN_STAT_REL if args.token_stat == "rel" else fl.FL_TOKEN_STAT_ABS
+    cs = fl.FL_COL_STAT_VNORM if args.col_stat == "vnorm" else fl.FL_COL_STAT_MASS
+    return ts, cs
+
+
+def cpu_baseline(w, inp, run, n_act, loops, m, torch, np, rel=False, vw=False):
     """The oracle, as is, on a bounded sample of the same workload: token
     statistic + selection, quantisation and column selection in full; the
     per-row work (attention, cache rebuild, column statistics) on m evenly
@@ -297,7 +314,7 @@ def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
             _, _, _, vhat_n = oracle.quantize_rows(x["v"][0], None, g, w.bits[0])
         else:
             prev = run.active[r - 2].cpu().numpy()
-            stat = oracle.delta_norm(x["h"][r - 1], x["h"][r - 2], prev)
+            stat = oracle.delta_norm(x["h"][r - 1], x["h"][r - 2], prev, relative=rel)
             oracle.top_select(stat, n_act[r - 1], prev)
             _, _, _, kr = oracle.quantize_rows(x["k"][r - 1][act], khat[act], g, w.bits[r - 1])
             _, _, _, vr = oracle.quantize_rows(x["v"][r - 1][act], vhat[act], g, w.bits[r - 1])
@@ -321,7 +338,8 @@ def cpu_baseline(w, inp, run, n_act, loops, m, torch, np):
         o, l = oracle.attend(x["q"][r - 1], khat_n, vhat_n, samp, sel, sm,
                              None if r == 1 else mu_s, None if r == 1 else ou_s)
         if loops[r - 1]["colstat"]:
-            oracle.column_stats(x["q"][r - 1], khat_n, samp, sel, l, sm, None if r == 1 else mu_s)
+            oracle.column_stats(x["q"][r - 1], khat_n, samp, sel, l, sm, None if r == 1 else mu_s,
+                                vhat=vhat_n if vw else None)
         t_rows = time.perf_counter() - t
         t_loop = t_full + t_rows * len(act) / len(samp)
         per_loop.append(dict(r=r, full_s=round(t_full, 3), sampled_rows=len(samp),
@@ -360,8 +378,12 @@ def bench_block(args, w, np, torch, fl, synth):
     n_act = [N]
     for r in range(1, R):
         n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
+    ts, cs = stat_kinds(args, fl)
+    if args.calibrate:
+        return bench_calibrate(args, w, h1, wdev, fl, torch, ts, cs)
     run = fl.BlockRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, wdev, F,
-                         rope_theta=w.extra["theta"], norm_eps=w.extra["eps"])
+                         rope_theta=w.extra["theta"], norm_eps=w.extra["eps"], token_stat=ts,
+                         col_stat=cs)
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -421,7 +443,8 @@ def bench_block(args, w, np, torch, fl, synth):
         "data": "synthetic (random-init shared weights)",
         "config": {"workload": w.name, "N": N, "layers": L, "hidden": D, "heads": H, "head_dim": d,
                    "ffn": F, "R": R, "active_per_loop": n_act, "k_per_loop": w.kcols,
-                   "bits_per_loop": w.bits},
+                   "bits_per_loop": w.bits, "token_stat": args.token_stat,
+                   "col_stat": args.col_stat},
         "loops": [dict(r=r + 1, n=n_act[r], ms=round(float(np.mean(loop_ms[:, r])), 3))
                   for r in range(R)],
         "kernels": kernels,
@@ -432,11 +455,12 @@ def bench_block(args, w, np, torch, fl, synth):
         "gemm_flops_dense_equivalent": sum(per_tok.values()) * N * R * L,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_block(w, inp, n_act, np)
+        out["cpu_baseline"] = cpu_baseline_block(w, inp, n_act, np, rel=args.token_stat == "rel",
+                                                 vw=args.col_stat == "vnorm")
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_block(w, inp, n_act, np, m=32):
+def cpu_baseline_block(w, inp, n_act, np, m=32, rel=False, vw=False):
     """The block oracle's step functions, as they are, on a bounded sample of
     the same workload: the first layer through all R loops.  Token
     selection, RMSNorm, the four projections, RoPE, quantisation and column
@@ -461,7 +485,7 @@ def cpu_baseline_block(w, inp, n_act, np, m=32):
         t_full = t_rows = 0.0
         t = time.perf_counter()
         if r > 1:
-            stat = oracle.delta_norm(h, h_entry, A)
+            stat = oracle.delta_norm(h, h_entry, A, relative=rel)
             A = oracle.top_select(stat, n_act[r - 1], A)
         h_entry = h.copy()
         a = ob.bf16(ob.rmsnorm(h[A], lw["norm1"], w.extra["eps"]))
@@ -486,7 +510,7 @@ def cpu_baseline_block(w, inp, n_act, np, m=32):
             oracle.unselected_cache(qd, khat, vhat, samp, S, S_new, lse[samp], sm)
         o, l_s = oracle.attend(qn, kh, vh, samp, S_new, sm)
         if r < R:
-            cstat_s = oracle.column_stats(qn, kh, samp, S_new, l_s, sm)
+            cstat_s = oracle.column_stats(qn, kh, samp, S_new, l_s, sm, vhat=vh if vw else None)
         t_rows = time.perf_counter() - t
         t = time.perf_counter()
         # the rest of the layer on the active rows (outputs of the rows not
@@ -514,6 +538,38 @@ def cpu_baseline_block(w, inp, n_act, np, m=32):
                        f"statistics on {m} evenly spaced active rows per loop (all {H} heads), "
                        f"extrapolated to n_r rows, then x{L} layers"),
             "extrapolated_step_s": round(step_s, 1)}
+
+
+def bench_calibrate(args, w, h1, wdev, fl, torch, ts, cs):
+    """Retention calibration (App. E reading: smallest ratio per loop with
+    hidden-state error below 5% against the all-tokens run) of the block
+    workload, timed end to end: value = candidate loops evaluated per second."""
+    from sparse_attention_kv_amd import calibrate
+    N, R = w.N, w.R
+    run = fl.BlockRunner(N, w.H, w.d, w.g, R, w.n_sink, [N] * R, w.kcols, w.bits, wdev,
+                         w.extra["ffn"], rope_theta=w.extra["theta"], norm_eps=w.extra["eps"],
+                         token_stat=ts, col_stat=cs, row_capacity=[N] * R)
+    grid = [0.1 * i for i in range(1, 11)]
+    calibrate.calibrate_retention(run, h1, [1.0], tol=0.05)      # warm-up (one ratio)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    res = calibrate.calibrate_retention(run, h1, grid, tol=0.05)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    loops_run = R + sum(r * len(tr) for r, tr in res["trials"].items())
+    out = {"metric": "retention calibration of the looped block (loops evaluated per second)",
+           "value": round(loops_run / wall, 2), "unit": "block loops/s", "n_gpus": 1,
+           "steps": 1, "warmup": 1, "ms_per_step": round(wall * 1e3, 1), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (random-init shared weights)",
+           "config": {"workload": w.name, "N": N, "layers": w.extra["layers"], "R": R,
+                      "grid": [round(g_, 2) for g_ in grid], "bound": 0.05,
+                      "token_stat": args.token_stat, "col_stat": args.col_stat},
+           "calibrated": {"rho": [round(x, 2) for x in res["rho"]], "n_active": res["n_active"],
+                          "err": [round(e, 5) for e in res["err"]]},
+           "trials": {str(r): [[round(c, 2), n, round(e, 5)] for c, n, e in tr]
+                      for r, tr in res["trials"].items()}}
+    print(json.dumps(out), flush=True)
 
 
 def bench_decode(args, w, np, torch, fl, synth):

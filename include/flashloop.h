@@ -97,16 +97,21 @@ enum fl_ws_op {
     FL_WS_SELECT_COLUMNS = 2, /* a = H, b = n_cand                             */
     FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = cache levels used (level+1; <= 0: max) */
     FL_WS_LOOP_STEP = 4,      /* a = H, b = N (largest k), c = d, e = R        */
-    FL_WS_BLOCK_STEP = 5      /* a = N, b = H, c = d, e = ffn width            */
+    FL_WS_BLOCK_STEP = 5,     /* a = N, b = H, c = d, e = ffn width            */
+    FL_WS_SQ_ERR = 6          /* a = n                                         */
 };
 size_t fl_workspace_size(int op, long a, long b, long c, long e);
 
 /* ------------------------------------------------------------------------
  * fl_select_active -- paper Sec. 4.1 (cross-loop token-sparse updates).
  * For each candidate token cand[t] (the tokens active in the previous loop;
- * NULL = all positions 0..n_cand-1) computes the statistic
- *   stat_out[t] = || h_cur[cand[t]] - h_prev[cand[t]] ||_2   (fp32)
- * over D channels (h_* are [N][D], dtype FL_BF16 or FL_F32), then selects the
+ * NULL = all positions 0..n_cand-1) computes the statistic (stat_kind)
+ *   FL_TOKEN_STAT_ABS: stat_out[t] = || h_cur[i] - h_prev[i] ||_2
+ *   FL_TOKEN_STAT_REL: stat_out[t] = || h_cur[i] - h_prev[i] ||_2 / || h_prev[i] ||_2
+ *                      (Sec. 4.1's normalised change; 0 when h_prev[i] = 0 and
+ *                      h_cur[i] = h_prev[i], +inf when only h_prev[i] = 0)
+ * with i = cand[t], in fp32 over D channels (h_* are [N][D], dtype FL_BF16 or
+ * FL_F32), then selects the
  * n_select candidates with the largest statistic; equal statistics go to the
  * lower position; -0 ranks as +0; statistics must be finite.
  * If stat_in != NULL the statistic is not computed and stat_in[n_cand] is
@@ -115,8 +120,10 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e);
  * gets slot_out[active_out[s]] = s and -1 for every other position.
  * Workspace: fl_workspace_size(FL_WS_SELECT_ACTIVE, n_cand, ...).
  * Errors: FL_ERR_INVALID_ARG for null required pointers, n_select outside
- * [1, n_cand], n_cand > N, D < 1. */
-int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, int D,
+ * [1, n_cand], n_cand > N, D < 1, an unknown stat_kind. */
+enum fl_token_stat { FL_TOKEN_STAT_ABS = 0, FL_TOKEN_STAT_REL = 1 };
+
+int fl_select_active(int dtype, int stat_kind, const void* h_cur, const void* h_prev, int N, int D,
                      const int32_t* cand, int n_cand, int n_select, const float* stat_in,
                      float* stat_out, int32_t* active_out, int32_t* slot_out, void* ws,
                      size_t ws_bytes, fl_stream_t stream);
@@ -181,10 +188,17 @@ int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const v
  * Column statistics (col_stat != NULL): after the attention,
  *   col_stat[h][p] = sum_{active i >= sel[h][p]} (1 - M_U(i)) *
  *                    exp(sm*q(i).khat(sel[h][p]) - lse(i))
- * (the previous-loop statistic that ranks the next loop's columns).
+ * (the previous-loop statistic that ranks the next loop's columns).  With
+ * col_stat_kind = FL_COL_STAT_VNORM each column's value is multiplied by
+ * || vhat(sel[h][p]) ||_2 (fp32, of the dequantised value vector the loop
+ * attended to): the size of the column's contribution to the loop's outputs.
  * With sel == NULL (all N columns, k == N) and M_U = O_U = 0 this is the
  * dense first loop.
  */
+enum fl_col_stat {
+    FL_COL_STAT_MASS = 0,  /* probability mass of the column (default)          */
+    FL_COL_STAT_VNORM = 1  /* mass times the column's dequantised value norm     */
+};
 enum fl_attn_mode {
     FL_DEQ_AUTO = 0,    /* library choice (currently FL_DEQ_ONCE, the faster)  */
     FL_DEQ_ONCE = 1,    /* dequantise the selected columns once per head into a
@@ -220,6 +234,7 @@ typedef struct fl_attn_args {
     /* rebuild input: the previous loop's queries (same layout rules as q) */
     const void* q_prev;
     int q_prev_gathered;
+    int col_stat_kind;         /* fl_col_stat (used when col_stat != NULL)      */
 } fl_attn_args;
 
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void* ws,
@@ -244,6 +259,8 @@ typedef struct fl_loop_cfg {
     int k_cols[FL_MAX_LEVELS];   /* column budget per loop; [0] = N             */
     int bits[FL_MAX_LEVELS];     /* [0] base bits (8/32), [r-1] residual bits   */
     int mode;               /* fl_attn_mode                                    */
+    int token_stat;         /* fl_token_stat: ranking of active tokens         */
+    int col_stat;           /* fl_col_stat: ranking of columns                 */
 } fl_loop_cfg;
 
 typedef struct fl_loop_state {
@@ -301,6 +318,8 @@ typedef struct fl_block_cfg {
     int k_cols[FL_MAX_LEVELS];
     int bits[FL_MAX_LEVELS];
     int mode;               /* fl_attn_mode */
+    int token_stat;         /* fl_token_stat */
+    int col_stat;           /* fl_col_stat   */
 } fl_block_cfg;
 
 typedef struct fl_layer_weights {
@@ -396,6 +415,22 @@ int fl_timing_report(char* buf, size_t len);
 /* ------------------------------------------------------------------------ */
 const char* fl_last_error(void);
 const char* fl_version(void);
+
+/* ------------------------------------------------------------------------
+ * fl_sq_err -- the reconstruction error behind the retention calibration of
+ * the paper's App. E ("Quantization Setting": each loop keeps the smallest
+ * retention ratio whose hidden states or attention outputs stay below a
+ * relative reconstruction error of 5% against the reference).  Computes, over
+ * n fp32 values,
+ *   out[0] = sum_i (x[i] - ref[i])^2,   out[1] = sum_i ref[i]^2
+ * in fp64 (out: device pointer to 2 doubles); the relative error is
+ * sqrt(out[0] / out[1]).  x and ref are device pointers aligned to 16 bytes.
+ * The summation order depends only on n (deterministic).
+ * Workspace: fl_workspace_size(FL_WS_SQ_ERR, n).
+ * Errors: FL_ERR_INVALID_ARG for null or misaligned pointers or n < 1;
+ * FL_ERR_WORKSPACE. */
+int fl_sq_err(const float* x, const float* ref, long n, double* out, void* ws, size_t ws_bytes,
+              fl_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashloop.so")
 
-SOURCES = ["abi.hip", "select.hip", "quant.hip", "attn.hip", "block.hip", "decode.hip"]
+SOURCES = ["abi.hip", "select.hip", "quant.hip", "attn.hip", "block.hip", "decode.hip", "calib.hip"]
 NO_CONTRACT = {"select.hip", "quant.hip"}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

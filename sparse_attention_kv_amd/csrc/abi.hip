@@ -47,7 +47,7 @@ long kpad(long k) { return (k + 63) / 64 * 64; }
 // workspace of fl_sparse_loop_attn: two compact bf16 copies (K, V^T) for the
 // current loop and, for a cache rebuild, two for the previous loop, each with
 // a "lo" copy (used when the cache has residual levels or inputs are fp32),
-// plus the column positions.
+// plus the column positions and the fp32 value norms of the selected columns.
 // The in-tile path adds per-level quantised planes (codes <= 8 bits, fp32
 // scales per group of >= 32 channels) for K and V.
 long quant_plane_bytes(long H, long kp, long d) {
@@ -56,8 +56,8 @@ long quant_plane_bytes(long H, long kp, long d) {
 long attn_ws_bytes(long H, long k, long d, long levels) {
     const long kp = kpad(k);
     if (levels <= 0 || levels > FL_MAX_LEVELS) levels = FL_MAX_LEVELS;
-    return 8 * align_up(H * kp * d * 2) + align_up(H * kp * 4) + levels * quant_plane_bytes(H, kp, d) +
-           kAlign;
+    return 8 * align_up(H * kp * d * 2) + 2 * align_up(H * kp * 4) +
+           levels * quant_plane_bytes(H, kp, d) + kAlign;
 }
 
 // workspace of fl_block_step: compact bf16 activations of the active rows
@@ -109,6 +109,10 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
 }
 
 bool dtype_ok(int dt) { return dt == FL_F32 || dt == FL_BF16; }
+bool stat_kinds_ok(int token_stat, int col_stat) {
+    return (token_stat == FL_TOKEN_STAT_ABS || token_stat == FL_TOKEN_STAT_REL) &&
+           (col_stat == FL_COL_STAT_MASS || col_stat == FL_COL_STAT_VNORM);
+}
 
 int check_cache(const fl_kv_cache* c, int upto) {
     FL_REQUIRE(c != nullptr, "cache is NULL");
@@ -150,6 +154,8 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     case FL_WS_BLOCK_STEP:
         if (a <= 0 || b <= 0 || !(c == 64 || c == 128) || e <= 0) return 0;
         return (size_t)block_ws_bytes(a, b, c, e);
+    case FL_WS_SQ_ERR:
+        return a > 0 ? (size_t)(align_up(16L * fl::sq_err_blocks(a)) + kAlign) : 0;
     case FL_WS_SPARSE_ATTN:
     case FL_WS_LOOP_STEP:
         if (a <= 0 || b <= 0 || !(c == 64 || c == 128)) return 0;
@@ -193,7 +199,7 @@ int fl_timing_report(char* buf, size_t len) {
     return rc;
 }
 
-int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, int D,
+int fl_select_active(int dtype, int stat_kind, const void* h_cur, const void* h_prev, int N, int D,
                      const int32_t* cand, int n_cand, int n_select, const float* stat_in,
                      float* stat_out, int32_t* active_out, int32_t* slot_out, void* ws,
                      size_t ws_bytes, fl_stream_t stream) {
@@ -202,6 +208,8 @@ int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, in
     FL_REQUIRE(n_cand >= 1 && n_cand <= N, "n_cand %d not in [1, N=%d]", n_cand, N);
     FL_REQUIRE(n_select >= 1 && n_select <= n_cand, "n_select %d not in [1, n_cand=%d]", n_select, n_cand);
     FL_REQUIRE(active_out != nullptr, "active_out is NULL");
+    FL_REQUIRE(stat_kind == FL_TOKEN_STAT_ABS || stat_kind == FL_TOKEN_STAT_REL, "stat_kind %d",
+               stat_kind);
     if (!stat_in) {
         FL_REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
         FL_REQUIRE(h_cur && h_prev && stat_out, "h_cur/h_prev/stat_out NULL");
@@ -211,7 +219,8 @@ int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, in
     const float* keys = stat_in;
     if (!stat_in) {
         FL_HIP(timed("delta_norm", st, [&] {
-                   return fl::launch_delta_norm(h_cur, h_prev, dtype, D, cand, n_cand, stat_out, st);
+                   return fl::launch_delta_norm(h_cur, h_prev, dtype, D, cand, n_cand,
+                                                stat_kind == FL_TOKEN_STAT_REL, stat_out, st);
                }),
                "delta_norm");
         keys = stat_out;
@@ -221,6 +230,20 @@ int fl_select_active(int dtype, const void* h_cur, const void* h_prev, int N, in
                                       slot_out ? N : 0, 1, st);
            }),
            "topk");
+    return FL_OK;
+}
+
+int fl_sq_err(const float* x, const float* ref, long n, double* out, void* ws, size_t ws_bytes,
+              fl_stream_t stream) {
+    FL_REQUIRE(n >= 1, "n = %ld", n);
+    FL_REQUIRE(x && ref && out, "x/ref/out NULL");
+    FL_REQUIRE(((uintptr_t)x % 16) == 0 && ((uintptr_t)ref % 16) == 0, "x/ref not 16-byte aligned");
+    const long need = align_up(16L * fl::sq_err_blocks(n)) + kAlign;
+    if (!ws || (long)ws_bytes < need)
+        return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
+    double* part = (double*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+    hipStream_t st = (hipStream_t)stream;
+    FL_HIP(timed("sq_err", st, [&] { return fl::launch_sq_err(x, ref, n, part, out, st); }), "sq_err");
     return FL_OK;
 }
 
@@ -279,6 +302,8 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
         FL_REQUIRE(a->q_prev != nullptr, "q_prev NULL");
     }
     FL_REQUIRE(a->mode >= FL_DEQ_AUTO && a->mode <= FL_DEQ_IN_TILE, "mode %d", a->mode);
+    FL_REQUIRE(a->col_stat_kind == FL_COL_STAT_MASS || a->col_stat_kind == FL_COL_STAT_VNORM,
+               "col_stat_kind %d", a->col_stat_kind);
     const int prec = attn_prec(a->dtype, a->level);
     const int prec_old = attn_prec(a->dtype, a->level - 1);
     // FL_DEQ_AUTO resolves to FL_DEQ_ONCE: on the 32K, 4-loop workload the
@@ -300,7 +325,10 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     __bf16* buf[8];
     for (int i = 0; i < 8; ++i) buf[i] = (__bf16*)(base + i * kvb);
     int32_t* cpos = (int32_t*)(base + 8 * kvb);
-    char* qbase = base + 8 * kvb + align_up((long)H * kp * 4);
+    float* vnorm_buf = (float*)(base + 8 * kvb + align_up((long)H * kp * 4));
+    char* qbase = base + 8 * kvb + 2 * align_up((long)H * kp * 4);
+    // value norms of the current loop's columns, written by its gather
+    float* vn = (a->col_stat && a->col_stat_kind == FL_COL_STAT_VNORM) ? vnorm_buf : nullptr;
     // new side: K, V^T (+ lo parts); previous-loop side for a rebuild
     __bf16 *Kc = buf[0], *Vt = buf[1], *Kc_old = buf[2], *Vt_old = buf[3];
     __bf16 *Kl = buf[4], *Vl = buf[5], *Kl_old = buf[6], *Vl_old = buf[7];
@@ -331,7 +359,7 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     } else {
         FL_HIP(timed("gather", st, [&] {
                    return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc, Vt,
-                                                 Kl, Vl, cpos, st);
+                                                 Kl, Vl, cpos, vn, st);
                }),
                "gather");
     }
@@ -343,7 +371,7 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
             FL_HIP(timed("gather", st, [&] {
                        return fl::launch_gather_bf16(*cache, a->level - 1, a->sel, a->k, kp,
                                                      prec_old >= 1, Kc_old, Vt_old, Kl_old, Vl_old,
-                                                     cpos, st);
+                                                     cpos, nullptr, st);
                    }),
                    "gather(prev)");
             R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
@@ -364,14 +392,14 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
         if (in_tile) // the statistics sweep reads the keys as compact bf16
             FL_HIP(timed("gather", st, [&] {
                        return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc,
-                                                     Vt, Kl, Vl, cpos, st);
+                                                     Vt, Kl, Vl, cpos, vn, st);
                    }),
                    "gather");
         fl::ColParams C{};
         C.H = H; C.n = a->n; C.k = a->k; C.kp = kp; C.dtype = a->dtype; C.q_gathered = a->q_gathered;
         C.cache_op = a->cache_op == FL_CACHE_ZERO ? FL_CACHE_ZERO : FL_CACHE_CARRY;
         C.c2 = c2; C.q = a->q; C.active = a->active; C.Kc = Kc; C.Kc_lo = Kl; C.cpos = cpos;
-        C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat;
+        C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat; C.vnorm = vn;
         FL_HIP(timed(prec ? "colstat_split" : "colstat", st,
                      [&] { return fl::launch_colstat(d, prec, C, st); }),
                "colstat");
@@ -383,6 +411,8 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
                  void* ws, size_t ws_bytes, fl_stream_t stream) {
     FL_REQUIRE(cfg && S && in, "cfg/state/inputs NULL");
     FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
+    FL_REQUIRE(stat_kinds_ok(cfg->token_stat, cfg->col_stat), "token_stat %d / col_stat %d",
+               cfg->token_stat, cfg->col_stat);
     const int N = cfg->N, H = cfg->H, d = cfg->d;
     fl_kv_cache& C = S->cache;
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
@@ -392,6 +422,7 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
     const float sm = 1.0f / sqrtf((float)d);
     fl_attn_args A{};
     A.dtype = cfg->dtype; A.q = in->q; A.q_gathered = 0; A.sm = sm; A.mode = cfg->mode;
+    A.col_stat_kind = cfg->col_stat;
     A.out = S->out; A.lse = S->lse; A.mass_u = S->mass_u; A.out_u = S->out_u;
     if (r == 1) {
         FL_REQUIRE(S->active[0] != nullptr, "active[0] (iota buffer) NULL");
@@ -416,7 +447,8 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
     const int n_r = cfg->n_active[r - 1];
     FL_REQUIRE(n_r >= 1 && n_r <= n_prev, "n_active[%d] = %d (prev %d)", r - 1, n_r, n_prev);
     FL_REQUIRE(S->active[r - 1] && S->slot[r - 1] && S->stat, "active/slot/stat buffers NULL");
-    int rc = fl_select_active(cfg->dtype, in->h_cur, in->h_prev, N, H * d, S->active[r - 2], n_prev,
+    int rc = fl_select_active(cfg->dtype, cfg->token_stat, in->h_cur, in->h_prev, N, H * d,
+                              S->active[r - 2], n_prev,
                               n_r, nullptr, S->stat, S->active[r - 1], S->slot[r - 1], ws, ws_bytes,
                               stream);
     if (rc) return rc;
@@ -459,6 +491,8 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
     FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
     const int N = cfg->N, H = cfg->H, d = cfg->d, D = H * d, F = cfg->ffn, L = cfg->n_layers;
     FL_REQUIRE(N > 0 && L >= 1, "N=%d layers=%d", N, L);
+    FL_REQUIRE(stat_kinds_ok(cfg->token_stat, cfg->col_stat), "token_stat %d / col_stat %d",
+               cfg->token_stat, cfg->col_stat);
     if (!(d == 64 || d == 128)) return fail(FL_ERR_UNSUPPORTED, "head dim %d", d);
     if (D % 128 || F % 128) return fail(FL_ERR_UNSUPPORTED, "D=%d and ffn=%d must be multiples of 128", D, F);
     FL_REQUIRE(S->h && S->h_entry && S->stat, "h/h_entry/stat NULL");
@@ -489,7 +523,8 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         n = cfg->n_active[r - 1];
         FL_REQUIRE(n >= 1 && n <= n_prev, "n_active[%d] = %d (prev %d)", r - 1, n, n_prev);
         FL_REQUIRE(S->active[r - 1] && S->slot[r - 1], "active/slot buffers NULL");
-        int rc = fl_select_active(FL_F32, S->h, S->h_entry, N, D, S->active[r - 2], n_prev, n, nullptr,
+        int rc = fl_select_active(FL_F32, cfg->token_stat, S->h, S->h_entry, N, D, S->active[r - 2],
+                                  n_prev, n, nullptr,
                                   S->stat, S->active[r - 1], S->slot[r - 1], nullptr, 0, stream);
         if (rc) return rc;
     }
@@ -537,7 +572,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         if (rc) return rc;
         fl_attn_args A{};
         A.dtype = FL_BF16; A.q = qc; A.q_gathered = 1; A.active = act; A.n = n; A.sm = sm;
-        A.level = r - 1; A.mode = cfg->mode;
+        A.level = r - 1; A.mode = cfg->mode; A.col_stat_kind = cfg->col_stat;
         A.out = Ls.out; A.lse = Ls.lse; A.mass_u = Ls.mass_u; A.out_u = Ls.out_u;
         A.q_prev = Ls.q_state; A.q_prev_gathered = 0;
         if (r == 1) {

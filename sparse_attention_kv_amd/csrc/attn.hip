@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      __bf16* __restrict__ Vt,
                                                      __bf16* __restrict__ Kc_lo,
                                                      __bf16* __restrict__ Vt_lo,
-                                                     int32_t* __restrict__ cpos) {
+                                                     int32_t* __restrict__ cpos,
+                                                     float* __restrict__ vnorm) {
     __shared__ __bf16 sV[X3 ? 2 : 1][BN][D + 8];
     const int h = blockIdx.y;
     const int p0 = blockIdx.x * BN;
@@ -126,6 +127,14 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                 const __bf16 hi = (__bf16)x[e];
                 sV[0][col][c0 + e] = hi;
                 if (X3) sV[X3 ? 1 : 0][col][c0 + e] = (__bf16)(x[e] - (float)hi);
+            }
+            if (vnorm) { // ||vhat(j)||_2 in fp32 for the value-weighted column statistic
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e) ss = ss + x[e] * x[e];
+                ss = ss + __shfl_xor(ss, 1);
+                ss = ss + __shfl_xor(ss, 2);
+                if ((tid & 3) == 0) vnorm[(long)h * kp + p] = sqrtf(ss);
             }
         }
     }
@@ -897,7 +906,8 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
         __syncthreads();
     }
     csum += __shfl_xor(csum, 32);
-    if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
+    if (colv && half == 0)
+        P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
 }
 
 // Column statistics for bf16 queries (PREC 0/1): 64-row steps through a
@@ -1025,7 +1035,8 @@ __global__ __launch_bounds__(256, 2) void k_colstat_pipe(ColParams P) {
         __syncthreads();
     }
     csum += __shfl_xor(csum, 32);
-    if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
+    if (colv && half == 0)
+        P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
 }
 
 // Column statistics with the Q steps copied by LDS-DMA into two distinct LDS
@@ -1193,18 +1204,19 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
         }
     }
     csum += __shfl_xor(csum, 32);
-    if (colv && half == 0) P.col_stat[(long)h * P.k + p] = csum;
+    if (colv && half == 0)
+        P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, hipStream_t st) {
+                              int32_t* cpos, float* vnorm, hipStream_t st) {
     dim3 grid(kp / BN, c.H);
 #define FL_GATHER(D_, X_)                                                                       \
     hipLaunchKernelGGL((k_gather_bf16<D_, X_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
-                       Vt, Kc_lo, Vt_lo, cpos)
+                       Vt, Kc_lo, Vt_lo, cpos, vnorm)
     if (c.d == 128) { if (x3) FL_GATHER(128, true); else FL_GATHER(128, false); }
     else { if (x3) FL_GATHER(64, true); else FL_GATHER(64, false); }
 #undef FL_GATHER

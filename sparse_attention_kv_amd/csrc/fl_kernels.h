@@ -53,6 +53,7 @@ struct ColParams {
     const int32_t* cpos;
     const float* lse;
     const float* mass_u;
+    const float* vnorm;    // [H][kp] value norms (value-weighted statistic) or NULL
     float* col_stat;
 };
 
@@ -85,7 +86,8 @@ struct GemmParams {
 
 // select.hip
 hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, int D,
-                             const int32_t* cand, int n_cand, float* stat, hipStream_t st);
+                             const int32_t* cand, int n_cand, bool relative, float* stat,
+                             hipStream_t st);
 hipError_t launch_topk(const float* keys, long key_stride, const int32_t* pos, long pos_stride,
                        int n, int n_sel, int n_prefix, int32_t* out, long out_stride,
                        int32_t* slot, int n_slot, int n_seg, hipStream_t st);
@@ -96,12 +98,16 @@ hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const vo
 // attn.hip
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool split, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, hipStream_t st);
+                              int32_t* cpos, float* vnorm, hipStream_t st);
 // prec: 0 bf16 operands, 1 K/V/P as hi+lo bf16 pairs, 2 also q (fp32 inputs)
 hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                            const QTiles& out, int32_t* cpos, hipStream_t st);
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st);
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st);
+// calib.hip
+int sq_err_blocks(long n);
+hipError_t launch_sq_err(const float* x, const float* ref, long n, double* part, double* out,
+                         hipStream_t st);
 // block.hip
 hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int D,
                                  const __bf16* w, float eps, __bf16* out, hipStream_t st);

@@ -1,6 +1,7 @@
 // Token and column selection (FlashLoop paper, Sec. 4.1 and Sec. 4.2).
 //
 //  k_delta_norm  stat[t] = ||h_cur[i] - h_prev[i]||_2 for candidate i = cand[t]
+//                (REL: divided by ||h_prev[i]||_2, the normalised change)
 //                one wavefront per row; HBM-streaming (two rows of D values in,
 //                one float out).
 //  k_topk        exact top-n selection of one segment (the token set, or one
@@ -20,7 +21,7 @@
 
 namespace fl {
 
-template <int kChunk>
+template <int kChunk, bool REL>
 __global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_cur,
                                                     const void* __restrict__ h_prev, int dtype,
                                                     int D, const int32_t* __restrict__ cand,
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_c
     if (t >= n_cand) return;
     const long i = cand ? cand[t] : t;
     const long base = i * (long)D;
-    float acc = 0.0f;
+    float acc = 0.0f, pacc = 0.0f;
     int c = lane * 8;
     for (; c + 8 <= D; c += 64 * 8) {
         float a[8], b[8];
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_c
         for (int e = 0; e < 8; ++e) {
             const float df = a[e] - b[e];
             acc = acc + df * df;
+            if (REL) pacc = pacc + b[e] * b[e];
         }
     }
     // tail (D not a multiple of 8 * lanes handled above)
@@ -54,9 +56,16 @@ __global__ __launch_bounds__(256) void k_delta_norm(const void* __restrict__ h_c
         }
         const float df = a - b;
         acc = acc + df * df;
+        if (REL) pacc = pacc + b * b;
     }
     acc = wave_sum(acc);
-    if (lane == 0) stat[t] = sqrtf(acc);
+    if (REL) {
+        pacc = wave_sum(pacc);
+        const float dn = sqrtf(acc), pn = sqrtf(pacc);
+        if (lane == 0) stat[t] = pn > 0.0f ? dn / pn : (dn > 0.0f ? __builtin_inff() : 0.0f);
+    } else if (lane == 0) {
+        stat[t] = sqrtf(acc);
+    }
 }
 
 // Ordered key: larger float -> larger unsigned; -0 ranks as +0.
@@ -331,10 +340,15 @@ __global__ void k_copy_or_iota(const int32_t* __restrict__ src, int32_t* __restr
 
 // ---- launchers ----
 hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, int D,
-                             const int32_t* cand, int n_cand, float* stat, hipStream_t st) {
+                             const int32_t* cand, int n_cand, bool relative, float* stat,
+                             hipStream_t st) {
     const int blocks = (n_cand + 3) / 4;
-    hipLaunchKernelGGL(k_delta_norm<8>, dim3(blocks), dim3(256), 0, st, h_cur, h_prev, dtype, D,
-                       cand, n_cand, stat);
+    if (relative)
+        hipLaunchKernelGGL((k_delta_norm<8, true>), dim3(blocks), dim3(256), 0, st, h_cur, h_prev,
+                           dtype, D, cand, n_cand, stat);
+    else
+        hipLaunchKernelGGL((k_delta_norm<8, false>), dim3(blocks), dim3(256), 0, st, h_cur, h_prev,
+                           dtype, D, cand, n_cand, stat);
     return hipGetLastError();
 }
 

@@ -19,14 +19,17 @@ LIB_PATH = os.path.join(_PKG, "libflashloop.so")
 FL_F32, FL_BF16 = 0, 1
 FL_DEQ_AUTO, FL_DEQ_ONCE, FL_DEQ_IN_TILE = 0, 1, 2
 FL_CACHE_CARRY, FL_CACHE_ZERO, FL_CACHE_REBUILD = 0, 1, 2
+FL_TOKEN_STAT_ABS, FL_TOKEN_STAT_REL = 0, 1
+FL_COL_STAT_MASS, FL_COL_STAT_VNORM = 0, 1
 FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 1, 2, 3, 4
 MAX_LEVELS = 16
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
-           "fl_workspace_size",
+           "fl_sq_err", "fl_workspace_size",
            "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
 FL_WS_BLOCK_STEP = 5
+FL_WS_SQ_ERR = 6
 
 
 class FlError(RuntimeError):
@@ -51,13 +54,15 @@ class FlAttnArgs(ctypes.Structure):
                 ("n", c_int), ("sel", c_void_p), ("k", c_int), ("sm", c_float),
                 ("level", c_int), ("mode", c_int), ("cache_op", c_int), ("out", c_void_p),
                 ("lse", c_void_p), ("mass_u", c_void_p), ("out_u", c_void_p),
-                ("col_stat", c_void_p), ("q_prev", c_void_p), ("q_prev_gathered", c_int)]
+                ("col_stat", c_void_p), ("q_prev", c_void_p), ("q_prev_gathered", c_int),
+                ("col_stat_kind", c_int)]
 
 
 class FlLoopCfg(ctypes.Structure):
     _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
                 ("n_sink", c_int), ("dtype", c_int), ("n_active", c_int * MAX_LEVELS),
-                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int)]
+                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int),
+                ("token_stat", c_int), ("col_stat", c_int)]
 
 
 class FlLoopState(ctypes.Structure):
@@ -77,7 +82,8 @@ class FlBlockCfg(ctypes.Structure):
     _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
                 ("n_sink", c_int), ("n_layers", c_int), ("ffn", c_int), ("rope_theta", c_float),
                 ("norm_eps", c_float), ("n_active", c_int * MAX_LEVELS),
-                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int)]
+                ("k_cols", c_int * MAX_LEVELS), ("bits", c_int * MAX_LEVELS), ("mode", c_int),
+                ("token_stat", c_int), ("col_stat", c_int)]
 
 
 class FlLayerWeights(ctypes.Structure):
@@ -128,7 +134,7 @@ def lib():
         L.fl_version.restype = ctypes.c_char_p
         L.fl_workspace_size.restype = c_size_t
         L.fl_workspace_size.argtypes = [c_int, c_long, c_long, c_long, c_long]
-        L.fl_select_active.argtypes = [c_int, c_void_p, c_void_p, c_int, c_int, c_void_p, c_int,
+        L.fl_select_active.argtypes = [c_int, c_int, c_void_p, c_void_p, c_int, c_int, c_void_p, c_int,
                                        c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
         L.fl_select_columns.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p,
@@ -143,6 +149,7 @@ def lib():
                                     POINTER(FlBlockState), c_int, c_void_p, c_size_t, c_void_p]
         L.fl_decode_step.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
                                      POINTER(FlDecodeInputs), c_int, c_void_p]
+        L.fl_sq_err.argtypes = [c_void_p, c_void_p, c_long, c_void_p, c_void_p, c_size_t, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
         for name in EXPORTS:
@@ -201,7 +208,7 @@ def fl_timing_report():
 
 
 def fl_select_active(h_cur, h_prev, cand, n_select, stat_out, active_out, slot_out=None,
-                     stat_in=None, N=None, stream=None):
+                     stat_in=None, N=None, stat_kind=FL_TOKEN_STAT_ABS, stream=None):
     """Sec. 4.1: token statistic over candidates and nested top-k (see header)."""
     if stat_in is not None:
         n_cand = stat_in.numel()
@@ -211,7 +218,8 @@ def fl_select_active(h_cur, h_prev, cand, n_select, stat_out, active_out, slot_o
         N, D = h_cur.shape
         dt = _dtype_code(h_cur)
         n_cand = N if cand is None else cand.numel()
-    rc = lib().fl_select_active(dt, _p(h_cur), _p(h_prev), N, D, _p(cand), n_cand, n_select,
+    rc = lib().fl_select_active(dt, stat_kind, _p(h_cur), _p(h_prev), N, D, _p(cand), n_cand,
+                                n_select,
                                 _p(stat_in), _p(stat_out), _p(active_out), _p(slot_out), None, 0,
                                 _stream(stream))
     _check("fl_select_active", rc)
@@ -260,6 +268,17 @@ def fl_decode_step(cfg: FlDecodeCfg, state: FlDecodeState, inputs: FlDecodeInput
     _check("fl_decode_step", rc)
 
 
+def fl_sq_err(x, ref, out, ws=None, stream=None):
+    """App. E calibration error: out[0] = sum (x - ref)^2, out[1] = sum ref^2
+    (fp64 device tensor of 2) over two fp32 device tensors of equal size."""
+    n = x.numel()
+    assert ref.numel() == n and out.dtype == torch.float64 and out.numel() >= 2
+    if ws is None:
+        ws = torch.empty(fl_workspace_size(FL_WS_SQ_ERR, n), dtype=torch.uint8, device=x.device)
+    _check("fl_sq_err", lib().fl_sq_err(_p(x), _p(ref), n, _p(out), _p(ws), ws.numel(),
+                                        _stream(stream)))
+
+
 # --------------------------------------------------------------------------
 # Device-memory holder for a whole R-loop run (buffers only; no arithmetic).
 
@@ -272,7 +291,8 @@ class LoopRunner:
     N tokens and runs ``fl_loop_step`` for r = 1..R."""
 
     def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, dtype=torch.bfloat16,
-                 mode=FL_DEQ_AUTO, device="cuda"):
+                 mode=FL_DEQ_AUTO, token_stat=FL_TOKEN_STAT_ABS, col_stat=FL_COL_STAT_MASS,
+                 device="cuda"):
         self.N, self.H, self.d, self.g, self.R = N, H, d, g, R
         dev = torch.device(device)
         self.dev = dev
@@ -280,6 +300,7 @@ class LoopRunner:
         cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = N, H, d, g, R, n_sink
         cfg.dtype = FL_BF16 if dtype == torch.bfloat16 else FL_F32
         cfg.mode = mode
+        cfg.token_stat, cfg.col_stat = token_stat, col_stat
         for r in range(R):
             cfg.n_active[r] = n_active[r]
             cfg.k_cols[r] = k_cols[r]
@@ -357,9 +378,15 @@ class BlockRunner:
     (rows 2j gate, 2j+1 up), w_down [D][F], norm1 [D], norm2 [D]."""
 
     def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, weights, ffn,
-                 rope_theta=10000.0, norm_eps=1e-6, mode=FL_DEQ_AUTO, device="cuda"):
+                 rope_theta=10000.0, norm_eps=1e-6, mode=FL_DEQ_AUTO,
+                 token_stat=FL_TOKEN_STAT_ABS, col_stat=FL_COL_STAT_MASS, row_capacity=None,
+                 device="cuda"):
+        """row_capacity: per-loop row counts to allocate (default n_active),
+        so that ``set_active_counts`` can later run other schedules."""
         dev = torch.device(device)
         self.N, self.H, self.d, self.R = N, H, d, R
+        cap = list(row_capacity) if row_capacity is not None else list(n_active)
+        self.cap = cap
         self.L = len(weights)
         D = H * d
         self._keep = []
@@ -372,6 +399,7 @@ class BlockRunner:
         cfg = FlBlockCfg()
         cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = N, H, d, g, R, n_sink
         cfg.n_layers, cfg.ffn, cfg.rope_theta, cfg.norm_eps, cfg.mode = self.L, ffn, rope_theta, norm_eps, mode
+        cfg.token_stat, cfg.col_stat = token_stat, col_stat
         for r in range(R):
             cfg.n_active[r], cfg.k_cols[r], cfg.bits[r] = n_active[r], k_cols[r], bits[r]
         self.cfg = cfg
@@ -388,7 +416,7 @@ class BlockRunner:
             Ls.cache.N, Ls.cache.H, Ls.cache.d, Ls.cache.g = N, H, d, g
             lb = dict(codes=[])
             for r in range(R):
-                rows = N if r == 0 else n_active[r]
+                rows = N if r == 0 else cap[r]
                 b = bits[r]
                 kc = buf((rows, H, d * b // 8), torch.uint8)
                 vc = buf((rows, H, d * b // 8), torch.uint8)
@@ -420,7 +448,7 @@ class BlockRunner:
         self.stat = buf((N,), torch.float32)
         self.active, self.slot = [], []
         for r in range(R):
-            a = buf((n_active[r],), torch.int32)
+            a = buf((cap[r],), torch.int32)
             s_ = buf((N,), torch.int32) if r > 0 else None
             st.active[r], st.slot[r] = _p(a), _p(s_)
             self.active.append(a); self.slot.append(s_)
@@ -431,6 +459,17 @@ class BlockRunner:
 
     def step(self, r, stream=None):
         fl_block_step(self.cfg, self.W, self.state, r, self.ws, stream)
+
+    def set_active_counts(self, n_active):
+        """Use another nested schedule of active-row counts (within the
+        allocated capacity); takes effect from the next loop 1."""
+        assert len(n_active) == self.R and n_active[0] == self.N
+        for r in range(1, self.R):
+            if not 1 <= n_active[r] <= min(n_active[r - 1], self.cap[r]):
+                raise ValueError(f"n_active[{r}] = {n_active[r]} outside [1, "
+                                 f"{min(n_active[r - 1], self.cap[r])}]")
+        for r in range(self.R):
+            self.cfg.n_active[r] = n_active[r]
 
 
 class DecodeRunner:

@@ -23,13 +23,15 @@ def counts(w):
     return n
 
 
-def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None):
+def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None, token_stat=fl.FL_TOKEN_STAT_ABS,
+            col_stat=fl.FL_COL_STAT_MASS):
     bits = bits or w.bits
     dt = inp["dtype"]
     dev = {key: [to_dev(a, dt) for a in inp[key]] for key in ("h", "q", "k", "v")}
     n_act = counts(w)
     runner = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, bits,
-                           dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode)
+                           dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode,
+                           token_stat=token_stat, col_stat=col_stat)
     res = []
     for r in range(1, w.R + 1):
         hp = dev["h"][r - 2] if r > 1 else None
@@ -60,9 +62,16 @@ def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None):
     return res, runner
 
 
-def run_oracle_lockstep(w, inp, gres, bits=None):
+def oracle_stat_names(token_stat, col_stat):
+    return dict(token_stat="rel" if token_stat == fl.FL_TOKEN_STAT_REL else "abs",
+                col_stat="vnorm" if col_stat == fl.FL_COL_STAT_VNORM else "mass")
+
+
+def run_oracle_lockstep(w, inp, gres, bits=None, token_stat=fl.FL_TOKEN_STAT_ABS,
+                        col_stat=fl.FL_COL_STAT_MASS):
     x = synth.as_f32_inputs(inp)
     sched = w.sched()
+    sched.update(oracle_stat_names(token_stat, col_stat))
     if bits:
         sched["bits"] = list(bits)
     ov = {}

@@ -48,14 +48,16 @@ def _err(L):
 
 
 def test_select_active_rejects(L):
-    rc = L.fl_select_active(1, FAKE, FAKE, 100, 64, None, 100, 0, None, FAKE, FAKE, None, None, 0, None)
+    rc = L.fl_select_active(1, 0, FAKE, FAKE, 100, 64, None, 100, 0, None, FAKE, FAKE, None, None, 0, None)
     assert rc == -1 and "n_select" in _err(L)
-    rc = L.fl_select_active(1, FAKE, FAKE, 100, 64, None, 101, 5, None, FAKE, FAKE, None, None, 0, None)
+    rc = L.fl_select_active(1, 0, FAKE, FAKE, 100, 64, None, 101, 5, None, FAKE, FAKE, None, None, 0, None)
     assert rc == -1 and "n_cand" in _err(L)
-    rc = L.fl_select_active(1, FAKE, FAKE, 100, 60, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
+    rc = L.fl_select_active(1, 0, FAKE, FAKE, 100, 60, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
     assert rc == -1 and "multiple of 8" in _err(L)
-    rc = L.fl_select_active(1, None, FAKE, 100, 64, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
+    rc = L.fl_select_active(1, 0, None, FAKE, 100, 64, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
     assert rc == -1
+    rc = L.fl_select_active(1, 2, FAKE, FAKE, 100, 64, None, 100, 5, None, FAKE, FAKE, None, None, 0, None)
+    assert rc == -1 and "stat_kind" in _err(L)
 
 
 def test_select_columns_rejects(L):
@@ -120,6 +122,9 @@ def test_attn_rejects(L):
     assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) in (-2, -3)
     a = _args(n=0)
     assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+    a = _args(col_stat_kind=2)
+    assert L.fl_sparse_loop_attn(ctypes.byref(c), ctypes.byref(a), None, 0, None) == -1
+    assert "col_stat_kind" in _err(L)
 
 
 def test_block_step_rejects(L):
@@ -137,6 +142,10 @@ def test_block_step_rejects(L):
     assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -2
     cfg.ffn, cfg.d = 512, 96
     assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -2
+    cfg.d, cfg.token_stat = 128, 2
+    assert L.fl_block_step(ctypes.byref(cfg), W, ctypes.byref(st), 1, None, 0, None) == -1
+    assert "token_stat" in _err(L)
+    cfg.token_stat = 0
     assert fl.fl_workspace_size(fl.FL_WS_BLOCK_STEP, 8192, 16, 128, 5632) > 8192 * 2048 * 2 * 5
 
 
@@ -147,6 +156,10 @@ def test_loop_step_rejects(L):
     inp = fl.FlLoopInputs()
     assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 3, None, 0, None) == -1
     assert L.fl_loop_step(None, ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
+    cfg.col_stat = 7
+    assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
+    assert "col_stat" in _err(L)
+    cfg.col_stat = 0
     st.cache.N, st.cache.H, st.cache.d, st.cache.g = 64, 2, 128, 64
     assert L.fl_loop_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None, 0, None) == -1
     assert "q/k/v" in _err(L)

@@ -24,7 +24,8 @@ import oracle
 from oracle import block as ob
 from sparse_attention_kv_amd import fl, synth
 
-from gpu_chain import assert_close, to_dev
+from gpu_block_chain import capture_block, oracle_block
+from gpu_chain import assert_close, oracle_stat_names, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -36,13 +37,20 @@ def _workload(N=640, H=2, d=128, L=2, F=512, R=3):
     return w
 
 
-@pytest.mark.parametrize("N,H,d,L,F,raw", [(640, 2, 128, 2, 512, False), (389, 4, 64, 1, 256, False),
-                                           (512, 2, 128, 2, 256, True)])
-def test_block_matches_oracle(N, H, d, L, F, raw):
+@pytest.mark.parametrize("N,H,d,L,F,raw,variants", [(640, 2, 128, 2, 512, False, False),
+                                                    (389, 4, 64, 1, 256, False, False),
+                                                    (512, 2, 128, 2, 256, True, False),
+                                                    (450, 2, 128, 2, 256, False, True)])
+def test_block_matches_oracle(N, H, d, L, F, raw, variants):
+    """variants: relative token statistic and value-norm-weighted columns."""
     w = _workload(N, H, d, L, F)
     if raw:
         w.bits = [32, 32, 32]
-    print("block", w.sched(), "layers", L, "ffn", F, flush=True)
+    ts = fl.FL_TOKEN_STAT_REL if variants else fl.FL_TOKEN_STAT_ABS
+    cs = fl.FL_COL_STAT_VNORM if variants else fl.FL_COL_STAT_MASS
+    sched = w.sched()
+    sched.update(oracle_stat_names(ts, cs))
+    print("block", sched, "layers", L, "ffn", F, flush=True)
     inp = synth.generate(w)
     R = w.R
     n_act = [N]
@@ -50,40 +58,12 @@ def test_block_matches_oracle(N, H, d, L, F, raw):
         n_act.append(oracle.active_count(w.rho[r], N, n_act[-1]))
     wdev = [{k: to_dev(v, "bf16") for k, v in lw.items()} for lw in inp["layers"]]
     run = fl.BlockRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, wdev, F,
-                         rope_theta=w.extra["theta"], norm_eps=w.extra["eps"])
-    run.h.copy_(torch.from_numpy(inp["h1"]).cuda())
-    G = []
+                         rope_theta=w.extra["theta"], norm_eps=w.extra["eps"], token_stat=ts,
+                         col_stat=cs)
+    G = capture_block(run, inp["h1"], n_act, w.kcols)
     for r in range(1, R + 1):
-        run.step(r)
-        torch.cuda.synchronize()
-        rec = dict(active=run.active[r - 1].cpu().numpy(), h=run.h.cpu().numpy())
-        if r > 1:
-            rec["stat"] = run.stat[: n_act[r - 2]].cpu().numpy().copy()
-        rec["layers"] = []
-        for l in range(L):
-            lb = run.layer_bufs[l]
-            k_used = run.layers[l].k_cur[r - 1]
-            lr = dict(out=lb["out"].cpu().numpy()[rec["active"]],
-                      lse=lb["lse"].cpu().numpy()[rec["active"]], k=k_used)
-            if r < R and w.kcols[r] < k_used:
-                lr["cstat"] = lb["col_stat"][r - 1][:, :k_used].cpu().numpy().copy()
-            cb = lb["codes"][r - 1]
-            lr["kv"] = {key: cb[key].cpu().numpy() for key in ("k", "v", "ks", "vs")}
-            rec["layers"].append(lr)
-        G.append(rec)
-        print(f"  gpu loop {r}: n={len(rec['active'])}", flush=True)
-    ov = {}
-    for r in range(2, R + 1):
-        ov[("stat", r)] = G[r - 1]["stat"]
-        for l in range(L):
-            if "cstat" in G[r - 2]["layers"][l]:
-                ov[("cstat", r, l)] = G[r - 2]["layers"][l]["cstat"]
-    for r in range(1, R + 1):
-        for l in range(L):
-            ov[("kv", r, l)] = G[r - 1]["layers"][l]["kv"]
-    layers = [{k: synth.bf16_bits_to_f32(v) for k, v in lw.items()} for lw in inp["layers"]]
-    res = ob.run_block(inp["h1"], layers, w.sched(), theta=w.extra["theta"], eps=w.extra["eps"],
-                       override=ov, bf16_acts=True)
+        print(f"  gpu loop {r}: n={len(G[r - 1]['active'])}", flush=True)
+    res = oracle_block(inp, w, sched, G)
     for r in range(1, R + 1):
         g, o = G[r - 1], res[r - 1]
         np.testing.assert_array_equal(g["active"], o["active"], err_msg=f"loop {r} active")

@@ -66,6 +66,35 @@ def test_delta_norm_matches_oracle(dtype):
     np.testing.assert_array_equal(act.cpu().numpy(), oracle.top_select(g, 300, cand))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_delta_norm_rel_matches_oracle(dtype):
+    """Normalised token change (Sec. 4.1): ratio within 1e-5, zero previous
+    states (unchanged -> 0, changed -> +inf) exact, and the selection equal
+    to the oracle's top-k of the GPU's own statistic."""
+    _say("delta_norm_rel", dtype)
+    rng = np.random.default_rng(5)
+    N, D = 2051, 2048 if dtype == "bf16" else 64
+    b = (rng.standard_normal((N, D)) * np.exp(rng.normal(0, 1, (N, 1)))).astype(np.float32)
+    a = b + (rng.standard_normal((N, D)) * np.exp(rng.normal(-3, 1, (N, 1)))).astype(np.float32)
+    b[7] = 0; a[7] = 0            # unchanged zero state
+    b[11] = 0                     # changed zero state
+    if dtype == "bf16":
+        a, b = synth.f32_to_bf16_bits(a), synth.f32_to_bf16_bits(b)
+    cand = np.sort(np.concatenate([[7, 11], 12 + rng.choice(N - 12, 1198, replace=False)])).astype(np.int32)
+    stat = torch.empty(1200, dtype=torch.float32, device="cuda")
+    act = torch.empty(250, dtype=torch.int32, device="cuda")
+    fl.fl_select_active(to_dev(a, dtype), to_dev(b, dtype), torch.from_numpy(cand).cuda(), 250,
+                        stat, act, stat_kind=fl.FL_TOKEN_STAT_REL)
+    torch.cuda.synchronize()
+    g = stat.cpu().numpy()
+    want = oracle.delta_norm(synth.to_f32(a, dtype), synth.to_f32(b, dtype), cand, relative=True)
+    assert g[0] == 0 and np.isposinf(g[1]) and want[0] == 0 and np.isposinf(want[1])
+    np.testing.assert_allclose(g[2:], want[2:], rtol=1e-5)
+    got_act = act.cpu().numpy()
+    np.testing.assert_array_equal(got_act, oracle.top_select(g, 250, cand))
+    assert 11 in got_act and 7 not in got_act
+
+
 @pytest.mark.parametrize("H,n_cand,k,ident", [(3, 3000, 500, True), (16, 2048, 1024, False),
                                               (2, 100, 5, False), (4, 700, 700, False)])
 def test_select_columns_matches_oracle(H, n_cand, k, ident):
@@ -147,11 +176,13 @@ def test_quant_chain_bit_exact(d, g, bits):
 
 
 # ------------------------------------------------------- whole loops --
-def _chain(w, bits=None, mode=fl.FL_DEQ_AUTO):
-    _say("chain", w.name, w.N, w.H, w.d, w.R, w.rho, w.kcols, bits or w.bits, "mode", mode)
+def _chain(w, bits=None, mode=fl.FL_DEQ_AUTO, token_stat=fl.FL_TOKEN_STAT_ABS,
+           col_stat=fl.FL_COL_STAT_MASS):
+    _say("chain", w.name, w.N, w.H, w.d, w.R, w.rho, w.kcols, bits or w.bits, "mode", mode,
+         "stats", token_stat, col_stat)
     inp = synth.generate(w)
-    gres, _ = run_gpu(w, inp, mode=mode, bits=bits)
-    ores = run_oracle_lockstep(w, inp, gres, bits=bits)
+    gres, _ = run_gpu(w, inp, mode=mode, bits=bits, token_stat=token_stat, col_stat=col_stat)
+    ores = run_oracle_lockstep(w, inp, gres, bits=bits, token_stat=token_stat, col_stat=col_stat)
     rep = compare_chain(w, gres, ores, bits=bits)
     _say("  per-loop (r, rel-L2 out, rel-L2 lse):", [(r, f"{a[0]:.2e}", f"{b[0]:.2e}") for r, a, b in rep])
     return gres, ores
@@ -196,3 +227,20 @@ def test_dense_reduction_raw():
     w = synth.WORKLOADS["layer4k"].scaled(N=700, H=8, R=3, rho=[1.0, 1.0, 1.0],
                                           kcols=[700, 700, 700], bits=[8, 32, 32])
     _chain(w)
+
+
+@pytest.mark.parametrize("mode", [fl.FL_DEQ_ONCE, fl.FL_DEQ_IN_TILE])
+def test_stat_variants_chain(mode):
+    """Relative token statistic and value-norm-weighted column statistic on
+    the pruning layer recipe (ragged N, rebuilds at loops 2-4): active sets
+    and column sets exact given the GPU's statistics, statistics within the
+    usual bounds, outputs as for the default statistics."""
+    w = synth.WORKLOADS["layer4k"].scaled(N=1000, H=8, kcols=[1000, 300, 150, 100], seed=31)
+    _chain(w, mode=mode, token_stat=fl.FL_TOKEN_STAT_REL, col_stat=fl.FL_COL_STAT_VNORM)
+
+
+def test_stat_variants_f32_d64():
+    """The same variants with fp32 inputs (hi/lo operand gather) at d = 64."""
+    w = synth.WORKLOADS["layer4k"].scaled(N=515, H=3, d=64, g=32, kcols=[515, 160, 90, 90],
+                                          bits=[8, 4, 2, 4], dtype="f32", seed=32)
+    _chain(w, token_stat=fl.FL_TOKEN_STAT_REL, col_stat=fl.FL_COL_STAT_VNORM)
