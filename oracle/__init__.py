@@ -72,6 +72,9 @@ def lib():
         L.flo_quantize_rows.argtypes = [_f32p, _vp, _long, _int, _int, _int, _int,
                                         _vp, _vp, _vp, _f32p]
         L.flo_pack_codes.argtypes = [_i8p, _long, _int, _u8p]
+        L.flo_quant_asym_group.argtypes = [_f32p, _int, _long, _int, _u8p, _long, _f32p, _f32p]
+        L.flo_quantize_rows_asym.argtypes = [_f32p, _vp, _long, _int, _int, _int, _int, _int,
+                                             _u8p, _f32p, _f32p, _f32p]
         L.flo_attend.argtypes = [_int, _int, _int, _flt, _f32p, _f32p, _f32p, _vp, _int,
                                  _vp, _int, _vp, _vp, _f32p, _f32p]
         L.flo_unselected_cache.argtypes = [_int, _int, _int, _flt, _f32p, _f32p, _f32p,
@@ -167,7 +170,39 @@ def quantize_rows(x_new, xhat_prev, g, bits):
     return codes, scales, None, xhat
 
 
+def quant_asym_group(x, bits):
+    """App. E: one asymmetric min/max group -> (unsigned codes, scale, zero)."""
+    x = _c(x, np.float32)
+    code = np.empty(len(x), np.uint8)
+    s = np.empty(1, np.float32); z = np.empty(1, np.float32)
+    lib().flo_quant_asym_group(x, len(x), 1, int(bits), code, 1, s, z)
+    return code, s[0], z[0]
+
+
+def quantize_rows_asym(x_new, xhat_prev, g, bits, per_channel):
+    """App. E: one level under the paper's quantiser for [n][H][d] packed rows.
+
+    per_channel=True (keys): groups of g consecutive rows per (head, channel),
+    scales/zeros [ceil(n/g)][H][d]; False (values): groups of g channels per
+    (row, head), scales/zeros [n][H][d/g].  Returns (codes uint8 [n][H][d],
+    scales, zeros, xhat)."""
+    x_new = _c(x_new, np.float32)
+    n, H, d = x_new.shape
+    xp = None if xhat_prev is None else _c(xhat_prev, np.float32)
+    shp = ((n + g - 1) // g, H, d) if per_channel else (n, H, d // g)
+    codes = np.empty((n, H, d), np.uint8)
+    scales = np.empty(shp, np.float32)
+    zeros = np.empty(shp, np.float32)
+    xhat = np.empty_like(x_new)
+    lib().flo_quantize_rows_asym(x_new, _ptr(xp), n, H, d, g, int(bits), int(bool(per_channel)),
+                                 codes, scales, zeros, xhat)
+    return codes, scales, zeros, xhat
+
+
 def pack_codes(codes, bits):
+    codes = np.asarray(codes)
+    if codes.dtype == np.uint8:          # unsigned codes: same bits
+        codes = codes.view(np.int8)
     codes = _c(codes, np.int8)
     flat = codes.reshape(-1)
     out = np.empty(len(flat) * bits // 8, np.uint8)

@@ -30,8 +30,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (active_count, attend, column_stats, delta_norm, quantize_rows, select_columns,
-               top_select, unselected_cache)
+from . import (active_count, attend, column_stats, delta_norm, quantize_rows,
+               quantize_rows_asym, select_columns, top_select, unselected_cache)
 
 F32 = np.float32
 
@@ -67,20 +67,41 @@ def silu(x):
     return x / (F32(1) + np.exp(-x))
 
 
-def _level(xnew, xprev, g, bits):
+def _level(xnew, xprev, g, bits, asym=False, per_channel=False):
+    if asym:
+        codes, scales, zeros, xhat = quantize_rows_asym(xnew, xprev, g, bits, per_channel)
+        return dict(codes=codes, scales=scales, zeros=zeros, raw=None), xhat
     codes, scales, raw, xhat = quantize_rows(xnew, xprev, g, bits)
     return dict(codes=codes, scales=scales, raw=raw), xhat
 
 
-def unpack_codes(packed, bits, d):
-    """Two's-complement codes from their packed bytes ([..][d*bits/8] -> [..][d])."""
+def unpack_codes(packed, bits, d, unsigned=False):
+    """Codes from their packed bytes ([..][d*bits/8] -> [..][d]): two's
+    complement, or unsigned (the asymmetric quantiser's codes)."""
     b = np.asarray(packed, np.uint8)
     per = 8 // bits
-    out = np.empty(b.shape[:-1] + (b.shape[-1] * per,), np.int8)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * per,), np.int16)
     for i in range(per):
         v = ((b >> (bits * i)) & ((1 << bits) - 1)).astype(np.int16)
-        out[..., i::per] = np.where(v >= (1 << (bits - 1)), v - (1 << bits), v).astype(np.int8)
+        out[..., i::per] = v if unsigned else np.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
     return out[..., :d]
+
+
+def dequant_rows_asym(codes_packed, scales, zeros, bits, g, xhat_prev, per_channel):
+    """Rows of one level of the asymmetric quantiser from stored codes:
+    code*s + z per element (keys: s, z per (row group of g, channel); values:
+    per (row, channel group of g)), plus the previous level's value."""
+    n = np.asarray(codes_packed).shape[0]
+    d = np.asarray(codes_packed).shape[-1] * 8 // bits
+    c = unpack_codes(codes_packed, bits, d, unsigned=True).astype(F32)
+    if per_channel:
+        sc = np.repeat(np.asarray(scales, F32), g, axis=0)[:n]
+        zc = np.repeat(np.asarray(zeros, F32), g, axis=0)[:n]
+    else:
+        sc = np.repeat(np.asarray(scales, F32), g, axis=-1)
+        zc = np.repeat(np.asarray(zeros, F32), g, axis=-1)
+    deq = ((c * sc).astype(F32) + zc).astype(F32)
+    return deq if xhat_prev is None else (np.asarray(xhat_prev, F32) + deq).astype(F32)
 
 
 def dequant_rows(codes_packed, scales, bits, g, xhat_prev):
@@ -117,6 +138,7 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
     A = np.arange(N, dtype=np.int32)
     rel = sched.get("token_stat", "abs") == "rel"
     vw = sched.get("col_stat", "mass") == "vnorm"
+    asym = sched.get("quant", "absmax") == "asym"
     out = []
     for r in range(1, R + 1):
         rec = dict(r=r)
@@ -138,10 +160,13 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
             bits = sched["bits"][r - 1]
             kp = None if r == 1 else s["khat"][A]
             vp = None if r == 1 else s["vhat"][A]
-            lk, krows = _level(k, kp, g, bits)
-            lv, vrows = _level(v, vp, g, bits)
+            lk, krows = _level(k, kp, g, bits, asym, True)
+            lv, vrows = _level(v, vp, g, bits, asym, False)
             ext = override.get(("kv", r, l))
-            if ext is not None and bits != 32:
+            if ext is not None and asym:
+                krows = dequant_rows_asym(ext["k"], ext["ks"], ext["kz"], bits, g, kp, True)
+                vrows = dequant_rows_asym(ext["v"], ext["vs"], ext["vz"], bits, g, vp, False)
+            elif ext is not None and bits != 32:
                 krows = dequant_rows(ext["k"], ext["ks"], bits, g, kp)
                 vrows = dequant_rows(ext["v"], ext["vs"], bits, g, vp)
             if r == 1:

@@ -267,6 +267,82 @@ void flo_pack_codes(const int8_t* codes, long count, int bits, uint8_t* out) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* App. E ("Quantization Setting"): the paper's own quantiser, asymmetric
+ * min/max group quantisation.  For the n values x[i*stride] of one group:
+ *   z = min x,  s = (max x - min x) / qmax  (qmax = 2^b - 1: 15 for INT4),
+ *   code = round-half-even((x - z) / s) clamped to [0, qmax],
+ *   dequantised value = code*s + z  (product and sum rounded separately).
+ * A constant group (or one whose range underflows to s = 0) gets codes 0 and
+ * is reproduced exactly by z.  Codes are unsigned. */
+void flo_quant_asym_group(const float* x, int n, long stride, int bits, uint8_t* code,
+                          long code_stride, float* scale, float* zero) {
+    int qmax = (1 << bits) - 1;
+    float mn = x[0], mx = x[0];
+    for (int i = 1; i < n; ++i) {
+        float v = x[(long)i * stride];
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    float range = mx - mn;
+    float s = range / (float)qmax;
+    for (int i = 0; i < n; ++i) {
+        uint8_t c = 0;
+        if (s != 0.0f) {
+            float t = x[(long)i * stride] - mn;
+            float r = rintf(t / s);
+            if (r > (float)qmax) r = (float)qmax;
+            if (r < 0.0f) r = 0.0f;
+            c = (uint8_t)r;
+        }
+        code[(long)i * code_stride] = c;
+    }
+    *scale = s;
+    *zero = mn;
+}
+
+/* One level of the KV cache under the paper's quantiser, for n packed rows
+ * ([n][H][d]).  The quantised quantity is x = x_new - xhat_prev (xhat_prev ==
+ * NULL: the base level, x = x_new), and xhat = xhat_prev + (code*s + z).
+ *   per_channel = 0 (values, per token): groups of g contiguous channels of a
+ *     (row, head); scales / zeros [n][H][d/g].
+ *   per_channel = 1 (post-RoPE keys, per channel): for each (head, channel),
+ *     groups of g consecutive packed rows (the last group may be shorter);
+ *     scales / zeros [ceil(n/g)][H][d].
+ * codes: unpacked unsigned [n][H][d]. */
+void flo_quantize_rows_asym(const float* x_new, const float* xhat_prev, long n, int H, int d,
+                            int g, int bits, int per_channel, uint8_t* codes, float* scales,
+                            float* zeros, float* xhat_out) {
+    long HD = (long)H * d;
+    float* x = (float*)malloc(sizeof(float) * (size_t)(n * HD > 0 ? n * HD : 1));
+    for (long e = 0; e < n * HD; ++e) x[e] = xhat_prev ? x_new[e] - xhat_prev[e] : x_new[e];
+    if (per_channel) {
+        long ng = (n + g - 1) / g;
+        #pragma omp parallel for schedule(static)
+        for (long gc = 0; gc < ng * HD; ++gc) {
+            long grp = gc / HD, ch = gc % HD;
+            long r0 = grp * g;
+            int len = (int)((n - r0) < g ? (n - r0) : g);
+            flo_quant_asym_group(x + r0 * HD + ch, len, HD, bits, codes + r0 * HD + ch, HD,
+                                 scales + gc, zeros + gc);
+        }
+    } else {
+        int G = d / g;
+        #pragma omp parallel for schedule(static)
+        for (long q = 0; q < n * H * G; ++q)
+            flo_quant_asym_group(x + q * g, g, 1, bits, codes + q * g, 1, scales + q, zeros + q);
+    }
+    #pragma omp parallel for schedule(static)
+    for (long e = 0; e < n * HD; ++e) {
+        long row = e / HD, ch = e % HD;
+        long si = per_channel ? (row / g) * HD + ch : e / g;
+        float deq = (float)codes[e] * scales[si];
+        deq = deq + zeros[si];
+        xhat_out[e] = xhat_prev ? xhat_prev[e] + deq : deq;
+    }
+    free(x);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sec. 4.2: sparse attention of loop r for the active rows.  For row i (a
  * token position) and head h the causal selected columns are
  * S(i) = { j in sel[h] : j <= i }.  Logits s = sm * q(i).khat(j); lse = log of

@@ -29,11 +29,16 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (active_count, attend, column_stats, delta_norm, quantize_rows,
+from . import (active_count, attend, column_stats, delta_norm, quantize_rows, quantize_rows_asym,
                select_columns, top_select, unselected_cache)
 
 
-def _level(xnew, xprev, g, bits):
+def _level(xnew, xprev, g, bits, asym=False, per_channel=False):
+    """One cache level: the spec's absmax quantiser, or (asym) the paper's
+    App. E min/max quantiser with keys per channel and values per token."""
+    if asym:
+        codes, scales, zeros, xhat = quantize_rows_asym(xnew, xprev, g, bits, per_channel)
+        return dict(codes=codes, scales=scales, zeros=zeros, raw=None), xhat
     codes, scales, raw, xhat = quantize_rows(xnew, xprev, g, bits)
     return dict(codes=codes, scales=scales, raw=raw), xhat
 
@@ -47,7 +52,10 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
     sched: dict with N, H, d, g, R, n_sink, rho[R], kcols[R], bits[R]
     (bits[0] is the base level: 8 or 32); optional token_stat "abs" (default)
     or "rel" (normalised change, Sec. 4.1) and col_stat "mass" (default) or
-    "vnorm" (mass weighted by the column's value norm, Sec. 4.2).
+    "vnorm" (mass weighted by the column's value norm, Sec. 4.2); optional
+    quant "absmax" (default, the spec's quantiser) or "asym" (App. E: min/max
+    with scale and offset, keys per channel over g packed rows, values per
+    token).
     override: optional dict {('stat', r): array, ('cstat', r): array} used in
     place of the oracle's own statistic for the selection made at loop r.
     Returns a list of per-loop dicts.
@@ -58,9 +66,10 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
     n_sink = sched["n_sink"]
     out = []
 
+    asym = sched.get("quant", "absmax") == "asym"
     # ---- loop 1: dense ----
-    lk, khat = _level(k[0], None, g, sched["bits"][0])
-    lv, vhat = _level(v[0], None, g, sched["bits"][0])
+    lk, khat = _level(k[0], None, g, sched["bits"][0], asym, True)
+    lv, vhat = _level(v[0], None, g, sched["bits"][0], asym, False)
     o1, lse1 = attend(q[0], khat, vhat, None, None, sm)
     need_c = R > 1 and (stats_every_loop or sched["kcols"][1] < N)
     vw = sched.get("col_stat", "mass") == "vnorm"
@@ -86,8 +95,8 @@ def run_prefill(h, q, k, v, sched, override=None, stats_every_loop=False,
         n_r = active_count(sched["rho"][r - 1], N, len(A))
         A_new = top_select(stat_sel, n_r, pos=A)
         # (3) residual level for the active rows
-        lk, krows = _level(k[r - 1][A_new], khat[A_new], g, sched["bits"][r - 1])
-        lv, vrows = _level(v[r - 1][A_new], vhat[A_new], g, sched["bits"][r - 1])
+        lk, krows = _level(k[r - 1][A_new], khat[A_new], g, sched["bits"][r - 1], asym, True)
+        lv, vrows = _level(v[r - 1][A_new], vhat[A_new], g, sched["bits"][r - 1], asym, False)
         khat_new = khat.copy(); khat_new[A_new] = krows
         vhat_new = vhat.copy(); vhat_new[A_new] = vrows
         # (4) column selection
