@@ -273,7 +273,8 @@ void flo_pack_codes(const int8_t* codes, long count, int bits, uint8_t* out) {
  *   code = round-half-even((x - z) / s) clamped to [0, qmax],
  *   dequantised value = code*s + z  (product and sum rounded separately).
  * A constant group (or one whose range underflows to s = 0) gets codes 0 and
- * is reproduced exactly by z.  Codes are unsigned. */
+ * is reproduced exactly by z.  Codes are unsigned; a zero offset or scale is
+ * stored as +0. */
 void flo_quant_asym_group(const float* x, int n, long stride, int bits, uint8_t* code,
                           long code_stride, float* scale, float* zero) {
     int qmax = (1 << bits) - 1;
@@ -283,8 +284,12 @@ void flo_quant_asym_group(const float* x, int n, long stride, int bits, uint8_t*
         if (v < mn) mn = v;
         if (v > mx) mx = v;
     }
+    /* a signed zero in the group could make min / max (hence z and s) -0 or
+     * +0 depending on the order of comparison; both are stored as +0 (x + 0
+     * leaves every other value unchanged), so the stored words are unique */
+    mn = mn + 0.0f;
     float range = mx - mn;
-    float s = range / (float)qmax;
+    float s = range / (float)qmax + 0.0f;
     for (int i = 0; i < n; ++i) {
         uint8_t c = 0;
         if (s != 0.0f) {

@@ -204,6 +204,14 @@ def test_asym_golden():
         assert oracle.pack_codes(codes, bits).tobytes() == packed
 
 
+def test_asym_signed_zero_stored_as_plus_zero():
+    """Groups of signed zeros: offset and scale are +0 whatever the order."""
+    for x in ([0.0, -0.0], [-0.0, 0.0, -0.0], [-0.0, -0.0]):
+        c, s, z = oracle.quant_asym_group(np.array(x, np.float32), 4)
+        assert np.float32(s).view(np.uint32) == 0 and np.float32(z).view(np.uint32) == 0
+        assert not c.any()
+
+
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_asym_bounds_random(bits):
     """|code*s + z - x| <= s/2 (plus fp32 rounding of the two steps); the
