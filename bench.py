@@ -58,6 +58,11 @@ def parse():
                     help="token ranking: absolute or normalised hidden-state change")
     ap.add_argument("--col-stat", default="mass", choices=["mass", "vnorm"],
                     help="column ranking: probability mass, or mass x value norm")
+    ap.add_argument("--quant", default="absmax", choices=["absmax", "asym"],
+                    help="cache quantiser: absmax int8 base + int4/int2 residuals, or the "
+                         "paper's asymmetric INT4 (keys per channel, values per token)")
+    ap.add_argument("--quant-study", action="store_true",
+                    help="residual vs direct quantisation error by loop on the prefill inputs")
     ap.add_argument("--calibrate", action="store_true",
                     help="block workloads: time the retention calibration instead of the step")
     ap.add_argument("--mode", default="auto", choices=["auto", "once", "in_tile"],
@@ -123,6 +128,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"[bench] reference copy of {args.calib_copy_mib} MiB done")
+    if args.quant == "asym":
+        w = w.scaled(bits=[4] * w.R)          # the paper's INT4 base and residuals
+    if args.quant_study:
+        return bench_quant_study(args, w, np, torch, fl, synth)
     if w.kind == "block":
         return bench_block(args, w, np, torch, fl, synth)
     if w.kind == "decode":
@@ -146,7 +155,7 @@ def main():
     ts, cs = stat_kinds(args, fl)
     run = fl.LoopRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
                         dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode,
-                        token_stat=ts, col_stat=cs)
+                        token_stat=ts, col_stat=cs, quant=quant_scheme(args, fl))
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -263,7 +272,8 @@ def main():
         "config": {"workload": w.name, "N": N, "H": H, "d": d, "R": R, "g": w.g,
                    "active_per_loop": n_act, "k_per_loop": [L["k"] for L in loops],
                    "bits_per_loop": w.bits, "n_sink": w.n_sink, "dequant": args.mode,
-                   "token_stat": args.token_stat, "col_stat": args.col_stat},
+                   "token_stat": args.token_stat, "col_stat": args.col_stat,
+                   "quant": args.quant},
         "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.mean(loop_ms[:, i])), 4),
                        pairs=L["pairs"], rebuilt=L["rebuilt"], colstat=L["colstat"])
                   for i, L in enumerate(loops)],
@@ -278,8 +288,19 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, run, n_act, loops, args.cpu_rows, torch, np,
                                            rel=args.token_stat == "rel",
-                                           vw=args.col_stat == "vnorm")
+                                           vw=args.col_stat == "vnorm", asym=args.quant == "asym")
     print(json.dumps(out), flush=True)
+
+
+def quant_scheme(args, fl):
+    return fl.FL_QUANT_ASYM if args.quant == "asym" else fl.FL_QUANT_ABSMAX
+
+
+def oracle_level(oracle, x, prev, g, bits, asym, per_channel):
+    """One cache level's reconstruction by the oracle's quantiser."""
+    if asym:
+        return oracle.quantize_rows_asym(x, prev, g, bits, per_channel)[3]
+    return oracle.quantize_rows(x, prev, g, bits)[3]
 
 
 def stat_kinds(args, fl):
@@ -288,7 +309,7 @@ def stat_kinds(args, fl):
     return ts, cs
 
 
-def cpu_baseline(w, inp, run, n_act, loops, m, torch, np, rel=False, vw=False):
+def cpu_baseline(w, inp, run, n_act, loops, m, torch, np, rel=False, vw=False, asym=False):
     """The oracle, as is, on a bounded sample of the same workload: token
     statistic + selection, quantisation and column selection in full; the
     per-row work (attention, cache rebuild, column statistics) on m evenly
@@ -310,14 +331,14 @@ def cpu_baseline(w, inp, run, n_act, loops, m, torch, np, rel=False, vw=False):
         t_full = t_rows = 0.0
         t = time.perf_counter()
         if r == 1:
-            _, _, _, khat_n = oracle.quantize_rows(x["k"][0], None, g, w.bits[0])
-            _, _, _, vhat_n = oracle.quantize_rows(x["v"][0], None, g, w.bits[0])
+            khat_n = oracle_level(oracle, x["k"][0], None, g, w.bits[0], asym, True)
+            vhat_n = oracle_level(oracle, x["v"][0], None, g, w.bits[0], asym, False)
         else:
             prev = run.active[r - 2].cpu().numpy()
             stat = oracle.delta_norm(x["h"][r - 1], x["h"][r - 2], prev, relative=rel)
             oracle.top_select(stat, n_act[r - 1], prev)
-            _, _, _, kr = oracle.quantize_rows(x["k"][r - 1][act], khat[act], g, w.bits[r - 1])
-            _, _, _, vr = oracle.quantize_rows(x["v"][r - 1][act], vhat[act], g, w.bits[r - 1])
+            kr = oracle_level(oracle, x["k"][r - 1][act], khat[act], g, w.bits[r - 1], asym, True)
+            vr = oracle_level(oracle, x["v"][r - 1][act], vhat[act], g, w.bits[r - 1], asym, False)
             khat_n = khat.copy(); khat_n[act] = kr
             vhat_n = vhat.copy(); vhat_n[act] = vr
             if loops[r - 1]["rebuilt"]:
@@ -383,7 +404,7 @@ def bench_block(args, w, np, torch, fl, synth):
         return bench_calibrate(args, w, h1, wdev, fl, torch, ts, cs)
     run = fl.BlockRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, wdev, F,
                          rope_theta=w.extra["theta"], norm_eps=w.extra["eps"], token_stat=ts,
-                         col_stat=cs)
+                         col_stat=cs, quant=quant_scheme(args, fl))
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -444,7 +465,7 @@ def bench_block(args, w, np, torch, fl, synth):
         "config": {"workload": w.name, "N": N, "layers": L, "hidden": D, "heads": H, "head_dim": d,
                    "ffn": F, "R": R, "active_per_loop": n_act, "k_per_loop": w.kcols,
                    "bits_per_loop": w.bits, "token_stat": args.token_stat,
-                   "col_stat": args.col_stat},
+                   "col_stat": args.col_stat, "quant": args.quant},
         "loops": [dict(r=r + 1, n=n_act[r], ms=round(float(np.mean(loop_ms[:, r])), 3))
                   for r in range(R)],
         "kernels": kernels,
@@ -456,11 +477,12 @@ def bench_block(args, w, np, torch, fl, synth):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_block(w, inp, n_act, np, rel=args.token_stat == "rel",
-                                                 vw=args.col_stat == "vnorm")
+                                                 vw=args.col_stat == "vnorm",
+                                                 asym=args.quant == "asym")
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_block(w, inp, n_act, np, m=32, rel=False, vw=False):
+def cpu_baseline_block(w, inp, n_act, np, m=32, rel=False, vw=False, asym=False):
     """The block oracle's step functions, as they are, on a bounded sample of
     the same workload: the first layer through all R loops.  Token
     selection, RMSNorm, the four projections, RoPE, quantisation and column
@@ -493,8 +515,8 @@ def cpu_baseline_block(w, inp, n_act, np, m=32, rel=False, vw=False):
         q = ob.bf16(ob.rope(qkv[:, :D].reshape(-1, H, d), A, w.extra["theta"]))
         k = ob.bf16(ob.rope(qkv[:, D:2 * D].reshape(-1, H, d), A, w.extra["theta"]))
         v = np.ascontiguousarray(qkv[:, 2 * D:].reshape(-1, H, d))
-        _, _, _, kx = oracle.quantize_rows(k, None if r == 1 else khat[A], g, w.bits[r - 1])
-        _, _, _, vx = oracle.quantize_rows(v, None if r == 1 else vhat[A], g, w.bits[r - 1])
+        kx = oracle_level(oracle, k, None if r == 1 else khat[A], g, w.bits[r - 1], asym, True)
+        vx = oracle_level(oracle, v, None if r == 1 else vhat[A], g, w.bits[r - 1], asym, False)
         kh = kx if r == 1 else khat.copy()
         vh = vx if r == 1 else vhat.copy()
         if r > 1:
@@ -569,6 +591,47 @@ def bench_calibrate(args, w, h1, wdev, fl, torch, ts, cs):
                           "err": [round(e, 5) for e in res["err"]]},
            "trials": {str(r): [[round(c, 2), n, round(e, 5)] for c, n, e in tr]
                       for r, tr in res["trials"].items()}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_quant_study(args, w, np, torch, fl, synth):
+    """Residual vs direct quantisation error by loop (Sec. 3.3, Fig. 2(c),
+    Table 2's per-loop direct quantisation) on the workload's K/V with every
+    token active: the paper's quantiser (INT4 asymmetric, keys per channel,
+    values per token) and the absmax int8 base + int4/int2 residual one."""
+    from sparse_attention_kv_amd import quant_study
+    if w.kind != "prefill":
+        raise SystemExit("--quant-study needs a prefill workload")
+    inp = synth.generate(w)
+
+    def dev(a):
+        if inp["dtype"] == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    ks = [dev(a) for a in inp["k"]]
+    vs = [dev(a) for a in inp["v"]]
+    base = synth.WORKLOADS[w.name].bits
+    res = {}
+    t = time.perf_counter()
+    for name, scheme, bits in (("asym_int4", fl.FL_QUANT_ASYM, [4] * w.R),
+                               ("absmax_spec", fl.FL_QUANT_ABSMAX, base)):
+        rows = quant_study.residual_vs_direct(ks, vs, w.g, bits, scheme)
+        res[name] = dict(bits=bits, loops=[{k: (round(v, 6) if isinstance(v, float) else v)
+                                            for k, v in r.items()} for r in rows])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    ratios = [r[kv + "_dir"] / r[kv + "_res"] for r in res["asym_int4"]["loops"][1:]
+              for kv in ("k", "v") if r[kv + "_res"] > 0]
+    out = {"metric": "direct / residual relative reconstruction error of the per-loop KV "
+                     "(paper's INT4 quantiser, loops >= 2, geometric mean over K and V)",
+           "value": round(float(np.exp(np.mean(np.log(ratios)))), 3) if ratios else None,
+           "unit": "x", "n_gpus": 1, "steps": 1,
+           "warmup": 0, "ms_per_step": round(wall * 1e3, 1), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": inp["dtype"], "data": "synthetic",
+           "config": {"workload": w.name, "N": w.N, "H": w.H, "d": w.d, "R": w.R, "g": w.g,
+                      "tokens_active": "all"},
+           "schemes": res}
     print(json.dumps(out), flush=True)
 
 

@@ -70,7 +70,26 @@ enum fl_dtype { FL_F32 = 0, FL_BF16 = 1 };
  * (unused for bits 32).  The dequantised value of a token at loop r is
  *   xhat = code_0*s_0, then xhat = xhat + code_l*s_l for l = 1..r-1 while the
  * token is present in level l (sets are nested, so presence stops at the first
- * absent level). */
+ * absent level).
+ *
+ * Scheme FL_QUANT_ASYM (the paper's own quantiser, App. E "Quantization
+ * Setting": asymmetric min/max groups; post-RoPE keys per channel, values per
+ * token) changes the format of every level:
+ *   bits 2, 4 or 8 at every level (the paper uses 4), unsigned codes packed
+ *   as above; per group z = min, s = (max - min)/(2^bits - 1), code =
+ *   round-half-even((x - z)/s) clamped to [0, 2^bits - 1] (s = 0 -> 0), a zero
+ *   z or s stored as +0; dequantised value code*s + z;
+ *   values: groups of g contiguous channels of a (row, head):
+ *     v_scale / v_zero [n_rows][H][d/g];
+ *   keys: per (head, channel), groups of g consecutive rows of the level
+ *     (packed order; the last group may be shorter):
+ *     k_scale / k_zero [ceil(n_rows/g)][H][d];
+ *   xhat = (code_0*s_0 + z_0), then xhat = xhat + (code_l*s_l + z_l). */
+enum fl_quant_scheme {
+    FL_QUANT_ABSMAX = 0, /* symmetric absmax, int8 base + 2/4/8-bit residuals   */
+    FL_QUANT_ASYM = 1    /* asymmetric min/max, keys per channel, values per token */
+};
+
 typedef struct fl_kv_level {
     int bits;
     int n_rows;
@@ -78,13 +97,16 @@ typedef struct fl_kv_level {
     const int32_t* slot; /* [N];      NULL for level 0 */
     void* k_codes;       /* [n_rows][H][d*bits/8] */
     void* v_codes;
-    float* k_scale;      /* [n_rows][H][d/g] */
-    float* v_scale;
+    float* k_scale;      /* [n_rows][H][d/g]; FL_QUANT_ASYM: [ceil(n_rows/g)][H][d] */
+    float* v_scale;      /* [n_rows][H][d/g] */
+    float* k_zero;       /* FL_QUANT_ASYM only: offsets, laid out as k_scale */
+    float* v_zero;       /* FL_QUANT_ASYM only: offsets, laid out as v_scale */
 } fl_kv_level;
 
 typedef struct fl_kv_cache {
     int N, H, d, g;
     int n_levels; /* levels 0..n_levels-1 hold data */
+    int scheme;   /* fl_quant_scheme */
     fl_kv_level level[FL_MAX_LEVELS];
 } fl_kv_cache;
 
@@ -158,11 +180,27 @@ int fl_select_columns(const float* col_stat, const int32_t* cand_cols, int H, in
  * multiply-add, so codes and scales are reproducible bit for bit.
  * k_new / v_new: dtype FL_BF16 or FL_F32, [N][H][d] by position
  * (new_gathered = 0) or [n_rows][H][d] aligned with rows (new_gathered = 1).
+ * Under FL_QUANT_ASYM the groups, codes and offsets follow that scheme's
+ * definition above (keys per channel over g consecutive rows of the level,
+ * values per token), with the same bit-for-bit arithmetic rules.
  * Errors: FL_ERR_INVALID_ARG (null buffers, level >= FL_MAX_LEVELS, levels
- * below `level` missing, n_rows > N), FL_ERR_UNSUPPORTED (bits not in
- * {2,4,8,32}, d or g unsupported). */
+ * below `level` missing, n_rows > N, unknown scheme), FL_ERR_UNSUPPORTED (bits
+ * not in {2,4,8,32}, or not in {2,4,8} under FL_QUANT_ASYM; d or g
+ * unsupported). */
 int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const void* k_new,
                          const void* v_new, int new_gathered, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_kv_dequant -- the reconstruction the cache stores (paper Sec. 3.3 / App.
+ * E: base state plus cross-loop residuals): out[i][h][c] = xhat of every
+ * token i = 0..N-1 at loop level+1, i.e. levels 0..level in order, each
+ * token's chain stopping at the first level it is absent from, with the
+ * arithmetic of fl_kv_residual_quant (so out equals the residual target that
+ * the next level's quantisation uses, bit for bit).
+ * which: 0 = keys, 1 = values.  out: fp32 [N][H][d] device buffer, 16-byte
+ * aligned.  Errors: as fl_kv_residual_quant for the cache; FL_ERR_INVALID_ARG
+ * for which outside {0, 1} or a NULL / misaligned out. */
+int fl_kv_dequant(const fl_kv_cache* cache, int level, int which, float* out, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * fl_sparse_loop_attn -- paper Sec. 4.2 (sparse attention over the selected
@@ -204,7 +242,8 @@ enum fl_attn_mode {
     FL_DEQ_ONCE = 1,    /* dequantise the selected columns once per head into a
                            compact bf16 buffer, then stream it per tile        */
     FL_DEQ_IN_TILE = 2  /* gather quantised codes compactly, dequantise inside
-                           the attention kernel's column-tile loop             */
+                           the attention kernel's column-tile loop (caches of
+                           scheme FL_QUANT_ABSMAX only)                        */
 };
 
 enum fl_cache_op {
@@ -371,8 +410,9 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
  * Cache layout: cache.level[l] describes sequence 0 with the usual fields;
  * sequence b's rows/slot/codes/scales follow at b * (n_rows, N, n_rows*H*
  * d*bits/8 bytes, n_rows*H*d/g floats) -- B sequences of equal geometry.
- * Requirements: N + 1 <= 12288 (the probabilities stay in LDS); base level
- * int8 and quantised residual levels (FL_ERR_UNSUPPORTED otherwise); a
+ * Requirements: N + 1 <= 12288 (the probabilities stay in LDS); scheme
+ * FL_QUANT_ABSMAX with an int8 base level and quantised residual levels
+ * (FL_ERR_UNSUPPORTED otherwise); a
  * sparse loop r keeps 4 * ((k + 1) + r * k) bytes in LDS, at most 48 KiB.
  */
 typedef struct fl_decode_cfg {

@@ -122,10 +122,18 @@ int check_cache(const fl_kv_cache* c, int upto) {
         return fail(FL_ERR_UNSUPPORTED, "group size %d (32 or 64, dividing d)", c->g);
     FL_REQUIRE(c->H * c->d <= 8192, "H*d = %d > 8192", c->H * c->d);
     FL_REQUIRE(upto >= 0 && upto < FL_MAX_LEVELS, "level %d out of range", upto);
+    FL_REQUIRE(c->scheme == FL_QUANT_ABSMAX || c->scheme == FL_QUANT_ASYM, "scheme %d", c->scheme);
+    const bool asym = c->scheme == FL_QUANT_ASYM;
     for (int l = 0; l <= upto; ++l) {
         const fl_kv_level& L = c->level[l];
+        if (asym) {
+            if (!(L.bits == 2 || L.bits == 4 || L.bits == 8))
+                return fail(FL_ERR_UNSUPPORTED, "level %d bits %d (2, 4 or 8 under FL_QUANT_ASYM)", l,
+                            L.bits);
+            FL_REQUIRE(L.k_zero && L.v_zero, "level %d: offset buffers NULL", l);
+        }
         if (l == 0) {
-            if (!(L.bits == 8 || L.bits == 32))
+            if (!asym && !(L.bits == 8 || L.bits == 32))
                 return fail(FL_ERR_UNSUPPORTED, "base level bits %d (8 or 32)", L.bits);
         } else {
             if (!(L.bits == 2 || L.bits == 4 || L.bits == 8 || L.bits == 32))
@@ -284,6 +292,17 @@ int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const v
     return FL_OK;
 }
 
+int fl_kv_dequant(const fl_kv_cache* cache, int level, int which, float* out, fl_stream_t stream) {
+    int rc = check_cache(cache, level);
+    if (rc) return rc;
+    FL_REQUIRE(which == 0 || which == 1, "which %d (0 keys, 1 values)", which);
+    FL_REQUIRE(out && ((uintptr_t)out % 16) == 0, "out NULL or not 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    FL_HIP(timed("kv_dequant", st, [&] { return fl::launch_dequant(*cache, level, which, out, st); }),
+           "kv_dequant");
+    return FL_OK;
+}
+
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
                         size_t ws_bytes, fl_stream_t stream) {
     FL_REQUIRE(a != nullptr, "args NULL");
@@ -311,6 +330,8 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     // tile and measured 1.6-2x slower on the sparse loops (20.9 vs 18.2 ms
     // per step).
     const bool in_tile = a->mode == FL_DEQ_IN_TILE;
+    if (in_tile && cache->scheme != FL_QUANT_ABSMAX)
+        return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE needs a FL_QUANT_ABSMAX cache");
     if (in_tile)
         for (int l = 0; l <= a->level; ++l)
             if (cache->level[l].bits == 32)
@@ -637,6 +658,7 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, r - 1);
     if (rc) return rc;
+    if (C.scheme != FL_QUANT_ABSMAX) return fail(FL_ERR_UNSUPPORTED, "decode: FL_QUANT_ABSMAX caches only");
     if (C.level[0].bits != 8) return fail(FL_ERR_UNSUPPORTED, "decode: base level bits %d (8)", C.level[0].bits);
     for (int l = 1; l < r; ++l)
         if (C.level[l].bits == 32)

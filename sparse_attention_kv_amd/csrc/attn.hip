@@ -66,7 +66,23 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
         float x[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) x[e] = 0.0f;
-        if (live) {
+        if (live && c.scheme == FL_QUANT_ASYM) {
+            // asymmetric levels: code*s + z per element, summed in level order
+#pragma unroll
+            for (int e8 = 0; e8 < CPT; e8 += 8)
+                deq8_asym(c.level[0], which, j, HD, h * D + c0 + e8, c.g, x + e8);
+            for (int l = 1; l <= upto; ++l) {
+                const int sl = c.level[l].slot[j];
+                if (sl < 0) break;
+#pragma unroll
+                for (int e8 = 0; e8 < CPT; e8 += 8) {
+                    float t[8];
+                    deq8_asym(c.level[l], which, sl, HD, h * D + c0 + e8, c.g, t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[e8 + i] += t[i];
+                }
+            }
+        } else if (live) {
             // base level
             const fl_kv_level& L0 = c.level[0];
             const long e0 = j * HD + (long)h * D + c0;

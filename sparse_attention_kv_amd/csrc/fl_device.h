@@ -67,6 +67,44 @@ __device__ __forceinline__ uint64_t load_codes8(const void* base, long code_off,
     return *reinterpret_cast<const uint16_t*>(p); // bits == 2
 }
 
+// Unsigned code c (0..7) of 8 consecutive codes (asymmetric quantiser).
+__device__ __forceinline__ uint32_t ucode_at(uint64_t packed, int bits, int c) {
+    return (uint32_t)(packed >> (bits * c)) & ((1u << bits) - 1u);
+}
+
+// One level of the asymmetric (min/max) scheme: the dequantised terms
+// code*s + z of 8 consecutive channels (offset ch, a multiple of 8, within a
+// row of HD = H*d) of row `row` of the level.  Keys carry a scale and offset
+// per channel for each group of g consecutive rows; values one per group of
+// g channels.  The product and the sum are separate roundings unless the
+// including file allows contraction.
+__device__ __forceinline__ void deq8_asym(const fl_kv_level& L, int which, long row, int HD,
+                                          int ch, int g, float* o) {
+    const long e = row * HD + ch;
+    const uint64_t w = load_codes8(which ? L.v_codes : L.k_codes, e, L.bits);
+    if (which == 0) {
+        const long si = (row / g) * HD + ch;
+        const float4 s0 = *reinterpret_cast<const float4*>(L.k_scale + si);
+        const float4 s1 = *reinterpret_cast<const float4*>(L.k_scale + si + 4);
+        const float4 z0 = *reinterpret_cast<const float4*>(L.k_zero + si);
+        const float4 z1 = *reinterpret_cast<const float4*>(L.k_zero + si + 4);
+        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = (float)ucode_at(w, L.bits, i) * s[i];
+            o[i] = p + z[i];
+        }
+    } else {
+        const float s = L.v_scale[e / g], z = L.v_zero[e / g];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = (float)ucode_at(w, L.bits, i) * s;
+            o[i] = p + z;
+        }
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -93,6 +93,8 @@ hipError_t launch_topk(const float* keys, long key_stride, const int32_t* pos, l
                        int32_t* slot, int n_slot, int n_seg, hipStream_t st);
 hipError_t launch_copy_or_iota(const int32_t* src, int32_t* dst, long n, long row, hipStream_t st);
 // quant.hip
+hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float* out,
+                          hipStream_t st);
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
                         const void* v_new, int gathered, hipStream_t st);
 // attn.hip

@@ -1,7 +1,10 @@
 // KV residual quantisation (FlashLoop paper, Sec. 3.3, Sec. 4.3, App. E
 // "Quantization Setting"): the loop-1 K/V are stored as an int8 group-quantised
 // base; every later loop stores, for its active tokens only, a low-bit
-// quantised residual against the previous loop's dequantised K/V.
+// quantised residual against the previous loop's dequantised K/V.  Under the
+// asymmetric scheme (the paper's own: min/max groups, keys per channel over g
+// consecutive packed rows, values per token) values take the same per-thread
+// path with a min/max group reduction and keys go through k_quant_kchan.
 //
 // One thread owns 8 consecutive channels of one (token, head); the g/8
 // threads of a quantisation group are adjacent lanes of one wavefront, so the
@@ -31,6 +34,18 @@ struct QuantArgs {
 __device__ __forceinline__ void dequant8_chain(const fl_kv_cache& c, int which, long pos,
                                                int ch, int upto, float* x) {
     const int HD = c.H * c.d;
+    if (c.scheme == FL_QUANT_ASYM) {
+        deq8_asym(c.level[0], which, pos, HD, ch, c.g, x);
+        for (int l = 1; l <= upto; ++l) {
+            const int sl = c.level[l].slot[pos];
+            if (sl < 0) break;
+            float t[8];
+            deq8_asym(c.level[l], which, sl, HD, ch, c.g, t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = x[i] + t[i];
+        }
+        return;
+    }
     {
         const fl_kv_level& L = c.level[0];
         const void* codes = which ? L.v_codes : L.k_codes;
@@ -69,9 +84,128 @@ __device__ __forceinline__ void dequant8_chain(const fl_kv_cache& c, int which, 
     }
 }
 
-__global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads) {
+// The value to quantise for 8 channels of packed row t: the new value, minus
+// the token's previous dequantised value for a residual level.
+__device__ __forceinline__ void quant_input8(const QuantArgs& a, int which, long t, long pos,
+                                             int ch, float* x) {
+    const int HD = a.H * a.d;
+    const void* src = which ? a.v_new : a.k_new;
+    const long row = a.gathered ? t : pos;
+    load8_f32(src, row * HD + ch, a.dtype, x);
+    if (a.level > 0) {
+        float xp[8];
+        dequant8_chain(a.cache, which, pos, ch, a.level - 1, xp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = x[i] - xp[i];
+    }
+}
+
+__device__ __forceinline__ void store_codes8(void* codes, long e, int bits, uint64_t packed) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + (e * bits) / 8;
+    if (bits == 8) *reinterpret_cast<uint64_t*>(dst) = packed;
+    else if (bits == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)packed;
+    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+}
+
+// Asymmetric code of x: round-half-even((x - z)/s) clamped to [0, qmax].
+__device__ __forceinline__ uint32_t asym_code(float x, float s, float z, int qmax) {
+    if (s == 0.0f) return 0u;
+    const float t = x - z;
+    float r = __builtin_rintf(t / s);
+    r = fminf(fmaxf(r, 0.0f), (float)qmax);
+    return (uint32_t)r;
+}
+
+// Keys of an asymmetric level: one workgroup per (group of G consecutive
+// packed rows, 256 channels).  Lane l of wave w owns 8 channels (l mod 32)
+// and the rows rl, rl + 8, ... of the group (rl = 2w + l/32), keeping their
+// inputs in registers; the per-channel minimum and maximum are reduced over
+// the 8 row lanes (exact, so independent of order; a signed zero is stored
+// as +0), then each lane writes its rows' codes.
+template <int G>
+__global__ __launch_bounds__(256) void k_quant_kchan(QuantArgs a) {
+    constexpr int RPT = G / 8; // rows per thread
+    __shared__ float s_mn[4][32][8], s_mx[4][32][8];
+    const int HD = a.H * a.d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cl = lane & 31;
+    const int rl = wave * 2 + (lane >> 5);
+    const long grp = blockIdx.x;
+    const int ch = blockIdx.y * 256 + cl * 8;
+    const bool live_ch = ch < HD;
+    const fl_kv_level& L = a.cache.level[a.level];
+    const long n_rows = a.level == 0 ? a.N : L.n_rows;
+    const long r0 = grp * G;
+    float x[RPT][8];
+    float mn[8], mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const long t = r0 + rl + 8 * j;
+        if (live_ch && t < n_rows) {
+            const long pos = a.level == 0 ? t : (long)L.rows[t];
+            quant_input8(a, 0, t, pos, ch, x[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (x[j][i] < mn[i]) mn[i] = x[j][i];
+                if (x[j][i] > mx[i]) mx[i] = x[j][i];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float omn = __shfl_xor(mn[i], 32), omx = __shfl_xor(mx[i], 32);
+        if (omn < mn[i]) mn[i] = omn;
+        if (omx > mx[i]) mx[i] = omx;
+    }
+    if (lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { s_mn[wave][cl][i] = mn[i]; s_mx[wave][cl][i] = mx[i]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mn[i] = s_mn[0][cl][i]; mx[i] = s_mx[0][cl][i];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            if (s_mn[w][cl][i] < mn[i]) mn[i] = s_mn[w][cl][i];
+            if (s_mx[w][cl][i] > mx[i]) mx[i] = s_mx[w][cl][i];
+        }
+    }
+    if (!live_ch) return;
+    const int qmax = (1 << a.bits) - 1;
+    float s[8], z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        z[i] = mn[i] + 0.0f;
+        const float range = mx[i] - z[i];
+        s[i] = range / (float)qmax + 0.0f;
+    }
+    if (rl == 0) {
+        const long si = grp * HD + ch;
+        *reinterpret_cast<float4*>(L.k_scale + si) = make_float4(s[0], s[1], s[2], s[3]);
+        *reinterpret_cast<float4*>(L.k_scale + si + 4) = make_float4(s[4], s[5], s[6], s[7]);
+        *reinterpret_cast<float4*>(L.k_zero + si) = make_float4(z[0], z[1], z[2], z[3]);
+        *reinterpret_cast<float4*>(L.k_zero + si + 4) = make_float4(z[4], z[5], z[6], z[7]);
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const long t = r0 + rl + 8 * j;
+        if (t < n_rows) {
+            uint64_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                packed |= (uint64_t)asym_code(x[j][i], s[i], z[i], qmax) << (a.bits * i);
+            store_codes8(L.k_codes, t * HD + ch, a.bits, packed);
+        }
+    }
+}
+
+// which0 = 0: keys and values (grid.y = 2); which0 = 1: values only.
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads, int which0) {
     const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
-    const int which = blockIdx.y; // 0 = K, 1 = V
+    const int which = which0 + blockIdx.y; // 0 = K, 1 = V
     const int HD = a.H * a.d;
     const int per_row = HD / 8;
     const long t = gid / per_row;
@@ -82,15 +216,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads) {
 
     float x[8];
     if (live) {
-        const void* src = which ? a.v_new : a.k_new;
-        const long row = a.gathered ? t : pos;
-        load8_f32(src, row * HD + ch, a.dtype, x);
-        if (a.level > 0) {
-            float xp[8];
-            dequant8_chain(a.cache, which, pos, ch, a.level - 1, xp);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = x[i] - xp[i];
-        }
+        quant_input8(a, which, t, pos, ch, x);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = 0.0f;
@@ -102,6 +228,34 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads) {
             float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(codes) + e);
             p[0] = make_float4(x[0], x[1], x[2], x[3]);
             p[1] = make_float4(x[4], x[5], x[6], x[7]);
+        }
+        return;
+    }
+    if (a.cache.scheme == FL_QUANT_ASYM) {
+        // group min / max across the g/8 adjacent lanes of this group
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            if (x[i] < mn) mn = x[i];
+            if (x[i] > mx) mx = x[i];
+        }
+        for (int o = 1; o < a.g / 8; o <<= 1) {
+            const float omn = __shfl_xor(mn, o), omx = __shfl_xor(mx, o);
+            if (omn < mn) mn = omn;
+            if (omx > mx) mx = omx;
+        }
+        if (!live) return;
+        const int qmax = (1 << a.bits) - 1;
+        const float z = mn + 0.0f;
+        const float range = mx - z;
+        const float s = range / (float)qmax + 0.0f;
+        uint64_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) packed |= (uint64_t)asym_code(x[i], s, z, qmax) << (a.bits * i);
+        store_codes8(codes, e, a.bits, packed);
+        if ((ch % a.g) == 0) {
+            L.v_scale[e / a.g] = s;
+            L.v_zero[e / a.g] = z;
         }
         return;
     }
@@ -124,11 +278,33 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads) {
         }
         packed |= (uint64_t)((uint32_t)q & ((1u << a.bits) - 1u)) << (a.bits * i);
     }
-    uint8_t* dst = reinterpret_cast<uint8_t*>(codes) + (e * a.bits) / 8;
-    if (a.bits == 8) *reinterpret_cast<uint64_t*>(dst) = packed;
-    else if (a.bits == 4) *reinterpret_cast<uint32_t*>(dst) = (uint32_t)packed;
-    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+    store_codes8(codes, e, a.bits, packed);
     if ((ch % a.g) == 0) (which ? L.v_scale : L.k_scale)[e / a.g] = s;
+}
+
+// Reconstruction of every token's K or V at loop level+1 (levels 0..level in
+// order, each token's chain stopping at its first absent level), fp32.
+__global__ __launch_bounds__(256) void k_dequant(fl_kv_cache c, int level, int which,
+                                                 float* __restrict__ out, long n_threads) {
+    const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    if (gid >= n_threads) return;
+    const int HD = c.H * c.d;
+    const int per_row = HD / 8;
+    const long pos = gid / per_row;
+    const int ch = (int)(gid % per_row) * 8;
+    float x[8];
+    dequant8_chain(c, which, pos, ch, level, x);
+    float4* o = reinterpret_cast<float4*>(out + pos * HD + ch);
+    o[0] = make_float4(x[0], x[1], x[2], x[3]);
+    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float* out,
+                          hipStream_t st) {
+    const long n_threads = (long)cache.N * (cache.H * cache.d / 8);
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
+                       cache, level, which, out, n_threads);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
@@ -141,7 +317,15 @@ hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const vo
     const long n_threads = rows * (cache.H * cache.d / 8);
     if (n_threads == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((n_threads + 255) / 256);
-    hipLaunchKernelGGL(k_quant, dim3(blocks, 2), dim3(256), 0, st, a, n_threads);
+    if (cache.scheme == FL_QUANT_ASYM) {
+        hipLaunchKernelGGL(k_quant, dim3(blocks, 1), dim3(256), 0, st, a, n_threads, 1);
+        const dim3 kgrid((unsigned)((rows + cache.g - 1) / cache.g),
+                         (unsigned)((cache.H * cache.d + 255) / 256));
+        if (cache.g == 64) hipLaunchKernelGGL(k_quant_kchan<64>, kgrid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(k_quant_kchan<32>, kgrid, dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(k_quant, dim3(blocks, 2), dim3(256), 0, st, a, n_threads, 0);
+    }
     return hipGetLastError();
 }
 

@@ -21,12 +21,13 @@ FL_DEQ_AUTO, FL_DEQ_ONCE, FL_DEQ_IN_TILE = 0, 1, 2
 FL_CACHE_CARRY, FL_CACHE_ZERO, FL_CACHE_REBUILD = 0, 1, 2
 FL_TOKEN_STAT_ABS, FL_TOKEN_STAT_REL = 0, 1
 FL_COL_STAT_MASS, FL_COL_STAT_VNORM = 0, 1
+FL_QUANT_ABSMAX, FL_QUANT_ASYM = 0, 1
 FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 1, 2, 3, 4
 MAX_LEVELS = 16
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
-           "fl_sq_err", "fl_workspace_size",
+           "fl_sq_err", "fl_kv_dequant", "fl_workspace_size",
            "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
 FL_WS_BLOCK_STEP = 5
 FL_WS_SQ_ERR = 6
@@ -41,12 +42,12 @@ class FlError(RuntimeError):
 class FlKvLevel(ctypes.Structure):
     _fields_ = [("bits", c_int), ("n_rows", c_int), ("rows", c_void_p), ("slot", c_void_p),
                 ("k_codes", c_void_p), ("v_codes", c_void_p), ("k_scale", c_void_p),
-                ("v_scale", c_void_p)]
+                ("v_scale", c_void_p), ("k_zero", c_void_p), ("v_zero", c_void_p)]
 
 
 class FlKvCache(ctypes.Structure):
     _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("n_levels", c_int),
-                ("level", FlKvLevel * MAX_LEVELS)]
+                ("scheme", c_int), ("level", FlKvLevel * MAX_LEVELS)]
 
 
 class FlAttnArgs(ctypes.Structure):
@@ -150,6 +151,7 @@ def lib():
         L.fl_decode_step.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
                                      POINTER(FlDecodeInputs), c_int, c_void_p]
         L.fl_sq_err.argtypes = [c_void_p, c_void_p, c_long, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.fl_kv_dequant.argtypes = [POINTER(FlKvCache), c_int, c_int, c_void_p, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
         for name in EXPORTS:
@@ -268,6 +270,13 @@ def fl_decode_step(cfg: FlDecodeCfg, state: FlDecodeState, inputs: FlDecodeInput
     _check("fl_decode_step", rc)
 
 
+def fl_kv_dequant(cache: FlKvCache, level, which, out, stream=None):
+    """Sec. 3.3 / App. E: fp32 reconstruction [N][H][d] of keys (which=0) or
+    values (1) at loop level+1."""
+    _check("fl_kv_dequant", lib().fl_kv_dequant(ctypes.byref(cache), level, which, _p(out),
+                                                _stream(stream)))
+
+
 def fl_sq_err(x, ref, out, ws=None, stream=None):
     """App. E calibration error: out[0] = sum (x - ref)^2, out[1] = sum ref^2
     (fp64 device tensor of 2) over two fp32 device tensors of equal size."""
@@ -286,13 +295,31 @@ def level_code_bytes(bits, H, d):
     return H * d * bits // 8
 
 
+def alloc_level(L, rows, H, d, g, bits, scheme, buf):
+    """Allocate one cache level's codes, scales (and offsets under the
+    asymmetric scheme) with ``buf(shape, dtype)`` and point descriptor L at
+    them; returns the tensors."""
+    kc = buf((rows, H, d * bits // 8), torch.uint8)
+    vc = buf((rows, H, d * bits // 8), torch.uint8)
+    vshape = (rows, H, d // g)
+    kshape = ((rows + g - 1) // g, H, d) if scheme == FL_QUANT_ASYM else vshape
+    t = dict(k=kc, v=vc, ks=buf(kshape, torch.float32), vs=buf(vshape, torch.float32))
+    if scheme == FL_QUANT_ASYM:
+        t["kz"] = buf(kshape, torch.float32)
+        t["vz"] = buf(vshape, torch.float32)
+    L.bits, L.n_rows = bits, rows
+    L.k_codes, L.v_codes, L.k_scale, L.v_scale = _p(kc), _p(vc), _p(t["ks"]), _p(t["vs"])
+    L.k_zero, L.v_zero = _p(t.get("kz")), _p(t.get("vz"))
+    return t
+
+
 class LoopRunner:
     """Allocates the cache levels and loop state for one attention layer of
     N tokens and runs ``fl_loop_step`` for r = 1..R."""
 
     def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, dtype=torch.bfloat16,
                  mode=FL_DEQ_AUTO, token_stat=FL_TOKEN_STAT_ABS, col_stat=FL_COL_STAT_MASS,
-                 device="cuda"):
+                 quant=FL_QUANT_ABSMAX, device="cuda"):
         self.N, self.H, self.d, self.g, self.R = N, H, d, g, R
         dev = torch.device(device)
         self.dev = dev
@@ -315,18 +342,11 @@ class LoopRunner:
             return t
 
         st.cache.N, st.cache.H, st.cache.d, st.cache.g = N, H, d, g
+        st.cache.scheme = quant
         self.codes = []
         for r in range(R):
             rows = N if r == 0 else n_active[r]
-            b = bits[r]
-            kc = buf((rows, H, d * b // 8), torch.uint8)
-            vc = buf((rows, H, d * b // 8), torch.uint8)
-            ks = buf((rows, H, d // g), torch.float32)
-            vs = buf((rows, H, d // g), torch.float32)
-            L = st.cache.level[r]
-            L.bits, L.n_rows = b, rows
-            L.k_codes, L.v_codes, L.k_scale, L.v_scale = _p(kc), _p(vc), _p(ks), _p(vs)
-            self.codes.append(dict(k=kc, v=vc, ks=ks, vs=vs))
+            self.codes.append(alloc_level(st.cache.level[r], rows, H, d, g, bits[r], quant, buf))
         self.active, self.slot, self.sel, self.col_stat = [], [], [], []
         for r in range(R):
             a = buf((n_active[r],), torch.int32)
@@ -380,11 +400,11 @@ class BlockRunner:
     def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, weights, ffn,
                  rope_theta=10000.0, norm_eps=1e-6, mode=FL_DEQ_AUTO,
                  token_stat=FL_TOKEN_STAT_ABS, col_stat=FL_COL_STAT_MASS, row_capacity=None,
-                 device="cuda"):
+                 quant=FL_QUANT_ABSMAX, device="cuda"):
         """row_capacity: per-loop row counts to allocate (default n_active),
         so that ``set_active_counts`` can later run other schedules."""
         dev = torch.device(device)
-        self.N, self.H, self.d, self.R = N, H, d, R
+        self.N, self.H, self.d, self.R, self.g = N, H, d, R, g
         cap = list(row_capacity) if row_capacity is not None else list(n_active)
         self.cap = cap
         self.L = len(weights)
@@ -414,18 +434,12 @@ class BlockRunner:
         for l in range(self.L):
             Ls = layers[l]
             Ls.cache.N, Ls.cache.H, Ls.cache.d, Ls.cache.g = N, H, d, g
+            Ls.cache.scheme = quant
             lb = dict(codes=[])
             for r in range(R):
                 rows = N if r == 0 else cap[r]
-                b = bits[r]
-                kc = buf((rows, H, d * b // 8), torch.uint8)
-                vc = buf((rows, H, d * b // 8), torch.uint8)
-                ks = buf((rows, H, d // g), torch.float32)
-                vs = buf((rows, H, d // g), torch.float32)
-                Lv = Ls.cache.level[r]
-                Lv.bits, Lv.n_rows = b, rows
-                Lv.k_codes, Lv.v_codes, Lv.k_scale, Lv.v_scale = _p(kc), _p(vc), _p(ks), _p(vs)
-                lb["codes"].append(dict(k=kc, v=vc, ks=ks, vs=vs))
+                lb["codes"].append(alloc_level(Ls.cache.level[r], rows, H, d, g, bits[r], quant,
+                                               buf))
             lb["q_state"] = buf((N, H, d), torch.bfloat16)
             lb["out"] = buf((N, H, d), torch.float32)
             lb["lse"] = buf((N, H), torch.float32)

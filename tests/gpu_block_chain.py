@@ -33,7 +33,12 @@ def capture_block(run, h1, n_act, kcols, loops=None):
                 lr["cstat"] = lb["col_stat"][r - 1][:, :k_used].cpu().numpy().copy()
             cb = lb["codes"][r - 1]
             rows = n_act[r - 1]
-            lr["kv"] = {key: cb[key][:rows].cpu().numpy() for key in ("k", "v", "ks", "vs")}
+            lr["kv"] = {key: cb[key][:rows].cpu().numpy() for key in ("k", "v", "vs", "vz")
+                        if key in cb}
+            kg = -(-rows // run.g) if "kz" in cb else rows     # key groups of g rows (asym)
+            lr["kv"]["ks"] = cb["ks"][:kg].cpu().numpy()
+            if "kz" in cb:
+                lr["kv"]["kz"] = cb["kz"][:kg].cpu().numpy()
             rec["layers"].append(lr)
         G.append(rec)
     return G

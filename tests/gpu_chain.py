@@ -24,14 +24,14 @@ def counts(w):
 
 
 def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None, token_stat=fl.FL_TOKEN_STAT_ABS,
-            col_stat=fl.FL_COL_STAT_MASS):
+            col_stat=fl.FL_COL_STAT_MASS, quant=fl.FL_QUANT_ABSMAX):
     bits = bits or w.bits
     dt = inp["dtype"]
     dev = {key: [to_dev(a, dt) for a in inp[key]] for key in ("h", "q", "k", "v")}
     n_act = counts(w)
     runner = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, bits,
                            dtype=torch.bfloat16 if dt == "bf16" else torch.float32, mode=mode,
-                           token_stat=token_stat, col_stat=col_stat)
+                           token_stat=token_stat, col_stat=col_stat, quant=quant)
     res = []
     for r in range(1, w.R + 1):
         hp = dev["h"][r - 2] if r > 1 else None
@@ -49,6 +49,9 @@ def run_gpu(w, inp, mode=fl.FL_DEQ_AUTO, bits=None, token_stat=fl.FL_TOKEN_STAT_
         rec["v_codes"] = cb["v"].cpu().numpy()
         rec["k_scale"] = cb["ks"].cpu().numpy()
         rec["v_scale"] = cb["vs"].cpu().numpy()
+        if "kz" in cb:
+            rec["k_zero"] = cb["kz"].cpu().numpy()
+            rec["v_zero"] = cb["vz"].cpu().numpy()
         sel = runner.sel_used(r)
         rec["sel"] = None if sel is None else sel.cpu().numpy()
         rec["k"] = runner.k_used(r)
@@ -68,10 +71,12 @@ def oracle_stat_names(token_stat, col_stat):
 
 
 def run_oracle_lockstep(w, inp, gres, bits=None, token_stat=fl.FL_TOKEN_STAT_ABS,
-                        col_stat=fl.FL_COL_STAT_MASS):
+                        col_stat=fl.FL_COL_STAT_MASS, quant=fl.FL_QUANT_ABSMAX):
     x = synth.as_f32_inputs(inp)
     sched = w.sched()
     sched.update(oracle_stat_names(token_stat, col_stat))
+    if quant == fl.FL_QUANT_ASYM:
+        sched["quant"] = "asym"
     if bits:
         sched["bits"] = list(bits)
     ov = {}
@@ -117,7 +122,7 @@ def assert_close_scaled(got, want, what, rel=1e-2, mabs=3e-2):
     return e, worst
 
 
-def compare_chain(w, gres, ores, bits=None, check_codes=True):
+def compare_chain(w, gres, ores, bits=None, check_codes=True, quant=fl.FL_QUANT_ABSMAX):
     bits = bits or w.bits
     report = []
     for r in range(1, w.R + 1):
@@ -131,7 +136,15 @@ def compare_chain(w, gres, ores, bits=None, check_codes=True):
         if check_codes:
             for kv in ("k", "v"):
                 lvl = o["level_" + kv]
-                if bits[r - 1] == 32:
+                if quant == fl.FL_QUANT_ASYM:
+                    np.testing.assert_array_equal(g[kv + "_codes"],
+                                                  oracle.pack_codes(lvl["codes"], bits[r - 1]),
+                                                  err_msg=f"loop {r} {kv} codes")
+                    for part, key in (("_scale", "scales"), ("_zero", "zeros")):
+                        np.testing.assert_array_equal(g[kv + part].view(np.uint32),
+                                                      lvl[key].view(np.uint32),
+                                                      err_msg=f"loop {r} {kv}{part}")
+                elif bits[r - 1] == 32:
                     raw = g[kv + "_codes"].view(np.float32).reshape(lvl["raw"].shape)
                     np.testing.assert_array_equal(raw, lvl["raw"], err_msg=f"loop {r} raw {kv}")
                 else:

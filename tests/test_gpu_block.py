@@ -37,19 +37,26 @@ def _workload(N=640, H=2, d=128, L=2, F=512, R=3):
     return w
 
 
-@pytest.mark.parametrize("N,H,d,L,F,raw,variants", [(640, 2, 128, 2, 512, False, False),
-                                                    (389, 4, 64, 1, 256, False, False),
-                                                    (512, 2, 128, 2, 256, True, False),
-                                                    (450, 2, 128, 2, 256, False, True)])
-def test_block_matches_oracle(N, H, d, L, F, raw, variants):
-    """variants: relative token statistic and value-norm-weighted columns."""
+@pytest.mark.parametrize("N,H,d,L,F,raw,variants,asym", [(640, 2, 128, 2, 512, False, False, False),
+                                                         (389, 4, 64, 1, 256, False, False, False),
+                                                         (512, 2, 128, 2, 256, True, False, False),
+                                                         (450, 2, 128, 2, 256, False, True, False),
+                                                         (600, 2, 128, 2, 256, False, False, True)])
+def test_block_matches_oracle(N, H, d, L, F, raw, variants, asym):
+    """variants: relative token statistic and value-norm-weighted columns;
+    asym: the paper's own quantiser (INT4 base and residuals, keys per
+    channel after RoPE, values per token)."""
     w = _workload(N, H, d, L, F)
     if raw:
         w.bits = [32, 32, 32]
+    if asym:
+        w.bits = [4, 4, 4]
     ts = fl.FL_TOKEN_STAT_REL if variants else fl.FL_TOKEN_STAT_ABS
     cs = fl.FL_COL_STAT_VNORM if variants else fl.FL_COL_STAT_MASS
     sched = w.sched()
     sched.update(oracle_stat_names(ts, cs))
+    if asym:
+        sched["quant"] = "asym"
     print("block", sched, "layers", L, "ffn", F, flush=True)
     inp = synth.generate(w)
     R = w.R
@@ -59,7 +66,7 @@ def test_block_matches_oracle(N, H, d, L, F, raw, variants):
     wdev = [{k: to_dev(v, "bf16") for k, v in lw.items()} for lw in inp["layers"]]
     run = fl.BlockRunner(N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, wdev, F,
                          rope_theta=w.extra["theta"], norm_eps=w.extra["eps"], token_stat=ts,
-                         col_stat=cs)
+                         col_stat=cs, quant=fl.FL_QUANT_ASYM if asym else fl.FL_QUANT_ABSMAX)
     G = capture_block(run, inp["h1"], n_act, w.kcols)
     for r in range(1, R + 1):
         print(f"  gpu loop {r}: n={len(G[r - 1]['active'])}", flush=True)
@@ -76,7 +83,8 @@ def test_block_matches_oracle(N, H, d, L, F, raw, variants):
             if not raw:
                 for kv in ("k", "v"):
                     mine = ol["level_" + kv]["codes"].astype(np.int16)
-                    theirs = ob.unpack_codes(gl["kv"][kv], w.bits[r - 1], d).astype(np.int16)
+                    theirs = ob.unpack_codes(gl["kv"][kv], w.bits[r - 1], d,
+                                             unsigned=asym).astype(np.int16)
                     diff = np.abs(mine - theirs)
                     frac = float(np.mean(diff != 0))
                     print(f"  loop {r} layer {l} {kv} codes: {frac:.2%} differ, max step {diff.max()}",

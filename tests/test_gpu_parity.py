@@ -175,15 +175,81 @@ def test_quant_chain_bit_exact(d, g, bits):
             xhv[rows[l]] = xv
 
 
+@pytest.mark.parametrize("d,g,bits,ties", [(128, 64, (4, 4, 4, 4), False), (64, 32, (4, 2, 8, 4), False),
+                                           (128, 64, (4, 4, 2), True)])
+def test_quant_asym_chain_bit_exact(d, g, bits, ties):
+    """The paper's quantiser (App. E): codes, scales and offsets of every
+    level bit-exact against the oracle, keys per channel over g packed rows
+    (ragged last group: 777 rows, nested subsets), values per token.
+    ties: bf16 inputs on a coarse grid (many equal values, signed zeros,
+    constant groups)."""
+    _say("quant asym", d, g, bits, ties)
+    rng = np.random.default_rng(7 * d + len(bits))
+    N, H = 777, 4
+    levels = len(bits)
+    x = [rng.standard_normal((N, H, d)).astype(np.float32)]
+    for l in range(1, levels):
+        x.append(x[-1] + (rng.standard_normal((N, H, d)) * 0.1 ** l).astype(np.float32))
+    if ties:
+        x = [np.round(a * 2) / 2 for a in x]
+        x[0][:, 1, :] = -0.0                                  # constant (signed zero) groups
+        x[0][5:70, 2, 3] = 1.5                                # a constant key channel
+    xb = [synth.f32_to_bf16_bits(a.astype(np.float32)) for a in x]
+    xf = [synth.bf16_bits_to_f32(a) for a in xb]
+    rows = [np.arange(N, dtype=np.int32)]
+    for l in range(1, levels):
+        m = len(rows[-1]) * 2 // 3
+        rows.append(np.sort(rng.choice(rows[-1], m, replace=False)).astype(np.int32))
+    cache = fl.FlKvCache()
+    cache.N, cache.H, cache.d, cache.g, cache.n_levels = N, H, d, g, levels
+    cache.scheme = fl.FL_QUANT_ASYM
+    keep = []
+    xhk = xhv = None
+
+    def buf(shape, dt):
+        t = torch.zeros(shape, dtype=dt, device="cuda")
+        keep.append(t)
+        return t
+
+    for l in range(levels):
+        n = len(rows[l])
+        t = fl.alloc_level(cache.level[l], n, H, d, g, bits[l], fl.FL_QUANT_ASYM, buf)
+        if l > 0:
+            rt = torch.from_numpy(rows[l]).cuda()
+            slot = np.full(N, -1, np.int32); slot[rows[l]] = np.arange(n)
+            st = torch.from_numpy(slot).cuda()
+            cache.level[l].rows, cache.level[l].slot = rt.data_ptr(), st.data_ptr()
+            keep += [rt, st]
+        kn = to_dev(xb[l], "bf16")
+        vn = to_dev(xb[(l + 1) % levels], "bf16")
+        fl.fl_kv_residual_quant(cache, l, kn, vn)
+        torch.cuda.synchronize()
+        ck, sk, zk, xk = oracle.quantize_rows_asym(xf[l][rows[l]], None if l == 0 else xhk[rows[l]],
+                                                   g, bits[l], True)
+        cv, sv, zv, xv = oracle.quantize_rows_asym(xf[(l + 1) % levels][rows[l]],
+                                                   None if l == 0 else xhv[rows[l]], g, bits[l], False)
+        np.testing.assert_array_equal(t["k"].cpu().numpy(), oracle.pack_codes(ck, bits[l]))
+        np.testing.assert_array_equal(t["v"].cpu().numpy(), oracle.pack_codes(cv, bits[l]))
+        for got, want in ((t["ks"], sk), (t["kz"], zk), (t["vs"], sv), (t["vz"], zv)):
+            np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        if l == 0:
+            xhk, xhv = xk.copy(), xv.copy()
+        else:
+            xhk[rows[l]] = xk
+            xhv[rows[l]] = xv
+
+
 # ------------------------------------------------------- whole loops --
 def _chain(w, bits=None, mode=fl.FL_DEQ_AUTO, token_stat=fl.FL_TOKEN_STAT_ABS,
-           col_stat=fl.FL_COL_STAT_MASS):
+           col_stat=fl.FL_COL_STAT_MASS, quant=fl.FL_QUANT_ABSMAX):
     _say("chain", w.name, w.N, w.H, w.d, w.R, w.rho, w.kcols, bits or w.bits, "mode", mode,
-         "stats", token_stat, col_stat)
+         "stats", token_stat, col_stat, "quant", quant)
     inp = synth.generate(w)
-    gres, _ = run_gpu(w, inp, mode=mode, bits=bits, token_stat=token_stat, col_stat=col_stat)
-    ores = run_oracle_lockstep(w, inp, gres, bits=bits, token_stat=token_stat, col_stat=col_stat)
-    rep = compare_chain(w, gres, ores, bits=bits)
+    gres, _ = run_gpu(w, inp, mode=mode, bits=bits, token_stat=token_stat, col_stat=col_stat,
+                      quant=quant)
+    ores = run_oracle_lockstep(w, inp, gres, bits=bits, token_stat=token_stat, col_stat=col_stat,
+                               quant=quant)
+    rep = compare_chain(w, gres, ores, bits=bits, quant=quant)
     _say("  per-loop (r, rel-L2 out, rel-L2 lse):", [(r, f"{a[0]:.2e}", f"{b[0]:.2e}") for r, a, b in rep])
     return gres, ores
 
@@ -244,3 +310,20 @@ def test_stat_variants_f32_d64():
     w = synth.WORKLOADS["layer4k"].scaled(N=515, H=3, d=64, g=32, kcols=[515, 160, 90, 90],
                                           bits=[8, 4, 2, 4], dtype="f32", seed=32)
     _chain(w, token_stat=fl.FL_TOKEN_STAT_REL, col_stat=fl.FL_COL_STAT_VNORM)
+
+
+def test_asym_quant_chain_prefill_recipe():
+    """The paper's own quantiser (INT4 base and residuals, keys per channel,
+    values per token) through whole loops on the 32K recipe at N = 2048:
+    codes, scales and offsets bit-exact, outputs within the usual bounds."""
+    w = synth.WORKLOADS["prefill32k"].scaled(N=2048, H=8, kcols=[2048, 256, 256, 256],
+                                             bits=[4, 4, 4, 4], seed=33)
+    _chain(w, quant=fl.FL_QUANT_ASYM)
+
+
+def test_asym_quant_ragged_d64_f32():
+    """Asymmetric scheme with d = 64, g = 32, ragged N (last key group short),
+    2-bit residuals, fp32 inputs and pruning at every loop."""
+    w = synth.WORKLOADS["layer4k"].scaled(N=515, H=3, d=64, g=32, kcols=[515, 160, 90, 60],
+                                          bits=[4, 4, 2, 8], dtype="f32", seed=34)
+    _chain(w, quant=fl.FL_QUANT_ASYM)
