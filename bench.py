@@ -63,6 +63,8 @@ def parse():
                          "paper's asymmetric INT4 (keys per channel, values per token)")
     ap.add_argument("--quant-study", action="store_true",
                     help="residual vs direct quantisation error by loop on the prefill inputs")
+    ap.add_argument("--sweep", default=None, choices=["length", "depth"],
+                    help="context-length (4K-32K) or depth (R = 4..32) sweep of the step")
     ap.add_argument("--calibrate", action="store_true",
                     help="block workloads: time the retention calibration instead of the step")
     ap.add_argument("--mode", default="auto", choices=["auto", "once", "in_tile"],
@@ -136,6 +138,16 @@ def main():
         return bench_block(args, w, np, torch, fl, synth)
     if w.kind == "decode":
         return bench_decode(args, w, np, torch, fl, synth)
+    if args.sweep:
+        return bench_sweep(args, w, np, torch, fl, synth)
+    out = bench_prefill(args, w, np, torch, fl, synth, cpu=not args.no_cpu_baseline)
+    print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args, w, np, torch, fl, synth, cpu=True, steps=None):
+    """R loops of the lazy-update attention step on one layer's synthetic
+    inputs (resident in HBM): returns the JSON record."""
+    steps = steps or args.steps
     t0 = time.time()
     inp = synth.generate(w)
     log(f"[bench] generated {w.name} inputs in {time.time() - t0:.1f}s")
@@ -192,10 +204,10 @@ def main():
     if not args.no_kernel_timing:
         fl.fl_timing_report()          # discard warmup records
         fl.fl_timing_enable(True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -204,7 +216,7 @@ def main():
         fl.fl_timing_enable(False)
         ktab = fl.fl_timing_report()
     loop_ms = np.array([[evs[s][r].elapsed_time(evs[s][r + 1]) for r in range(R)]
-                        for s in range(args.steps)])
+                        for s in range(steps)])
     step_ms = loop_ms.sum(axis=1)
     ms_per_step = float(np.mean(step_ms))
     tokens = sum(n_act)
@@ -225,8 +237,8 @@ def main():
                   "colstat_split": fl_sum(lambda L: L["colstat"] and L["r"] > 1, 2.0)}
     kernels = {}
     for name, (cnt, ms) in ktab.items():
-        per_step_ms = ms / args.steps
-        e = dict(launches_per_step=cnt / args.steps, ms_per_step=round(per_step_ms, 4),
+        per_step_ms = ms / steps
+        e = dict(launches_per_step=cnt / steps, ms_per_step=round(per_step_ms, 4),
                  avg_launch_us=round(1e3 * ms / max(cnt, 1), 2))
         if name in flops_step and ms > 0 and flops_step[name] > 0:
             e["tflops"] = round(flops_step[name] / (per_step_ms / 1e3) / 1e12, 2)
@@ -261,7 +273,7 @@ def main():
         "value": round(value, 1),
         "unit": "active-query tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
@@ -284,11 +296,48 @@ def main():
         "kv_bytes_per_token": kv,
     }
 
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
-    if not args.no_cpu_baseline:
+    log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step")
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, run, n_act, loops, args.cpu_rows, torch, np,
                                            rel=args.token_stat == "rel",
                                            vw=args.col_stat == "vnorm", asym=args.quant == "asym")
+    return out
+
+
+def bench_sweep(args, w, np, torch, fl, synth):
+    """Depth and length sweeps of the lazy-update step (paper Fig. 6 and
+    Fig. 7): --sweep length runs the workload's recipe at N = 4K..32K with its
+    column budgets and kept fractions; --sweep depth runs the deep recipe
+    truncated to its first R = 4, 8, 16, 32 loops.  One JSON line with
+    tokens/s, step time and KV bytes per token per point."""
+    pts = []
+    if args.sweep == "length":
+        for N in (4096, 8192, 16384, 32768):
+            kc = [N] + [min(c, N) for c in w.kcols[1:]]
+            pts.append(w.scaled(N=N, kcols=kc, name=f"{w.name}-N{N}"))
+    else:
+        base = synth.WORKLOADS["depth32x8k"] if w.R < 32 else w
+        for R in (4, 8, 16, 32):
+            pts.append(base.scaled(R=R, rho=base.rho[:R], kcols=base.kcols[:R], bits=base.bits[:R],
+                                   name=f"{base.name}-R{R}"))
+    rows = []
+    t = time.perf_counter()
+    for p in pts:
+        o = bench_prefill(args, p, np, torch, fl, synth, cpu=False)
+        rows.append(dict(N=p.N, R=p.R, value=o["value"], ms_per_step=o["ms_per_step"],
+                         lazy_loops_tokens_per_s=o["lazy_loops_tokens_per_s"],
+                         active_tokens=sum(o["config"]["active_per_loop"]),
+                         kv_bytes_per_token=o["kv_bytes_per_token"],
+                         dominant=(o["roofline"] or {}).get("kernel"),
+                         frac=(o["roofline"] or {}).get("frac")))
+        log(f"[bench] sweep point N={p.N} R={p.R}: {o['value']:.0f} tok/s, {o['ms_per_step']:.2f} ms")
+    out = {"metric": f"{args.sweep} sweep of the lazy-update attention step (active-query tokens/s)",
+           "value": rows[-1]["value"], "unit": "active-query tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": rows[-1]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": pts[-1].name, "sweep": args.sweep, "quant": args.quant},
+           "points": rows, "wall_s": round(time.perf_counter() - t, 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -54,7 +54,7 @@ enum fl_status {
 
 enum fl_dtype { FL_F32 = 0, FL_BF16 = 1 };
 
-#define FL_MAX_LEVELS 16
+#define FL_MAX_LEVELS 32
 
 /* One level of the loop-indexed KV cache (paper Sec. 3.3 / 4.3: a quantised
  * base state plus quantised cross-loop residuals; residuals exist only for
@@ -356,7 +356,7 @@ typedef struct fl_block_cfg {
     int n_active[FL_MAX_LEVELS];
     int k_cols[FL_MAX_LEVELS];
     int bits[FL_MAX_LEVELS];
-    int mode;               /* fl_attn_mode */
+    int mode;               /* fl_attn_mode: FL_DEQ_AUTO or FL_DEQ_ONCE        */
     int token_stat;         /* fl_token_stat */
     int col_stat;           /* fl_col_stat   */
 } fl_block_cfg;

@@ -59,6 +59,11 @@ long attn_ws_bytes(long H, long k, long d, long levels) {
     return 8 * align_up(H * kp * d * 2) + 2 * align_up(H * kp * 4) +
            levels * quant_plane_bytes(H, kp, d) + kAlign;
 }
+// the compact-gather (FL_DEQ_ONCE) path alone: no per-level code planes
+long attn_ws_bytes_once(long H, long k, long d) {
+    const long kp = kpad(k);
+    return 8 * align_up(H * kp * d * 2) + 2 * align_up(H * kp * 4) + kAlign;
+}
 
 // workspace of fl_block_step: compact bf16 activations of the active rows
 // (normed input, qkv, q/k/v, attention output, SwiGLU output) followed by the
@@ -66,7 +71,7 @@ long attn_ws_bytes(long H, long k, long d, long levels) {
 long block_ws_bytes(long N, long H, long d, long F) {
     const long D = H * d;
     return align_up(N * D * 2) * 5 + align_up(N * 3 * D * 2) + align_up(N * F * 2) +
-           attn_ws_bytes(H, N, d, FL_MAX_LEVELS) + kAlign;
+           attn_ws_bytes_once(H, N, d) + kAlign;
 }
 
 // Operand precision of the attention products: residual levels hold the
@@ -336,7 +341,7 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
         for (int l = 0; l <= a->level; ++l)
             if (cache->level[l].bits == 32)
                 return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE needs quantised levels (level %d is raw)", l);
-    const long need = attn_ws_bytes(H, a->k, d, a->level + 1);
+    const long need = in_tile ? attn_ws_bytes(H, a->k, d, a->level + 1) : attn_ws_bytes_once(H, a->k, d);
     if (!ws || (long)ws_bytes < need)
         return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
     hipStream_t st = (hipStream_t)stream;
@@ -514,6 +519,10 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
     FL_REQUIRE(N > 0 && L >= 1, "N=%d layers=%d", N, L);
     FL_REQUIRE(stat_kinds_ok(cfg->token_stat, cfg->col_stat), "token_stat %d / col_stat %d",
                cfg->token_stat, cfg->col_stat);
+    FL_REQUIRE(cfg->mode == FL_DEQ_AUTO || cfg->mode == FL_DEQ_ONCE || cfg->mode == FL_DEQ_IN_TILE,
+               "mode %d", cfg->mode);
+    if (cfg->mode == FL_DEQ_IN_TILE)
+        return fail(FL_ERR_UNSUPPORTED, "fl_block_step uses the compact-gather path (FL_DEQ_ONCE)");
     if (!(d == 64 || d == 128)) return fail(FL_ERR_UNSUPPORTED, "head dim %d", d);
     if (D % 128 || F % 128) return fail(FL_ERR_UNSUPPORTED, "D=%d and ffn=%d must be multiples of 128", D, F);
     FL_REQUIRE(S->h && S->h_entry && S->stat, "h/h_entry/stat NULL");
@@ -531,7 +540,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
     __bf16* qkv = (__bf16*)take((long)N * 3 * D * 2);
     __bf16* act_buf = (__bf16*)take((long)N * F * 2);
     void* aws = p;
-    const size_t aws_bytes = (size_t)attn_ws_bytes(H, N, d, FL_MAX_LEVELS);
+    const size_t aws_bytes = (size_t)attn_ws_bytes_once(H, N, d);
 
     // ---- the loop's active tokens (Sec. 4.1) ----
     int n;

@@ -71,6 +71,17 @@ struct DecodeParams {
     float* out; float* lse; float* mass_u; float* out_u; float* col_stat;
 };
 
+// Kernels take the cache descriptor (and, on the in-tile path, the level
+// code planes) by value.  A 3648-byte by-value argument was checked to arrive
+// intact on gfx950; every kernel's arguments stay within that size.
+constexpr size_t kKernargChecked = 3648;
+static_assert(sizeof(fl_kv_cache) + sizeof(QTiles) + 48 <= kKernargChecked,
+              "k_gather_q arguments exceed the checked kernel-argument size");
+static_assert(sizeof(DecodeParams) + 16 <= kKernargChecked,
+              "k_decode arguments exceed the checked kernel-argument size");
+static_assert(sizeof(fl_kv_cache) + 64 <= kKernargChecked,
+              "cache-descriptor kernels exceed the checked kernel-argument size");
+
 // C = A[M][K] . B[N][K]^T (bf16 in, fp32 accumulate); N % 128 == 0, K % 32 == 0
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 struct GemmParams {

@@ -23,7 +23,7 @@ FL_TOKEN_STAT_ABS, FL_TOKEN_STAT_REL = 0, 1
 FL_COL_STAT_MASS, FL_COL_STAT_VNORM = 0, 1
 FL_QUANT_ABSMAX, FL_QUANT_ASYM = 0, 1
 FL_WS_SELECT_ACTIVE, FL_WS_SELECT_COLUMNS, FL_WS_SPARSE_ATTN, FL_WS_LOOP_STEP = 1, 2, 3, 4
-MAX_LEVELS = 16
+MAX_LEVELS = 32
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",

@@ -84,6 +84,18 @@ class Workload:
         return w
 
 
+def depth_schedule(R: int, N: int):
+    """Per-loop budgets of the deep recipe: kept fraction 0.5 at loop 2,
+    shrinking by 0.9 a loop down to 0.02; columns 2048 shrinking by 0.9 a loop
+    down to 256; int8 base, int4 residuals at loops 2-8, int2 after."""
+    rho = [1.0] + [round(max(0.02, 0.5 * 0.9 ** (r - 2)), 4) for r in range(2, R + 1)]
+    kc = [N] + [max(256, int(2048 * 0.9 ** (r - 2))) for r in range(2, R + 1)]
+    bits = [8] + [4 if r <= 8 else 2 for r in range(2, R + 1)]
+    return rho, kc, bits
+
+
+_DEPTH_RHO, _DEPTH_K, _DEPTH_BITS = depth_schedule(32, 8192)
+
 WORKLOADS = {
     # 1 head x 64, seq 256, R=2, fp32; rho 0.25, 64 columns incl. 4 sinks;
     # int8 base / int4 residual, group 32.
@@ -108,6 +120,12 @@ WORKLOADS = {
     # residuals at every loop), one new query per sequence per loop, R=4,
     # 16 x 128; loop 1 dense over the prefix, loops 2-4 on 256 columns
     # (4 sinks), plus the token's own column.
+    # deep looping: 32 loops at seq 8192 (16 x 128, bf16), per-loop kept
+    # fractions and column budgets shrinking with depth (depth_schedule);
+    # per-token loop updates decay slowly, log sigma = -2.4 - 0.09 r.
+    "depth32x8k": Workload("depth32x8k", N=8192, H=16, d=128, R=32, g=64, n_sink=4,
+                           rho=_DEPTH_RHO, kcols=_DEPTH_K, bits=_DEPTH_BITS, dtype="bf16",
+                           seed=5, sigma_mu=(-2.4, -0.09), sigma_sd=1.0),
     "decode64x8k": Workload("decode64x8k", N=8192, H=16, d=128, R=4, g=64, n_sink=4,
                             rho=[1.0, 0.4, 0.2, 0.1], kcols=[8192, 256, 256, 256],
                             bits=[8, 4, 4, 4], dtype="bf16", seed=3, kind="decode",
