@@ -11,7 +11,9 @@ r-1 against the dequantised previous value; the other tokens keep theirs.
 
 The new token at position N runs R loops.  At loop r its query attends
 causally to the prefix's loop-r dequantised keys/values on the selected
-columns S_r plus its own fresh key/value (column N, always selected):
+columns S_r plus its own fresh key/value (column N, always selected) -- and,
+during generation, the unquantised window of recent generated tokens (also
+always selected; ``run_generation``):
 
   loop 1   dense over all N + 1 columns; M_U = O_U = 0; the column
            statistic is the token's probability of every prefix column.
@@ -63,35 +65,36 @@ def build_cache(k, v, stat, sched):
     return out
 
 
-def _extend(x_prefix, x_self):
-    """[N][H][d] prefix rows + the new token's [H][d] row at position N."""
-    return np.concatenate([np.asarray(x_prefix, F32), np.asarray(x_self, F32)[None]], axis=0)
+def _with_tail(sel, N, T):
+    """Per-head selected prefix columns plus the T always-included columns
+    at positions N .. N+T-1."""
+    tail = np.broadcast_to(np.arange(N, N + T, dtype=np.int32), (sel.shape[0], T))
+    return np.concatenate([sel, tail], axis=1)
 
 
-def _with_self(sel, N):
-    return np.concatenate([sel, np.full((sel.shape[0], 1), N, np.int32)], axis=1)
+def decode_token(khat, vhat, q, tail_k, tail_v, sched, override=None):
+    """Loops 1..R of one new token over a prefix cache plus bf16 columns.
 
-
-def run_decode(cache, q, k_self, v_self, sched, override=None):
-    """Loops 1..R of one sequence's new token.
-
-    cache: output of ``build_cache``; q, k_self, v_self: lists of R fp32
-    arrays [H][d].  override: {('cstat', r): [H][k_{r-1}]} -- the GPU's own
-    statistic for the column selection made at loop r.
-    Returns per-loop dicts: sel [H][k] prefix columns (None when dense), k,
-    out [H][d], lse [H], mass_u [H], out_u [H][d], cstat [H][k] or None."""
+    khat, vhat: lists of R arrays [N][H][d], the prefix's dequantised loop-r
+    cache; tail_k, tail_v: lists of R arrays [T][H][d], the always-included
+    columns at positions N..N+T-1 (the last is the token itself); q: list of
+    R arrays [H][d].  Every step is a call of the pinned C oracle on an
+    (N + T)-position problem with one query row at position N + T - 1.
+    Returns per-loop dicts as ``run_decode``."""
     override = override or {}
-    N, H, d, R = (sched[x] for x in ("N", "H", "d", "R"))
+    H, d, R = (sched[x] for x in ("H", "d", "R"))
+    N = np.asarray(khat[0]).shape[0]
+    T = np.asarray(tail_k[0]).shape[0]
     sm = F32(1.0 / np.sqrt(d))
-    rows = np.array([N], np.int32)
+    rows = np.array([N + T - 1], np.int32)
     S, k_cur, cstat = None, N, None
     prev = None   # (Q, K, V, lse, mu, ou) of the previous loop
     recs = []
     for r in range(1, R + 1):
-        Q = np.zeros((N + 1, H, d), F32)
-        Q[N] = np.asarray(q[r - 1], F32)
-        K = _extend(cache[r - 1]["khat"], k_self[r - 1])
-        V = _extend(cache[r - 1]["vhat"], v_self[r - 1])
+        Q = np.zeros((N + T, H, d), F32)
+        Q[N + T - 1] = np.asarray(q[r - 1], F32)
+        K = np.concatenate([np.asarray(khat[r - 1], F32), np.asarray(tail_k[r - 1], F32)], axis=0)
+        V = np.concatenate([np.asarray(vhat[r - 1], F32), np.asarray(tail_v[r - 1], F32)], axis=0)
         if r == 1:
             o, lse = attend(Q, K, V, rows, None, sm)
             mu = np.zeros((1, H), F32); ou = np.zeros((1, H, d), F32)
@@ -108,13 +111,13 @@ def run_decode(cache, q, k_self, v_self, sched, override=None):
             Qp, Kp, Vp, lse_p, mu_p, ou_p = prev
             if changed:
                 mu, ou = unselected_cache(Qp, Kp, Vp, rows,
-                                          None if S is None else _with_self(S, N),
-                                          _with_self(S_new, N), lse_p, sm,
+                                          None if S is None else _with_tail(S, N, T),
+                                          _with_tail(S_new, N, T), lse_p, sm,
                                           None if S is None else mu_p,
                                           None if S is None else ou_p)
             else:
                 mu, ou = mu_p, ou_p
-            ext = None if S_new is None else _with_self(S_new, N)
+            ext = None if S_new is None else _with_tail(S_new, N, T)
             o, lse = attend(Q, K, V, rows, ext, sm, mu, ou)
             need_c = r < R and sched["kcols"][r] < k_new
             c = column_stats(Q, K, rows, ext, lse, sm, mu)[:, :k_new] if need_c else None
@@ -123,3 +126,69 @@ def run_decode(cache, q, k_self, v_self, sched, override=None):
         prev = (Q, K, V, lse, mu, ou)
         S, k_cur, cstat = S_new, k_new, c
     return recs
+
+
+def run_decode(cache, q, k_self, v_self, sched, override=None):
+    """Loops 1..R of one sequence's new token.
+
+    cache: output of ``build_cache``; q, k_self, v_self: lists of R fp32
+    arrays [H][d].  override: {('cstat', r): [H][k_{r-1}]} -- the GPU's own
+    statistic for the column selection made at loop r.
+    Returns per-loop dicts: sel [H][k] prefix columns (None when dense), k,
+    out [H][d], lse [H], mass_u [H], out_u [H][d], cstat [H][k] or None."""
+    R = sched["R"]
+    return decode_token([cache[r]["khat"] for r in range(R)], [cache[r]["vhat"] for r in range(R)],
+                        q, [np.asarray(k_self[r], F32)[None] for r in range(R)],
+                        [np.asarray(v_self[r], F32)[None] for r in range(R)], sched, override)
+
+
+def append_token(k_loops, v_loops, sched):
+    """Generation-time growth of the cache (Sec. 4.3, App. E): a generated
+    token, computed in every loop, stored as a base level (its loop-1 K/V)
+    plus one residual level per later loop against its dequantised value.
+    k_loops, v_loops: lists of R arrays [H][d].  Returns per level the codes
+    and scales ([1][H][d], [1][H][d/g]) and the token's dequantised loop-r
+    K/V ([H][d]) for r = 1..R."""
+    g = sched["g"]
+    out = []
+    kh = vh = None
+    for r in range(1, sched["R"] + 1):
+        bits = sched["bits"][r - 1]
+        kc, ks, _, kh = quantize_rows(np.asarray(k_loops[r - 1], F32)[None], kh, g, bits)
+        vc, vs, _, vh = quantize_rows(np.asarray(v_loops[r - 1], F32)[None], vh, g, bits)
+        out.append(dict(k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs, khat=kh[0], vhat=vh[0]))
+    return out
+
+
+def run_generation(cache, gen_q, gen_k, gen_v, sched, window=64, override=None):
+    """Generation after a prompt whose cache ``build_cache`` made.
+
+    gen_q/k/v[t]: lists of R arrays [H][d], the t-th generated token's
+    per-loop query / key / value.  The most recent ``window`` generated tokens
+    stay unquantised (App. E keeps the most recent 64 tokens in BF16): token
+    t attends to the quantised cache plus generated tokens max(0, t-window)..t;
+    before token t is decoded, token t - window - 1 (if any) leaves the window
+    and is appended to the cache (``append_token``).
+    override: {t: {('cstat', r): ...}} per token.
+    Returns per token a dict: recs (per-loop records of ``decode_token``), N
+    (cached positions), T (window columns incl. the token), appended (None or
+    the ``append_token`` record of the token appended before it)."""
+    override = override or {}
+    R = sched["R"]
+    khat = [np.asarray(cache[r]["khat"], F32) for r in range(R)]
+    vhat = [np.asarray(cache[r]["vhat"], F32) for r in range(R)]
+    out = []
+    for t in range(len(gen_q)):
+        appended = None
+        if t >= window + 1:
+            u = t - window - 1
+            appended = append_token(gen_k[u], gen_v[u], sched)
+            for r in range(R):
+                khat[r] = np.concatenate([khat[r], appended[r]["khat"][None]], axis=0)
+                vhat[r] = np.concatenate([vhat[r], appended[r]["vhat"][None]], axis=0)
+        lo = max(0, t - window)
+        tk = [np.stack([np.asarray(gen_k[u][r], F32) for u in range(lo, t + 1)]) for r in range(R)]
+        tv = [np.stack([np.asarray(gen_v[u][r], F32) for u in range(lo, t + 1)]) for r in range(R)]
+        recs = decode_token(khat, vhat, gen_q[t], tk, tv, sched, override.get(t))
+        out.append(dict(recs=recs, N=khat[0].shape[0], T=t + 1 - lo, appended=appended))
+    return out

@@ -223,7 +223,7 @@ def decode_seeds(w: Workload):
     return np.random.SeedSequence(w.seed).spawn(w.extra["B"])
 
 
-def gen_decode_seq(w: Workload, b: int) -> dict:
+def gen_decode_seq(w: Workload, b: int, n_gen: int = 0) -> dict:
     """Sequence b of the decode batch.
 
     Prefix of N cached tokens, drawn with the prefill recipe: per-head mean
@@ -238,7 +238,12 @@ def gen_decode_seq(w: Workload, b: int) -> dict:
 
     The new token: q_1 = m_h + N(0, I), k_1, v_1 ~ N(0, I) [H][d]; loop
     r >= 2 adds s_r * N(0, I) to each, s_r = exp(N(a + b*r, sigma_sd)).
-    All K/V/q tensors are bf16 bits."""
+    All K/V/q tensors are bf16 bits.
+
+    n_gen > 0 also draws that many generated tokens after the above (their
+    draws come last, so the rest does not change): each like the new token,
+    q = m_h + N(0, I), k, v ~ N(0, I), loop r >= 2 adding s_r * N(0, I) with
+    its own s_r; returned as gen_q / gen_k / gen_v [t][r] of [H][d]."""
     rng = np.random.Generator(np.random.PCG64(decode_seeds(w)[b]))
     N, H, d, D = w.N, w.H, w.d, w.D
     m = rng.standard_normal((H, d), dtype=np.float32)
@@ -267,7 +272,23 @@ def gen_decode_seq(w: Workload, b: int) -> dict:
         vn = vn + s1 * rng.standard_normal((H, d), dtype=np.float32)
         ks.append(cast(k)); vs.append(cast(v))
         qs.append(cast(qn)); kns.append(cast(kn)); vns.append(cast(vn))
-    return dict(stat=stats, k=ks, v=vs, q_new=qs, k_new=kns, v_new=vns, dtype="bf16")
+    out = dict(stat=stats, k=ks, v=vs, q_new=qs, k_new=kns, v_new=vns, dtype="bf16")
+    if n_gen:
+        gq, gk, gv = [], [], []
+        for _ in range(n_gen):
+            tq = m + rng.standard_normal((H, d), dtype=np.float32)
+            tk = rng.standard_normal((H, d), dtype=np.float32)
+            tv = rng.standard_normal((H, d), dtype=np.float32)
+            lq, lk, lv = [cast(tq)], [cast(tk)], [cast(tv)]
+            for r in range(2, w.R + 1):
+                s1 = np.float32(np.exp(rng.normal(a + bb * r, w.sigma_sd)))
+                tq = tq + s1 * rng.standard_normal((H, d), dtype=np.float32)
+                tk = tk + s1 * rng.standard_normal((H, d), dtype=np.float32)
+                tv = tv + s1 * rng.standard_normal((H, d), dtype=np.float32)
+                lq.append(cast(tq)); lk.append(cast(tk)); lv.append(cast(tv))
+            gq.append(lq); gk.append(lk); gv.append(lv)
+        out.update(gen_q=gq, gen_k=gk, gen_v=gv)
+    return out
 
 
 def generate(w: Workload) -> dict:
