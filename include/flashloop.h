@@ -408,9 +408,12 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
  * fl_sparse_loop_attn.  The previous loop's P over the kept prefix columns
  * is the column statistic (col_stat).
  * Cache layout: cache.level[l] describes sequence 0 with the usual fields;
- * sequence b's rows/slot/codes/scales follow at b * (n_rows, N, n_rows*H*
- * d*bits/8 bytes, n_rows*H*d/g floats) -- B sequences of equal geometry.
- * Requirements: N + 1 <= 12288 (the probabilities stay in LDS); scheme
+ * sequence b's rows/slot/codes/scales follow at b * (R_l, P, R_l*H*d*bits/8
+ * bytes, R_l*H*d/g floats) -- B sequences of equal geometry -- with the
+ * per-sequence capacities P = N_cap (or N) positions and R_l = rows_cap[l]
+ * (or n_rows; level 0: P) rows.
+ * Requirements: N + T <= 12288 (T bf16 columns: 1, or the window count; the
+ * probabilities stay in LDS); scheme
  * FL_QUANT_ABSMAX with an int8 base level and quantised residual levels
  * (FL_ERR_UNSUPPORTED otherwise); a
  * sparse loop r keeps 4 * ((k + 1) + r * k) bytes in LDS, at most 48 KiB.
@@ -418,7 +421,25 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
 typedef struct fl_decode_cfg {
     int B, N, H, d, g, R, n_sink;
     int k_cols[FL_MAX_LEVELS];  /* [0] = N */
+    /* per-sequence capacities of a cache that grows during generation
+     * (fl_decode_append); 0 = exactly N positions / n_rows rows: */
+    int N_cap;                  /* positions (slot maps, level-0 rows)       */
+    int rows_cap[FL_MAX_LEVELS]; /* rows of level l >= 1 (index l)           */
 } fl_decode_cfg;
+
+/* Generation-time bf16 window (App. E: the most recent 64 tokens stay in
+ * BF16).  Per loop r a ring of `cap` slots per sequence holds the loop-r
+ * keys / values of the most recent generated tokens and of the token being
+ * decoded: k[r-1], v[r-1] bf16 [B][cap][H][d].  The `count` valid slots are
+ * 0..count-1 (which slot holds which token does not matter to attention: all
+ * are earlier than or equal to the new token).  Every valid slot is an extra
+ * key column of every loop, always included like the self column. */
+typedef struct fl_decode_window {
+    int cap;
+    int count;
+    const void* k[FL_MAX_LEVELS];
+    const void* v[FL_MAX_LEVELS];
+} fl_decode_window;
 
 typedef struct fl_decode_state {
     fl_kv_cache cache;
@@ -436,10 +457,30 @@ typedef struct fl_decode_inputs {
     const void* q_prev;  /* loop r-1 values (r >= 2)                            */
     const void* k_self_prev;
     const void* v_self_prev;
+    /* generation: when win != NULL its `count` slots of loop r (and r-1 for a
+     * rebuild) are the bf16 columns in place of k_self / v_self (the caller
+     * has written the new token into one of them) */
+    const fl_decode_window* win;
 } fl_decode_inputs;
 
 int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* st, const fl_decode_inputs* in,
                    int r, fl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fl_decode_append -- generation-time growth of the quantised cache (Sec.
+ * 4.3, App. E): the token in ring slot `slot` of every loop's window (a
+ * generated token, computed in all R loops) is appended to every sequence's
+ * cache at position p = cfg->N: level 0 stores its loop-1 K/V quantised as
+ * the base, level l >= 1 appends row n_rows_l holding the residual of its
+ * loop-(l+1) K/V against its dequantised loop-l value (rows[n_rows_l] = p,
+ * slot[p] = n_rows_l), with the arithmetic of fl_kv_residual_quant.  Then
+ * cfg->N, st->cache.N and every st->cache.level[l].n_rows (l = 1..R-1) grow
+ * by one.  The cache must have been allocated with capacities cfg->N_cap and
+ * cfg->rows_cap, scheme FL_QUANT_ABSMAX, an int8 base and quantised levels.
+ * Errors: FL_ERR_INVALID_ARG (NULL pointers, slot outside the ring, a
+ * capacity exceeded), FL_ERR_UNSUPPORTED (cache format). */
+int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* st, const fl_decode_window* win,
+                     int slot, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later

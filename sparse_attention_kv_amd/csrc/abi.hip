@@ -152,6 +152,18 @@ int check_cache(const fl_kv_cache* c, int upto) {
     return FL_OK;
 }
 
+// per-sequence capacities of the batched decode cache
+int decode_caps(const fl_decode_cfg* cfg, const fl_kv_cache& C, int upto, fl::DecodeParams& P) {
+    P.pos_cap = cfg->N_cap ? cfg->N_cap : cfg->N;
+    FL_REQUIRE(cfg->N <= P.pos_cap, "N=%d exceeds N_cap=%d", cfg->N, P.pos_cap);
+    for (int l = 1; l <= upto; ++l) {
+        P.rows_cap[l] = cfg->rows_cap[l] ? cfg->rows_cap[l] : C.level[l].n_rows;
+        FL_REQUIRE(C.level[l].n_rows <= P.rows_cap[l], "level %d: n_rows %d exceeds rows_cap %d", l,
+                   C.level[l].n_rows, P.rows_cap[l]);
+    }
+    return FL_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -662,7 +674,16 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
     const int B = cfg->B, N = cfg->N, H = cfg->H, d = cfg->d;
     FL_REQUIRE(B >= 1 && N >= 1 && H >= 1, "B=%d N=%d H=%d", B, N, H);
-    FL_REQUIRE(N + 1 <= 12288, "N=%d: decode keeps N+1 probabilities in LDS (<= 12288)", N);
+    const fl_decode_window* W = in->win;
+    if (W) {
+        FL_REQUIRE(W->cap >= 1 && W->count >= 1 && W->count <= W->cap, "window count %d / cap %d",
+                   W->count, W->cap);
+        for (int l = (r >= 2 ? r - 2 : 0); l < r; ++l)
+            FL_REQUIRE(W->k[l] && W->v[l], "window buffers of loop %d NULL", l + 1);
+    }
+    const int T = W ? W->count : 1;
+    FL_REQUIRE(N + T <= 12288, "N=%d + %d bf16 columns: decode keeps the probabilities in LDS (<= 12288)",
+               N, T);
     fl_kv_cache& C = S->cache;
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, r - 1);
@@ -672,17 +693,27 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     for (int l = 1; l < r; ++l)
         if (C.level[l].bits == 32)
             return fail(FL_ERR_UNSUPPORTED, "decode: level %d is raw (quantised levels only)", l);
-    FL_REQUIRE(in->q && in->k_self && in->v_self, "q/k_self/v_self NULL");
+    FL_REQUIRE(in->q && (W || (in->k_self && in->v_self)), "q/k_self/v_self NULL");
     FL_REQUIRE(S->out && S->lse && S->mass_u && S->out_u, "state arrays NULL");
     hipStream_t st = (hipStream_t)stream;
     fl::DecodeParams P{};
+    rc = decode_caps(cfg, C, r - 1, P);
+    if (rc) return rc;
     P.B = B; P.H = H; P.sm = 1.0f / sqrtf((float)d); P.cache = C;
     P.out = S->out; P.lse = S->lse; P.mass_u = S->mass_u; P.out_u = S->out_u;
+    P.n_tail = T;
+    P.tail_cap = W ? W->cap : 1;
+    // the bf16 columns of loop r (and r - 1, for a rebuild)
+    auto tails = [&](fl::DecodeParams& Q, int loop, const void* ks, const void* vs) {
+        Q.tail_k = W ? W->k[loop - 1] : ks;
+        Q.tail_v = W ? W->v[loop - 1] : vs;
+    };
     if (r == 1) {
         S->k_cur[0] = N;
         S->sel_used[0] = nullptr;
         P.k = N; P.sel = nullptr; P.level = 0; P.cache_op = FL_CACHE_ZERO;
-        P.q = in->q; P.kself = in->k_self; P.vself = in->v_self;
+        P.q = in->q;
+        tails(P, 1, in->k_self, in->v_self);
         P.col_stat = (cfg->R > 1 && cfg->k_cols[1] < N) ? S->col_stat[0] : nullptr;
         FL_HIP(fl::launch_fill_f32(S->mass_u, (long)B * H, 0.0f, st), "fill");
         FL_HIP(fl::launch_fill_f32(S->out_u, (long)B * H * d, 0.0f, st), "fill");
@@ -690,7 +721,7 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
                "decode");
         return FL_OK;
     }
-    FL_REQUIRE(in->q_prev && in->k_self_prev && in->v_self_prev, "previous-loop inputs NULL");
+    FL_REQUIRE(in->q_prev && (W || (in->k_self_prev && in->v_self_prev)), "previous-loop inputs NULL");
     const int k_prev = S->k_cur[r - 2], k_r = cfg->k_cols[r - 1];
     bool changed = false;
     if (k_prev <= k_r) {
@@ -709,22 +740,67 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     P.sel = S->sel_used[r - 1];
     // a sparse loop keeps the probabilities and every level's row of each
     // selected column in LDS
-    if (P.sel && (size_t)(P.k + 1) * 4 + (size_t)r * P.k * 4 > 48 * 1024)
+    if (P.sel && (size_t)(P.k + T) * 4 + (size_t)r * P.k * 4 > 48 * 1024)
         return fail(FL_ERR_UNSUPPORTED, "decode: %d columns x %d levels exceed the LDS budget", P.k, r);
     if (changed) {
         fl::DecodeParams R = P;
         R.level = r - 2; R.cache_op = FL_CACHE_REBUILD;
-        R.q = in->q_prev; R.kself = in->k_self_prev; R.vself = in->v_self_prev; R.col_stat = nullptr;
+        R.q = in->q_prev; R.col_stat = nullptr;
+        tails(R, r - 1, in->k_self_prev, in->v_self_prev);
         FL_HIP(timed("decode_rebuild", st, [&] { return fl::launch_decode(d, fl::MODE_REBUILD, R, st); }),
                "decode(rebuild)");
     }
     P.level = r - 1; P.cache_op = FL_CACHE_CARRY;
-    P.q = in->q; P.kself = in->k_self; P.vself = in->v_self;
+    P.q = in->q;
+    tails(P, r, in->k_self, in->v_self);
     const bool need_c = r < cfg->R && cfg->k_cols[r] < S->k_cur[r - 1];
     P.col_stat = need_c ? S->col_stat[r - 1] : nullptr;
     FL_REQUIRE(!need_c || P.col_stat, "col_stat[%d] NULL", r - 1);
     FL_HIP(timed(P.sel ? "decode" : "decode_dense", st,
                  [&] { return fl::launch_decode(d, fl::MODE_ATTN, P, st); }), "decode");
+    return FL_OK;
+}
+
+int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode_window* W, int slot,
+                     fl_stream_t stream) {
+    FL_REQUIRE(cfg && S && W, "cfg/state/window NULL");
+    const int B = cfg->B, N = cfg->N, H = cfg->H, d = cfg->d, R = cfg->R;
+    FL_REQUIRE(B >= 1 && R >= 1 && R <= FL_MAX_LEVELS, "B=%d R=%d", B, R);
+    fl_kv_cache& C = S->cache;
+    FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
+    int rc = check_cache(&C, R - 1);
+    if (rc) return rc;
+    if (C.scheme != FL_QUANT_ABSMAX || C.level[0].bits != 8)
+        return fail(FL_ERR_UNSUPPORTED, "append: FL_QUANT_ABSMAX caches with an int8 base only");
+    for (int l = 1; l < R; ++l)
+        if (C.level[l].bits == 32)
+            return fail(FL_ERR_UNSUPPORTED, "append: level %d is raw (quantised levels only)", l);
+    FL_REQUIRE(slot >= 0 && slot < W->cap, "slot %d outside the window of %d", slot, W->cap);
+    for (int l = 0; l < R; ++l) FL_REQUIRE(W->k[l] && W->v[l], "window buffers of loop %d NULL", l + 1);
+    fl::DecodeParams caps{};
+    rc = decode_caps(cfg, C, R - 1, caps);
+    if (rc) return rc;
+    FL_REQUIRE(N + 1 <= caps.pos_cap, "append: N_cap %d reached", caps.pos_cap);
+    fl::AppendParams P{};
+    P.B = B; P.H = H; P.g = C.g; P.R = R; P.pos = N; P.slot = slot; P.win_cap = W->cap;
+    P.pos_cap = caps.pos_cap;
+    for (int l = 0; l < R; ++l) {
+        P.lev[l] = C.level[l];
+        P.bits[l] = C.level[l].bits;
+        P.wk[l] = W->k[l];
+        P.wv[l] = W->v[l];
+        if (l >= 1) {
+            P.rows_cap[l] = caps.rows_cap[l];
+            P.n_rows[l] = C.level[l].n_rows;
+            FL_REQUIRE(C.level[l].n_rows + 1 <= caps.rows_cap[l], "append: level %d rows_cap %d reached",
+                       l, caps.rows_cap[l]);
+        }
+    }
+    hipStream_t st = (hipStream_t)stream;
+    FL_HIP(timed("decode_append", st, [&] { return fl::launch_decode_append(d, P, st); }), "append");
+    cfg->N = N + 1;
+    C.N = N + 1;
+    for (int l = 1; l < R; ++l) C.level[l].n_rows += 1;
     return FL_OK;
 }
 

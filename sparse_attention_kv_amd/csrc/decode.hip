@@ -5,7 +5,8 @@
 //
 // One workgroup per (sequence, head) and one new query token.  The key
 // columns are the selected prefix columns (all of them in the dense first
-// loop) plus the token's own fresh bf16 key/value ("self" column).
+// loop) plus T always-included bf16 columns: the token's own fresh key/value
+// ("self" column) and, during generation, the window of recent tokens.
 // A column's row of d codes is read by d/16 neighbouring lanes, 16 codes
 // each, so every wave load covers whole 2^k-byte code rows (coalesced), and
 // several column groups are in flight per wave.
@@ -38,18 +39,32 @@ struct SeqLevel {
     int bits;
 };
 
-// level l of sequence b: rows of the B sequences are stored back to back
+// level l of sequence b: the B sequences are stored back to back with the
+// per-sequence capacities (positions pos_cap; rows rows_cap[l] for l >= 1)
 template <int D>
-__device__ __forceinline__ SeqLevel seq_level(const fl_kv_cache& c, int l, int b, int which) {
+__device__ __forceinline__ SeqLevel seq_level(const DecodeParams& P, int l, int b, int which) {
+    const fl_kv_cache& c = P.cache;
     const fl_kv_level& L = c.level[l];
-    const long rows = l == 0 ? c.N : L.n_rows;
+    const long rows = l == 0 ? P.pos_cap : P.rows_cap[l];
     SeqLevel s;
     s.bits = L.bits;
     s.codes = reinterpret_cast<const uint8_t*>(which ? L.v_codes : L.k_codes) +
               b * (rows * c.H * D * L.bits / 8);
     s.scales = (which ? L.v_scale : L.k_scale) + b * (rows * c.H * (D / c.g));
-    s.slot = l == 0 ? nullptr : L.slot + (long)b * c.N;
+    s.slot = l == 0 ? nullptr : L.slot + (long)b * P.pos_cap;
     return s;
+}
+
+// 16 consecutive bf16 values as fp32
+__device__ __forceinline__ void load_bf16x16(const void* base, long e, float (&x)[16]) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + e);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[2 * i] = __uint_as_float(wd[i] << 16);
+        x[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+    }
 }
 
 // 16 consecutive codes starting at code index e (16-aligned)
@@ -77,7 +92,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     constexpr int CPW = 64 / LPC;   // columns per wave per load
     constexpr int CPI = CPW * DNW;  // columns per workgroup pass
     constexpr int U = 4;            // passes in flight (8 measured no faster)
-    extern __shared__ float dyn[];  // sc[k + 1], then (sparse) rows[level + 1][k]
+    extern __shared__ float dyn[];  // sc[k + T], then (sparse) rows[level + 1][k]
     __shared__ float qs[D];
     __shared__ float red[DNW];
     __shared__ float ored[DNW][D];
@@ -99,10 +114,14 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     const fl_kv_cache& C = P.cache;
     const int H = C.H, G = D / C.g;
     const int k = P.k;
+    const int T = P.n_tail;
+    const int kt = k + T;
     const int nlev = L0 ? 1 : P.level + 1;
     const long qo = (long)bh * D;
     float* sc = dyn;
-    int* rowtab = reinterpret_cast<int*>(dyn + k + 1);
+    int* rowtab = reinterpret_cast<int*>(dyn + kt);
+    // tail column t of this (sequence, head): element offset of its row
+    auto tail_off = [&](int t) -> long { return (((long)b * P.tail_cap + t) * H + h) * D; };
     for (int c = tid; c < D; c += DT)
         qs[c] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.q)[qo + c]);
     if (SPARSE) {
@@ -110,7 +129,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         for (int c = tid; c < k; c += DT) {
             const int j = sel[c];
             rowtab[c] = j;
-            for (int l = 1; l < nlev; ++l) rowtab[l * k + c] = seq_level<D>(C, l, b, 0).slot[j];
+            for (int l = 1; l < nlev; ++l) rowtab[l * k + c] = seq_level<D>(P, l, b, 0).slot[j];
         }
     }
     __syncthreads();
@@ -123,7 +142,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     auto row_of = [&](int l, int c) -> int {
         if (SPARSE) return rowtab[l * k + c];
         if (l == 0) return c;
-        return seq_level<D>(C, l, b, 0).slot[c];
+        return seq_level<D>(P, l, b, 0).slot[c];
     };
 
     // ---- phase 1: scores (log2 units) ----
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 for (int l = 0; l < nlev; ++l) {
                     const int row = row_of(l, c);
                     if (row >= 0) {
-                        const SeqLevel L = seq_level<D>(C, l, b, 0);
+                        const SeqLevel L = seq_level<D>(P, l, b, 0);
                         const long rr = (long)row * H + h;
                         float x[16];
                         load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
@@ -161,12 +180,19 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
             if (cs == 0 && c < k) sc[c] = v * c2;
         }
     }
-    if (tid < 64) { // self column: the token's own bf16 key
-        float s = 0.0f;
-        for (int c = tid; c < D; c += 64)
-            s += qs[c] * bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.kself)[qo + c]);
-        s = wave_sum(s);
-        if (tid == 0) sc[k] = s * c2;
+    // the T always-included bf16 columns (self, window), laid out like the cache
+    for (int t0 = 0; t0 < T; t0 += CPI) {
+        const int t = t0 + w * CPW + cl;
+        float v = 0.0f;
+        if (t < T) {
+            float x[16];
+            load_bf16x16(P.tail_k, tail_off(t) + cs * 16, x);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v = fmaf(qv[i], x[i], v);
+        }
+#pragma unroll
+        for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
+        if (cs == 0 && t < T) sc[k + t] = v * c2;
     }
     __syncthreads();
 
@@ -174,7 +200,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     float wgt, lse2;
     if (MODE == MODE_ATTN) {
         float m = -INFINITY;
-        for (int c = tid; c <= k; c += DT) m = fmaxf(m, sc[c]);
+        for (int c = tid; c < kt; c += DT) m = fmaxf(m, sc[c]);
         m = wave_max(m);
         if (lane == 0) red[w] = m;
         __syncthreads();
@@ -183,7 +209,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         for (int i = 1; i < DNW; ++i) m = fmaxf(m, red[i]);
         __syncthreads();
         float z = 0.0f;
-        for (int c = tid; c <= k; c += DT) z += __builtin_amdgcn_exp2f(sc[c] - m);
+        for (int c = tid; c < kt; c += DT) z += __builtin_amdgcn_exp2f(sc[c] - m);
         z = wave_sum(z);
         if (lane == 0) red[w] = z;
         __syncthreads();
@@ -197,7 +223,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         wgt = 1.0f - P.mass_u[bh];
     }
     float psum = 0.0f;
-    for (int c = tid; c <= k; c += DT) {
+    for (int c = tid; c < kt; c += DT) {
         const float p = wgt * __builtin_amdgcn_exp2f(sc[c] - lse2);
         sc[c] = p;
         psum += p;
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 for (int l = 0; l < nlev; ++l) {
                     const int row = row_of(l, c);
                     if (row >= 0) {
-                        const SeqLevel L = seq_level<D>(C, l, b, 1);
+                        const SeqLevel L = seq_level<D>(P, l, b, 1);
                         const long rr = (long)row * H + h;
                         float x[16];
                         load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
@@ -228,6 +254,16 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                     }
                 }
             }
+        }
+    }
+    for (int t0 = 0; t0 < T; t0 += CPI) {
+        const int t = t0 + w * CPW + cl;
+        if (t < T) {
+            const float p = sc[k + t];
+            float x[16];
+            load_bf16x16(P.tail_v, tail_off(t) + cs * 16, x);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], p, acc[i]);
         }
     }
     // lanes with the same channel slice hold partial sums over different columns
@@ -246,12 +282,10 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     float ptot = 0.0f;
 #pragma unroll
     for (int i = 0; i < DNW; ++i) ptot += red[i];
-    const float pself = sc[k];
     for (int c = tid; c < D; c += DT) {
         float o = 0.0f;
 #pragma unroll
         for (int i = 0; i < DNW; ++i) o += ored[i][c];
-        o = fmaf(pself, bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.vself)[qo + c]), o);
         if (MODE == MODE_ATTN) {
             const float u = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.out_u[qo + c];
             P.out[qo + c] = o + u;
@@ -269,7 +303,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
 
 hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st) {
     const bool sp = P.sel != nullptr;
-    const size_t shm = (size_t)(P.k + 1) * sizeof(float) + (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
+    const size_t shm = (size_t)(P.k + P.n_tail) * sizeof(float) +
+                       (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
     dim3 grid(P.B * P.H);
     const bool l0 = P.level == 0;
 #define FL_DEC(D_, M_, S_, L_) hipLaunchKernelGGL((k_decode<D_, M_, S_, L_>), grid, dim3(DT), shm, st, P)

@@ -64,11 +64,24 @@ struct DecodeParams {
     int B, H, k, level, cache_op;
     float sm;
     fl_kv_cache cache;      // one sequence's geometry; level buffers hold B sequences
+    int pos_cap;            // per-sequence stride of slot maps and level-0 rows
+    int rows_cap[FL_MAX_LEVELS]; // per-sequence row stride of level l >= 1
     const int32_t* sel;     // [B*H][k] selected prefix columns, or NULL (all N)
     const void* q;          // bf16 [B][H][d]
-    const void* kself;      // bf16 [B][H][d] the token's own key / value
-    const void* vself;
+    const void* tail_k;     // bf16 [B][tail_cap][H][d]: the always-included columns
+    const void* tail_v;     //   (the token's own, and the generation window)
+    int n_tail, tail_cap;
     float* out; float* lse; float* mass_u; float* out_u; float* col_stat;
+};
+
+struct AppendParams {
+    int B, H, g, R, pos, slot, win_cap, pos_cap;
+    int rows_cap[FL_MAX_LEVELS];
+    int n_rows[FL_MAX_LEVELS];   // rows already stored per level (the new row's index)
+    int bits[FL_MAX_LEVELS];
+    fl_kv_level lev[FL_MAX_LEVELS];
+    const void* wk[FL_MAX_LEVELS];
+    const void* wv[FL_MAX_LEVELS];
 };
 
 // Kernels take the cache descriptor (and, on the in-tile path, the level
@@ -79,6 +92,8 @@ static_assert(sizeof(fl_kv_cache) + sizeof(QTiles) + 48 <= kKernargChecked,
               "k_gather_q arguments exceed the checked kernel-argument size");
 static_assert(sizeof(DecodeParams) + 16 <= kKernargChecked,
               "k_decode arguments exceed the checked kernel-argument size");
+static_assert(sizeof(AppendParams) <= kKernargChecked,
+              "k_decode_append arguments exceed the checked kernel-argument size");
 static_assert(sizeof(fl_kv_cache) + 64 <= kKernargChecked,
               "cache-descriptor kernels exceed the checked kernel-argument size");
 
@@ -106,6 +121,7 @@ hipError_t launch_copy_or_iota(const int32_t* src, int32_t* dst, long n, long ro
 // quant.hip
 hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float* out,
                           hipStream_t st);
+hipError_t launch_decode_append(int d, const AppendParams& P, hipStream_t st);
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
                         const void* v_new, int gathered, hipStream_t st);
 // attn.hip

@@ -307,6 +307,86 @@ hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float*
     return hipGetLastError();
 }
 
+// Generation-time append: the token in window slot P.slot (computed in all R
+// loops) becomes position P.pos of every sequence's cache.  One workgroup per
+// (sequence, K or V); a thread owns 8 channels per pass.  Level 0 quantises
+// the loop-1 value (row = position); level l >= 1 appends row n_rows[l] with
+// the residual of the loop-(l+1) value against the running dequantised value,
+// which is then updated with the level's own dequantised term -- the same
+// roundings, in the same order, as k_quant and its dequantisation chain.
+__global__ __launch_bounds__(256) void k_decode_append(AppendParams P, int D) {
+    const int b = blockIdx.x, which = blockIdx.y;
+    const int HD = P.H * D;
+    const int g = P.g;
+    for (int base = 0; base < HD; base += 256 * 8) {
+        const int ch = base + threadIdx.x * 8;
+        const bool live = ch < HD;
+        float xh[8];
+        for (int l = 0; l < P.R; ++l) {
+            const void* src = which ? P.wv[l] : P.wk[l];
+            float x[8];
+            if (live) {
+                load8_f32(src, ((long)b * P.win_cap + P.slot) * HD + ch, FL_BF16, x);
+                if (l > 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[i] = x[i] - xh[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+            for (int o = 1; o < g / 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            const int bits = P.bits[l];
+            const int qmax = (1 << (bits - 1)) - 1;
+            const float s = amax / (float)qmax;
+            uint64_t packed = 0;
+            int q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                q[i] = 0;
+                if (s != 0.0f) {
+                    float r = __builtin_rintf(x[i] / s);
+                    r = fminf(fmaxf(r, -(float)qmax), (float)qmax);
+                    q[i] = (int)r;
+                }
+                packed |= (uint64_t)((uint32_t)q[i] & ((1u << bits) - 1u)) << (bits * i);
+            }
+            if (live) {
+                const fl_kv_level& L = P.lev[l];
+                const long rows = l == 0 ? P.pos_cap : P.rows_cap[l];
+                const long row = l == 0 ? P.pos : P.n_rows[l];
+                uint8_t* codes = reinterpret_cast<uint8_t*>(which ? L.v_codes : L.k_codes) +
+                                 (long)b * (rows * HD * bits / 8);
+                float* scales = (which ? L.v_scale : L.k_scale) + (long)b * (rows * (HD / g));
+                const long e = row * HD + ch;
+                store_codes8(codes, e, bits, packed);
+                if ((ch % g) == 0) scales[e / g] = s;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float dq = (float)q[i] * s;
+                    xh[i] = l == 0 ? dq : xh[i] + dq;
+                }
+            }
+        }
+    }
+    if (which == 0 && threadIdx.x == 0) {
+        for (int l = 1; l < P.R; ++l) {
+            int32_t* rows = const_cast<int32_t*>(P.lev[l].rows) + (long)b * P.rows_cap[l];
+            int32_t* slot = const_cast<int32_t*>(P.lev[l].slot) + (long)b * P.pos_cap;
+            rows[P.n_rows[l]] = P.pos;
+            slot[P.pos] = P.n_rows[l];
+        }
+    }
+}
+
+hipError_t launch_decode_append(int d, const AppendParams& P, hipStream_t st) {
+    hipLaunchKernelGGL(k_decode_append, dim3(P.B, 2), dim3(256), 0, st, P, d);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
                         const void* v_new, int gathered, hipStream_t st) {
     QuantArgs a;

@@ -27,7 +27,7 @@ MAX_LEVELS = 32
 
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
-           "fl_sq_err", "fl_kv_dequant", "fl_workspace_size",
+           "fl_decode_append", "fl_sq_err", "fl_kv_dequant", "fl_workspace_size",
            "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
 FL_WS_BLOCK_STEP = 5
 FL_WS_SQ_ERR = 6
@@ -107,7 +107,13 @@ class FlBlockState(ctypes.Structure):
 
 class FlDecodeCfg(ctypes.Structure):
     _fields_ = [("B", c_int), ("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
-                ("n_sink", c_int), ("k_cols", c_int * MAX_LEVELS)]
+                ("n_sink", c_int), ("k_cols", c_int * MAX_LEVELS), ("N_cap", c_int),
+                ("rows_cap", c_int * MAX_LEVELS)]
+
+
+class FlDecodeWindow(ctypes.Structure):
+    _fields_ = [("cap", c_int), ("count", c_int), ("k", c_void_p * MAX_LEVELS),
+                ("v", c_void_p * MAX_LEVELS)]
 
 
 class FlDecodeState(ctypes.Structure):
@@ -119,7 +125,8 @@ class FlDecodeState(ctypes.Structure):
 
 class FlDecodeInputs(ctypes.Structure):
     _fields_ = [("q", c_void_p), ("k_self", c_void_p), ("v_self", c_void_p), ("q_prev", c_void_p),
-                ("k_self_prev", c_void_p), ("v_self_prev", c_void_p)]
+                ("k_self_prev", c_void_p), ("v_self_prev", c_void_p),
+                ("win", POINTER(FlDecodeWindow))]
 
 
 _lib = None
@@ -151,6 +158,8 @@ def lib():
         L.fl_decode_step.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
                                      POINTER(FlDecodeInputs), c_int, c_void_p]
         L.fl_sq_err.argtypes = [c_void_p, c_void_p, c_long, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.fl_decode_append.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
+                                       POINTER(FlDecodeWindow), c_int, c_void_p]
         L.fl_kv_dequant.argtypes = [POINTER(FlKvCache), c_int, c_int, c_void_p, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
@@ -268,6 +277,14 @@ def fl_decode_step(cfg: FlDecodeCfg, state: FlDecodeState, inputs: FlDecodeInput
     rc = lib().fl_decode_step(ctypes.byref(cfg), ctypes.byref(state), ctypes.byref(inputs), r,
                               _stream(stream))
     _check("fl_decode_step", rc)
+
+
+def fl_decode_append(cfg: FlDecodeCfg, state: FlDecodeState, win: FlDecodeWindow, slot,
+                     stream=None):
+    """Sec. 4.3 / App. E during generation: append the token in window slot
+    `slot` to every sequence's cache (cfg.N and the level row counts grow)."""
+    _check("fl_decode_append", lib().fl_decode_append(ctypes.byref(cfg), ctypes.byref(state),
+                                                      ctypes.byref(win), slot, _stream(stream)))
 
 
 def fl_kv_dequant(cache: FlKvCache, level, which, out, stream=None):
@@ -493,10 +510,15 @@ class DecodeRunner:
     sequence b's cache through the library (``fl_select_active`` on the given
     statistic, ``fl_kv_residual_quant`` per level); ``step`` runs loop r."""
 
-    def __init__(self, B, N, H, d, g, R, n_sink, n_active, k_cols, bits, device="cuda"):
+    def __init__(self, B, N, H, d, g, R, n_sink, n_active, k_cols, bits, gen_tokens=0, window=64,
+                 device="cuda"):
+        """gen_tokens > 0 prepares generation: caches with room for that many
+        appended positions and per-loop bf16 window rings of window + 1 slots
+        (the window and the token being decoded)."""
         dev = torch.device(device)
         self.B, self.N, self.H, self.d, self.g, self.R = B, N, H, d, g, R
         self.n_active, self.k_cols, self.bits = list(n_active), list(k_cols), list(bits)
+        self.gen_tokens, self.window = gen_tokens, window
         self._keep = []
 
         def buf(shape, dt):
@@ -508,6 +530,11 @@ class DecodeRunner:
         cfg.B, cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = B, N, H, d, g, R, n_sink
         for r in range(R):
             cfg.k_cols[r] = k_cols[r]
+        cap_pos = N + gen_tokens
+        if gen_tokens:
+            cfg.N_cap = cap_pos
+            for r in range(1, R):
+                cfg.rows_cap[r] = n_active[r] + gen_tokens
         self.cfg = cfg
         st = FlDecodeState()
         C = st.cache
@@ -515,12 +542,14 @@ class DecodeRunner:
         self.codes, self.rows, self.slot = [], [], []
         for r in range(R):
             n = N if r == 0 else n_active[r]
-            cb = dict(k=buf((B, n, H, d * bits[r] // 8), torch.uint8),
-                      v=buf((B, n, H, d * bits[r] // 8), torch.uint8),
-                      ks=buf((B, n, H, d // g), torch.float32),
-                      vs=buf((B, n, H, d // g), torch.float32))
-            rows = buf((B, n), torch.int32) if r > 0 else None
-            slot = buf((B, N), torch.int32) if r > 0 else None
+            nc = cap_pos if r == 0 else n + gen_tokens
+            cb = dict(k=buf((B, nc, H, d * bits[r] // 8), torch.uint8),
+                      v=buf((B, nc, H, d * bits[r] // 8), torch.uint8),
+                      ks=buf((B, nc, H, d // g), torch.float32),
+                      vs=buf((B, nc, H, d // g), torch.float32))
+            # row lists and slot maps start as -1 (no row) beyond what is filled
+            rows = buf((B, nc), torch.int32).fill_(-1) if r > 0 else None
+            slot = buf((B, cap_pos), torch.int32).fill_(-1) if r > 0 else None
             Lv = C.level[r]
             Lv.bits, Lv.n_rows = bits[r], n
             Lv.rows, Lv.slot = _p(rows), _p(slot)
@@ -532,12 +561,24 @@ class DecodeRunner:
         self.out_u = buf((B, H, d), torch.float32)
         st.out, st.lse, st.mass_u, st.out_u = _p(self.out), _p(self.lse), _p(self.mass_u), _p(self.out_u)
         self.sel, self.col_stat = [], []
+        # budgets with loop 1 at the largest context the cache can reach
+        kce = [cap_pos] + list(k_cols[1:])
         for r in range(R):
-            sl = buf((B, H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < min(k_cols[:r]) else None
-            cs = buf((B, H, min(k_cols[: r + 1])), torch.float32)
+            sl = buf((B, H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < min(kce[:r]) else None
+            cs = buf((B, H, min(kce[: r + 1])), torch.float32)
             st.sel[r], st.col_stat[r] = _p(sl), _p(cs)
             self.sel.append(sl); self.col_stat.append(cs)
         self.state = st
+        self.win = None
+        if gen_tokens:
+            wn = FlDecodeWindow()
+            wn.cap, wn.count = window + 1, 0
+            self.win_k = [buf((B, window + 1, H, d), torch.bfloat16) for _ in range(R)]
+            self.win_v = [buf((B, window + 1, H, d), torch.bfloat16) for _ in range(R)]
+            for r in range(R):
+                wn.k[r], wn.v[r] = _p(self.win_k[r]), _p(self.win_v[r])
+            self.win = wn
+            self.t = 0
 
     def seq_cache(self, b):
         """FlKvCache of sequence b alone (pointers into the batched buffers)."""
@@ -546,7 +587,7 @@ class DecodeRunner:
         for r in range(self.R):
             Lv = c.level[r]
             cb = self.codes[r]
-            Lv.bits, Lv.n_rows = self.bits[r], cb["k"].shape[1]
+            Lv.bits, Lv.n_rows = self.bits[r], (self.N if r == 0 else self.n_active[r])
             Lv.rows = None if r == 0 else _p(self.rows[r][b])
             Lv.slot = None if r == 0 else _p(self.slot[r][b])
             Lv.k_codes, Lv.v_codes = _p(cb["k"][b]), _p(cb["v"][b])
@@ -559,7 +600,8 @@ class DecodeRunner:
         c = self.seq_cache(b)
         for r in range(self.R):
             if r > 0:
-                cand = None if r == 1 else self.rows[r - 1][b]
+                # the previous loop's active rows (the buffer may have room for more)
+                cand = None if r == 1 else self.rows[r - 1][b][: self.n_active[r - 1]]
                 key = stat[r] if cand is None else stat[r].index_select(0, cand.long())
                 fl_select_active(None, None, cand, self.n_active[r], None, self.rows[r][b],
                                  self.slot[r][b], stat_in=key, N=self.N, stream=stream)
@@ -572,12 +614,38 @@ class DecodeRunner:
         inp.q_prev, inp.k_self_prev, inp.v_self_prev = _p(q_prev), _p(k_prev), _p(v_prev)
         fl_decode_step(self.cfg, self.state, inp, r, stream)
 
+    def generate(self, q, k, v, stream=None, after_loop=None):
+        """Decode the next generated token of every sequence through all R
+        loops.  q, k, v: lists of R bf16 device tensors [B][H][d].  The ring
+        slot of the oldest window token is appended to the cache first (once
+        the window is full), then overwritten with this token's K/V."""
+        win, t = self.win, self.t
+        slot = t % win.cap
+        if t >= win.cap:
+            fl_decode_append(self.cfg, self.state, win, slot, stream)
+        for r in range(self.R):
+            self.win_k[r][:, slot].copy_(k[r])
+            self.win_v[r][:, slot].copy_(v[r])
+        win.count = min(t + 1, win.cap)
+        inp = FlDecodeInputs()
+        inp.win = ctypes.pointer(win)
+        for r in range(1, self.R + 1):
+            inp.q = _p(q[r - 1])
+            inp.q_prev = _p(q[r - 2]) if r > 1 else None
+            fl_decode_step(self.cfg, self.state, inp, r, stream)
+            if after_loop is not None:
+                after_loop(r)
+        self.t = t + 1
+
     def k_used(self, r):
         return self.state.k_cur[r - 1]
 
     def sel_used(self, r):
         """Selected prefix columns of loop r ([B][H][k]) or None (dense)."""
-        for j in range(r, 0, -1):
-            if self.sel[j - 1] is not None and self.k_cols[j - 1] < min(self.k_cols[: j - 1] or [self.N]):
-                return self.sel[j - 1]
-        return None
+        p = self.state.sel_used[r - 1]
+        if not p:
+            return None
+        for t in self.sel:
+            if t is not None and t.data_ptr() == p:
+                return t
+        raise RuntimeError("unknown selection buffer")

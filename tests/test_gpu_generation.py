@@ -1,0 +1,133 @@
+"""GPU parity of generation-time decode (App. E's bf16 window of recent
+tokens, cache appends; Sec. 4.2 per-token column re-selection) against the
+generation oracle: for every generated token and loop, the column sets
+exactly (given the GPU's own statistics), outputs / lse / cached mass and
+partial output within rel-L2 1e-2 and max-abs 3e-2; every appended token's
+cache rows (codes, scales, row lists, slot maps) bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import decode as od
+from sparse_attention_kv_amd import fl, synth
+
+from gpu_chain import assert_close, assert_close_scaled, counts, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(B, N, H, d, g, kcols, bits, rho, seed):
+    w = synth.WORKLOADS["decode64x8k"].scaled(N=N, H=H, d=d, g=g, R=len(kcols), kcols=list(kcols),
+                                              bits=list(bits), rho=list(rho), seed=seed)
+    w.extra = dict(B=B)
+    return w
+
+
+def _run_gpu(w, n_gen, window):
+    B, N, H, d, R = w.extra["B"], w.N, w.H, w.d, w.R
+    n_act = counts(w)
+    run = fl.DecodeRunner(B, N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
+                          gen_tokens=n_gen, window=window)
+    xs = {}
+    tok = {key: np.empty((n_gen, R, B, H, d), np.uint16) for key in ("gen_q", "gen_k", "gen_v")}
+    for b in range(B):
+        x = synth.gen_decode_seq(w, b, n_gen=n_gen)
+        k = [to_dev(a, "bf16") for a in x["k"]]
+        v = [to_dev(a, "bf16") for a in x["v"]]
+        st = [None] + [torch.from_numpy(s).cuda() for s in x["stat"][1:]]
+        run.load_sequence(b, k, v, st)
+        for key in tok:
+            for t in range(n_gen):
+                for r in range(R):
+                    tok[key][t, r, b] = x[key][t][r]
+        xs[b] = x
+    torch.cuda.synchronize()
+    G = []
+    for t in range(n_gen):
+        recs = []
+
+        def after(r):
+            torch.cuda.synchronize()
+            kk = run.k_used(r)
+            sel = run.sel_used(r)
+            need_c = r < R and w.kcols[r] < kk
+            recs.append(dict(k=kk, sel=None if sel is None else sel.cpu().numpy(),
+                             out=run.out.cpu().numpy(), lse=run.lse.cpu().numpy(),
+                             mass_u=run.mass_u.cpu().numpy(), out_u=run.out_u.cpu().numpy(),
+                             # written compactly as [B*H][k] (the buffer is sized for the
+                             # largest context the cache can reach)
+                             cstat=run.col_stat[r - 1].reshape(-1)[:B * H * kk].reshape(B, H, kk)
+                             .cpu().numpy() if need_c else None))
+
+        dv = {key: [to_dev(tok[key][t, r], "bf16") for r in range(R)] for key in tok}
+        run.generate(dv["gen_q"], dv["gen_k"], dv["gen_v"], after_loop=after)
+        G.append(dict(recs=recs, N=run.cfg.N, count=run.win.count))
+    torch.cuda.synchronize()
+    return G, xs, run
+
+
+def _check(w, b, x, G, run, window):
+    sched = w.sched()
+    f = synth.bf16_bits_to_f32
+    cache = od.build_cache([f(a) for a in x["k"]], [f(a) for a in x["v"]], x["stat"], sched)
+    gq = [[f(a) for a in tt] for tt in x["gen_q"]]
+    gk = [[f(a) for a in tt] for tt in x["gen_k"]]
+    gv = [[f(a) for a in tt] for tt in x["gen_v"]]
+    ov = {t: {("cstat", r): G[t]["recs"][r - 2]["cstat"][b] for r in range(2, w.R + 1)
+              if G[t]["recs"][r - 2]["cstat"] is not None} for t in range(len(G))}
+    ores = od.run_generation(cache, gq, gk, gv, sched, window=window, override=ov)
+    n_act = counts(w)
+    worst = 0.0
+    for t, (g, o) in enumerate(zip(G, ores)):
+        assert g["N"] == o["N"] and g["count"] == o["T"], (t, g["N"], o["N"], g["count"], o["T"])
+        for r in range(1, w.R + 1):
+            gr, orr = g["recs"][r - 1], o["recs"][r - 1]
+            assert gr["k"] == orr["k"], (t, r)
+            if orr["sel"] is None:
+                assert gr["sel"] is None
+            else:
+                np.testing.assert_array_equal(gr["sel"][b], orr["sel"], err_msg=f"token {t} loop {r}")
+            e = assert_close(gr["out"][b], orr["out"], f"token {t} loop {r} out")
+            worst = max(worst, e[0])
+            assert_close(gr["lse"][b], orr["lse"], f"token {t} loop {r} lse")
+            assert_close(gr["mass_u"][b], orr["mass_u"], f"token {t} loop {r} mass_u")
+            assert_close(gr["out_u"][b], orr["out_u"], f"token {t} loop {r} out_u",
+                         ref_norm=float(np.linalg.norm(orr["out"])))
+            if orr["cstat"] is not None:
+                assert_close_scaled(gr["cstat"][b], orr["cstat"], f"token {t} loop {r} cstat")
+        app = o["appended"]
+        if app is not None:
+            u = o["N"] - w.N - 1                  # index of the appended token
+            pos = w.N + u
+            for r in range(1, w.R + 1):
+                row = pos if r == 1 else n_act[r - 1] + u
+                cb = run.codes[r - 1]
+                for kv in ("k", "v"):
+                    np.testing.assert_array_equal(
+                        cb[kv][b, row].cpu().numpy(),
+                        oracle.pack_codes(app[r - 1][kv + "_codes"], w.bits[r - 1])[0],
+                        err_msg=f"token {t}: appended {kv} codes, level {r - 1}")
+                    np.testing.assert_array_equal(
+                        cb[kv + "s"][b, row].cpu().numpy().view(np.uint32),
+                        app[r - 1][kv + "_scale"][0].view(np.uint32))
+                if r > 1:
+                    assert int(run.rows[r - 1][b, row]) == pos
+                    assert int(run.slot[r - 1][b, pos]) == row
+    print(f"  seq {b}: {len(G)} tokens, {G[-1]['N'] - w.N} appended, worst out rel-L2 {worst:.2e}",
+          flush=True)
+
+
+@pytest.mark.parametrize("name,B,N,H,d,g,kcols,bits,rho,n_gen,window", [
+    ("small_window", 2, 300, 2, 128, 64, (300, 96, 64), (8, 4, 2), (1.0, 0.4, 0.2), 14, 4),
+    ("window64", 2, 257, 2, 128, 64, (257, 100, 60, 60), (8, 4, 4, 2), (1.0, 0.5, 0.25, 0.1), 70, 64),
+    ("d64_g32", 3, 411, 3, 64, 32, (411, 128, 128), (8, 2, 4), (1.0, 0.3, 0.3), 12, 6),
+    # no window: every earlier generated token is appended before the next one
+    ("no_window", 2, 200, 2, 128, 64, (200, 80, 48), (8, 4, 2), (1.0, 0.4, 0.2), 6, 0),
+])
+def test_generation_matches_oracle(name, B, N, H, d, g, kcols, bits, rho, n_gen, window):
+    w = _w(B, N, H, d, g, kcols, bits, rho, seed=21)
+    print("generation", name, w.sched(), "B", B, "tokens", n_gen, "window", window, flush=True)
+    G, xs, run = _run_gpu(w, n_gen, window)
+    for b in range(B):
+        _check(w, b, xs[b], G, run, window)
