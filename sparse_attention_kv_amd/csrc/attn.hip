@@ -40,6 +40,14 @@ __device__ __forceinline__ int vt_key_of_slot(int so) {
 // Compact gather + dequantisation of the selected columns (levels 0..upto).
 // With X3 (fp32 inputs) a second "lo" copy holds the bf16 rounding of
 // x - bf16(x), so that products can be formed as hi*hi + hi*lo + lo*hi.
+// One thread per 8 channels of a column (D/8 threads per column), so a
+// workgroup covers GC = 2048/D columns -- one or two of the 16-key groups of
+// the transposed V tile, which it writes on its own; a column's dequantisation
+// chain walks the levels in order, stopping at the first one the token is
+// absent from (the sets are nested).
+template <int D>
+constexpr int gather_cols() { return 256 / (D / 8); }
+
 template <int D, bool X3>
 __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      const int32_t* __restrict__ sel, int k,
@@ -49,97 +57,80 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      __bf16* __restrict__ Vt_lo,
                                                      int32_t* __restrict__ cpos,
                                                      float* __restrict__ vnorm) {
-    __shared__ __bf16 sV[X3 ? 2 : 1][BN][D + 8];
+    constexpr int TPC = D / 8;            // threads per column
+    constexpr int GC = gather_cols<D>();  // columns per workgroup (16 or 32)
+    __shared__ __bf16 sV[X3 ? 2 : 1][GC][D + 8];
     const int h = blockIdx.y;
-    const int p0 = blockIdx.x * BN;
+    const int p0 = blockIdx.x * GC;
     const int tid = threadIdx.x;
-    const int col = tid >> 2;                 // 0..63
-    constexpr int CPT = D / 4;                // channels per thread
-    const int c0 = (tid & 3) * CPT;
+    const int col = tid / TPC;
+    const int c0 = (tid % TPC) * 8;
     const int p = p0 + col;
     const bool live = p < k;
     const long j = live ? (sel ? (long)sel[(long)h * k + p] : (long)p) : 0;
-    if ((tid & 3) == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
+    if (c0 == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
     const int HD = c.H * D;
+    const int ch = h * D + c0;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        float x[CPT];
+        float x[8];
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) x[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
         if (live && c.scheme == FL_QUANT_ASYM) {
             // asymmetric levels: code*s + z per element, summed in level order
-#pragma unroll
-            for (int e8 = 0; e8 < CPT; e8 += 8)
-                deq8_asym(c.level[0], which, j, HD, h * D + c0 + e8, c.g, x + e8);
+            deq8_asym(c.level[0], which, j, HD, ch, c.g, x);
             for (int l = 1; l <= upto; ++l) {
                 const int sl = c.level[l].slot[j];
                 if (sl < 0) break;
+                float t[8];
+                deq8_asym(c.level[l], which, sl, HD, ch, c.g, t);
 #pragma unroll
-                for (int e8 = 0; e8 < CPT; e8 += 8) {
-                    float t[8];
-                    deq8_asym(c.level[l], which, sl, HD, h * D + c0 + e8, c.g, t);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[e8 + i] += t[i];
-                }
+                for (int i = 0; i < 8; ++i) x[i] += t[i];
             }
         } else if (live) {
-            // base level
             const fl_kv_level& L0 = c.level[0];
-            const long e0 = j * HD + (long)h * D + c0;
+            const long e0 = j * HD + ch;
             const void* codes = which ? L0.v_codes : L0.k_codes;
             if (L0.bits == 32) {
                 const float* src = reinterpret_cast<const float*>(codes) + e0;
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) x[e] = src[e];
+                for (int e = 0; e < 8; ++e) x[e] = src[e];
             } else {
-                const float* sc = which ? L0.v_scale : L0.k_scale;
+                const float s = (which ? L0.v_scale : L0.k_scale)[e0 / c.g];
+                const uint64_t w = load_codes8(codes, e0, 8);
 #pragma unroll
-                for (int e8 = 0; e8 < CPT; e8 += 8) {
-                    const float s = sc[(e0 + e8) / c.g];
-                    const uint64_t w = load_codes8(codes, e0 + e8, 8);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[e8 + i] = (float)code_at(w, 8, i) * s;
-                }
+                for (int i = 0; i < 8; ++i) x[i] = (float)code_at(w, 8, i) * s;
             }
             for (int l = 1; l <= upto; ++l) {
                 const fl_kv_level& L = c.level[l];
                 const int sl = L.slot[j];
                 if (sl < 0) break;
-                const long el = (long)sl * HD + (long)h * D + c0;
+                const long el = (long)sl * HD + ch;
                 const void* cl = which ? L.v_codes : L.k_codes;
                 if (L.bits == 32) {
                     const float* src = reinterpret_cast<const float*>(cl) + el;
 #pragma unroll
-                    for (int e = 0; e < CPT; ++e) x[e] += src[e];
+                    for (int e = 0; e < 8; ++e) x[e] += src[e];
                 } else {
-                    const float* sc = which ? L.v_scale : L.k_scale;
+                    const float s = (which ? L.v_scale : L.k_scale)[el / c.g];
+                    const uint64_t w = load_codes8(cl, el, L.bits);
 #pragma unroll
-                    for (int e8 = 0; e8 < CPT; e8 += 8) {
-                        const float s = sc[(el + e8) / c.g];
-                        const uint64_t w = load_codes8(cl, el + e8, L.bits);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) x[e8 + i] += (float)code_at(w, L.bits, i) * s;
-                    }
+                    for (int i = 0; i < 8; ++i) x[i] += (float)code_at(w, L.bits, i) * s;
                 }
             }
         }
         if (which == 0) {
-            __bf16* dst = Kc + ((long)h * kp + p) * D + c0;
-            __bf16* dlo = X3 ? Kc_lo + ((long)h * kp + p) * D + c0 : nullptr;
+            bf16x8 v, vl;
 #pragma unroll
-            for (int e8 = 0; e8 < CPT; e8 += 8) {
-                bf16x8 v, vl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    v[i] = (__bf16)x[e8 + i];
-                    if (X3) vl[i] = (__bf16)(x[e8 + i] - (float)v[i]);
-                }
-                *reinterpret_cast<bf16x8*>(dst + e8) = v;
-                if (X3) *reinterpret_cast<bf16x8*>(dlo + e8) = vl;
+            for (int i = 0; i < 8; ++i) {
+                v[i] = (__bf16)x[i];
+                if (X3) vl[i] = (__bf16)(x[i] - (float)v[i]);
             }
+            *reinterpret_cast<bf16x8*>(Kc + ((long)h * kp + p) * D + c0) = v;
+            if (X3) *reinterpret_cast<bf16x8*>(Kc_lo + ((long)h * kp + p) * D + c0) = vl;
         } else {
 #pragma unroll
-            for (int e = 0; e < CPT; ++e) {
+            for (int e = 0; e < 8; ++e) {
                 const __bf16 hi = (__bf16)x[e];
                 sV[0][col][c0 + e] = hi;
                 if (X3) sV[X3 ? 1 : 0][col][c0 + e] = (__bf16)(x[e] - (float)hi);
@@ -147,25 +138,27 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
             if (vnorm) { // ||vhat(j)||_2 in fp32 for the value-weighted column statistic
                 float ss = 0.0f;
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) ss = ss + x[e] * x[e];
-                ss = ss + __shfl_xor(ss, 1);
-                ss = ss + __shfl_xor(ss, 2);
-                if ((tid & 3) == 0) vnorm[(long)h * kp + p] = sqrtf(ss);
+                for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
+#pragma unroll
+                for (int o = 1; o < TPC; o <<= 1) ss = ss + __shfl_xor(ss, o);
+                if (c0 == 0) vnorm[(long)h * kp + p] = sqrtf(ss);
             }
         }
     }
     __syncthreads();
-    // transpose the V tile: rows d, 64 keys in permuted order, 16-byte stores
+    // transpose this workgroup's columns of the V tile: rows d, its GC keys
+    // (whole 16-key groups, key order permuted inside each group), 16-byte stores
+    const int tile = p0 / BN, kbase = p0 % BN;
 #pragma unroll
     for (int part = 0; part < (X3 ? 2 : 1); ++part) {
-        __bf16* vdst = (part ? Vt_lo : Vt) + ((long)h * (kp / BN) + blockIdx.x) * D * BN;
-        for (int idx = tid; idx < D * (BN / 8); idx += 256) {
-            const int dd = idx / (BN / 8);
-            const int oct = idx % (BN / 8);
+        __bf16* vdst = (part ? Vt_lo : Vt) + ((long)h * (kp / BN) + tile) * D * BN + kbase;
+        for (int idx = tid; idx < D * (GC / 8); idx += 256) {
+            const int dd = idx / (GC / 8);
+            const int oct = idx % (GC / 8);
             bf16x8 v;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int so = oct * 8 + i;                      // stored position in tile
+                const int so = oct * 8 + i;                      // stored position in the group(s)
                 const int key = (so & ~15) + vt_key_of_slot(so & 15);
                 v[i] = sV[part][key][dd];
             }
@@ -1229,7 +1222,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
                               int32_t* cpos, float* vnorm, hipStream_t st) {
-    dim3 grid(kp / BN, c.H);
+    dim3 grid(kp / (c.d == 128 ? gather_cols<128>() : gather_cols<64>()), c.H);
 #define FL_GATHER(D_, X_)                                                                       \
     hipLaunchKernelGGL((k_gather_bf16<D_, X_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
                        Vt, Kc_lo, Vt_lo, cpos, vnorm)
