@@ -32,8 +32,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
 KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn<128, 0, 1, false>",
-                 "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0>",
-                 "colstat_split": "k_colstat_lds<128, 1>", "decode_dense": "k_decode<128, 0, false, true>",
+                 "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 8>",
+                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true>",
                  "decode": "k_decode<128, 0, true, false>", "decode_rebuild": "k_decode<128, 1, true, true>"}
 # projections of the 2048-hidden block: epilogue (0 store, 1 residual, 2 SwiGLU)
 # and tile width; o and down share one instantiation, so only the others are

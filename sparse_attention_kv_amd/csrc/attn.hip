@@ -919,152 +919,36 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
         P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
 }
 
-// Column statistics for bf16 queries (PREC 0/1): 64-row steps through a
-// two-buffer LDS pipeline (the next rows are loaded into registers while the
-// current ones are used), each wave covering its 32 columns for both 32-row
-// halves of a step; steps run from the last row down to the diagonal.  The weight 1 - M_U is folded into a per-row exponent
-// offset (off = lse*log2(e) - log2(1 - M_U)), so a pair costs one fma, one
-// exp2 and one add; the causal mask is only applied on diagonal steps.
+// Column statistics for bf16 queries (PREC 0/1): the query rows are swept
+// in 64-row steps from the last row down to the block's diagonal, each wave
+// covering its 32 columns for both 32-row halves of a step (steps from the
+// bottom keep the column blocks of a head on the same query rows in L2).  The
+// weight 1 - M_U is folded into a per-row exponent offset (off = lse*log2(e)
+// - log2(1 - M_U)), so a pair costs one fma, one exp2 and one add; the causal
+// mask is only applied on diagonal steps.
 constexpr int RT2 = 64;
-
-template <int D, int PREC>
-__global__ __launch_bounds__(256, 2) void k_colstat_pipe(ColParams P) {
-    constexpr bool X3 = PREC >= 1;
-    constexpr int CHQ = (RT2 * D / 8) / 256; // 16-byte chunks per thread per step
-    __shared__ __bf16 Qs[2][RT2][D + 8];
-    __shared__ int rpos[2][RT2];
-    __shared__ float roff[2][RT2];
-    __shared__ int s_start, s_cmax;
-    const int h = blockIdx.y;
-    const int pc0 = blockIdx.x * CT;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r = lane & 31, half = lane >> 5;
-    const int p = pc0 + w * 32 + r;
-    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    const bool colv = p < P.k;
-    const int cp = colv ? cpos_h[p] : 0x7fffffff;
-    bf16x8 kf[D / 16], kl[X3 ? D / 16 : 1];
-    {
-        const long ko = ((long)h * P.kp + (colv ? p : 0)) * D + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(P.Kc + ko + 16 * kk);
-            if (X3) kl[X3 ? kk : 0] = *reinterpret_cast<const bf16x8*>(P.Kc_lo + ko + 16 * kk);
-        }
-    }
-    if (tid == 0) {
-        s_start = lower_bound_i32(P.active, P.n, cpos_h[pc0]);
-        s_cmax = cpos_h[min(pc0 + CT, P.k) - 1];
-    }
-    __syncthreads();
-    const int t_start = __builtin_amdgcn_readfirstlane(s_start);
-    const int cmax = __builtin_amdgcn_readfirstlane(s_cmax);
-    uint4 qr[CHQ];
-    int pr = -1;
-    float orr = 0.0f;
-    auto gload = [&](int t0) {
-#pragma unroll
-        for (int m = 0; m < CHQ; ++m) {
-            const int idx = tid + m * 256;
-            const int rr = idx / (D / 8), c8 = idx % (D / 8);
-            const int t = t0 + rr;
-            if (t < P.n) {
-                const long qrow = P.q_gathered ? (long)t : (long)P.active[t];
-                qr[m] = *reinterpret_cast<const uint4*>(
-                    reinterpret_cast<const uint16_t*>(P.q) + (qrow * P.H + h) * D + c8 * 8);
-            } else {
-                qr[m] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        if (tid < RT2) {
-            const int t = t0 + tid;
-            if (t < P.n) {
-                const int pos = P.active[t];
-                const long rh = (long)pos * P.H + h;
-                pr = pos;
-                const float wgt = P.cache_op == FL_CACHE_ZERO ? 1.0f : fmaxf(1.0f - P.mass_u[rh], 0.0f);
-                orr = P.lse[rh] * 1.4426950408889634f - __log2f(wgt); // wgt 0 -> +inf -> P 0
-            } else {
-                pr = -1; orr = INFINITY;
-            }
-        }
-    };
-    auto lstore = [&](int bb) {
-#pragma unroll
-        for (int m = 0; m < CHQ; ++m) {
-            const int idx = tid + m * 256;
-            const int rr = idx / (D / 8), c8 = idx % (D / 8);
-            *reinterpret_cast<uint4*>(&Qs[bb][rr][c8 * 8]) = qr[m];
-        }
-        if (tid < RT2) { rpos[bb][tid] = pr; roff[bb][tid] = orr; }
-    };
-    // the steps are taken from the last one down to the block's diagonal, so
-    // every block of a head starts on the same rows: blocks resident together
-    // on one XCD then read each query step once through its L2
-    const int nsteps = t_start < P.n ? (P.n - t_start + RT2 - 1) / RT2 : 0;
-    const int t_last = t_start + (nsteps - 1) * RT2;
-    if (nsteps > 0) {
-        gload(t_last);
-        lstore(0);
-    }
-    __syncthreads();
-    float csum = 0.0f;
-    for (int it = 0; it < nsteps; ++it) {
-        const int t0 = t_last - it * RT2;
-        const int b = it & 1;
-        const bool more = it + 1 < nsteps;
-        if (more) gload(t0 - RT2);
-        // every row of the step at or after every column of the block?
-        const bool full = rpos[b][0] >= cmax && t0 + RT2 <= P.n;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            f32x16 s = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qs[b][32 * sub + r][16 * kk + 8 * half]);
-                s = mfma32(a, kf[kk], s);
-                if (X3) s = mfma32(a, kl[X3 ? kk : 0], s);
-            }
-            if (full) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int row = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
-                    csum += __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[b][row]));
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int row = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
-                    const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[b][row]));
-                    csum += (rpos[b][row] >= cp) ? pj : 0.0f;
-                }
-            }
-        }
-        if (more) lstore(b ^ 1);
-        __syncthreads();
-    }
-    csum += __shfl_xor(csum, 32);
-    if (colv && half == 0)
-        P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
-}
 
 // Column statistics with the Q steps copied by LDS-DMA into two distinct LDS
 // buffers (swizzled as in k_attn_lds): one barrier per 64-row step, the next
 // step's rows land while the current one is computed.  The per-row exponent
 // offsets and positions are prefetched through registers by one wave.
-// Arithmetic as k_colstat_pipe.
-template <int D, int PREC>
-__global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
+// NW waves per workgroup, 32 columns each: every query tile copied into LDS
+// feeds 32 * NW columns, so the queries are streamed from memory
+// k / (32 * NW) times per head.
+template <int D, int PREC, int NW>
+__global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
     constexpr bool X3 = PREC >= 1;
+    constexpr int CTW = 32 * NW;             // columns per workgroup
     constexpr int QB = RT2 * D * 2;         // bytes of one step's query rows
-    constexpr int MPW = QB / 1024 / 4;      // LDS-DMA instructions per wave per step
+    constexpr int MPW = QB / 1024 / NW;     // LDS-DMA instructions per wave per step
+    static_assert(MPW >= 1 && QB % (1024 * NW) == 0, "step copy split over the waves");
     __shared__ __attribute__((aligned(1024))) __bf16 sQ0[RT2 * D];
     __shared__ __attribute__((aligned(1024))) __bf16 sQ1[RT2 * D];
     __shared__ int rp0[RT2], rp1[RT2];
     __shared__ float ro0[RT2], ro1[RT2];
     __shared__ int s_start, s_cmax;
     const int h = blockIdx.y;
-    const int pc0 = blockIdx.x * CT;
+    const int pc0 = blockIdx.x * CTW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
@@ -1083,7 +967,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
     }
     if (tid == 0) {
         s_start = lower_bound_i32(P.active, P.n, cpos_h[pc0]);
-        s_cmax = cpos_h[min(pc0 + CT, P.k) - 1];
+        s_cmax = cpos_h[min(pc0 + CTW, P.k) - 1];
     }
     __syncthreads();
     const int t_start = __builtin_amdgcn_readfirstlane(s_start);
@@ -1190,7 +1074,7 @@ __global__ __launch_bounds__(256, 2) void k_colstat_lds(ColParams P) {
             if (w == 0) meta_pos(t_last - RT2);
         }
     }
-    // steps from the last one down to the block's diagonal (see k_colstat_pipe);
+    // steps from the last one down to the block's diagonal;
     // iteration it computes step it, copies step it+1, loads positions of it+2
     for (int it = 0; it < nsteps;) {
 #pragma unroll
@@ -1274,17 +1158,23 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
     return hipGetLastError();
 }
 
+// waves per workgroup of the LDS-DMA column statistics: 8 (256 columns) with
+// plain bf16 keys; hi/lo keys take more registers, so 4 keep 3 waves per SIMD
+template <int PREC>
+constexpr int colstat_waves() { return PREC == 0 ? 8 : 4; }
+
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
-    dim3 grid((P.k + CT - 1) / CT, P.H);
+    const dim3 grid((P.k + CT - 1) / CT, P.H);
 #define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
-#define FL_COLP(D_, P_) hipLaunchKernelGGL((k_colstat_pipe<D_, P_>), grid, dim3(256), 0, st, P)
-#define FL_COLL(D_, P_) hipLaunchKernelGGL((k_colstat_lds<D_, P_>), grid, dim3(256), 0, st, P)
+#define FL_COLL(D_, P_)                                                                    \
+    hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>()>),                       \
+                       dim3((P.k + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>()), P.H), \
+                       dim3(64 * colstat_waves<P_>()), 0, st, P)
 #define FL_COL_D(D_) \
     if (prec == 0) FL_COLL(D_, 0); else if (prec == 1) FL_COLL(D_, 1); else FL_COL(D_, 2);
     if (d == 128) { FL_COL_D(128) } else { FL_COL_D(64) }
 #undef FL_COL_D
 #undef FL_COLL
-#undef FL_COLP
 #undef FL_COL
     return hipGetLastError();
 }
