@@ -828,6 +828,23 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
 constexpr int CT = 128; // columns per workgroup (4 waves x 32)
 constexpr int RT = 32;  // query rows per step
 
+// Column block and head of this workgroup (one-dimensional grid of n_blk * H
+// blocks).  The first columns of a head are seen by the most query rows, so
+// blocks are started heaviest first with the heads interleaved; when H is a
+// multiple of 8 each head's blocks stay on one XCD (workgroups are dealt to
+// the 8 XCDs round-robin), so its query rows stream through one L2.
+__device__ __forceinline__ void col_coords(int H, int& blk, int& h) {
+    const int b = blockIdx.x;
+    if ((H & 7) == 0) {
+        const int x = b & 7, m = b >> 3, hp = H >> 3;
+        h = x + 8 * (m % hp);
+        blk = m / hp;
+    } else {
+        h = b % H;
+        blk = b / H;
+    }
+}
+
 template <int D, int PREC>
 __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
     constexpr bool X3 = PREC >= 1;  // keys as hi + lo
@@ -837,8 +854,9 @@ __global__ __launch_bounds__(256, 2) void k_colstat(ColParams P) {
     __shared__ int rpos[RT];
     __shared__ float rlse[RT], rw[RT];
     __shared__ int s_start;
-    const int h = blockIdx.y;
-    const int pc0 = blockIdx.x * CT;
+    int blk, h;
+    col_coords(P.H, blk, h);
+    const int pc0 = blk * CT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 31, half = lane >> 5;
     const int p = pc0 + w * 32 + r; // this lane's column (slot in the selection)
@@ -947,8 +965,9 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
     __shared__ int rp0[RT2], rp1[RT2];
     __shared__ float ro0[RT2], ro1[RT2];
     __shared__ int s_start, s_cmax;
-    const int h = blockIdx.y;
-    const int pc0 = blockIdx.x * CTW;
+    int blk, h;
+    col_coords(P.H, blk, h);
+    const int pc0 = blk * CTW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
@@ -1164,11 +1183,12 @@ template <int PREC>
 constexpr int colstat_waves() { return PREC == 0 ? 8 : 4; }
 
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
-    const dim3 grid((P.k + CT - 1) / CT, P.H);
+    // one-dimensional grids of column blocks x heads (see col_coords)
+    const dim3 grid(((P.k + CT - 1) / CT) * P.H);
 #define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
-#define FL_COLL(D_, P_)                                                                    \
-    hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>()>),                       \
-                       dim3((P.k + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>()), P.H), \
+#define FL_COLL(D_, P_)                                                                        \
+    hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>()>),                           \
+                       dim3(((P.k + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>())) * P.H), \
                        dim3(64 * colstat_waves<P_>()), 0, st, P)
 #define FL_COL_D(D_) \
     if (prec == 0) FL_COLL(D_, 0); else if (prec == 1) FL_COLL(D_, 1); else FL_COL(D_, 2);
