@@ -13,7 +13,10 @@
 //                order.  The result is unique given the keys, so it matches any
 //                correct selector bit for bit.
 //  k_topk_res    the same for segments of up to 32K candidates, held in
-//                registers (contiguous runs per thread).
+//                registers (contiguous runs of a multiple of 4 per thread,
+//                read with 16-byte loads); 256-thread workgroups when many
+//                segments of up to 8K candidates fill the GPU (the decode's
+//                per-(sequence, head) column selections), 1024 otherwise.
 #include "fl_device.h"
 #include "fl_kernels.h"
 
@@ -78,8 +81,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-// Exclusive block scan of v (0/1 or small counts) over 1024 threads; returns
-// the exclusive prefix and stores the block total in *total.
+// Exclusive block scan of v (0/1 or small counts) over the NW waves of the
+// workgroup; returns the exclusive prefix and stores the block total in *total.
+template <int NW = kSelWaves>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int incl = v;
@@ -91,19 +95,19 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
     if (lane == 63) s_wave[w] = incl;
     __syncthreads();
     if (w == 0) {
-        int x = lane < kSelWaves ? s_wave[lane] : 0;
+        int x = lane < NW ? s_wave[lane] : 0;
         int xi = x;
 #pragma unroll
-        for (int o = 1; o < kSelWaves; o <<= 1) {
+        for (int o = 1; o < NW; o <<= 1) {
             const int y = __shfl_up(xi, o);
             if (lane >= o) xi += y;
         }
-        if (lane < kSelWaves) s_wave[kSelWaves + lane] = xi - x;
-        if (lane == kSelWaves - 1) s_wave[2 * kSelWaves] = xi;
+        if (lane < NW) s_wave[NW + lane] = xi - x;
+        if (lane == NW - 1) s_wave[2 * NW] = xi;
     }
     __syncthreads();
-    const int r = s_wave[kSelWaves + w] + incl - v;
-    *total = s_wave[2 * kSelWaves];
+    const int r = s_wave[NW + w] + incl - v;
+    *total = s_wave[2 * NW];
     __syncthreads();
     return r;
 }
@@ -218,12 +222,14 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(
 // instead of two per 1024 candidates.
 constexpr int kRes = 32;
 
-__global__ __launch_bounds__(kSelThreads) void k_topk_res(
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_res(
     const float* __restrict__ keys, long key_stride, const int32_t* __restrict__ pos,
     long pos_stride, int n, int n_sel, int n_prefix, int32_t* __restrict__ out,
     long out_stride, int32_t* __restrict__ slot, int n_slot) {
     __shared__ int s_hist[256];
-    __shared__ int s_wave[2 * kSelWaves + 1];
+    constexpr int NW = NT / 64;
+    __shared__ int s_wave[2 * NW + 1];
     __shared__ uint32_t s_prefix;
     __shared__ int s_need;
     const int seg = blockIdx.x;
@@ -231,13 +237,15 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_res(
     if (pos) pos += seg * pos_stride;
     out += seg * out_stride;
     const int tid = threadIdx.x;
-    const int C = (n + kSelThreads - 1) / kSelThreads;  // <= kRes
+    // runs of a multiple of 4 candidates (at most kRes), so that with
+    // 16-byte aligned key / position arrays every run is read in 16-byte loads
+    const int C = (((n + NT - 1) / NT) + 3) & ~3;
     const int t0 = min(tid * C, n), t1 = min(t0 + C, n);
 
     if (slot) {
-        for (int i = tid; i < n_slot; i += kSelThreads) slot[i] = -1;
+        for (int i = tid; i < n_slot; i += NT) slot[i] = -1;
     }
-    for (int q = tid; q < n_prefix; q += kSelThreads) {
+    for (int q = tid; q < n_prefix; q += NT) {
         out[q] = q;
         if (slot && q < n_slot) slot[q] = q;
     }
@@ -246,17 +254,40 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_res(
     uint32_t u[kRes];
     int pp[kRes];
     uint32_t ranked = 0;   // bit e: entry e takes part in the ranking
+    const bool vec = ((reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(pos)) & 15) == 0;
 #pragma unroll
-    for (int e = 0; e < kRes; ++e) {
-        const int t = t0 + e;
-        u[e] = 0;
-        pp[e] = -1;
-        if (t < t1) {
-            const int p = pos ? pos[t] : t;
-            pp[e] = p;
-            if (p >= n_prefix) {
-                u[e] = order_key(keys[t]);
-                ranked |= 1u << e;
+    for (int e4 = 0; e4 < kRes / 4; ++e4) {
+        const int t = t0 + 4 * e4;
+        float kv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        int pv[4] = {-1, -1, -1, -1};
+        if (vec && t + 3 < t1) {
+            const float4 k4 = *reinterpret_cast<const float4*>(keys + t);
+            kv[0] = k4.x; kv[1] = k4.y; kv[2] = k4.z; kv[3] = k4.w;
+            if (pos) {
+                const int4 p4 = *reinterpret_cast<const int4*>(pos + t);
+                pv[0] = p4.x; pv[1] = p4.y; pv[2] = p4.z; pv[3] = p4.w;
+            } else {
+                pv[0] = t; pv[1] = t + 1; pv[2] = t + 2; pv[3] = t + 3;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (t + i < t1) {
+                    kv[i] = keys[t + i];
+                    pv[i] = pos ? pos[t + i] : t + i;
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * e4 + i;
+            u[e] = 0;
+            pp[e] = -1;
+            if (t + i < t1) {
+                pp[e] = pv[i];
+                if (pv[i] >= n_prefix) {
+                    u[e] = order_key(kv[i]);
+                    ranked |= 1u << e;
+                }
             }
         }
     }
@@ -267,7 +298,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_res(
     if (n_sel > 0) {
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            for (int b = tid; b < 256; b += kSelThreads) s_hist[b] = 0;
+            for (int b = tid; b < 256; b += NT) s_hist[b] = 0;
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < kRes; ++e)
@@ -313,10 +344,10 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_res(
         n_eq += r && u[e] == T;
     }
     int eq_tot;
-    const int eq_before = block_excl_scan(n_eq, s_wave, &eq_tot);
+    const int eq_before = block_excl_scan<NW>(n_eq, s_wave, &eq_tot);
     const int eq_take = min(max(need - eq_before, 0), n_eq);  // this run's first eq_take ties
     int take_tot;
-    int o = n_prefix + block_excl_scan(n_gt + eq_take, s_wave, &take_tot);
+    int o = n_prefix + block_excl_scan<NW>(n_gt + eq_take, s_wave, &take_tot);
     int eq_seen = 0;
 #pragma unroll
     for (int e = 0; e < kRes; ++e) {
@@ -355,8 +386,11 @@ hipError_t launch_delta_norm(const void* h_cur, const void* h_prev, int dtype, i
 hipError_t launch_topk(const float* keys, long key_stride, const int32_t* pos, long pos_stride,
                        int n, int n_sel, int n_prefix, int32_t* out, long out_stride,
                        int32_t* slot, int n_slot, int n_seg, hipStream_t st) {
-    if (n <= kRes * kSelThreads)
-        hipLaunchKernelGGL(k_topk_res, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
+    if (n <= kRes * 256 && n_seg >= 256)
+        hipLaunchKernelGGL(k_topk_res<256>, dim3(n_seg), dim3(256), 0, st, keys, key_stride, pos,
+                           pos_stride, n, n_sel, n_prefix, out, out_stride, slot, n_slot);
+    else if (n <= kRes * kSelThreads)
+        hipLaunchKernelGGL(k_topk_res<kSelThreads>, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
                            pos_stride, n, n_sel, n_prefix, out, out_stride, slot, n_slot);
     else
         hipLaunchKernelGGL(k_topk, dim3(n_seg), dim3(kSelThreads), 0, st, keys, key_stride, pos,
