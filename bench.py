@@ -31,10 +31,11 @@ METRIC = "active-query tokens/s of loop-r sparse attention @32K, R=4; KV bytes/t
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
-KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn<128, 0, 1, false>",
+KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn_lds<128, 0, 1, 32>",
                  "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 8>",
-                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true>",
-                 "decode": "k_decode<128, 0, true, false>", "decode_rebuild": "k_decode<128, 1, true, true>"}
+                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true, false>",
+                 "decode": "k_decode<128, 0, true, false, false>",
+                 "decode_rebuild": "k_decode<128, 1, true, true, false>"}
 # projections of the 2048-hidden block: epilogue (0 store, 1 residual, 2 SwiGLU)
 # and tile width; o and down share one instantiation, so only the others are
 # separable in a trace
@@ -701,10 +702,11 @@ def bench_decode(args, w, np, torch, fl, synth):
     writes, and the token's q/k/v in and output out."""
     from concurrent.futures import ThreadPoolExecutor
     B, N, H, d, R, g = w.extra["B"], w.N, w.H, w.d, w.R, w.g
+    asym = args.quant == "asym"
     n_act = [N]
     for r in range(1, R):
         n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
-    run = fl.DecodeRunner(B, N, H, d, g, R, w.n_sink, n_act, w.kcols, w.bits)
+    run = fl.DecodeRunner(B, N, H, d, g, R, w.n_sink, n_act, w.kcols, w.bits, quant=quant_scheme(args, fl))
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -758,13 +760,18 @@ def bench_decode(args, w, np, torch, fl, synth):
 
     # algorithmic bytes per launch
     G = d // g
-    col_b = [2 * d * b_ // 8 + 2 * G * 4 for b_ in w.bits]       # K+V codes + scales of one row
+    if asym:
+        # K+V codes, the values' scale and offset per g channels, and the keys'
+        # per-channel scale and offset shared by g rows (their share per row)
+        col_b = [2 * d * b_ // 8 + 2 * G * 4 + 2 * d * 4 // g for b_ in w.bits]
+    else:
+        col_b = [2 * d * b_ // 8 + 2 * G * 4 for b_ in w.bits]   # K+V codes + scales of one row
     tok_io = 3 * d * 2 + d * 4 + 4                               # q,k,v in; out, lse out
     need_c1 = R > 1 and w.kcols[1] < N
     dense_bytes = B * H * (N * col_b[0] + (N * 4 if need_c1 else 0) + tok_io)
     # sparse loops: selected columns' present levels (from the GPU's sets)
     sparse_bytes = {}
-    for r in range(2, R + 1):
+    for r in range(2 if not asym else R + 1, R + 1):   # (asym: scattered key groups, not counted)
         sel = run.sel_used(r)
         if sel is None:
             continue
@@ -787,7 +794,7 @@ def bench_decode(args, w, np, torch, fl, synth):
         per_launch = dense_bytes
         ach = per_launch / (kd["avg_launch_us"] / 1e6) / 1e9
         kd["gbs"] = round(ach, 1)
-        sym = KERNEL_SYMBOL["decode_dense"]
+        sym = KERNEL_SYMBOL["decode_dense"].replace("false>", "true>") if asym else KERNEL_SYMBOL["decode_dense"]
         roof = dict(kernel="decode_dense", kernel_symbol=sym, bound="hbm", achieved=round(ach, 1),
                     peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
                     traffic=kernel_traffic(w.name, sym), bytes_per_launch=per_launch)
@@ -802,6 +809,8 @@ def bench_decode(args, w, np, torch, fl, synth):
         import oracle
         f = synth.bf16_bits_to_f32
         sched = w.sched()
+        if asym:
+            sched["quant"] = "asym"
         t_or = 0.0
         for b, x in sample_inputs.items():
             cache = od.build_cache([f(a) for a in x["k"]], [f(a) for a in x["v"]], x["stat"], sched)
@@ -817,10 +826,12 @@ def bench_decode(args, w, np, torch, fl, synth):
         "metric": f"decoded tokens/s, {B} sequences x {N} cached tokens, R={R}",
         "value": round(B / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8/int4 codes, f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "unsigned min/max codes, f32" if asym else "int8/int4 codes, f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "N": N, "H": H, "d": d, "R": R, "g": g,
-                   "active_per_loop": n_act, "k_per_loop": w.kcols, "bits_per_loop": w.bits},
+                   "active_per_loop": n_act, "k_per_loop": w.kcols, "bits_per_loop": w.bits,
+                   "quant": args.quant},
         "loops": [dict(r=r + 1, ms=round(float(np.mean(loop_ms[:, r])), 4)) for r in range(R)],
         "kernels": kernels,
         "roofline": roof,

@@ -411,10 +411,12 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
  * sequence b's rows/slot/codes/scales follow at b * (R_l, P, R_l*H*d*bits/8
  * bytes, R_l*H*d/g floats) -- B sequences of equal geometry -- with the
  * per-sequence capacities P = N_cap (or N) positions and R_l = rows_cap[l]
- * (or n_rows; level 0: P) rows.
+ * (or n_rows; level 0: P) rows.  Under FL_QUANT_ASYM the value offsets
+ * follow the value scales' layout, and the key scales and offsets (one per
+ * channel for every g rows) follow at b * ceil(R_l / g)*H*d floats.
  * Requirements: N + T <= 12288 (T bf16 columns: 1, or the window count; the
- * probabilities stay in LDS); scheme
- * FL_QUANT_ABSMAX with an int8 base level and quantised residual levels
+ * probabilities stay in LDS); quantised levels: FL_QUANT_ABSMAX with an
+ * int8 base, or FL_QUANT_ASYM (2-, 4- or 8-bit levels) without a window
  * (FL_ERR_UNSUPPORTED otherwise); a
  * sparse loop r keeps 4 * ((k + 1) + r * k) bytes in LDS, at most 48 KiB.
  */

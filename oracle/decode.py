@@ -31,8 +31,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (active_count, attend, column_stats, quantize_rows, select_columns, top_select,
-               unselected_cache)
+from . import (active_count, attend, column_stats, quantize_rows, quantize_rows_asym, select_columns,
+               top_select, unselected_cache)
 
 F32 = np.float32
 
@@ -42,9 +42,14 @@ def build_cache(k, v, stat, sched):
 
     k, v: lists of R fp32 arrays [N][H][d] (the prefix tokens' loop-r K/V);
     stat: list of R entries, stat[r-1] [N] the loop-r selection statistic
-    (stat[0] unused).  Returns a list of per-loop dicts with the active set,
-    the level's codes/scales and the dequantised cache khat/vhat [N][H][d]."""
+    (stat[0] unused).  sched["quant"] "asym" takes the paper's quantiser
+    (App. E: keys per channel over g consecutive rows of the level, values per
+    g channels of a row; the level's rows in ascending position order) instead
+    of the spec's absmax one.  Returns a list of per-loop dicts with the active
+    set, the level's codes/scales (and, asym, zeros) and the dequantised cache
+    khat/vhat [N][H][d]."""
     N, g = sched["N"], sched["g"]
+    asym = sched.get("quant", "absmax") == "asym"
     A = np.arange(N, dtype=np.int32)
     khat = vhat = None
     out = []
@@ -53,15 +58,22 @@ def build_cache(k, v, stat, sched):
             n_r = active_count(sched["rho"][r - 1], N, len(A))
             A = top_select(np.asarray(stat[r - 1], F32)[A], n_r, A)
         bits = sched["bits"][r - 1]
-        kc, ks, _, kx = quantize_rows(np.asarray(k[r - 1], F32)[A], None if r == 1 else khat[A], g, bits)
-        vc, vs, _, vx = quantize_rows(np.asarray(v[r - 1], F32)[A], None if r == 1 else vhat[A], g, bits)
+        kp = None if r == 1 else khat[A]
+        vp = None if r == 1 else vhat[A]
+        if asym:
+            kc, ks, kz, kx = quantize_rows_asym(np.asarray(k[r - 1], F32)[A], kp, g, bits, True)
+            vc, vs, vz, vx = quantize_rows_asym(np.asarray(v[r - 1], F32)[A], vp, g, bits, False)
+        else:
+            kc, ks, _, kx = quantize_rows(np.asarray(k[r - 1], F32)[A], kp, g, bits)
+            vc, vs, _, vx = quantize_rows(np.asarray(v[r - 1], F32)[A], vp, g, bits)
+            kz = vz = None
         if r == 1:
             khat, vhat = kx, vx
         else:
             khat = khat.copy(); khat[A] = kx
             vhat = vhat.copy(); vhat[A] = vx
-        out.append(dict(active=A, k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs,
-                        khat=khat, vhat=vhat))
+        out.append(dict(active=A, k_codes=kc, k_scale=ks, k_zero=kz, v_codes=vc, v_scale=vs,
+                        v_zero=vz, khat=khat, vhat=vhat))
     return out
 
 

@@ -688,8 +688,13 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, r - 1);
     if (rc) return rc;
-    if (C.scheme != FL_QUANT_ABSMAX) return fail(FL_ERR_UNSUPPORTED, "decode: FL_QUANT_ABSMAX caches only");
-    if (C.level[0].bits != 8) return fail(FL_ERR_UNSUPPORTED, "decode: base level bits %d (8)", C.level[0].bits);
+    // the asymmetric scheme's keys are quantised per channel over g rows of a
+    // level, which a token appended one at a time cannot complete: decode over
+    // such a cache runs without a generation window
+    if (C.scheme == FL_QUANT_ASYM && W)
+        return fail(FL_ERR_UNSUPPORTED, "decode: a generation window needs a FL_QUANT_ABSMAX cache");
+    if (C.scheme == FL_QUANT_ABSMAX && C.level[0].bits != 8)
+        return fail(FL_ERR_UNSUPPORTED, "decode: base level bits %d (8)", C.level[0].bits);
     for (int l = 1; l < r; ++l)
         if (C.level[l].bits == 32)
             return fail(FL_ERR_UNSUPPORTED, "decode: level %d is raw (quantised levels only)", l);

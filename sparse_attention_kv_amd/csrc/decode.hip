@@ -35,13 +35,17 @@ constexpr int DNW = DT / 64; // waves
 struct SeqLevel {
     const uint8_t* codes;
     const float* scales;
+    const float* zeros;     // asymmetric scheme: the offsets beside the scales
     const int32_t* slot;
     int bits;
 };
 
 // level l of sequence b: the B sequences are stored back to back with the
-// per-sequence capacities (positions pos_cap; rows rows_cap[l] for l >= 1)
-template <int D>
+// per-sequence capacities (positions pos_cap; rows rows_cap[l] for l >= 1).
+// Absmax and value scales: one per (row, head, g channels); asymmetric key
+// scales and offsets: one per (g rows, head, channel), so a sequence holds
+// ceil(rows / g) row groups of them.
+template <int D, bool ASYM>
 __device__ __forceinline__ SeqLevel seq_level(const DecodeParams& P, int l, int b, int which) {
     const fl_kv_cache& c = P.cache;
     const fl_kv_level& L = c.level[l];
@@ -50,9 +54,40 @@ __device__ __forceinline__ SeqLevel seq_level(const DecodeParams& P, int l, int 
     s.bits = L.bits;
     s.codes = reinterpret_cast<const uint8_t*>(which ? L.v_codes : L.k_codes) +
               b * (rows * c.H * D * L.bits / 8);
-    s.scales = (which ? L.v_scale : L.k_scale) + b * (rows * c.H * (D / c.g));
+    const long sstride = (ASYM && which == 0) ? ((rows + c.g - 1) / c.g) * c.H * D : rows * c.H * (D / c.g);
+    s.scales = (which ? L.v_scale : L.k_scale) + b * sstride;
+    s.zeros = ASYM ? (which ? L.v_zero : L.k_zero) + b * sstride : nullptr;
     s.slot = l == 0 ? nullptr : L.slot + (long)b * P.pos_cap;
     return s;
+}
+
+// 16 consecutive unsigned codes (asymmetric scheme) starting at code index e
+// (16-aligned)
+__device__ __forceinline__ void load_ucodes16(const uint8_t* base, long e, int bits, float (&x)[16]) {
+    if (bits == 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(base + e);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((wd[i >> 2] >> (8 * (i & 3))) & 255u);
+    } else if (bits == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(base + e / 2);
+        const uint64_t wd = ((uint64_t)u.y << 32) | u.x;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((uint32_t)(wd >> (4 * i)) & 15u);
+    } else { // bits == 2
+        const uint32_t wd = *reinterpret_cast<const uint32_t*>(base + e / 4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((wd >> (2 * i)) & 3u);
+    }
+}
+
+// 16 consecutive fp32 values
+__device__ __forceinline__ void load_f32x16(const float* p, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 v = reinterpret_cast<const float4*>(p)[i];
+        x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+    }
 }
 
 // 16 consecutive bf16 values as fp32
@@ -86,7 +121,10 @@ __device__ __forceinline__ void load_codes16(const uint8_t* base, long e, int bi
     }
 }
 
-template <int D, int MODE, bool SPARSE, bool L0>
+// ASYM: the cache holds the asymmetric scheme (unsigned codes, code * s + z;
+// keys with a scale and offset per channel for every g rows of a level,
+// values per g channels of a row); L0 then only restricts the walk to level 0.
+template <int D, int MODE, bool SPARSE, bool L0, bool ASYM>
 __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     constexpr int LPC = D / 16;     // lanes per column
     constexpr int CPW = 64 / LPC;   // columns per wave per load
@@ -129,7 +167,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         for (int c = tid; c < k; c += DT) {
             const int j = sel[c];
             rowtab[c] = j;
-            for (int l = 1; l < nlev; ++l) rowtab[l * k + c] = seq_level<D>(P, l, b, 0).slot[j];
+            for (int l = 1; l < nlev; ++l) rowtab[l * k + c] = seq_level<D, ASYM>(P, l, b, 0).slot[j];
         }
     }
     __syncthreads();
@@ -142,7 +180,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     auto row_of = [&](int l, int c) -> int {
         if (SPARSE) return rowtab[l * k + c];
         if (l == 0) return c;
-        return seq_level<D>(P, l, b, 0).slot[c];
+        return seq_level<D, ASYM>(P, l, b, 0).slot[c];
     };
 
     // ---- phase 1: scores (log2 units) ----
@@ -159,14 +197,27 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 for (int l = 0; l < nlev; ++l) {
                     const int row = row_of(l, c);
                     if (row >= 0) {
-                        const SeqLevel L = seq_level<D>(P, l, b, 0);
+                        const SeqLevel L = seq_level<D, ASYM>(P, l, b, 0);
                         const long rr = (long)row * H + h;
                         float x[16];
-                        load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
-                        float dot = 0.0f;
+                        if (ASYM) {
+                            // x = code * s + z per channel (scale / offset of the row's group)
+                            load_ucodes16(L.codes, rr * D + cs * 16, L.bits, x);
+                            const long si = ((long)(row / C.g) * H + h) * D + cs * 16;
+                            float sv[16], zv[16];
+                            load_f32x16(L.scales + si, sv);
+                            load_f32x16(L.zeros + si, zv);
+                            float dot = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
-                        part[u] = fmaf(dot, L.scales[rr * G + grp], part[u]);
+                            for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i] * sv[i] + zv[i], dot);
+                            part[u] += dot;
+                        } else {
+                            load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                            float dot = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
+                            part[u] = fmaf(dot, L.scales[rr * G + grp], part[u]);
+                        }
                     }
                 }
             }
@@ -244,13 +295,22 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 for (int l = 0; l < nlev; ++l) {
                     const int row = row_of(l, c);
                     if (row >= 0) {
-                        const SeqLevel L = seq_level<D>(P, l, b, 1);
+                        const SeqLevel L = seq_level<D, ASYM>(P, l, b, 1);
                         const long rr = (long)row * H + h;
                         float x[16];
-                        load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
-                        const float ps = p * L.scales[rr * G + grp];
+                        if (ASYM) {
+                            // p * (code * s + z) = code * (p s) + p z
+                            load_ucodes16(L.codes, rr * D + cs * 16, L.bits, x);
+                            const float ps = p * L.scales[rr * G + grp];
+                            const float pz = p * L.zeros[rr * G + grp];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                            for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i] + pz);
+                        } else {
+                            load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                            const float ps = p * L.scales[rr * G + grp];
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                        }
                     }
                 }
             }
@@ -307,7 +367,12 @@ hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st)
                        (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
     dim3 grid(P.B * P.H);
     const bool l0 = P.level == 0;
-#define FL_DEC(D_, M_, S_, L_) hipLaunchKernelGGL((k_decode<D_, M_, S_, L_>), grid, dim3(DT), shm, st, P)
+    const bool asym = P.cache.scheme == FL_QUANT_ASYM;
+#define FL_DEC(D_, M_, S_, L_)                                                                  \
+    do {                                                                                        \
+        if (asym) hipLaunchKernelGGL((k_decode<D_, M_, S_, L_, true>), grid, dim3(DT), shm, st, P);  \
+        else hipLaunchKernelGGL((k_decode<D_, M_, S_, L_, false>), grid, dim3(DT), shm, st, P);      \
+    } while (0)
 #define FL_DEC_D(D_)                                                                     \
     if (mode == MODE_REBUILD) { if (l0) FL_DEC(D_, MODE_REBUILD, true, true); else FL_DEC(D_, MODE_REBUILD, true, false); } \
     else if (sp) { if (l0) FL_DEC(D_, MODE_ATTN, true, true); else FL_DEC(D_, MODE_ATTN, true, false); } \

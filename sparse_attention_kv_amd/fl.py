@@ -511,12 +511,16 @@ class DecodeRunner:
     statistic, ``fl_kv_residual_quant`` per level); ``step`` runs loop r."""
 
     def __init__(self, B, N, H, d, g, R, n_sink, n_active, k_cols, bits, gen_tokens=0, window=64,
-                 device="cuda"):
+                 quant=FL_QUANT_ABSMAX, device="cuda"):
         """gen_tokens > 0 prepares generation: caches with room for that many
         appended positions and per-loop bf16 window rings of window + 1 slots
-        (the window and the token being decoded)."""
+        (the window and the token being decoded).  quant: the caches' scheme
+        (FL_QUANT_ASYM: the paper's quantiser, decode without generation)."""
+        if quant == FL_QUANT_ASYM and gen_tokens:
+            raise ValueError("generation appends need the FL_QUANT_ABSMAX scheme")
         dev = torch.device(device)
         self.B, self.N, self.H, self.d, self.g, self.R = B, N, H, d, g, R
+        self.quant = quant
         self.n_active, self.k_cols, self.bits = list(n_active), list(k_cols), list(bits)
         self.gen_tokens, self.window = gen_tokens, window
         self._keep = []
@@ -538,15 +542,21 @@ class DecodeRunner:
         self.cfg = cfg
         st = FlDecodeState()
         C = st.cache
-        C.N, C.H, C.d, C.g, C.n_levels = N, H, d, g, R
+        C.N, C.H, C.d, C.g, C.n_levels, C.scheme = N, H, d, g, R, quant
         self.codes, self.rows, self.slot = [], [], []
         for r in range(R):
             n = N if r == 0 else n_active[r]
             nc = cap_pos if r == 0 else n + gen_tokens
             cb = dict(k=buf((B, nc, H, d * bits[r] // 8), torch.uint8),
                       v=buf((B, nc, H, d * bits[r] // 8), torch.uint8),
-                      ks=buf((B, nc, H, d // g), torch.float32),
                       vs=buf((B, nc, H, d // g), torch.float32))
+            if quant == FL_QUANT_ASYM:
+                # keys: a scale and offset per channel for every g rows
+                ng = (nc + g - 1) // g
+                cb.update(ks=buf((B, ng, H, d), torch.float32), kz=buf((B, ng, H, d), torch.float32),
+                          vz=buf((B, nc, H, d // g), torch.float32))
+            else:
+                cb["ks"] = buf((B, nc, H, d // g), torch.float32)
             # row lists and slot maps start as -1 (no row) beyond what is filled
             rows = buf((B, nc), torch.int32).fill_(-1) if r > 0 else None
             slot = buf((B, cap_pos), torch.int32).fill_(-1) if r > 0 else None
@@ -554,6 +564,7 @@ class DecodeRunner:
             Lv.bits, Lv.n_rows = bits[r], n
             Lv.rows, Lv.slot = _p(rows), _p(slot)
             Lv.k_codes, Lv.v_codes, Lv.k_scale, Lv.v_scale = _p(cb["k"]), _p(cb["v"]), _p(cb["ks"]), _p(cb["vs"])
+            Lv.k_zero, Lv.v_zero = _p(cb.get("kz")), _p(cb.get("vz"))
             self.codes.append(cb); self.rows.append(rows); self.slot.append(slot)
         self.out = buf((B, H, d), torch.float32)
         self.lse = buf((B, H), torch.float32)
@@ -583,7 +594,7 @@ class DecodeRunner:
     def seq_cache(self, b):
         """FlKvCache of sequence b alone (pointers into the batched buffers)."""
         c = FlKvCache()
-        c.N, c.H, c.d, c.g, c.n_levels = self.N, self.H, self.d, self.g, self.R
+        c.N, c.H, c.d, c.g, c.n_levels, c.scheme = self.N, self.H, self.d, self.g, self.R, self.quant
         for r in range(self.R):
             Lv = c.level[r]
             cb = self.codes[r]
@@ -592,6 +603,8 @@ class DecodeRunner:
             Lv.slot = None if r == 0 else _p(self.slot[r][b])
             Lv.k_codes, Lv.v_codes = _p(cb["k"][b]), _p(cb["v"][b])
             Lv.k_scale, Lv.v_scale = _p(cb["ks"][b]), _p(cb["vs"][b])
+            if "kz" in cb:
+                Lv.k_zero, Lv.v_zero = _p(cb["kz"][b]), _p(cb["vz"][b])
         return c
 
     def load_sequence(self, b, k, v, stat, stream=None):

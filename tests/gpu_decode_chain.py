@@ -23,10 +23,21 @@ def _draw(w, B, threads):
                 yield b0 + i, f.result()
 
 
+def _quant(w):
+    return fl.FL_QUANT_ASYM if w.extra.get("quant") == "asym" else fl.FL_QUANT_ABSMAX
+
+
+def _sched(w):
+    sched = w.sched()
+    if w.extra.get("quant") == "asym":
+        sched["quant"] = "asym"
+    return sched
+
+
 def run_decode_gpu(w, keep=(), threads=8):
     B, N, H, d, R = w.extra["B"], w.N, w.H, w.d, w.R
     n_act = counts(w)
-    run = fl.DecodeRunner(B, N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits)
+    run = fl.DecodeRunner(B, N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits, quant=_quant(w))
     tok = {key: np.empty((R, B, H, d), np.uint16) for key in ("q_new", "k_new", "v_new")}
     kept = {}
     for b, x in _draw(w, B, threads):
@@ -60,7 +71,8 @@ def run_decode_gpu(w, keep=(), threads=8):
 
 def check_sequence(w, b, x, gres, run):
     """Cache levels of sequence b bit-exact, then every loop's results."""
-    sched = w.sched()
+    sched = _sched(w)
+    asym = sched.get("quant") == "asym"
     f = synth.bf16_bits_to_f32
     cache = od.build_cache([f(a) for a in x["k"]], [f(a) for a in x["v"]], x["stat"], sched)
     for r in range(1, w.R + 1):
@@ -76,6 +88,10 @@ def check_sequence(w, b, x, gres, run):
             np.testing.assert_array_equal(cb[kv + "s"][b].cpu().numpy().view(np.uint32),
                                           lv[kv + "_scale"].view(np.uint32),
                                           err_msg=f"seq {b} loop {r} {kv} scales")
+            if asym:
+                np.testing.assert_array_equal(cb[kv + "z"][b].cpu().numpy().view(np.uint32),
+                                              lv[kv + "_zero"].view(np.uint32),
+                                              err_msg=f"seq {b} loop {r} {kv} zeros")
     ov = {("cstat", r): gres[r - 2]["cstat"][b] for r in range(2, w.R + 1)
           if gres[r - 2]["cstat"] is not None}
     recs = od.run_decode(cache, [f(a) for a in x["q_new"]], [f(a) for a in x["k_new"]],

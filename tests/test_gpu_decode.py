@@ -1,5 +1,6 @@
 """GPU parity of batched decode (fl_decode_step) against the decode oracle:
-every sequence's cache levels bit-exact (active sets, packed codes, scales),
+every sequence's cache levels bit-exact (active sets, packed codes, scales,
+and the offsets of the asymmetric scheme),
 column selections exact given the GPU's statistics, outputs / lse / cached
 mass and partial output within rel-L2 1e-2 and max-abs 3e-2.
 
@@ -16,11 +17,11 @@ from gpu_decode_chain import check_sequence, run_decode_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _w(B, N, H, d, g, kcols, bits=(8, 4, 4, 2), rho=(1.0, 0.4, 0.2, 0.1), seed=11):
+def _w(B, N, H, d, g, kcols, bits=(8, 4, 4, 2), rho=(1.0, 0.4, 0.2, 0.1), seed=11, quant="absmax"):
     w = synth.WORKLOADS["decode64x8k"].scaled(N=N, H=H, d=d, g=g, R=len(kcols), kcols=list(kcols),
                                               bits=list(bits[: len(kcols)]),
                                               rho=list(rho[: len(kcols)]), seed=seed)
-    w.extra = dict(B=B)
+    w.extra = dict(B=B, quant=quant)
     return w
 
 
@@ -29,6 +30,12 @@ CASES = {
     "d64_g32": _w(2, 515, 3, 64, 32, (515, 128, 128, 60), seed=12),
     "short37": _w(2, 37, 2, 128, 64, (37, 16, 8, 8), seed=13),
     "unpruned": _w(2, 300, 2, 128, 64, (300, 300, 300), bits=(8, 4, 4), seed=14),
+    # the paper's quantiser (App. E): INT4 asymmetric at every level, keys
+    # per channel over 64 (32) consecutive rows of a level (ragged last group)
+    "asym_int4_ragged": _w(3, 700, 2, 128, 64, (700, 96, 64, 40), bits=(4, 4, 4, 4), seed=15,
+                           quant="asym"),
+    "asym_d64_g32_mixed": _w(2, 515, 3, 64, 32, (515, 128, 128, 60), bits=(8, 4, 2, 2), seed=16,
+                             quant="asym"),
 }
 
 

@@ -125,3 +125,55 @@ def test_frozen_loops_restore_dense_output():
         np.testing.assert_allclose(recs[r - 1]["out"], recs[0]["out"], rtol=0, atol=3e-5)
         np.testing.assert_allclose(recs[r - 1]["lse"] - np.log1p(-recs[r - 1]["mass_u"].astype(np.float64)),
                                    recs[0]["lse"], rtol=0, atol=3e-5)
+
+
+def _asym_deq64(codes, s, z, g, per_channel):
+    """float64 reconstruction code * s + z of one asymmetric level, the group
+    of every element written out here: keys per channel over g consecutive
+    rows, values per g consecutive channels of a row."""
+    n, H, d = codes.shape
+    c = codes.astype(np.float64)
+    if per_channel:
+        grp = np.arange(n) // g
+        return c * s.astype(np.float64)[grp] + z.astype(np.float64)[grp]
+    ch = np.arange(d) // g
+    return c * s.astype(np.float64)[:, :, ch] + z.astype(np.float64)[:, :, ch]
+
+
+def test_asym_cache_levels_rebuild_the_chain():
+    """The paper's quantiser in the decode cache (App. E): every level's codes
+    lie in [0, 2^b - 1]; the dequantised cache of loop r is the previous one
+    plus level r's code * s + z on the level's rows (keys grouped per channel
+    over 64 packed rows, values per 32 channels); each stored level is within
+    half a step of its target; and unpruned loops over it are plain softmax
+    attention."""
+    sc = _sched(kcols=(300, 300, 300), bits=(4, 4, 2))
+    sc["g"] = 32
+    sc["quant"] = "asym"
+    k, v, stat, q, ks, vs = _inputs(sc)
+    cache = od.build_cache(k, v, stat, sc)
+    g = sc["g"]
+    prev_k = prev_v = None
+    for r, lv in enumerate(cache, start=1):
+        A, b = lv["active"], sc["bits"][r - 1]
+        for kv, per_ch, x, prev in (("k", True, k, prev_k), ("v", False, v, prev_v)):
+            codes = lv[kv + "_codes"]
+            assert codes.dtype == np.uint8 and codes.max() <= (1 << b) - 1
+            step = _asym_deq64(codes, lv[kv + "_scale"], lv[kv + "_zero"], g, per_ch)
+            base = np.zeros_like(step) if prev is None else prev[A].astype(np.float64)
+            got = lv[kv + "hat"][A].astype(np.float64)
+            np.testing.assert_allclose(got, base + step, rtol=1e-6, atol=1e-6)
+            # within half a step (+ float32 rounding) of this loop's values
+            target = x[r - 1][A].astype(np.float64) - base
+            s = lv[kv + "_scale"].astype(np.float64)
+            half = 0.5 * (s[np.arange(len(A)) // g] if per_ch else s[:, :, np.arange(sc["d"]) // g])
+            assert np.all(np.abs(step - target) <= half + 1e-5 * (1 + np.abs(target)))
+        prev_k, prev_v = lv["khat"], lv["vhat"]
+    recs = od.run_decode(cache, q, ks, vs, sc)
+    sm = 1.0 / np.sqrt(sc["d"])
+    for r in range(1, sc["R"] + 1):
+        K = np.concatenate([cache[r - 1]["khat"], ks[r - 1][None]], axis=0)
+        V = np.concatenate([cache[r - 1]["vhat"], vs[r - 1][None]], axis=0)
+        o, lse, _ = _dense64(q[r - 1], K, V, sm)
+        np.testing.assert_allclose(recs[r - 1]["out"], o, rtol=1e-4, atol=1e-5)
+        np.testing.assert_allclose(recs[r - 1]["lse"], lse, rtol=1e-5, atol=1e-5)
