@@ -184,6 +184,55 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     };
 
     // ---- phase 1: scores (log2 units) ----
+    if (ASYM && L0 && !SPARSE) {
+        // the level-0 rows in order: a wave takes CPW * U consecutive columns
+        // per pass, so a key group's per-channel scales and offsets (shared by
+        // g rows) are loaded once per group for this lane's 16 channels and
+        // folded into the query: q . (code * s + z) = (q s) . code + q . z
+        // (g is a multiple of CPW, so the CPW columns of a step share a group)
+        const SeqLevel L = seq_level<D, ASYM>(P, 0, b, 0);
+        int gcur = -1;
+        float qs[16], qz = 0.0f;
+        for (int c0 = 0; c0 < k; c0 += CPI * U) {
+            float part[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cb = c0 + w * (CPW * U) + u * CPW;   // first column of this step
+                const int c = cb + cl;
+                part[u] = 0.0f;
+                const int cg = cb / C.g;
+                if (cb < k && cg != gcur) {
+                    const long si = ((long)cg * H + h) * D + cs * 16;
+                    float sv[16], zv[16];
+                    load_f32x16(L.scales + si, sv);
+                    load_f32x16(L.zeros + si, zv);
+                    qz = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        qs[i] = qv[i] * sv[i];
+                        qz = fmaf(qv[i], zv[i], qz);
+                    }
+                    gcur = cg;
+                }
+                if (c < k) {
+                    float x[16];
+                    load_ucodes16(L.codes, ((long)c * H + h) * D + cs * 16, L.bits, x);
+                    float dot = qz;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) dot = fmaf(qs[i], x[i], dot);
+                    part[u] = dot;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float v = part[u];
+#pragma unroll
+                for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
+                const int c = c0 + w * (CPW * U) + u * CPW + cl;
+                if (cs == 0 && c < k) sc[c] = v * c2;
+            }
+        }
+    } else
     for (int c0 = 0; c0 < k; c0 += CPI * U) {
         float part[U];
 #pragma unroll
