@@ -320,8 +320,10 @@ int fl_kv_dequant(const fl_kv_cache* cache, int level, int which, float* out, fl
     return FL_OK;
 }
 
-int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
-                        size_t ws_bytes, fl_stream_t stream) {
+// fl_sparse_loop_attn, optionally also writing the output as bf16 [n][H][d]
+// by active index (out_bf; the block step's input of the output projection)
+static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
+                            size_t ws_bytes, fl_stream_t stream, __bf16* out_bf) {
     FL_REQUIRE(a != nullptr, "args NULL");
     int rc = check_cache(cache, a->level);
     if (rc) return rc;
@@ -375,7 +377,7 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     fl::AttnParams P{};
     P.H = H; P.n = a->n; P.k = a->k; P.kp = kp; P.dtype = a->dtype; P.cache_op = a->cache_op;
     P.c2 = c2; P.active = a->active; P.cpos = cpos;
-    P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u;
+    P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u; P.out_bf = out_bf;
     if (in_tile) {
         fl::QTiles& qt = P.qt;
         qt.n_levels = a->level + 1;
@@ -443,6 +445,11 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
                "colstat");
     }
     return FL_OK;
+}
+
+int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
+                        size_t ws_bytes, fl_stream_t stream) {
+    return sparse_loop_attn(cache, a, ws, ws_bytes, stream, nullptr);
 }
 
 int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs* in, int r,
@@ -643,10 +650,11 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
             A.col_stat = need_c ? Ls.col_stat[r - 1] : nullptr;
             FL_REQUIRE(!need_c || A.col_stat, "layer %d col_stat[%d] NULL", l, r - 1);
         }
-        rc = fl_sparse_loop_attn(&C, &A, aws, aws_bytes, stream);
+        // the attention output lands in the state (fp32, by position) and as the
+        // bf16 compact input of the output projection
+        rc = sparse_loop_attn(&C, &A, aws, aws_bytes, stream, attn_in);
         if (rc) return rc;
         FL_HIP(fl::launch_scatter_rows_bf16(qc, act, n, D, (__bf16*)Ls.q_state, st), "scatter");
-        FL_HIP(fl::launch_rows_f32_to_bf16(Ls.out, act, n, D, attn_in, st), "gather");
         G = fl::GemmParams{};
         G.M = n; G.N = D; G.K = D; G.A = attn_in; G.lda = D; G.B = (const __bf16*)w.w_o;
         G.Cf = S->h; G.ldc = D; G.rows = act;

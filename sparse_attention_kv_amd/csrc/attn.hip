@@ -26,6 +26,14 @@
 
 namespace fl {
 
+// four fp32 values rounded to bf16 (nearest-even) and stored as 8 bytes
+__device__ __forceinline__ void store_bf16x4(__bf16* dst, float4 v) {
+    const __bf16 b[4] = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    uint16_t u[4];
+    __builtin_memcpy(u, b, sizeof(u));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(u[0] | ((uint32_t)u[1] << 16), u[2] | ((uint32_t)u[3] << 16));
+}
+
 constexpr int BM = 128; // query rows per workgroup (4 waves x 32)
 constexpr int BN = 64;  // columns per tile
 
@@ -538,6 +546,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
                 v.z = o[dt][4 * jq + 2] * scale + u.z;
                 v.w = o[dt][4 * jq + 3] * scale + u.w;
                 *reinterpret_cast<float4*>(orow + d0) = v;
+                if (P.out_bf) store_bf16x4(P.out_bf + ((long)t * P.H + h) * D + d0, v);
             }
         if (half == 0)
             P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
@@ -792,6 +801,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
                 v.z = o[dt][4 * jq + 2] * scale + u.z;
                 v.w = o[dt][4 * jq + 3] * scale + u.w;
                 *reinterpret_cast<float4*>(orow + d0) = v;
+                if (P.out_bf) store_bf16x4(P.out_bf + ((long)t * P.H + h) * D + d0, v);
             }
         if (half == 0)
             P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;

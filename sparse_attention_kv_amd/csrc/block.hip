@@ -14,7 +14,7 @@
 //   k_rope_split      [n][3D] bf16 -> q, k, v [n][H][d] bf16 with rotary
 //                     position embedding (rotate-half) on q and k at the rows'
 //                     token positions (keys are quantised after RoPE).
-//   k_rows_f32_to_bf16, k_scatter_rows_bf16: row gather / scatter helpers.
+//   k_scatter_rows_bf16: row scatter helper.
 #include "fl_device.h"
 #include "fl_kernels.h"
 
@@ -312,16 +312,6 @@ __global__ __launch_bounds__(256) void k_rope_split(const __bf16* __restrict__ q
     v[o + i + halfd] = src[2 * D + i + halfd];
 }
 
-__global__ void k_rows_f32_to_bf16(const float* __restrict__ src, const int32_t* __restrict__ rows,
-                                   long n, int D, __bf16* __restrict__ dst) {
-    const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
-    if (gid >= n * D) return;
-    const long m = gid / D;
-    const int c = (int)(gid % D);
-    const long row = rows ? rows[m] : m;
-    dst[gid] = (__bf16)src[row * D + c];
-}
-
 __global__ void k_scatter_rows_bf16(const __bf16* __restrict__ src, const int32_t* __restrict__ rows,
                                     long n, int D, __bf16* __restrict__ dst) {
     const long gid = blockIdx.x * (long)blockDim.x + threadIdx.x;
@@ -375,14 +365,6 @@ hipError_t launch_rope_split(const __bf16* qkv, const int32_t* rows, int n, int 
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_rope_split, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, qkv,
                        rows, n, H, d, log2f(theta), q, k, v);
-    return hipGetLastError();
-}
-
-hipError_t launch_rows_f32_to_bf16(const float* src, const int32_t* rows, long n, int D,
-                                   __bf16* dst, hipStream_t st) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rows_f32_to_bf16, dim3((unsigned)((n * D + 255) / 256)), dim3(256), 0, st,
-                       src, rows, n, D, dst);
     return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct AttnParams {
     float* lse;
     float* mass_u;
     float* out_u;
+    __bf16* out_bf;        // optional: the output also as bf16 [n][H][d] by active index
     int xcd_remap;
     int deq_levels;        // in-tile dequantisation: levels 0..deq_levels-1 of q
     QTiles qt;
@@ -143,8 +144,6 @@ hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int
 hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st);
 hipError_t launch_rope_split(const __bf16* qkv, const int32_t* rows, int n, int H, int d,
                              float theta, __bf16* q, __bf16* k, __bf16* v, hipStream_t st);
-hipError_t launch_rows_f32_to_bf16(const float* src, const int32_t* rows, long n, int D,
-                                   __bf16* dst, hipStream_t st);
 hipError_t launch_scatter_rows_bf16(const __bf16* src, const int32_t* rows, long n, int D,
                                     __bf16* dst, hipStream_t st);
 // decode.hip
