@@ -172,35 +172,75 @@ def append_token(k_loops, v_loops, sched):
     return out
 
 
+def append_block(k_block, v_block, sched):
+    """Generation-time growth under the paper's quantiser (App. E): its keys
+    are quantised per channel over g consecutive rows, so generated tokens
+    join the cache g at a time, as one new key group per level (the prompt's
+    last, possibly partial, group is left as it is).  Every generated token
+    is computed in all loops, so each level gains the same g rows: the base
+    level quantises their loop-1 K/V, level r - 1 the residual of their
+    loop-r K/V against the dequantised chain below it.
+    k_block, v_block: lists of g per-token lists of R arrays [H][d].  Returns
+    per level codes ([g][H][d]), scales / zeros (keys [1][H][d], values
+    [g][H][d/g]) and the block's dequantised loop-r K/V [g][H][d]."""
+    g = sched["g"]
+    assert len(k_block) == g and len(v_block) == g
+    out = []
+    kh = vh = None
+    for r in range(1, sched["R"] + 1):
+        bits = sched["bits"][r - 1]
+        kx = np.stack([np.asarray(t[r - 1], F32) for t in k_block])
+        vx = np.stack([np.asarray(t[r - 1], F32) for t in v_block])
+        kc, ks, kz, kh = quantize_rows_asym(kx, kh, g, bits, True)
+        vc, vs, vz, vh = quantize_rows_asym(vx, vh, g, bits, False)
+        out.append(dict(k_codes=kc, k_scale=ks, k_zero=kz, v_codes=vc, v_scale=vs, v_zero=vz,
+                        khat=kh, vhat=vh))
+    return out
+
+
 def run_generation(cache, gen_q, gen_k, gen_v, sched, window=64, override=None):
     """Generation after a prompt whose cache ``build_cache`` made.
 
     gen_q/k/v[t]: lists of R arrays [H][d], the t-th generated token's
     per-loop query / key / value.  The most recent ``window`` generated tokens
-    stay unquantised (App. E keeps the most recent 64 tokens in BF16): token
-    t attends to the quantised cache plus generated tokens max(0, t-window)..t;
-    before token t is decoded, token t - window - 1 (if any) leaves the window
-    and is appended to the cache (``append_token``).
-    override: {t: {('cstat', r): ...}} per token.
+    stay unquantised (App. E keeps the most recent 64 tokens in BF16) and
+    leave the window in blocks of F tokens, oldest first: F = 1 under the
+    absmax scheme (per-token groups; ``append_token``), F = g under the
+    paper's quantiser (a key group is g rows; ``append_block``).  Before token
+    t is decoded, while more than window + F - 1 earlier generated tokens are
+    unquantised, the oldest F are appended to the cache; token t then attends
+    to the quantised cache plus the generated tokens not yet appended and
+    itself (between window and window + F - 1 earlier ones once appends have
+    begun).  override: {t: {('cstat', r): ...}} per token.
     Returns per token a dict: recs (per-loop records of ``decode_token``), N
     (cached positions), T (window columns incl. the token), appended (None or
-    the ``append_token`` record of the token appended before it)."""
+    the list of ``append_token`` / ``append_block`` records made before it)."""
     override = override or {}
     R = sched["R"]
+    asym = sched.get("quant", "absmax") == "asym"
+    F = sched["g"] if asym else 1
     khat = [np.asarray(cache[r]["khat"], F32) for r in range(R)]
     vhat = [np.asarray(cache[r]["vhat"], F32) for r in range(R)]
     out = []
+    f = 0                                   # generated tokens appended so far
     for t in range(len(gen_q)):
         appended = None
-        if t >= window + 1:
-            u = t - window - 1
-            appended = append_token(gen_k[u], gen_v[u], sched)
+        while t - f >= window + F:
+            if asym:
+                rec = append_block(gen_k[f:f + F], gen_v[f:f + F], sched)
+                new_k = [rec[r]["khat"] for r in range(R)]
+                new_v = [rec[r]["vhat"] for r in range(R)]
+            else:
+                rec = append_token(gen_k[f], gen_v[f], sched)
+                new_k = [rec[r]["khat"][None] for r in range(R)]
+                new_v = [rec[r]["vhat"][None] for r in range(R)]
             for r in range(R):
-                khat[r] = np.concatenate([khat[r], appended[r]["khat"][None]], axis=0)
-                vhat[r] = np.concatenate([vhat[r], appended[r]["vhat"][None]], axis=0)
-        lo = max(0, t - window)
-        tk = [np.stack([np.asarray(gen_k[u][r], F32) for u in range(lo, t + 1)]) for r in range(R)]
-        tv = [np.stack([np.asarray(gen_v[u][r], F32) for u in range(lo, t + 1)]) for r in range(R)]
+                khat[r] = np.concatenate([khat[r], new_k[r]], axis=0)
+                vhat[r] = np.concatenate([vhat[r], new_v[r]], axis=0)
+            appended = (appended or []) + [rec]
+            f += F
+        tk = [np.stack([np.asarray(gen_k[u][r], F32) for u in range(f, t + 1)]) for r in range(R)]
+        tv = [np.stack([np.asarray(gen_v[u][r], F32) for u in range(f, t + 1)]) for r in range(R)]
         recs = decode_token(khat, vhat, gen_q[t], tk, tv, sched, override.get(t))
-        out.append(dict(recs=recs, N=khat[0].shape[0], T=t + 1 - lo, appended=appended))
+        out.append(dict(recs=recs, N=khat[0].shape[0], T=t + 1 - f, appended=appended))
     return out
