@@ -846,7 +846,8 @@ def bench_generate(args, w, np, torch, fl, synth):
     per-token latency over the next 16).  B sequences with resident prompt
     caches; each generated token runs R loops over the cache plus a bf16
     window of the most recent 64 generated tokens (App. E); once the window
-    is full, the token leaving it is appended to the quantised cache first.
+    is full, the token leaving it is appended to the quantised cache first
+    (under --quant asym the oldest g tokens leave together, as one key group).
     value = generated tokens/s over the timed tokens, B * timed / time."""
     from concurrent.futures import ThreadPoolExecutor
     B, N, H, d, R, g = w.extra["B"], w.N, w.H, w.d, w.R, w.g
@@ -856,7 +857,7 @@ def bench_generate(args, w, np, torch, fl, synth):
     for r in range(1, R):
         n_act.append(min(n_act[-1], max(1, int(np.ceil(w.rho[r] * N - 1e-9)))))
     run = fl.DecodeRunner(B, N, H, d, g, R, w.n_sink, n_act, w.kcols, w.bits, gen_tokens=n_gen,
-                          window=64)
+                          window=64, quant=quant_scheme(args, fl))
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -904,8 +905,10 @@ def bench_generate(args, w, np, torch, fl, synth):
         "value": round(B / (ms_per_tok / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": n_timed, "warmup": n_warm, "ms_per_step": round(ms_per_tok, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8/int4 codes, bf16 window, f32", "data": "synthetic",
-        "config": {"workload": w.name, "mode": "generate", "B": B, "N_prompt": N, "H": H, "d": d,
+        "dtype": ("uint4 codes" if args.quant == "asym" else "int8/int4 codes") + ", bf16 window, f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": "generate", "quant": args.quant, "B": B, "N_prompt": N,
+                   "H": H, "d": d,
                    "R": R, "g": g, "window": 64, "k_per_loop": w.kcols, "bits_per_loop": w.bits,
                    "context_at_timing": [n_before, run.cfg.N], "window_tokens_at_end": run.win.count - 1},
         "ms_per_token_min_max": [round(min(tok_ms), 4), round(max(tok_ms), 4)],

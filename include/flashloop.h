@@ -413,10 +413,15 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* w, fl_block_s
  * per-sequence capacities P = N_cap (or N) positions and R_l = rows_cap[l]
  * (or n_rows; level 0: P) rows.  Under FL_QUANT_ASYM the value offsets
  * follow the value scales' layout, and the key scales and offsets (one per
- * channel for every g rows) follow at b * ceil(R_l / g)*H*d floats.
+ * channel for every g rows) follow at b * G_l*H*d floats.  Key group i of a
+ * level covers rows [i*g, (i+1)*g) below the level's origin
+ * o_l = cfg->key_group_origin[l] (the last of them possibly partial) and,
+ * from the origin on, rows [o_l + j*g, o_l + (j+1)*g) for i = ceil(o_l/g) + j
+ * (the groups that generation appends); G_l = ceil(o_l/g) + ceil((R_l-o_l)/g)
+ * (ceil(R_l/g) with the default origin 0).
  * Requirements: N + T <= 12288 (T bf16 columns: 1, or the window count; the
  * probabilities stay in LDS); quantised levels: FL_QUANT_ABSMAX with an
- * int8 base, or FL_QUANT_ASYM (2-, 4- or 8-bit levels) without a window
+ * int8 base, or FL_QUANT_ASYM with 2-, 4- or 8-bit levels
  * (FL_ERR_UNSUPPORTED otherwise); a
  * sparse loop r keeps 4 * ((k + 1) + r * k) bytes in LDS, at most 48 KiB.
  */
@@ -427,18 +432,25 @@ typedef struct fl_decode_cfg {
      * (fl_decode_append); 0 = exactly N positions / n_rows rows: */
     int N_cap;                  /* positions (slot maps, level-0 rows)       */
     int rows_cap[FL_MAX_LEVELS]; /* rows of level l >= 1 (index l)           */
+    /* FL_QUANT_ASYM: the row (index 0: position) of each level at which the
+     * appended key groups begin -- the prompt's N and n_rows when the cache
+     * grows during generation; 0 (the default) = groups of g rows from row 0
+     * throughout.  Ignored under FL_QUANT_ABSMAX. */
+    int key_group_origin[FL_MAX_LEVELS];
 } fl_decode_cfg;
 
 /* Generation-time bf16 window (App. E: the most recent 64 tokens stay in
  * BF16).  Per loop r a ring of `cap` slots per sequence holds the loop-r
  * keys / values of the most recent generated tokens and of the token being
  * decoded: k[r-1], v[r-1] bf16 [B][cap][H][d].  The `count` valid slots are
- * 0..count-1 (which slot holds which token does not matter to attention: all
- * are earlier than or equal to the new token).  Every valid slot is an extra
- * key column of every loop, always included like the self column. */
+ * (start + i) mod cap, i = 0..count-1, 0 <= start < cap (which slot holds
+ * which token does not matter to attention: all are earlier than or equal to
+ * the new token).  Every valid slot is an extra key column of every loop,
+ * always included like the self column. */
 typedef struct fl_decode_window {
     int cap;
     int count;
+    int start;
     const void* k[FL_MAX_LEVELS];
     const void* v[FL_MAX_LEVELS];
 } fl_decode_window;
@@ -470,19 +482,28 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* st, const fl_decod
 
 /* ------------------------------------------------------------------------
  * fl_decode_append -- generation-time growth of the quantised cache (Sec.
- * 4.3, App. E): the token in ring slot `slot` of every loop's window (a
- * generated token, computed in all R loops) is appended to every sequence's
- * cache at position p = cfg->N: level 0 stores its loop-1 K/V quantised as
- * the base, level l >= 1 appends row n_rows_l holding the residual of its
- * loop-(l+1) K/V against its dequantised loop-l value (rows[n_rows_l] = p,
- * slot[p] = n_rows_l), with the arithmetic of fl_kv_residual_quant.  Then
- * cfg->N, st->cache.N and every st->cache.level[l].n_rows (l = 1..R-1) grow
- * by one.  The cache must have been allocated with capacities cfg->N_cap and
- * cfg->rows_cap, scheme FL_QUANT_ABSMAX, an int8 base and quantised levels.
- * Errors: FL_ERR_INVALID_ARG (NULL pointers, slot outside the ring, a
- * capacity exceeded), FL_ERR_UNSUPPORTED (cache format). */
+ * 4.3, App. E): the n tokens in ring slots (slot + j) mod cap, j = 0..n-1, of
+ * every loop's window (generated tokens, computed in all R loops) are
+ * appended, in that order, to every sequence's cache at positions
+ * p_j = cfg->N + j: level 0 stores their loop-1 K/V quantised as the base,
+ * level l >= 1 appends rows n_rows_l + j holding the residual of their
+ * loop-(l+1) K/V against their dequantised loop-l values
+ * (rows[n_rows_l + j] = p_j, slot[p_j] = n_rows_l + j), with the arithmetic
+ * of fl_kv_residual_quant.  Under FL_QUANT_ABSMAX each token is quantised on
+ * its own (any n >= 1).  Under FL_QUANT_ASYM the keys are quantised per
+ * channel over g rows, so n must be g and the block becomes one new key
+ * group of every level: cfg->N and each n_rows_l must lie a whole number of
+ * groups past cfg->key_group_origin (set the origins to the prompt's sizes
+ * before the first append); the value groups stay per token.  Then cfg->N,
+ * st->cache.N and every st->cache.level[l].n_rows (l = 1..R-1) grow by n.
+ * The cache must have been allocated with capacities cfg->N_cap and
+ * cfg->rows_cap (and, FL_QUANT_ASYM, the key groups those and the origins
+ * imply), quantised levels and, FL_QUANT_ABSMAX, an int8 base.
+ * Errors: FL_ERR_INVALID_ARG (NULL pointers, slots outside the ring, a
+ * capacity exceeded, a block not on a key-group boundary),
+ * FL_ERR_UNSUPPORTED (cache format, n != g under FL_QUANT_ASYM). */
 int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* st, const fl_decode_window* win,
-                     int slot, fl_stream_t stream);
+                     int slot, int n, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later

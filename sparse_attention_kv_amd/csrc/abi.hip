@@ -161,6 +161,18 @@ int decode_caps(const fl_decode_cfg* cfg, const fl_kv_cache& C, int upto, fl::De
         FL_REQUIRE(C.level[l].n_rows <= P.rows_cap[l], "level %d: n_rows %d exceeds rows_cap %d", l,
                    C.level[l].n_rows, P.rows_cap[l]);
     }
+    // asymmetric key groups: g rows from row 0 below the origin, g rows from
+    // the origin on (the groups appended during generation)
+    const int g = C.g;
+    for (int l = 0; l <= upto; ++l) {
+        const int o = C.scheme == FL_QUANT_ASYM ? cfg->key_group_origin[l] : 0;
+        const int cap = l == 0 ? P.pos_cap : P.rows_cap[l];
+        FL_REQUIRE(o >= 0 && o <= cap, "level %d: key_group_origin %d outside 0..%d", l, o, cap);
+        const int below = (o + g - 1) / g;
+        P.kg_origin[l] = o;
+        P.kg_pad[l] = below * g - o;
+        P.kg_count[l] = below + (cap - o + g - 1) / g;
+    }
     return FL_OK;
 }
 
@@ -686,6 +698,7 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     if (W) {
         FL_REQUIRE(W->cap >= 1 && W->count >= 1 && W->count <= W->cap, "window count %d / cap %d",
                    W->count, W->cap);
+        FL_REQUIRE(W->start >= 0 && W->start < W->cap, "window start %d / cap %d", W->start, W->cap);
         for (int l = (r >= 2 ? r - 2 : 0); l < r; ++l)
             FL_REQUIRE(W->k[l] && W->v[l], "window buffers of loop %d NULL", l + 1);
     }
@@ -696,11 +709,6 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, r - 1);
     if (rc) return rc;
-    // the asymmetric scheme's keys are quantised per channel over g rows of a
-    // level, which a token appended one at a time cannot complete: decode over
-    // such a cache runs without a generation window
-    if (C.scheme == FL_QUANT_ASYM && W)
-        return fail(FL_ERR_UNSUPPORTED, "decode: a generation window needs a FL_QUANT_ABSMAX cache");
     if (C.scheme == FL_QUANT_ABSMAX && C.level[0].bits != 8)
         return fail(FL_ERR_UNSUPPORTED, "decode: base level bits %d (8)", C.level[0].bits);
     for (int l = 1; l < r; ++l)
@@ -716,6 +724,7 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     P.out = S->out; P.lse = S->lse; P.mass_u = S->mass_u; P.out_u = S->out_u;
     P.n_tail = T;
     P.tail_cap = W ? W->cap : 1;
+    P.tail_start = W ? W->start : 0;
     // the bf16 columns of loop r (and r - 1, for a rebuild)
     auto tails = [&](fl::DecodeParams& Q, int loop, const void* ks, const void* vs) {
         Q.tail_k = W ? W->k[loop - 1] : ks;
@@ -775,7 +784,7 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
 }
 
 int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode_window* W, int slot,
-                     fl_stream_t stream) {
+                     int n, fl_stream_t stream) {
     FL_REQUIRE(cfg && S && W, "cfg/state/window NULL");
     const int B = cfg->B, N = cfg->N, H = cfg->H, d = cfg->d, R = cfg->R;
     FL_REQUIRE(B >= 1 && R >= 1 && R <= FL_MAX_LEVELS, "B=%d R=%d", B, R);
@@ -783,37 +792,50 @@ int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode_win
     FL_REQUIRE(C.N == N && C.H == H && C.d == d && C.g == cfg->g, "cache dims differ from cfg");
     int rc = check_cache(&C, R - 1);
     if (rc) return rc;
-    if (C.scheme != FL_QUANT_ABSMAX || C.level[0].bits != 8)
+    const bool asym = C.scheme == FL_QUANT_ASYM;
+    if (!asym && C.level[0].bits != 8)
         return fail(FL_ERR_UNSUPPORTED, "append: FL_QUANT_ABSMAX caches with an int8 base only");
     for (int l = 1; l < R; ++l)
         if (C.level[l].bits == 32)
             return fail(FL_ERR_UNSUPPORTED, "append: level %d is raw (quantised levels only)", l);
+    if (asym && n != C.g)
+        return fail(FL_ERR_UNSUPPORTED, "append: FL_QUANT_ASYM appends one key group (n = g = %d, not %d)",
+                    C.g, n);
+    FL_REQUIRE(n >= 1 && n <= W->cap, "append: %d tokens from a window of %d", n, W->cap);
     FL_REQUIRE(slot >= 0 && slot < W->cap, "slot %d outside the window of %d", slot, W->cap);
     for (int l = 0; l < R; ++l) FL_REQUIRE(W->k[l] && W->v[l], "window buffers of loop %d NULL", l + 1);
     fl::DecodeParams caps{};
     rc = decode_caps(cfg, C, R - 1, caps);
     if (rc) return rc;
-    FL_REQUIRE(N + 1 <= caps.pos_cap, "append: N_cap %d reached", caps.pos_cap);
+    FL_REQUIRE(N + n <= caps.pos_cap, "append: N_cap %d reached", caps.pos_cap);
     fl::AppendParams P{};
-    P.B = B; P.H = H; P.g = C.g; P.R = R; P.pos = N; P.slot = slot; P.win_cap = W->cap;
+    P.B = B; P.H = H; P.g = C.g; P.R = R; P.pos = N; P.slot = slot; P.n = n; P.win_cap = W->cap;
     P.pos_cap = caps.pos_cap;
     for (int l = 0; l < R; ++l) {
         P.lev[l] = C.level[l];
         P.bits[l] = C.level[l].bits;
         P.wk[l] = W->k[l];
         P.wv[l] = W->v[l];
+        P.kg_pad[l] = caps.kg_pad[l];
+        P.kg_count[l] = caps.kg_count[l];
+        const int row0 = l == 0 ? N : C.level[l].n_rows;
         if (l >= 1) {
             P.rows_cap[l] = caps.rows_cap[l];
-            P.n_rows[l] = C.level[l].n_rows;
-            FL_REQUIRE(C.level[l].n_rows + 1 <= caps.rows_cap[l], "append: level %d rows_cap %d reached",
-                       l, caps.rows_cap[l]);
+            P.n_rows[l] = row0;
+            FL_REQUIRE(row0 + n <= caps.rows_cap[l], "append: level %d rows_cap %d reached", l,
+                       caps.rows_cap[l]);
         }
+        if (asym)
+            FL_REQUIRE(row0 >= caps.kg_origin[l] && (row0 - caps.kg_origin[l]) % C.g == 0,
+                       "append: level %d row %d does not start a key group (key_group_origin %d, g %d)", l,
+                       row0, caps.kg_origin[l], C.g);
     }
     hipStream_t st = (hipStream_t)stream;
-    FL_HIP(timed("decode_append", st, [&] { return fl::launch_decode_append(d, P, st); }), "append");
-    cfg->N = N + 1;
-    C.N = N + 1;
-    for (int l = 1; l < R; ++l) C.level[l].n_rows += 1;
+    FL_HIP(timed("decode_append", st, [&] { return fl::launch_decode_append(d, C.scheme, P, st); }),
+           "append");
+    cfg->N = N + n;
+    C.N = N + n;
+    for (int l = 1; l < R; ++l) C.level[l].n_rows += n;
     return FL_OK;
 }
 

@@ -43,8 +43,8 @@ struct SeqLevel {
 // level l of sequence b: the B sequences are stored back to back with the
 // per-sequence capacities (positions pos_cap; rows rows_cap[l] for l >= 1).
 // Absmax and value scales: one per (row, head, g channels); asymmetric key
-// scales and offsets: one per (g rows, head, channel), so a sequence holds
-// ceil(rows / g) row groups of them.
+// scales and offsets: one per (key group of g rows, head, channel), a
+// sequence holding kg_count[l] groups of them.
 template <int D, bool ASYM>
 __device__ __forceinline__ SeqLevel seq_level(const DecodeParams& P, int l, int b, int which) {
     const fl_kv_cache& c = P.cache;
@@ -54,11 +54,19 @@ __device__ __forceinline__ SeqLevel seq_level(const DecodeParams& P, int l, int 
     s.bits = L.bits;
     s.codes = reinterpret_cast<const uint8_t*>(which ? L.v_codes : L.k_codes) +
               b * (rows * c.H * D * L.bits / 8);
-    const long sstride = (ASYM && which == 0) ? ((rows + c.g - 1) / c.g) * c.H * D : rows * c.H * (D / c.g);
+    const long sstride = (ASYM && which == 0) ? (long)P.kg_count[l] * c.H * D : rows * c.H * (D / c.g);
     s.scales = (which ? L.v_scale : L.k_scale) + b * sstride;
     s.zeros = ASYM ? (which ? L.v_zero : L.k_zero) + b * sstride : nullptr;
     s.slot = l == 0 ? nullptr : L.slot + (long)b * P.pos_cap;
     return s;
+}
+
+// Asymmetric key group of row x of level l: groups of g rows from row 0 up
+// to the level's origin (the prompt's rows, the last group possibly
+// partial), then groups of g rows from the origin (appended during
+// generation).
+__device__ __forceinline__ int key_group(const DecodeParams& P, int l, int x) {
+    return (x >= P.kg_origin[l] ? x + P.kg_pad[l] : x) / P.cache.g;
 }
 
 // 16 consecutive unsigned codes (asymmetric scheme) starting at code index e
@@ -159,7 +167,11 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     float* sc = dyn;
     int* rowtab = reinterpret_cast<int*>(dyn + kt);
     // tail column t of this (sequence, head): element offset of its row
-    auto tail_off = [&](int t) -> long { return (((long)b * P.tail_cap + t) * H + h) * D; };
+    auto tail_off = [&](int t) -> long {
+        int sl = P.tail_start + t;
+        if (sl >= P.tail_cap) sl -= P.tail_cap;
+        return (((long)b * P.tail_cap + sl) * H + h) * D;
+    };
     for (int c = tid; c < D; c += DT)
         qs[c] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.q)[qo + c]);
     if (SPARSE) {
@@ -189,7 +201,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         // per pass, so a key group's per-channel scales and offsets (shared by
         // g rows) are loaded once per group for this lane's 16 channels and
         // folded into the query: q . (code * s + z) = (q s) . code + q . z
-        // (g is a multiple of CPW, so the CPW columns of a step share a group)
+        // (the columns of one step share a group except across the origin of
+        // the appended groups, where each lane follows its own column)
         const SeqLevel L = seq_level<D, ASYM>(P, 0, b, 0);
         int gcur = -1;
         float qs[16], qz = 0.0f;
@@ -197,11 +210,10 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
             float part[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int cb = c0 + w * (CPW * U) + u * CPW;   // first column of this step
-                const int c = cb + cl;
+                const int c = c0 + w * (CPW * U) + u * CPW + cl;
                 part[u] = 0.0f;
-                const int cg = cb / C.g;
-                if (cb < k && cg != gcur) {
+                const int cg = key_group(P, 0, c);
+                if (c < k && cg != gcur) {
                     const long si = ((long)cg * H + h) * D + cs * 16;
                     float sv[16], zv[16];
                     load_f32x16(L.scales + si, sv);
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                         if (ASYM) {
                             // x = code * s + z per channel (scale / offset of the row's group)
                             load_ucodes16(L.codes, rr * D + cs * 16, L.bits, x);
-                            const long si = ((long)(row / C.g) * H + h) * D + cs * 16;
+                            const long si = ((long)key_group(P, l, row) * H + h) * D + cs * 16;
                             float sv[16], zv[16];
                             load_f32x16(L.scales + si, sv);
                             load_f32x16(L.zeros + si, zv);

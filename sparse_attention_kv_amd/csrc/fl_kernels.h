@@ -72,11 +72,20 @@ struct DecodeParams {
     const void* tail_k;     // bf16 [B][tail_cap][H][d]: the always-included columns
     const void* tail_v;     //   (the token's own, and the generation window)
     int n_tail, tail_cap;
+    int tail_start;         // tail column t is ring slot (tail_start + t) mod tail_cap
+    // asymmetric keys: group of row x of level l is (x + (x >= origin ? pad : 0)) / g,
+    // and a sequence holds kg_count[l] groups of H*d scales / offsets
+    int kg_origin[FL_MAX_LEVELS];
+    int kg_pad[FL_MAX_LEVELS];
+    int kg_count[FL_MAX_LEVELS];
     float* out; float* lse; float* mass_u; float* out_u; float* col_stat;
 };
 
 struct AppendParams {
     int B, H, g, R, pos, slot, win_cap, pos_cap;
+    int n;                       // tokens appended (ring slots slot .. slot + n - 1 mod win_cap)
+    int kg_pad[FL_MAX_LEVELS];   // asymmetric keys: as in DecodeParams
+    int kg_count[FL_MAX_LEVELS];
     int rows_cap[FL_MAX_LEVELS];
     int n_rows[FL_MAX_LEVELS];   // rows already stored per level (the new row's index)
     int bits[FL_MAX_LEVELS];
@@ -93,7 +102,7 @@ static_assert(sizeof(fl_kv_cache) + sizeof(QTiles) + 48 <= kKernargChecked,
               "k_gather_q arguments exceed the checked kernel-argument size");
 static_assert(sizeof(DecodeParams) + 16 <= kKernargChecked,
               "k_decode arguments exceed the checked kernel-argument size");
-static_assert(sizeof(AppendParams) <= kKernargChecked,
+static_assert(sizeof(AppendParams) + 16 <= kKernargChecked,
               "k_decode_append arguments exceed the checked kernel-argument size");
 static_assert(sizeof(fl_kv_cache) + 64 <= kKernargChecked,
               "cache-descriptor kernels exceed the checked kernel-argument size");
@@ -122,7 +131,7 @@ hipError_t launch_copy_or_iota(const int32_t* src, int32_t* dst, long n, long ro
 // quant.hip
 hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float* out,
                           hipStream_t st);
-hipError_t launch_decode_append(int d, const AppendParams& P, hipStream_t st);
+hipError_t launch_decode_append(int d, int scheme, const AppendParams& P, hipStream_t st);
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
                         const void* v_new, int gathered, hipStream_t st);
 // attn.hip

@@ -307,17 +307,20 @@ hipError_t launch_dequant(const fl_kv_cache& cache, int level, int which, float*
     return hipGetLastError();
 }
 
-// Generation-time append: the token in window slot P.slot (computed in all R
-// loops) becomes position P.pos of every sequence's cache.  One workgroup per
-// (sequence, K or V); a thread owns 8 channels per pass.  Level 0 quantises
-// the loop-1 value (row = position); level l >= 1 appends row n_rows[l] with
-// the residual of the loop-(l+1) value against the running dequantised value,
-// which is then updated with the level's own dequantised term -- the same
-// roundings, in the same order, as k_quant and its dequantisation chain.
+// Generation-time append: the P.n tokens in window slots P.slot + z (mod the
+// ring; computed in all R loops) become positions P.pos + z of every
+// sequence's cache.  One workgroup per (sequence, K or V, token z); a thread
+// owns 8 channels per pass.  Level 0 quantises the loop-1 value (row =
+// position); level l >= 1 appends row n_rows[l] + z with the residual of the
+// loop-(l+1) value against the running dequantised value, which is then
+// updated with the level's own dequantised term -- the same roundings, in
+// the same order, as k_quant and its dequantisation chain.
 __global__ __launch_bounds__(256) void k_decode_append(AppendParams P, int D) {
-    const int b = blockIdx.x, which = blockIdx.y;
+    const int b = blockIdx.x, which = blockIdx.y, z = blockIdx.z;
     const int HD = P.H * D;
     const int g = P.g;
+    int wslot = P.slot + z;
+    if (wslot >= P.win_cap) wslot -= P.win_cap;
     for (int base = 0; base < HD; base += 256 * 8) {
         const int ch = base + threadIdx.x * 8;
         const bool live = ch < HD;
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(256) void k_decode_append(AppendParams P, int D) {
             const void* src = which ? P.wv[l] : P.wk[l];
             float x[8];
             if (live) {
-                load8_f32(src, ((long)b * P.win_cap + P.slot) * HD + ch, FL_BF16, x);
+                load8_f32(src, ((long)b * P.win_cap + wslot) * HD + ch, FL_BF16, x);
                 if (l > 0) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) x[i] = x[i] - xh[i];
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) void k_decode_append(AppendParams P, int D) {
             if (live) {
                 const fl_kv_level& L = P.lev[l];
                 const long rows = l == 0 ? P.pos_cap : P.rows_cap[l];
-                const long row = l == 0 ? P.pos : P.n_rows[l];
+                const long row = (l == 0 ? P.pos : P.n_rows[l]) + z;
                 uint8_t* codes = reinterpret_cast<uint8_t*>(which ? L.v_codes : L.k_codes) +
                                  (long)b * (rows * HD * bits / 8);
                 float* scales = (which ? L.v_scale : L.k_scale) + (long)b * (rows * (HD / g));
@@ -376,14 +379,180 @@ __global__ __launch_bounds__(256) void k_decode_append(AppendParams P, int D) {
         for (int l = 1; l < P.R; ++l) {
             int32_t* rows = const_cast<int32_t*>(P.lev[l].rows) + (long)b * P.rows_cap[l];
             int32_t* slot = const_cast<int32_t*>(P.lev[l].slot) + (long)b * P.pos_cap;
-            rows[P.n_rows[l]] = P.pos;
-            slot[P.pos] = P.n_rows[l];
+            rows[P.n_rows[l] + z] = P.pos + z;
+            slot[P.pos + z] = P.n_rows[l] + z;
         }
     }
 }
 
-hipError_t launch_decode_append(int d, const AppendParams& P, hipStream_t st) {
-    hipLaunchKernelGGL(k_decode_append, dim3(P.B, 2), dim3(256), 0, st, P, d);
+// Generation-time append under the asymmetric scheme: the G tokens in window
+// slots P.slot + j (mod the ring) become positions P.pos + j and one new key
+// group of every level (group (row0 + kg_pad) / G of the level's first new
+// row row0).  One workgroup per (sequence, 256 channels, K or V) with the
+// thread layout of k_quant_kchan: lane l of wave w owns 8 channels (l mod 32)
+// and the tokens rl, rl + 8, ... (rl = 2w + l/32), keeping their inputs and
+// running dequantised values in registers across the levels.  Keys: per
+// channel minimum / maximum over the G tokens (lane pairs, then the 4 waves
+// through LDS); values: per token over G channels (G/8 adjacent lanes).  The
+// codes, scales and offsets, and the chain xhat += code * s + z, round as
+// k_quant_kchan, k_quant and their dequantisation do.
+template <int G>
+__global__ __launch_bounds__(256) void k_decode_append_asym(AppendParams P, int D) {
+    constexpr int RPT = G / 8; // tokens per thread
+    __shared__ float s_mn[4][32][8], s_mx[4][32][8];
+    const int b = blockIdx.x, which = blockIdx.z;
+    const int HD = P.H * D;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cl = lane & 31;
+    const int rl = wave * 2 + (lane >> 5);
+    const int ch = blockIdx.y * 256 + cl * 8;
+    const bool live = ch < HD;
+    float xh[RPT][8];
+    for (int l = 0; l < P.R; ++l) {
+        const void* src = which ? P.wv[l] : P.wk[l];
+        float x[RPT][8];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            int ws = P.slot + rl + 8 * j;
+            if (ws >= P.win_cap) ws -= P.win_cap;
+            if (live) {
+                load8_f32(src, ((long)b * P.win_cap + ws) * HD + ch, FL_BF16, x[j]);
+                if (l > 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[j][i] = x[j][i] - xh[j][i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[j][i] = 0.0f;
+            }
+        }
+        const int bits = P.bits[l];
+        const int qmax = (1 << bits) - 1;
+        const fl_kv_level& L = P.lev[l];
+        const long rows = l == 0 ? P.pos_cap : P.rows_cap[l];
+        const long row0 = l == 0 ? P.pos : P.n_rows[l];
+        uint8_t* codes = reinterpret_cast<uint8_t*>(which ? L.v_codes : L.k_codes) +
+                         (long)b * (rows * HD * bits / 8);
+        if (which == 0) {
+            float mn[8], mx[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { mn[i] = x[0][i]; mx[i] = x[0][i]; }
+#pragma unroll
+            for (int j = 1; j < RPT; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (x[j][i] < mn[i]) mn[i] = x[j][i];
+                    if (x[j][i] > mx[i]) mx[i] = x[j][i];
+                }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float omn = __shfl_xor(mn[i], 32), omx = __shfl_xor(mx[i], 32);
+                if (omn < mn[i]) mn[i] = omn;
+                if (omx > mx[i]) mx[i] = omx;
+            }
+            __syncthreads(); // the previous level's reads of s_mn / s_mx are done
+            if (lane < 32) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { s_mn[wave][cl][i] = mn[i]; s_mx[wave][cl][i] = mx[i]; }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                mn[i] = s_mn[0][cl][i]; mx[i] = s_mx[0][cl][i];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+                    if (s_mn[w][cl][i] < mn[i]) mn[i] = s_mn[w][cl][i];
+                    if (s_mx[w][cl][i] > mx[i]) mx[i] = s_mx[w][cl][i];
+                }
+            }
+            float s[8], zz[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                zz[i] = mn[i] + 0.0f;
+                const float range = mx[i] - zz[i];
+                s[i] = range / (float)qmax + 0.0f;
+            }
+            if (live) {
+                if (rl == 0) {
+                    const long si = ((long)b * P.kg_count[l] + (row0 + P.kg_pad[l]) / G) * HD + ch;
+                    *reinterpret_cast<float4*>(L.k_scale + si) = make_float4(s[0], s[1], s[2], s[3]);
+                    *reinterpret_cast<float4*>(L.k_scale + si + 4) = make_float4(s[4], s[5], s[6], s[7]);
+                    *reinterpret_cast<float4*>(L.k_zero + si) = make_float4(zz[0], zz[1], zz[2], zz[3]);
+                    *reinterpret_cast<float4*>(L.k_zero + si + 4) = make_float4(zz[4], zz[5], zz[6], zz[7]);
+                }
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) {
+                    uint64_t packed = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t q = asym_code(x[j][i], s[i], zz[i], qmax);
+                        packed |= (uint64_t)q << (bits * i);
+                        const float p = (float)q * s[i];
+                        const float t = p + zz[i];
+                        xh[j][i] = l == 0 ? t : xh[j][i] + t;
+                    }
+                    store_codes8(codes, (row0 + rl + 8 * j) * HD + ch, bits, packed);
+                }
+            }
+        } else {
+            float* vs = L.v_scale + (long)b * (rows * (HD / G));
+            float* vz = L.v_zero + (long)b * (rows * (HD / G));
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                float mn = x[j][0], mx = x[j][0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) {
+                    if (x[j][i] < mn) mn = x[j][i];
+                    if (x[j][i] > mx) mx = x[j][i];
+                }
+#pragma unroll
+                for (int o = 1; o < G / 8; o <<= 1) {
+                    const float omn = __shfl_xor(mn, o), omx = __shfl_xor(mx, o);
+                    if (omn < mn) mn = omn;
+                    if (omx > mx) mx = omx;
+                }
+                const float zz = mn + 0.0f;
+                const float range = mx - zz;
+                const float s = range / (float)qmax + 0.0f;
+                if (live) {
+                    const long e = (row0 + rl + 8 * j) * HD + ch;
+                    uint64_t packed = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t q = asym_code(x[j][i], s, zz, qmax);
+                        packed |= (uint64_t)q << (bits * i);
+                        const float p = (float)q * s;
+                        const float t = p + zz;
+                        xh[j][i] = l == 0 ? t : xh[j][i] + t;
+                    }
+                    store_codes8(codes, e, bits, packed);
+                    if ((ch % G) == 0) {
+                        vs[e / G] = s;
+                        vz[e / G] = zz;
+                    }
+                }
+            }
+        }
+    }
+    if (which == 0 && blockIdx.y == 0 && threadIdx.x < G) {
+        const int j = threadIdx.x;
+        for (int l = 1; l < P.R; ++l) {
+            int32_t* rows = const_cast<int32_t*>(P.lev[l].rows) + (long)b * P.rows_cap[l];
+            int32_t* slot = const_cast<int32_t*>(P.lev[l].slot) + (long)b * P.pos_cap;
+            rows[P.n_rows[l] + j] = P.pos + j;
+            slot[P.pos + j] = P.n_rows[l] + j;
+        }
+    }
+}
+
+hipError_t launch_decode_append(int d, int scheme, const AppendParams& P, hipStream_t st) {
+    if (scheme == FL_QUANT_ASYM) {
+        const dim3 grid(P.B, (unsigned)((P.H * d + 255) / 256), 2);
+        if (P.g == 64) hipLaunchKernelGGL(k_decode_append_asym<64>, grid, dim3(256), 0, st, P, d);
+        else hipLaunchKernelGGL(k_decode_append_asym<32>, grid, dim3(256), 0, st, P, d);
+    } else {
+        hipLaunchKernelGGL(k_decode_append, dim3(P.B, 2, P.n), dim3(256), 0, st, P, d);
+    }
     return hipGetLastError();
 }
 

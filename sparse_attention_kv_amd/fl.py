@@ -108,11 +108,11 @@ class FlBlockState(ctypes.Structure):
 class FlDecodeCfg(ctypes.Structure):
     _fields_ = [("B", c_int), ("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("R", c_int),
                 ("n_sink", c_int), ("k_cols", c_int * MAX_LEVELS), ("N_cap", c_int),
-                ("rows_cap", c_int * MAX_LEVELS)]
+                ("rows_cap", c_int * MAX_LEVELS), ("key_group_origin", c_int * MAX_LEVELS)]
 
 
 class FlDecodeWindow(ctypes.Structure):
-    _fields_ = [("cap", c_int), ("count", c_int), ("k", c_void_p * MAX_LEVELS),
+    _fields_ = [("cap", c_int), ("count", c_int), ("start", c_int), ("k", c_void_p * MAX_LEVELS),
                 ("v", c_void_p * MAX_LEVELS)]
 
 
@@ -159,7 +159,7 @@ def lib():
                                      POINTER(FlDecodeInputs), c_int, c_void_p]
         L.fl_sq_err.argtypes = [c_void_p, c_void_p, c_long, c_void_p, c_void_p, c_size_t, c_void_p]
         L.fl_decode_append.argtypes = [POINTER(FlDecodeCfg), POINTER(FlDecodeState),
-                                       POINTER(FlDecodeWindow), c_int, c_void_p]
+                                       POINTER(FlDecodeWindow), c_int, c_int, c_void_p]
         L.fl_kv_dequant.argtypes = [POINTER(FlKvCache), c_int, c_int, c_void_p, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
@@ -279,12 +279,13 @@ def fl_decode_step(cfg: FlDecodeCfg, state: FlDecodeState, inputs: FlDecodeInput
     _check("fl_decode_step", rc)
 
 
-def fl_decode_append(cfg: FlDecodeCfg, state: FlDecodeState, win: FlDecodeWindow, slot,
+def fl_decode_append(cfg: FlDecodeCfg, state: FlDecodeState, win: FlDecodeWindow, slot, n=1,
                      stream=None):
-    """Sec. 4.3 / App. E during generation: append the token in window slot
-    `slot` to every sequence's cache (cfg.N and the level row counts grow)."""
+    """Sec. 4.3 / App. E during generation: append the n tokens in window
+    slots slot .. slot + n - 1 (mod the ring) to every sequence's cache (cfg.N
+    and the level row counts grow by n; n = g under the asymmetric scheme)."""
     _check("fl_decode_append", lib().fl_decode_append(ctypes.byref(cfg), ctypes.byref(state),
-                                                      ctypes.byref(win), slot, _stream(stream)))
+                                                      ctypes.byref(win), slot, n, _stream(stream)))
 
 
 def fl_kv_dequant(cache: FlKvCache, level, which, out, stream=None):
@@ -513,16 +514,18 @@ class DecodeRunner:
     def __init__(self, B, N, H, d, g, R, n_sink, n_active, k_cols, bits, gen_tokens=0, window=64,
                  quant=FL_QUANT_ABSMAX, device="cuda"):
         """gen_tokens > 0 prepares generation: caches with room for that many
-        appended positions and per-loop bf16 window rings of window + 1 slots
-        (the window and the token being decoded).  quant: the caches' scheme
-        (FL_QUANT_ASYM: the paper's quantiser, decode without generation)."""
-        if quant == FL_QUANT_ASYM and gen_tokens:
-            raise ValueError("generation appends need the FL_QUANT_ABSMAX scheme")
+        appended positions and per-loop bf16 window rings of window + F slots
+        (the window, the tokens waiting to leave it together and the token
+        being decoded); tokens leave the window F at a time, F = 1 under the
+        absmax scheme and F = g under FL_QUANT_ASYM (the paper's quantiser,
+        whose keys are quantised per channel over g rows: each appended block
+        is a key group of its own, from the prompt's sizes on)."""
         dev = torch.device(device)
         self.B, self.N, self.H, self.d, self.g, self.R = B, N, H, d, g, R
         self.quant = quant
         self.n_active, self.k_cols, self.bits = list(n_active), list(k_cols), list(bits)
         self.gen_tokens, self.window = gen_tokens, window
+        self.flush = g if quant == FL_QUANT_ASYM else 1
         self._keep = []
 
         def buf(shape, dt):
@@ -539,6 +542,9 @@ class DecodeRunner:
             cfg.N_cap = cap_pos
             for r in range(1, R):
                 cfg.rows_cap[r] = n_active[r] + gen_tokens
+            if quant == FL_QUANT_ASYM:
+                for r in range(R):
+                    cfg.key_group_origin[r] = N if r == 0 else n_active[r]
         self.cfg = cfg
         st = FlDecodeState()
         C = st.cache
@@ -551,8 +557,10 @@ class DecodeRunner:
                       v=buf((B, nc, H, d * bits[r] // 8), torch.uint8),
                       vs=buf((B, nc, H, d // g), torch.float32))
             if quant == FL_QUANT_ASYM:
-                # keys: a scale and offset per channel for every g rows
-                ng = (nc + g - 1) // g
+                # keys: a scale and offset per channel for every g rows, the
+                # appended rows in groups of their own from the origin on
+                o = cfg.key_group_origin[r]
+                ng = (o + g - 1) // g + (nc - o + g - 1) // g
                 cb.update(ks=buf((B, ng, H, d), torch.float32), kz=buf((B, ng, H, d), torch.float32),
                           vz=buf((B, nc, H, d // g), torch.float32))
             else:
@@ -583,9 +591,9 @@ class DecodeRunner:
         self.win = None
         if gen_tokens:
             wn = FlDecodeWindow()
-            wn.cap, wn.count = window + 1, 0
-            self.win_k = [buf((B, window + 1, H, d), torch.bfloat16) for _ in range(R)]
-            self.win_v = [buf((B, window + 1, H, d), torch.bfloat16) for _ in range(R)]
+            wn.cap, wn.count, wn.start = window + self.flush, 0, 0
+            self.win_k = [buf((B, wn.cap, H, d), torch.bfloat16) for _ in range(R)]
+            self.win_v = [buf((B, wn.cap, H, d), torch.bfloat16) for _ in range(R)]
             for r in range(R):
                 wn.k[r], wn.v[r] = _p(self.win_k[r]), _p(self.win_v[r])
             self.win = wn
@@ -629,17 +637,19 @@ class DecodeRunner:
 
     def generate(self, q, k, v, stream=None, after_loop=None):
         """Decode the next generated token of every sequence through all R
-        loops.  q, k, v: lists of R bf16 device tensors [B][H][d].  The ring
-        slot of the oldest window token is appended to the cache first (once
-        the window is full), then overwritten with this token's K/V."""
+        loops.  q, k, v: lists of R bf16 device tensors [B][H][d].  When the
+        ring is full, its oldest F tokens are appended to the cache first and
+        leave it; this token's K/V then take the next free slot."""
         win, t = self.win, self.t
-        slot = t % win.cap
-        if t >= win.cap:
-            fl_decode_append(self.cfg, self.state, win, slot, stream)
+        if win.count == win.cap:
+            fl_decode_append(self.cfg, self.state, win, win.start, self.flush, stream)
+            win.start = (win.start + self.flush) % win.cap
+            win.count -= self.flush
+        slot = (win.start + win.count) % win.cap
         for r in range(self.R):
             self.win_k[r][:, slot].copy_(k[r])
             self.win_v[r][:, slot].copy_(v[r])
-        win.count = min(t + 1, win.cap)
+        win.count += 1
         inp = FlDecodeInputs()
         inp.win = ctypes.pointer(win)
         for r in range(1, self.R + 1):

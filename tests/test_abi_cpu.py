@@ -181,3 +181,34 @@ def test_decode_step_rejects(L):
     st.cache = _cache(N=64, H=2, d=128, g=64, bits=(8, 4))
     assert L.fl_decode_step(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(inp), 1, None) == -1
     assert "q/k_self/v_self" in _err(L)
+
+
+def test_decode_append_rejects(L):
+    cfg = fl.FlDecodeCfg()
+    cfg.B, cfg.N, cfg.H, cfg.d, cfg.g, cfg.R, cfg.n_sink = 2, 64, 2, 128, 64, 2, 4
+    cfg.N_cap, cfg.rows_cap[1] = 256, 200
+    st = fl.FlDecodeState()
+    st.cache = _cache(N=64, bits=(4, 4))
+    st.cache.scheme = fl.FL_QUANT_ASYM
+    for lv in range(2):
+        st.cache.level[lv].k_zero = st.cache.level[lv].v_zero = FAKE
+    win = fl.FlDecodeWindow()
+    win.cap, win.count = 128, 128
+    for lv in range(2):
+        win.k[lv] = win.v[lv] = FAKE
+    app = lambda slot, n: L.fl_decode_append(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(win),
+                                             slot, n, None)
+    # one token cannot complete a per-channel key group of g rows
+    assert app(0, 1) == -2 and "key group" in _err(L)
+    # level 1 holds 32 rows: with the default origin 0 a block would straddle
+    # the prompt's partial group
+    assert app(0, 64) == -1 and "does not start a key group" in _err(L)
+    cfg.key_group_origin[1] = 300
+    assert app(0, 64) == -1 and "key_group_origin" in _err(L)
+    cfg.key_group_origin[1] = 32
+    assert app(128, 64) == -1 and "slot" in _err(L)
+    cfg.N_cap = 100
+    assert app(0, 64) == -1 and "N_cap" in _err(L)
+    # absmax: the base must be int8
+    st.cache.scheme = fl.FL_QUANT_ABSMAX
+    assert app(0, 1) == -2 and "base level bits 4" in _err(L)

@@ -3,7 +3,10 @@ tokens, cache appends; Sec. 4.2 per-token column re-selection) against the
 generation oracle: for every generated token and loop, the column sets
 exactly (given the GPU's own statistics), outputs / lse / cached mass and
 partial output within rel-L2 1e-2 and max-abs 3e-2; every appended token's
-cache rows (codes, scales, row lists, slot maps) bit-exact."""
+cache rows (codes, scales, row lists, slot maps) bit-exact.  Under the
+paper's quantiser (App. E) tokens leave the window g at a time as one key
+group per level; the block's codes, key scales / offsets (at the group past
+the prompt's own) and per-token value scales / offsets are bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -17,18 +20,19 @@ from gpu_chain import assert_close, assert_close_scaled, counts, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _w(B, N, H, d, g, kcols, bits, rho, seed):
+def _w(B, N, H, d, g, kcols, bits, rho, seed, quant="absmax"):
     w = synth.WORKLOADS["decode64x8k"].scaled(N=N, H=H, d=d, g=g, R=len(kcols), kcols=list(kcols),
                                               bits=list(bits), rho=list(rho), seed=seed)
-    w.extra = dict(B=B)
+    w.extra = dict(B=B, quant=quant)
     return w
 
 
 def _run_gpu(w, n_gen, window):
     B, N, H, d, R = w.extra["B"], w.N, w.H, w.d, w.R
     n_act = counts(w)
+    quant = fl.FL_QUANT_ASYM if w.extra["quant"] == "asym" else fl.FL_QUANT_ABSMAX
     run = fl.DecodeRunner(B, N, H, d, w.g, R, w.n_sink, n_act, w.kcols, w.bits,
-                          gen_tokens=n_gen, window=window)
+                          gen_tokens=n_gen, window=window, quant=quant)
     xs = {}
     tok = {key: np.empty((n_gen, R, B, H, d), np.uint16) for key in ("gen_q", "gen_k", "gen_v")}
     for b in range(B):
@@ -68,7 +72,7 @@ def _run_gpu(w, n_gen, window):
 
 
 def _check(w, b, x, G, run, window):
-    sched = w.sched()
+    sched = dict(w.sched(), quant=w.extra["quant"])
     f = synth.bf16_bits_to_f32
     cache = od.build_cache([f(a) for a in x["k"]], [f(a) for a in x["v"]], x["stat"], sched)
     gq = [[f(a) for a in tt] for tt in x["gen_q"]]
@@ -96,9 +100,11 @@ def _check(w, b, x, G, run, window):
                          ref_norm=float(np.linalg.norm(orr["out"])))
             if orr["cstat"] is not None:
                 assert_close_scaled(gr["cstat"][b], orr["cstat"], f"token {t} loop {r} cstat")
-        app = o["appended"]
-        if app is not None:
-            u = o["N"] - w.N - 1                  # index of the appended token
+        for i, app in enumerate(o["appended"] or []):
+            if sched["quant"] == "asym":
+                _check_block(w, b, o, i, app, run, n_act)
+                continue
+            u = o["N"] - w.N - len(o["appended"]) + i   # index of the appended token
             pos = w.N + u
             for r in range(1, w.R + 1):
                 row = pos if r == 1 else n_act[r - 1] + u
@@ -118,15 +124,49 @@ def _check(w, b, x, G, run, window):
           flush=True)
 
 
+def _check_block(w, b, o, i, app, run, n_act):
+    """Block i of the appends made before one token (asymmetric scheme): g
+    tokens as one new key group of every level."""
+    g = w.g
+    u0 = o["N"] - w.N - g * (len(o["appended"]) - i)   # first appended token's index
+    bits32 = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    for r in range(1, w.R + 1):
+        origin = w.N if r == 1 else n_act[r - 1]
+        row0 = origin + u0
+        grp = (origin + g - 1) // g + u0 // g
+        cb, lv = run.codes[r - 1], app[r - 1]
+        for kv in ("k", "v"):
+            np.testing.assert_array_equal(cb[kv][b, row0:row0 + g].cpu().numpy(),
+                                          oracle.pack_codes(lv[kv + "_codes"], w.bits[r - 1]),
+                                          err_msg=f"block at {u0}: {kv} codes, level {r - 1}")
+        np.testing.assert_array_equal(bits32(cb["ks"][b, grp].cpu().numpy()), bits32(lv["k_scale"][0]))
+        np.testing.assert_array_equal(bits32(cb["kz"][b, grp].cpu().numpy()), bits32(lv["k_zero"][0]))
+        np.testing.assert_array_equal(bits32(cb["vs"][b, row0:row0 + g].cpu().numpy()),
+                                      bits32(lv["v_scale"]))
+        np.testing.assert_array_equal(bits32(cb["vz"][b, row0:row0 + g].cpu().numpy()),
+                                      bits32(lv["v_zero"]))
+        if r > 1:
+            pos = w.N + u0 + np.arange(g)
+            np.testing.assert_array_equal(run.rows[r - 1][b, row0:row0 + g].cpu().numpy(), pos)
+            np.testing.assert_array_equal(run.slot[r - 1][b, pos].cpu().numpy(), row0 + np.arange(g))
+
+
 @pytest.mark.parametrize("name,B,N,H,d,g,kcols,bits,rho,n_gen,window", [
     ("small_window", 2, 300, 2, 128, 64, (300, 96, 64), (8, 4, 2), (1.0, 0.4, 0.2), 14, 4),
     ("window64", 2, 257, 2, 128, 64, (257, 100, 60, 60), (8, 4, 4, 2), (1.0, 0.5, 0.25, 0.1), 70, 64),
     ("d64_g32", 3, 411, 3, 64, 32, (411, 128, 128), (8, 2, 4), (1.0, 0.3, 0.3), 12, 6),
     # no window: every earlier generated token is appended before the next one
     ("no_window", 2, 200, 2, 128, 64, (200, 80, 48), (8, 4, 2), (1.0, 0.4, 0.2), 6, 0),
+    # the paper's quantiser: the window's oldest g tokens leave together as a
+    # key group of their own (prompts of ragged length, so the prompt's last
+    # group is partial and the appended groups start at its end)
+    ("asym_window64", 2, 257, 2, 128, 64, (257, 100, 60, 60), (4, 4, 4, 4), (1.0, 0.5, 0.25, 0.1),
+     132, 64),
+    ("asym_d64_g32", 3, 411, 3, 64, 32, (411, 128, 128), (8, 2, 4), (1.0, 0.3, 0.3), 72, 6),
+    ("asym_no_window", 2, 200, 2, 64, 32, (200, 80, 48), (4, 4, 2), (1.0, 0.4, 0.2), 66, 0),
 ])
 def test_generation_matches_oracle(name, B, N, H, d, g, kcols, bits, rho, n_gen, window):
-    w = _w(B, N, H, d, g, kcols, bits, rho, seed=21)
+    w = _w(B, N, H, d, g, kcols, bits, rho, seed=21, quant="asym" if name.startswith("asym") else "absmax")
     print("generation", name, w.sched(), "B", B, "tokens", n_gen, "window", window, flush=True)
     G, xs, run = _run_gpu(w, n_gen, window)
     for b in range(B):
