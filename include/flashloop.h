@@ -290,6 +290,9 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void
  *           column set changed, sparse attention, column statistics when the
  *           next loop prunes further.
  * All state lives in caller-owned device buffers listed in fl_loop_state.
+ * Loop 1 sets mass_u to 0 and leaves out_u unwritten (O_U is never read
+ * after a dense loop); a later loop that keeps all columns zeroes out_u,
+ * and one that prunes rebuilds it.
  */
 typedef struct fl_loop_cfg {
     int N, H, d, g, R, n_sink;

@@ -490,8 +490,9 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
         int rc = fl_kv_residual_quant(&C, 0, cfg->dtype, in->k, in->v, 0, stream);
         if (rc) return rc;
         FL_HIP(fl::launch_copy_or_iota(nullptr, S->active[0], N, N, st), "iota");
+        // M_U = 0 after the dense loop; O_U is zeroed only if a later loop
+        // carries it over without a rebuild (see below)
         FL_HIP(fl::launch_fill_f32(S->mass_u, (long)N * H, 0.0f, st), "fill");
-        FL_HIP(fl::launch_fill_f32(S->out_u, (long)N * H * d, 0.0f, st), "fill");
         S->k_cur[0] = N;
         S->sel_used[0] = nullptr;
         A.active = S->active[0]; A.n = N; A.sel = nullptr; A.k = N; A.level = 0;
@@ -523,6 +524,9 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
     if (k_prev <= k_r) {
         S->k_cur[r - 1] = k_prev;
         S->sel_used[r - 1] = S->sel_used[r - 2];
+        // every loop so far attended all columns: O_U = 0 is carried
+        if (!S->sel_used[r - 1])
+            FL_HIP(fl::launch_fill_f32(S->out_u, (long)N * H * d, 0.0f, st), "fill");
     } else {
         FL_REQUIRE(S->sel[r - 1] && S->col_stat[r - 2], "sel/col_stat buffers NULL");
         rc = fl_select_columns(S->col_stat[r - 2], S->sel_used[r - 2], H, k_prev, cfg->n_sink, k_r,
@@ -619,8 +623,9 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
             C.level[0].rows = nullptr;
             C.level[0].slot = nullptr;
             C.n_levels = 1;
+            // M_U = 0 after the dense loop; O_U is zeroed only if a later
+            // loop carries it over without a rebuild
             FL_HIP(fl::launch_fill_f32(Ls.mass_u, (long)N * H, 0.0f, st), "fill");
-            FL_HIP(fl::launch_fill_f32(Ls.out_u, (long)N * H * d, 0.0f, st), "fill");
         } else {
             fl_kv_level& Lv = C.level[r - 1];
             Lv.bits = cfg->bits[r - 1];
@@ -647,6 +652,8 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
             if (k_prev <= k_r) {
                 Ls.k_cur[r - 1] = k_prev;
                 Ls.sel_used[r - 1] = Ls.sel_used[r - 2];
+                if (!Ls.sel_used[r - 1])
+                    FL_HIP(fl::launch_fill_f32(Ls.out_u, (long)N * H * d, 0.0f, st), "fill");
             } else {
                 FL_REQUIRE(Ls.sel[r - 1] && Ls.col_stat[r - 2], "layer %d sel/col_stat buffers NULL", l);
                 rc = fl_select_columns(Ls.col_stat[r - 2], Ls.sel_used[r - 2], H, k_prev, cfg->n_sink,
