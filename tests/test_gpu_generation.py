@@ -7,6 +7,8 @@ cache rows (codes, scales, row lists, slot maps) bit-exact.  Under the
 paper's quantiser (App. E) tokens leave the window g at a time as one key
 group per level; the block's codes, key scales / offsets (at the group past
 the prompt's own) and per-token value scales / offsets are bit-exact."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -27,7 +29,16 @@ def _w(B, N, H, d, g, kcols, bits, rho, seed, quant="absmax"):
     return w
 
 
-def _run_gpu(w, n_gen, window):
+def _draw(w, B, n_gen, threads):
+    """Yields (b, inputs) in order, at most `threads` sequences in flight."""
+    with ThreadPoolExecutor(threads) as ex:
+        for b0 in range(0, B, threads):
+            futs = [ex.submit(synth.gen_decode_seq, w, b, n_gen) for b in range(b0, min(B, b0 + threads))]
+            for i, f in enumerate(futs):
+                yield b0 + i, f.result()
+
+
+def _run_gpu(w, n_gen, window, keep=None, threads=1):
     B, N, H, d, R = w.extra["B"], w.N, w.H, w.d, w.R
     n_act = counts(w)
     quant = fl.FL_QUANT_ASYM if w.extra["quant"] == "asym" else fl.FL_QUANT_ABSMAX
@@ -35,8 +46,7 @@ def _run_gpu(w, n_gen, window):
                           gen_tokens=n_gen, window=window, quant=quant)
     xs = {}
     tok = {key: np.empty((n_gen, R, B, H, d), np.uint16) for key in ("gen_q", "gen_k", "gen_v")}
-    for b in range(B):
-        x = synth.gen_decode_seq(w, b, n_gen=n_gen)
+    for b, x in _draw(w, B, n_gen, threads):
         k = [to_dev(a, "bf16") for a in x["k"]]
         v = [to_dev(a, "bf16") for a in x["v"]]
         st = [None] + [torch.from_numpy(s).cuda() for s in x["stat"][1:]]
@@ -45,7 +55,8 @@ def _run_gpu(w, n_gen, window):
             for t in range(n_gen):
                 for r in range(R):
                     tok[key][t, r, b] = x[key][t][r]
-        xs[b] = x
+        if keep is None or b in keep:
+            xs[b] = x
     torch.cuda.synchronize()
     G = []
     for t in range(n_gen):
@@ -171,3 +182,20 @@ def test_generation_matches_oracle(name, B, N, H, d, g, kcols, bits, rho, n_gen,
     G, xs, run = _run_gpu(w, n_gen, window)
     for b in range(B):
         _check(w, b, xs[b], G, run, window)
+
+
+def test_generation_fullsize_asym_sampled():
+    """64 sequences x 8192-token prompts, 16 x 128, R = 4, INT4 asymmetric at
+    every level and the 64-token window: 130 generated tokens, so the first
+    64-token group is appended at token 128 (the generation benchmark's
+    shape); two sequences checked token by token against the oracle."""
+    base = synth.WORKLOADS["decode64x8k"]
+    w = base.scaled(bits=[4] * base.R)
+    w.extra = dict(base.extra, quant="asym")
+    sample = (0, 63)
+    print("generation full size asym", w.sched(), "B", w.extra["B"], "checked", sample, flush=True)
+    G, xs, run = _run_gpu(w, 130, 64, keep=set(sample), threads=16)
+    print("  GPU generation done; checking", flush=True)
+    assert G[-1]["N"] == w.N + w.g
+    for b in sample:
+        _check(w, b, xs[b], G, run, 64)
