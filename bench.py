@@ -33,9 +33,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
 KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn_lds<128, 0, 1, 32>",
                  "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 8>",
-                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true, false>",
-                 "decode": "k_decode<128, 0, true, false, false>",
-                 "decode_rebuild": "k_decode<128, 1, true, true, false>"}
+                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true, false, 0>",
+                 "decode": "k_decode<128, 0, true, false, false, 0>",
+                 "decode_rebuild": "k_decode<128, 1, true, true, false, 0>"}
 # projections of the 2048-hidden block: epilogue (0 store, 1 residual, 2 SwiGLU)
 # and tile width; o and down share one instantiation, so only the others are
 # separable in a trace
@@ -794,7 +794,9 @@ def bench_decode(args, w, np, torch, fl, synth):
         per_launch = dense_bytes
         ach = per_launch / (kd["avg_launch_us"] / 1e6) / 1e9
         kd["gbs"] = round(ach, 1)
-        sym = KERNEL_SYMBOL["decode_dense"].replace("false>", "true>") if asym else KERNEL_SYMBOL["decode_dense"]
+        # the asymmetric kernel is specialised on the base level's code width
+        sym = (f"k_decode<128, 0, false, true, true, {w.bits[0]}>" if asym
+               else KERNEL_SYMBOL["decode_dense"])
         roof = dict(kernel="decode_dense", kernel_symbol=sym, bound="hbm", achieved=round(ach, 1),
                     peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
                     traffic=kernel_traffic(w.name, sym), bytes_per_launch=per_launch)

@@ -89,6 +89,27 @@ __device__ __forceinline__ void load_ucodes16(const uint8_t* base, long e, int b
     }
 }
 
+// The same 16 unsigned codes in two steps, for a width known at compile
+// time: the raw words (so the loads of several columns can be issued before
+// any is used), then the codes as floats.
+template <int BITS>
+__device__ __forceinline__ uint4 load_raw16(const uint8_t* base, long e) {
+    if (BITS == 8) return *reinterpret_cast<const uint4*>(base + e);
+    if (BITS == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(base + e / 2);
+        return make_uint4(u.x, u.y, 0u, 0u);
+    }
+    return make_uint4(*reinterpret_cast<const uint32_t*>(base + e / 4), 0u, 0u, 0u);
+}
+template <int BITS>
+__device__ __forceinline__ void decode_u16(const uint4 r, float (&x)[16]) {
+    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+    constexpr int PER = 32 / BITS;  // codes per word
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        x[i] = (float)((wd[i / PER] >> (BITS * (i % PER))) & ((1u << BITS) - 1u));
+}
+
 // 16 consecutive fp32 values
 __device__ __forceinline__ void load_f32x16(const float* p, float (&x)[16]) {
 #pragma unroll
@@ -132,12 +153,17 @@ __device__ __forceinline__ void load_codes16(const uint8_t* base, long e, int bi
 // ASYM: the cache holds the asymmetric scheme (unsigned codes, code * s + z;
 // keys with a scale and offset per channel for every g rows of a level,
 // values per g channels of a row); L0 then only restricts the walk to level 0.
-template <int D, int MODE, bool SPARSE, bool L0, bool ASYM>
+// B0: the base level's code width when fixed at compile time (0 = read it
+// from the cache).  A width known here lets the compiler issue the U column
+// loads of a pass together instead of one load-wait pair per column.
+template <int D, int MODE, bool SPARSE, bool L0, bool ASYM, int B0>
 __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     constexpr int LPC = D / 16;     // lanes per column
     constexpr int CPW = 64 / LPC;   // columns per wave per load
     constexpr int CPI = CPW * DNW;  // columns per workgroup pass
-    constexpr int U = 4;            // passes in flight (8 measured no faster)
+    // passes in flight: 4 for 16-byte code rows (8 measured no faster); a
+    // narrower fixed base keeps the bytes in flight per lane the same
+    constexpr int U = (ASYM && L0 && B0 == 4) ? 8 : (ASYM && L0 && B0 == 2) ? 16 : 4;
     extern __shared__ float dyn[];  // sc[k + T], then (sparse) rows[level + 1][k]
     __shared__ float qs[D];
     __shared__ float red[DNW];
@@ -188,6 +214,12 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     for (int i = 0; i < 16; ++i) qv[i] = qs[cs * 16 + i];
     const float c2 = P.sm * 1.4426950408889634f;
     const int grp = cs * 16 / C.g;  // this lane's scale group
+    // code width of level l
+    auto bits_of = [&](const SeqLevel& L, int l) -> int {
+        if (!ASYM && L0) return 8;
+        if (B0 && l == 0) return B0;
+        return L.bits;
+    };
 
     auto row_of = [&](int l, int c) -> int {
         if (SPARSE) return rowtab[l * k + c];
@@ -204,9 +236,17 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         // (the columns of one step share a group except across the origin of
         // the appended groups, where each lane follows its own column)
         const SeqLevel L = seq_level<D, ASYM>(P, 0, b, 0);
+        constexpr int BB = B0 ? B0 : 8;  // launched with the base width fixed
         int gcur = -1;
         float qs[16], qz = 0.0f;
         for (int c0 = 0; c0 < k; c0 += CPI * U) {
+            // the pass's code loads first (a column past k re-reads the last)
+            uint4 raw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + w * (CPW * U) + u * CPW + cl;
+                raw[u] = load_raw16<BB>(L.codes, ((long)(c < k ? c : k - 1) * H + h) * D + cs * 16);
+            }
             float part[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -228,7 +268,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 }
                 if (c < k) {
                     float x[16];
-                    load_ucodes16(L.codes, ((long)c * H + h) * D + cs * 16, L.bits, x);
+                    decode_u16<BB>(raw[u], x);
                     float dot = qz;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) dot = fmaf(qs[i], x[i], dot);
@@ -263,7 +303,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                         float x[16];
                         if (ASYM) {
                             // x = code * s + z per channel (scale / offset of the row's group)
-                            load_ucodes16(L.codes, rr * D + cs * 16, L.bits, x);
+                            load_ucodes16(L.codes, rr * D + cs * 16, bits_of(L, l), x);
                             const long si = ((long)key_group(P, l, row) * H + h) * D + cs * 16;
                             float sv[16], zv[16];
                             load_f32x16(L.scales + si, sv);
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                             for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i] * sv[i] + zv[i], dot);
                             part[u] += dot;
                         } else {
-                            load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                            load_codes16(L.codes, rr * D + cs * 16, bits_of(L, l), x);
                             float dot = 0.0f;
 #pragma unroll
                             for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
@@ -344,8 +384,41 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
 
     // ---- phase 3: P.V ----
     float acc[16];
+    float accz = 0.0f;  // asymmetric offsets: sum of p z, common to the 16 channels
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    if (ASYM && L0 && !SPARSE) {
+        // level 0 in column order: each pass issues its U columns' code,
+        // scale and offset loads before using any of them
+        const SeqLevel L = seq_level<D, ASYM>(P, 0, b, 1);
+        constexpr int BB = B0 ? B0 : 8;
+        for (int c0 = 0; c0 < k; c0 += CPI * U) {
+            uint4 raw[U];
+            float sv[U], zv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * CPI + w * CPW + cl;
+                const long rr = (long)(c < k ? c : k - 1) * H + h;
+                raw[u] = load_raw16<BB>(L.codes, rr * D + cs * 16);
+                sv[u] = L.scales[rr * G + grp];
+                zv[u] = L.zeros[rr * G + grp];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * CPI + w * CPW + cl;
+                if (c < k) {
+                    // p * (code * s + z) = code * (p s) + p z
+                    const float p = sc[c];
+                    const float ps = p * sv[u];
+                    accz = fmaf(p, zv[u], accz);
+                    float x[16];
+                    decode_u16<BB>(raw[u], x);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                }
+            }
+        }
+    } else
     for (int c0 = 0; c0 < k; c0 += CPI * U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -361,13 +434,13 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                         float x[16];
                         if (ASYM) {
                             // p * (code * s + z) = code * (p s) + p z
-                            load_ucodes16(L.codes, rr * D + cs * 16, L.bits, x);
+                            load_ucodes16(L.codes, rr * D + cs * 16, bits_of(L, l), x);
                             const float ps = p * L.scales[rr * G + grp];
-                            const float pz = p * L.zeros[rr * G + grp];
+                            accz = fmaf(p, L.zeros[rr * G + grp], accz);
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i] + pz);
+                            for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
                         } else {
-                            load_codes16(L.codes, rr * D + cs * 16, L0 ? 8 : L.bits, x);
+                            load_codes16(L.codes, rr * D + cs * 16, bits_of(L, l), x);
                             const float ps = p * L.scales[rr * G + grp];
 #pragma unroll
                             for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
@@ -386,6 +459,10 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], p, acc[i]);
         }
+    }
+    if (ASYM) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += accz;
     }
     // lanes with the same channel slice hold partial sums over different columns
 #pragma unroll
@@ -422,25 +499,46 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         for (int c = tid; c < k; c += DT) P.col_stat[(long)bh * k + c] = sc[c];
 }
 
+// One (D, MODE, SPARSE, L0) kernel: absmax, or the asymmetric scheme with
+// the base level's width fixed when only the base level is read.
+template <int D, int M, bool S, bool L>
+void launch_decode_one(bool asym, int b0, dim3 grid, size_t shm, const DecodeParams& P, hipStream_t st) {
+    if (!asym) {
+        hipLaunchKernelGGL((k_decode<D, M, S, L, false, 0>), grid, dim3(DT), shm, st, P);
+    } else if constexpr (!L) {
+        hipLaunchKernelGGL((k_decode<D, M, S, L, true, 0>), grid, dim3(DT), shm, st, P);
+    } else {
+        if (b0 == 8) hipLaunchKernelGGL((k_decode<D, M, S, L, true, 8>), grid, dim3(DT), shm, st, P);
+        else if (b0 == 4) hipLaunchKernelGGL((k_decode<D, M, S, L, true, 4>), grid, dim3(DT), shm, st, P);
+        else hipLaunchKernelGGL((k_decode<D, M, S, L, true, 2>), grid, dim3(DT), shm, st, P);
+    }
+}
+
+template <int D>
+void launch_decode_d(int mode, bool sp, bool l0, bool asym, int b0, dim3 grid, size_t shm,
+                     const DecodeParams& P, hipStream_t st) {
+    if (mode == MODE_REBUILD) {
+        if (l0) launch_decode_one<D, MODE_REBUILD, true, true>(asym, b0, grid, shm, P, st);
+        else launch_decode_one<D, MODE_REBUILD, true, false>(asym, b0, grid, shm, P, st);
+    } else if (sp) {
+        if (l0) launch_decode_one<D, MODE_ATTN, true, true>(asym, b0, grid, shm, P, st);
+        else launch_decode_one<D, MODE_ATTN, true, false>(asym, b0, grid, shm, P, st);
+    } else {
+        if (l0) launch_decode_one<D, MODE_ATTN, false, true>(asym, b0, grid, shm, P, st);
+        else launch_decode_one<D, MODE_ATTN, false, false>(asym, b0, grid, shm, P, st);
+    }
+}
+
 hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st) {
     const bool sp = P.sel != nullptr;
     const size_t shm = (size_t)(P.k + P.n_tail) * sizeof(float) +
                        (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
-    dim3 grid(P.B * P.H);
+    const dim3 grid(P.B * P.H);
     const bool l0 = P.level == 0;
     const bool asym = P.cache.scheme == FL_QUANT_ASYM;
-#define FL_DEC(D_, M_, S_, L_)                                                                  \
-    do {                                                                                        \
-        if (asym) hipLaunchKernelGGL((k_decode<D_, M_, S_, L_, true>), grid, dim3(DT), shm, st, P);  \
-        else hipLaunchKernelGGL((k_decode<D_, M_, S_, L_, false>), grid, dim3(DT), shm, st, P);      \
-    } while (0)
-#define FL_DEC_D(D_)                                                                     \
-    if (mode == MODE_REBUILD) { if (l0) FL_DEC(D_, MODE_REBUILD, true, true); else FL_DEC(D_, MODE_REBUILD, true, false); } \
-    else if (sp) { if (l0) FL_DEC(D_, MODE_ATTN, true, true); else FL_DEC(D_, MODE_ATTN, true, false); } \
-    else { if (l0) FL_DEC(D_, MODE_ATTN, false, true); else FL_DEC(D_, MODE_ATTN, false, false); }
-    if (d == 128) { FL_DEC_D(128) } else { FL_DEC_D(64) }
-#undef FL_DEC_D
-#undef FL_DEC
+    const int b0 = P.cache.level[0].bits;
+    if (d == 128) launch_decode_d<128>(mode, sp, l0, asym, b0, grid, shm, P, st);
+    else launch_decode_d<64>(mode, sp, l0, asym, b0, grid, shm, P, st);
     return hipGetLastError();
 }
 
