@@ -110,6 +110,32 @@ __device__ __forceinline__ void decode_u16(const uint4 r, float (&x)[16]) {
         x[i] = (float)((wd[i / PER] >> (BITS * (i % PER))) & ((1u << BITS) - 1u));
 }
 
+// 16 signed codes (absmax scheme) in two steps for a width known only at
+// run time (uniform across a level): the raw words, then the codes as
+// floats, so the loads of several columns are in flight before any is used.
+__device__ __forceinline__ uint4 load_raw16_rt(const uint8_t* base, long e, int bits) {
+    if (bits == 8) return *reinterpret_cast<const uint4*>(base + e);
+    if (bits == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(base + e / 2);
+        return make_uint4(u.x, u.y, 0u, 0u);
+    }
+    return make_uint4(*reinterpret_cast<const uint32_t*>(base + e / 4), 0u, 0u, 0u);
+}
+__device__ __forceinline__ void decode_s16_rt(const uint4 r, int bits, float (&x)[16]) {
+    if (bits == 8) {
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)(int8_t)(wd[i >> 2] >> (8 * (i & 3)));
+    } else if (bits == 4) {
+        const uint64_t wd = ((uint64_t)r.y << 32) | r.x;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((int)((int64_t)(wd << (60 - 4 * i)) >> 60));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (float)((int)((int32_t)(r.x << (30 - 2 * i)) >> 30));
+    }
+}
+
 // 16 consecutive fp32 values
 __device__ __forceinline__ void load_f32x16(const float* p, float (&x)[16]) {
 #pragma unroll
@@ -284,6 +310,54 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 if (cs == 0 && c < k) sc[c] = v * c2;
             }
         }
+    } else if (!ASYM && SPARSE) {
+        // selected columns: level by level, each pass issues its U columns'
+        // code and scale loads before using any (an absent level's row is
+        // -1 and its column is skipped); a column still sums its levels in
+        // level order
+        for (int c0 = 0; c0 < k; c0 += CPI * U) {
+            float part[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) part[u] = 0.0f;
+            for (int l = 0; l < nlev; ++l) {
+                const SeqLevel L = seq_level<D, ASYM>(P, l, b, 0);
+                const int bits = bits_of(L, l);
+                uint4 raw[U];
+                float sv[U];
+                int rowv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * CPI + w * CPW + cl;
+                    rowv[u] = c < k ? row_of(l, c) : -1;
+                    raw[u] = make_uint4(0u, 0u, 0u, 0u);
+                    sv[u] = 0.0f;
+                    if (rowv[u] >= 0) {
+                        const long rr = (long)rowv[u] * H + h;
+                        raw[u] = load_raw16_rt(L.codes, rr * D + cs * 16, bits);
+                        sv[u] = L.scales[rr * G + grp];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (rowv[u] >= 0) {
+                        float x[16];
+                        decode_s16_rt(raw[u], bits, x);
+                        float dot = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
+                        part[u] = fmaf(dot, sv[u], part[u]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float v = part[u];
+#pragma unroll
+                for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
+                const int c = c0 + u * CPI + w * CPW + cl;
+                if (cs == 0 && c < k) sc[c] = v * c2;
+            }
+        }
     } else
     for (int c0 = 0; c0 < k; c0 += CPI * U) {
         float part[U];
@@ -415,6 +489,45 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                     decode_u16<BB>(raw[u], x);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                }
+            }
+        }
+    } else if (!ASYM && SPARSE) {
+        // as in phase 1: level by level, a pass's loads issued together
+        for (int c0 = 0; c0 < k; c0 += CPI * U) {
+            float pu[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * CPI + w * CPW + cl;
+                pu[u] = c < k ? sc[c] : 0.0f;
+            }
+            for (int l = 0; l < nlev; ++l) {
+                const SeqLevel L = seq_level<D, ASYM>(P, l, b, 1);
+                const int bits = bits_of(L, l);
+                uint4 raw[U];
+                float sv[U];
+                int rowv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * CPI + w * CPW + cl;
+                    rowv[u] = c < k ? row_of(l, c) : -1;
+                    raw[u] = make_uint4(0u, 0u, 0u, 0u);
+                    sv[u] = 0.0f;
+                    if (rowv[u] >= 0) {
+                        const long rr = (long)rowv[u] * H + h;
+                        raw[u] = load_raw16_rt(L.codes, rr * D + cs * 16, bits);
+                        sv[u] = L.scales[rr * G + grp];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (rowv[u] >= 0) {
+                        const float ps = pu[u] * sv[u];
+                        float x[16];
+                        decode_s16_rt(raw[u], bits, x);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                    }
                 }
             }
         }
