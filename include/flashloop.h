@@ -381,6 +381,13 @@ typedef struct fl_layer_state {
     const int32_t* sel_used[FL_MAX_LEVELS];
     int k_cur[FL_MAX_LEVELS];
     float* col_stat[FL_MAX_LEVELS];
+    /* optional (NULL: not written): bf16 [n_active[r-1]][H][d] each; receive
+     * the loop's keys (after RoPE) and values of the active rows, in active
+     * order, exactly as the layer's quantiser reads them.  A checker can then
+     * re-quantise the same values independently (App. E: keys are quantised
+     * after RoPE). */
+    void* k_in;
+    void* v_in;
 } fl_layer_state;
 
 typedef struct fl_block_state {
@@ -509,13 +516,52 @@ int fl_decode_append(fl_decode_cfg* cfg, fl_decode_state* st, const fl_decode_wi
                      int slot, int n, fl_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * Per-kernel timing (profiling aid).  fl_timing_enable(1) makes every later
- * launch of the library record a HIP event pair around each kernel on the
- * launch stream.  fl_timing_report waits for those events and writes one line
- * per kernel name, "name launches total_ms\n", into buf (NUL-terminated,
- * truncated to len), then forgets the recorded launches.  Returns FL_OK, or
- * FL_ERR_INVALID_ARG when the report was truncated, FL_ERR_HIP on an event
- * error. */
+ * Input validation.  The entry points take index lists and statistics as
+ * device arrays and by default trust them (checking them would need a copy
+ * to the host and a synchronisation).  The paper's selections (Sec. 4.1,
+ * 4.2) assume ascending, unique positions and rankable statistics:
+ *
+ * fl_check_indices(idx, n, lo, hi): HOST array idx[0..n) strictly ascending
+ *   (hence unique) with every element in [lo, hi).  Returns FL_OK, or
+ *   FL_ERR_INVALID_ARG with fl_last_error() naming the first bad element.
+ * fl_check_finite(x, n): HOST array x[0..n) all finite (no NaN / inf);
+ *   FL_OK or FL_ERR_INVALID_ARG as above.
+ * fl_set_checks(on): check mode for this process (default off).  When on,
+ *   every entry point first waits for its stream, copies its device index
+ *   lists and statistics to the host and validates them as above, returning
+ *   FL_ERR_INVALID_ARG before anything of the call is enqueued:
+ *     fl_select_active: cand (ascending in [0, N)), stat_in (finite); the
+ *       computed statistic (no NaN; the normalised one may be +inf) before
+ *       the selection;
+ *     fl_select_columns: every head's cand_cols row (ascending, >= 0),
+ *       col_stat (finite);
+ *     fl_kv_residual_quant, fl_sparse_loop_attn, fl_loop_step,
+ *       fl_block_step, fl_decode_step: residual levels' row lists (ascending
+ *       in [0, N)), active (ascending in [0, N)), every head's sel row
+ *       (ascending in [0, N)).
+ *   Check mode synchronises the stream inside the calls; it is a debugging
+ *   aid, not for timed runs. */
+int fl_check_indices(const int32_t* idx, long n, long lo, long hi);
+int fl_check_finite(const float* x, long n);
+int fl_set_checks(int on);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel and per-phase timing (profiling aid).  fl_timing_enable(level):
+ *   0  off;
+ *   1  every later launch of the library records a HIP event pair around
+ *      each kernel on the launch stream, and fl_loop_step also records the
+ *      phases below;
+ *   2  phases only: fl_loop_step records an event pair around steps a1-a4
+ *      (token statistic, selection, quantisation; for r = 1 the base level)
+ *      named "loop<r>.a1-a4" and one around steps a5-a8 (column selection,
+ *      pruned-column caches, sparse attention, column statistics) named
+ *      "loop<r>.a5-a8" (paper Sec. 4.1-4.3), with no per-kernel events
+ *      between them.
+ * fl_timing_report waits for those events and writes one line per name,
+ * "name launches total_ms\n", into buf (NUL-terminated, truncated to len),
+ * then forgets the recorded launches.  Returns FL_OK, or FL_ERR_INVALID_ARG
+ * when the report was truncated or the level is unknown, FL_ERR_HIP on an
+ * event error. */
 int fl_timing_enable(int on);
 int fl_timing_report(char* buf, size_t len);
 

@@ -104,24 +104,17 @@ def dequant_rows_asym(codes_packed, scales, zeros, bits, g, xhat_prev, per_chann
     return deq if xhat_prev is None else (np.asarray(xhat_prev, F32) + deq).astype(F32)
 
 
-def dequant_rows(codes_packed, scales, bits, g, xhat_prev):
-    """Rows of one cache level from stored codes: code*s, plus the previous
-    level's value when there is one (the product and the sum rounded
-    separately, as the quantiser defines the reconstruction)."""
-    c = unpack_codes(codes_packed, bits, scales.shape[-1] * g).astype(F32)
-    sc = np.repeat(np.asarray(scales, F32), g, axis=-1)
-    deq = (c * sc).astype(F32)
-    return deq if xhat_prev is None else (np.asarray(xhat_prev, F32) + deq).astype(F32)
-
-
 def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_acts=False):
     """h1: [N][D] input hidden states; weights: list per layer of dicts of fp32
     arrays w_qkv [3D][D], w_o [D][D], w_gu [2F][D] (rows 2j gate, 2j+1 up),
     w_down [D][F], norm1 [D], norm2 [D].  sched as in ``loop.run_prefill``.
     override: {('stat', r): array, ('cstat', r, layer): array} -- the GPU's own
-    statistics for the selections of loop r; ('kv', r, layer): dict of packed
-    k/v codes and scales -- the GPU's stored cache level, used in place of the
-    oracle's own codes (which are still computed and returned for comparison).
+    statistics for the selections of loop r; ('kvin', r, layer): dict(k=, v=)
+    of [n_r][H][d] fp32 -- another implementation's keys (after RoPE) and
+    values of the active rows, which the oracle's quantiser then quantises in
+    place of the oracle's own projections (these are still computed and
+    returned as k_in / v_in for comparison).  The quantiser itself, the cache
+    it builds and everything downstream stay the oracle's.
     Returns per-loop records."""
     override = override or {}
     rd = bf16 if bf16_acts else (lambda z: np.asarray(z, F32))
@@ -160,22 +153,18 @@ def run_block(h1, weights, sched, theta=10000.0, eps=1e-6, override=None, bf16_a
             bits = sched["bits"][r - 1]
             kp = None if r == 1 else s["khat"][A]
             vp = None if r == 1 else s["vhat"][A]
-            lk, krows = _level(k, kp, g, bits, asym, True)
-            lv, vrows = _level(v, vp, g, bits, asym, False)
-            ext = override.get(("kv", r, l))
-            if ext is not None and asym:
-                krows = dequant_rows_asym(ext["k"], ext["ks"], ext["kz"], bits, g, kp, True)
-                vrows = dequant_rows_asym(ext["v"], ext["vs"], ext["vz"], bits, g, vp, False)
-            elif ext is not None and bits != 32:
-                krows = dequant_rows(ext["k"], ext["ks"], bits, g, kp)
-                vrows = dequant_rows(ext["v"], ext["vs"], bits, g, vp)
+            ext = override.get(("kvin", r, l))
+            kq = k if ext is None else np.asarray(ext["k"], F32).reshape(k.shape)
+            vq = v if ext is None else np.asarray(ext["v"], F32).reshape(v.shape)
+            lk, krows = _level(kq, kp, g, bits, asym, True)
+            lv, vrows = _level(vq, vp, g, bits, asym, False)
             if r == 1:
                 khat, vhat = krows, vrows
             else:
                 khat = s["khat"].copy(); khat[A] = krows
                 vhat = s["vhat"].copy(); vhat[A] = vrows
             qd = s["q"].copy(); qd[A] = q
-            lrec = dict(level_k=lk, level_v=lv)
+            lrec = dict(level_k=lk, level_v=lv, k_in=k, v_in=v)
             if r == 1:
                 o, lse = attend(qd, khat, vhat, None, None, sm)
                 mu = np.zeros((N, H), F32); ou = np.zeros((N, H, d), F32)

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -82,11 +83,14 @@ int attn_prec(int dtype, int level) { return dtype == FL_F32 ? 2 : (level >= 1 ?
 
 // ---- optional per-kernel HIP-event timing of the library's launches ----
 struct TimedLaunch {
-    const char* name;
+    std::string name;
     hipEvent_t a, b;
 };
 std::mutex g_tmu;
-bool g_timing = false;
+bool g_timing = false;  // per-kernel event pairs
+bool g_phases = false;  // per-phase event pairs of fl_loop_step
+// prefix of kernel timing names inside a phase of fl_loop_step ("loop<r>.a5-a8/")
+thread_local std::string g_prefix;
 std::vector<TimedLaunch> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -109,8 +113,101 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
     if (a) (void)hipEventRecord(a, st);
     const hipError_t e = f();
     if (b) (void)hipEventRecord(b, st);
-    if (a && b) g_recs.push_back({name, a, b});
+    if (a && b) g_recs.push_back({g_prefix + name, a, b});
     return e;
+}
+
+// An event recorded on the stream when phase timing is on (else NULL);
+// phase_end records the closing event and keeps the pair under `name`.
+hipEvent_t phase_begin(hipStream_t st) {
+    if (!g_phases) return nullptr;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t a = ev_get();
+    if (a && hipEventRecord(a, st) != hipSuccess) {
+        g_pool.push_back(a);
+        return nullptr;
+    }
+    return a;
+}
+void phase_end(hipEvent_t a, const std::string& name, hipStream_t st) {
+    if (!a) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t b = ev_get();
+    if (b && hipEventRecord(b, st) == hipSuccess) {
+        g_recs.push_back({name, a, b});
+    } else {
+        g_pool.push_back(a);
+        if (b) g_pool.push_back(b);
+    }
+}
+
+// timing names of the block's projections, by output tile width (64 / 128)
+const char* const kGemmQkv[2] = {"gemm_qkv.w64", "gemm_qkv.w128"};
+const char* const kGemmO[2] = {"gemm_o.w64", "gemm_o.w128"};
+const char* const kGemmGateUp[2] = {"gemm_gate_up.w64", "gemm_gate_up.w128"};
+const char* const kGemmDown[2] = {"gemm_down.w64", "gemm_down.w128"};
+const char* gemm_name(const char* const* names, const fl::GemmParams& G) {
+    return names[fl::gemm_tile_n(G) == 128 ? 1 : 0];
+}
+
+// ---- input validation (fl_check_indices / fl_check_finite / fl_set_checks) ----
+bool g_checks = false;
+
+// idx[0..n) strictly ascending, each in [lo, hi); on failure names `what`,
+// the row (for row-wise lists) and the first offending element
+int check_idx_host(const int32_t* idx, long n, long lo, long hi, const char* what, long row = -1) {
+    char rs[32] = "";
+    if (row >= 0) snprintf(rs, sizeof rs, " row %ld", row);
+    for (long i = 0; i < n; ++i) {
+        if (idx[i] < lo || idx[i] >= hi)
+            return fail(FL_ERR_INVALID_ARG, "%s%s: element %ld = %d outside [%ld, %ld)", what, rs, i,
+                        idx[i], lo, hi);
+        if (i > 0 && idx[i] <= idx[i - 1])
+            return fail(FL_ERR_INVALID_ARG, "%s%s: element %ld = %d not above element %ld = %d "
+                        "(ascending, unique)", what, rs, i, idx[i], i - 1, idx[i - 1]);
+    }
+    return FL_OK;
+}
+int check_finite_host(const float* x, long n, const char* what, bool allow_inf = false) {
+    for (long i = 0; i < n; ++i)
+        if (allow_inf ? std::isnan(x[i]) : !std::isfinite(x[i]))
+            return fail(FL_ERR_INVALID_ARG, "%s: element %ld = %g is not %s", what, i, (double)x[i],
+                        allow_inf ? "a number" : "finite");
+    return FL_OK;
+}
+// Check mode: device arrays copied to the host (after the stream's pending
+// work, which may produce them) and validated there before anything is
+// enqueued.  rows x n row-wise lists, each row checked on its own.
+int check_idx_dev(const int32_t* d_idx, long rows, long n, long lo, long hi, const char* what,
+                  hipStream_t st) {
+    if (!g_checks || !d_idx || rows * n == 0) return FL_OK;
+    std::vector<int32_t> h((size_t)(rows * n));
+    FL_HIP(hipStreamSynchronize(st), "check: sync");
+    FL_HIP(hipMemcpy(h.data(), d_idx, h.size() * 4, hipMemcpyDeviceToHost), "check: copy");
+    for (long r = 0; r < rows; ++r) {
+        const int rc = check_idx_host(h.data() + r * n, n, lo, hi, what, rows > 1 ? r : -1);
+        if (rc) return rc;
+    }
+    return FL_OK;
+}
+int check_finite_dev(const float* d_x, long n, const char* what, hipStream_t st,
+                     bool allow_inf = false) {
+    if (!g_checks || !d_x || n == 0) return FL_OK;
+    std::vector<float> h((size_t)n);
+    FL_HIP(hipStreamSynchronize(st), "check: sync");
+    FL_HIP(hipMemcpy(h.data(), d_x, h.size() * 4, hipMemcpyDeviceToHost), "check: copy");
+    return check_finite_host(h.data(), n, what, allow_inf);
+}
+// the row lists of residual levels 1..upto (ascending positions in [0, N))
+int check_levels_dev(const fl_kv_cache& C, int upto, hipStream_t st) {
+    if (!g_checks) return FL_OK;
+    for (int l = 1; l <= upto; ++l) {
+        char what[48];
+        snprintf(what, sizeof what, "level %d rows", l);
+        const int rc = check_idx_dev(C.level[l].rows, 1, C.level[l].n_rows, 0, C.N, what, st);
+        if (rc) return rc;
+    }
+    return FL_OK;
 }
 
 bool dtype_ok(int dt) { return dt == FL_F32 || dt == FL_BF16; }
@@ -184,6 +281,21 @@ const char* fl_last_error(void) { return g_err; }
 
 const char* fl_version(void) { return "flashloop-mi355x 0.1 (gfx950)"; }
 
+int fl_check_indices(const int32_t* idx, long n, long lo, long hi) {
+    FL_REQUIRE(n >= 0 && (n == 0 || idx), "idx NULL or n = %ld", n);
+    return check_idx_host(idx, n, lo, hi, "indices");
+}
+
+int fl_check_finite(const float* x, long n) {
+    FL_REQUIRE(n >= 0 && (n == 0 || x), "x NULL or n = %ld", n);
+    return check_finite_host(x, n, "values");
+}
+
+int fl_set_checks(int on) {
+    g_checks = on != 0;
+    return FL_OK;
+}
+
 size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     switch (op) {
     case FL_WS_SELECT_ACTIVE: return a > 0 ? (size_t)kAlign : 0;
@@ -201,9 +313,11 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     }
 }
 
-int fl_timing_enable(int on) {
+int fl_timing_enable(int level) {
+    if (level < 0 || level > 2) return fail(FL_ERR_INVALID_ARG, "timing level %d (0, 1 or 2)", level);
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_timing = on != 0;
+    g_timing = level == 1;
+    g_phases = level != 0;
     return FL_OK;
 }
 
@@ -253,6 +367,9 @@ int fl_select_active(int dtype, int stat_kind, const void* h_cur, const void* h_
         FL_REQUIRE(D >= 8 && D % 8 == 0, "D = %d (multiple of 8 required)", D);
     }
     hipStream_t st = (hipStream_t)stream;
+    int rc = check_idx_dev(cand, 1, n_cand, 0, N, "cand", st);
+    if (!rc) rc = check_finite_dev(stat_in, n_cand, "stat_in", st);
+    if (rc) return rc;
     const float* keys = stat_in;
     if (!stat_in) {
         FL_HIP(timed("delta_norm", st, [&] {
@@ -261,6 +378,10 @@ int fl_select_active(int dtype, int stat_kind, const void* h_cur, const void* h_
                }),
                "delta_norm");
         keys = stat_out;
+        // the normalised statistic is +inf for a changed zero state; NaN (from
+        // non-finite hidden states) cannot be ranked
+        rc = check_finite_dev(stat_out, n_cand, "statistic (from h_cur / h_prev)", st, true);
+        if (rc) return rc;
     }
     FL_HIP(timed("select_topk", st, [&] {
                return fl::launch_topk(keys, 0, cand, 0, n_cand, n_select, 0, active_out, 0, slot_out,
@@ -293,10 +414,14 @@ int fl_select_columns(const float* col_stat, const int32_t* cand_cols, int H, in
     FL_REQUIRE(n_sink >= 0, "n_sink %d", n_sink);
     FL_REQUIRE(k > n_sink, "k=%d must exceed n_sink=%d", k, n_sink);
     hipStream_t st = (hipStream_t)stream;
+    int rc = check_idx_dev(cand_cols, H, n_cand, 0, 0x7fffffff, "cand_cols", st);
+    if (rc) return rc;
     if (n_cand <= k) {
         FL_HIP(fl::launch_copy_or_iota(cand_cols, sel_out, (long)H * n_cand, n_cand, st), "copy");
         return FL_OK;
     }
+    rc = check_finite_dev(col_stat, (long)H * n_cand, "col_stat", st);
+    if (rc) return rc;
     FL_REQUIRE(col_stat != nullptr, "col_stat is NULL");
     FL_REQUIRE(n_sink <= n_cand, "n_sink %d > n_cand %d", n_sink, n_cand);
     FL_HIP(timed("select_columns", st, [&] {
@@ -314,6 +439,8 @@ int fl_kv_residual_quant(const fl_kv_cache* cache, int level, int dtype, const v
     FL_REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
     FL_REQUIRE(k_new && v_new, "k_new/v_new NULL");
     hipStream_t st = (hipStream_t)stream;
+    rc = check_levels_dev(*cache, level, st);
+    if (rc) return rc;
     FL_HIP(timed("kv_quant", st, [&] {
                return fl::launch_quant(*cache, level, dtype, k_new, v_new, new_gathered, st);
            }),
@@ -354,6 +481,13 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     FL_REQUIRE(a->mode >= FL_DEQ_AUTO && a->mode <= FL_DEQ_IN_TILE, "mode %d", a->mode);
     FL_REQUIRE(a->col_stat_kind == FL_COL_STAT_MASS || a->col_stat_kind == FL_COL_STAT_VNORM,
                "col_stat_kind %d", a->col_stat_kind);
+    {
+        hipStream_t st0 = (hipStream_t)stream;
+        rc = check_idx_dev(a->active, 1, a->n, 0, N, "active", st0);
+        if (!rc) rc = check_idx_dev(a->sel, H, a->k, 0, N, "sel", st0);
+        if (!rc) rc = check_levels_dev(*cache, a->level, st0);
+        if (rc) return rc;
+    }
     const int prec = attn_prec(a->dtype, a->level);
     const int prec_old = attn_prec(a->dtype, a->level - 1);
     // FL_DEQ_AUTO resolves to FL_DEQ_ONCE: on the 32K, 4-loop workload the
@@ -464,8 +598,49 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* w
     return sparse_loop_attn(cache, a, ws, ws_bytes, stream, nullptr);
 }
 
+// Phase events of fl_loop_step: e0 opens steps a1-a4 at the call's start;
+// at the split point (after the quantisation) it is closed and `mark` opens
+// steps a5-a8, which the caller closes at the end of the loop.
+struct LoopPhases {
+    hipEvent_t e0 = nullptr, mark = nullptr;
+    std::string tag;
+    void split(hipStream_t st) {
+        if (g_phases) g_prefix = tag + ".a5-a8/";
+        if (!e0) return;
+        phase_end(e0, tag + ".a1-a4", st);
+        e0 = nullptr;
+        mark = phase_begin(st);
+    }
+    void release() {
+        g_prefix.clear();
+        std::lock_guard<std::mutex> lk(g_tmu);
+        if (e0) g_pool.push_back(e0);
+        if (mark) g_pool.push_back(mark);
+        e0 = mark = nullptr;
+    }
+};
+
+static int loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs* in, int r,
+                     void* ws, size_t ws_bytes, fl_stream_t stream, LoopPhases& ph);
+
 int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs* in, int r,
                  void* ws, size_t ws_bytes, fl_stream_t stream) {
+    hipStream_t st = (hipStream_t)stream;
+    LoopPhases ph;
+    ph.tag = "loop" + std::to_string(r);
+    ph.e0 = phase_begin(st);
+    if (g_phases) g_prefix = ph.tag + ".a1-a4/";
+    const int rc = loop_step(cfg, S, in, r, ws, ws_bytes, stream, ph);
+    if (rc == FL_OK && ph.mark) {
+        phase_end(ph.mark, ph.tag + ".a5-a8", st);
+        ph.mark = nullptr;
+    }
+    ph.release();
+    return rc;
+}
+
+static int loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs* in, int r,
+                     void* ws, size_t ws_bytes, fl_stream_t stream, LoopPhases& ph) {
     FL_REQUIRE(cfg && S && in, "cfg/state/inputs NULL");
     FL_REQUIRE(r >= 1 && r <= cfg->R && cfg->R <= FL_MAX_LEVELS, "loop %d of R=%d", r, cfg->R);
     FL_REQUIRE(stat_kinds_ok(cfg->token_stat, cfg->col_stat), "token_stat %d / col_stat %d",
@@ -493,6 +668,7 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
         // M_U = 0 after the dense loop; O_U is zeroed only if a later loop
         // carries it over without a rebuild (see below)
         FL_HIP(fl::launch_fill_f32(S->mass_u, (long)N * H, 0.0f, st), "fill");
+        ph.split(st);
         S->k_cur[0] = N;
         S->sel_used[0] = nullptr;
         A.active = S->active[0]; A.n = N; A.sel = nullptr; A.k = N; A.level = 0;
@@ -518,6 +694,7 @@ int fl_loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inputs*
     C.n_levels = r;
     rc = fl_kv_residual_quant(&C, r - 1, cfg->dtype, in->k, in->v, 0, stream);
     if (rc) return rc;
+    ph.split(st);
     const int k_prev = S->k_cur[r - 2];
     const int k_r = cfg->k_cols[r - 1];
     bool changed = false;
@@ -612,7 +789,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         fl::GemmParams G{};
         G.M = n; G.N = 3 * D; G.K = D; G.A = a_buf; G.lda = D; G.B = (const __bf16*)w.w_qkv;
         G.Cb = qkv; G.ldc = 3 * D;
-        FL_HIP(timed("gemm_qkv", st, [&] { return fl::launch_gemm(fl::EPI_STORE, G, st); }), "gemm");
+        FL_HIP(timed(gemm_name(kGemmQkv, G), st, [&] { return fl::launch_gemm(fl::EPI_STORE, G, st); }), "gemm");
         FL_HIP(timed("rope", st, [&] {
                    return fl::launch_rope_split(qkv, act, n, H, d, cfg->rope_theta, qc, kc, vc, st);
                }), "rope");
@@ -634,6 +811,10 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
             Lv.slot = S->slot[r - 1];
             C.n_levels = r;
         }
+        if (Ls.k_in)
+            FL_HIP(hipMemcpyAsync(Ls.k_in, kc, (size_t)n * D * 2, hipMemcpyDeviceToDevice, st), "copy");
+        if (Ls.v_in)
+            FL_HIP(hipMemcpyAsync(Ls.v_in, vc, (size_t)n * D * 2, hipMemcpyDeviceToDevice, st), "copy");
         int rc = fl_kv_residual_quant(&C, r - 1, FL_BF16, kc, vc, 1, stream);
         if (rc) return rc;
         fl_attn_args A{};
@@ -677,7 +858,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         G = fl::GemmParams{};
         G.M = n; G.N = D; G.K = D; G.A = attn_in; G.lda = D; G.B = (const __bf16*)w.w_o;
         G.Cf = S->h; G.ldc = D; G.rows = act;
-        FL_HIP(timed("gemm_o", st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
+        FL_HIP(timed(gemm_name(kGemmO, G), st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
         // MLP sub-block
         FL_HIP(timed("rmsnorm", st, [&] {
                    return fl::launch_rmsnorm_gather(S->h, act, n, D, (const __bf16*)w.norm2,
@@ -686,11 +867,11 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         G = fl::GemmParams{};
         G.M = n; G.N = 2 * F; G.K = D; G.A = a_buf; G.lda = D; G.B = (const __bf16*)w.w_gu;
         G.Cb = act_buf; G.ldc = F;
-        FL_HIP(timed("gemm_gate_up", st, [&] { return fl::launch_gemm(fl::EPI_SWIGLU, G, st); }), "gemm");
+        FL_HIP(timed(gemm_name(kGemmGateUp, G), st, [&] { return fl::launch_gemm(fl::EPI_SWIGLU, G, st); }), "gemm");
         G = fl::GemmParams{};
         G.M = n; G.N = D; G.K = F; G.A = act_buf; G.lda = F; G.B = (const __bf16*)w.w_down;
         G.Cf = S->h; G.ldc = D; G.rows = act;
-        FL_HIP(timed("gemm_down", st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
+        FL_HIP(timed(gemm_name(kGemmDown, G), st, [&] { return fl::launch_gemm(fl::EPI_RESID, G, st); }), "gemm");
     }
     return FL_OK;
 }
@@ -767,6 +948,9 @@ int fl_decode_step(const fl_decode_cfg* cfg, fl_decode_state* S, const fl_decode
     }
     P.k = S->k_cur[r - 1];
     P.sel = S->sel_used[r - 1];
+    rc = check_idx_dev(P.sel, (long)B * H, P.k, 0, N, "sel", st);
+    if (!rc) rc = check_levels_dev(C, r - 1, st);
+    if (rc) return rc;
     // a sparse loop keeps the probabilities and every level's row of each
     // selected column in LDS
     if (P.sel && (size_t)(P.k + T) * 4 + (size_t)r * P.k * 4 > 48 * 1024)

@@ -5,12 +5,12 @@
 //
 //   k_rmsnorm_gather  active rows of the fp32 residual stream -> RMSNorm ->
 //                     compact bf16 [n][D] (the gather is fused into the norm)
-//   k_gemm<EPI>       C = A[M][K] . W[N][K]^T, bf16 MFMA 32x32x16 with fp32
-//                     accumulation; 128x128 output tile per workgroup (4 waves
-//                     of 64x64), 32-deep K tiles in a two-buffer LDS pipeline.
-//                     Epilogues: bf16 store; residual scatter-add into the fp32
-//                     stream at the active rows; SwiGLU on interleaved
-//                     (gate, up) column pairs.
+//   k_gemm_lds<EPI,TN> C = A[M][K] . W[N][K]^T, bf16 MFMA 32x32x16 with fp32
+//                     accumulation; 128 x TN output tile per workgroup (4 waves
+//                     of 64 x TN/2), 64-deep K tiles in a two-buffer LDS-DMA
+//                     pipeline.  Epilogues: bf16 store; residual scatter-add
+//                     into the fp32 stream at the active rows; SwiGLU on
+//                     interleaved (gate, up) column pairs.
 //   k_rope_split      [n][3D] bf16 -> q, k, v [n][H][d] bf16 with rotary
 //                     position embedding (rotate-half) on q and k at the rows'
 //                     token positions (keys are quantised after RoPE).
@@ -49,101 +49,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gather(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 32;
-
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmParams G) {
-    constexpr int TN = GBN, NJ = 2;
-    __shared__ __bf16 As[2][GBM][GBK + 8];
-    __shared__ __bf16 Bs[2][GBN][GBK + 8];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r = lane & 31, half = lane >> 5;
-    const int wm = w >> 1, wn = w & 1;
-    const int n0 = blockIdx.x * GBN;
-    const int m0 = blockIdx.y * GBM;
-    // 16-byte chunks: 128 rows x 4 chunks per tile for A and for B
-    uint4 ar[2], br[2];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int idx = tid + c * 256;
-            const int row = idx >> 2, ch = (idx & 3) * 8;
-            const int m = m0 + row;
-            ar[c] = m < G.M ? *reinterpret_cast<const uint4*>(G.A + (long)m * G.lda + k0 + ch)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            br[c] = *reinterpret_cast<const uint4*>(G.B + (long)(n0 + row) * G.K + k0 + ch);
-        }
-    };
-    auto lstore = [&](int b) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int idx = tid + c * 256;
-            const int row = idx >> 2, ch = (idx & 3) * 8;
-            *reinterpret_cast<uint4*>(&As[b][row][ch]) = ar[c];
-            *reinterpret_cast<uint4*>(&Bs[b][row][ch]) = br[c];
-        }
-    };
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const int nk = G.K / GBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int b = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) gload((kt + 1) * GBK);
-#pragma unroll
-        for (int ks = 0; ks < GBK / 16; ++ks) {
-            bf16x8 a[2], bb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(&As[b][wm * 64 + 32 * i + r][ks * 16 + 8 * half]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[j] = *reinterpret_cast<const bf16x8*>(&Bs[b][wn * 64 + 32 * j + r][ks * 16 + 8 * half]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
-        }
-        if (more) lstore(b ^ 1);
-        __syncthreads();
-    }
-    // acc[i][j][e]: row m0 + wm*64 + 32i + (e/4)*8 + half*4 + e%4,
-    // col n0 + wn*TN/2 + 32j + r
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int n = n0 + wn * (TN / 2) + 32 * j + r;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm * 64 + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
-                const float v = acc[i][j][e];
-                if (EPI == EPI_SWIGLU) {
-                    const float u = __shfl_xor(v, 1); // (gate, up) column pair
-                    if (m < G.M && (r & 1) == 0) {
-                        const float sg = v / (1.0f + __expf(-v));
-                        G.Cb[(long)m * G.ldc + (n >> 1)] = (__bf16)(sg * u);
-                    }
-                } else if (m < G.M) {
-                    if (EPI == EPI_STORE) {
-                        G.Cb[(long)m * G.ldc + n] = (__bf16)v;
-                    } else { // EPI_RESID: residual stream += C at the active row
-                        const long row = G.rows ? G.rows[m] : m;
-                        G.Cf[row * G.ldc + n] += v;
-                    }
-                }
-            }
-        }
-}
+constexpr int GBM = 128; // output rows per workgroup
 
 // ---------------------------------------------------------------------------
-// The same GEMM with 64-deep K tiles copied by LDS-DMA (buffer loads with a
+// C = A[M][K] . W[N][K]^T, bf16 MFMA 32x32x16 with fp32 accumulation, with
+// 64-deep K tiles copied by LDS-DMA (buffer loads with a
 // scalar base and constant per-lane offsets; rows past M read zeros) into two
 // distinct LDS buffers, XOR-swizzled as the attention tiles (16 rows at one
 // logical chunk hit 16 distinct slots of a 256-byte bank window): one barrier
@@ -330,32 +240,30 @@ hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int
     return hipGetLastError();
 }
 
-constexpr bool kGemmLds = true;
 constexpr long kNarrowTiles = 1024; // 128-wide tiles per two workgroup slots (512 and 2048 measured no better)
+
+// Output columns per workgroup: narrow outputs with few tiles take 64-wide
+// tiles, twice the workgroups (2048-wide o / down projections of the
+// 24-layer step: 9.7 -> 6.4 ms and 13.6 -> 12.5 ms); the rest 128.
+int gemm_tile_n(const GemmParams& G) {
+    const bool narrow = G.N <= 2048 && (long)(G.N / 128) * ((G.M + GBM - 1) / GBM) < kNarrowTiles;
+    return narrow ? 64 : 128;
+}
 
 hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st) {
     if (G.M <= 0) return hipSuccess;
-    dim3 grid(G.N / GBN, (G.M + GBM - 1) / GBM);
-    if (kGemmLds && G.K % LBK == 0) {
-        // narrow outputs with few tiles take 64-wide tiles: twice the
-        // workgroups (2048-wide o / down projections of the 24-layer step:
-        // 9.7 -> 6.4 ms and 13.6 -> 12.5 ms)
-        const bool narrow = G.N <= 2048 && (long)(G.N / GBN) * ((G.M + GBM - 1) / GBM) < kNarrowTiles;
-        if (narrow) {
-            dim3 g2(G.N / 64, (G.M + GBM - 1) / GBM);
-            if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemm_lds<EPI_STORE, 64>), g2, dim3(256), 0, st, G);
-            else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemm_lds<EPI_RESID, 64>), g2, dim3(256), 0, st, G);
-            else hipLaunchKernelGGL((k_gemm_lds<EPI_SWIGLU, 64>), g2, dim3(256), 0, st, G);
-        } else {
-            if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemm_lds<EPI_STORE, 128>), grid, dim3(256), 0, st, G);
-            else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemm_lds<EPI_RESID, 128>), grid, dim3(256), 0, st, G);
-            else hipLaunchKernelGGL((k_gemm_lds<EPI_SWIGLU, 128>), grid, dim3(256), 0, st, G);
-        }
-        return hipGetLastError();
+    if (G.K % LBK != 0 || G.N % 128 != 0) return hipErrorInvalidValue; // checked by the caller
+    const int tn = gemm_tile_n(G);
+    const dim3 grid(G.N / tn, (G.M + GBM - 1) / GBM);
+    if (tn == 64) {
+        if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemm_lds<EPI_STORE, 64>), grid, dim3(256), 0, st, G);
+        else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemm_lds<EPI_RESID, 64>), grid, dim3(256), 0, st, G);
+        else hipLaunchKernelGGL((k_gemm_lds<EPI_SWIGLU, 64>), grid, dim3(256), 0, st, G);
+    } else {
+        if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemm_lds<EPI_STORE, 128>), grid, dim3(256), 0, st, G);
+        else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemm_lds<EPI_RESID, 128>), grid, dim3(256), 0, st, G);
+        else hipLaunchKernelGGL((k_gemm_lds<EPI_SWIGLU, 128>), grid, dim3(256), 0, st, G);
     }
-    if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, G);
-    else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, G);
-    else hipLaunchKernelGGL(k_gemm<EPI_SWIGLU>, grid, dim3(256), 0, st, G);
     return hipGetLastError();
 }
 

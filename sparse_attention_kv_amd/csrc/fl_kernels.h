@@ -151,6 +151,8 @@ hipError_t launch_sq_err(const float* x, const float* ref, long n, double* part,
 hipError_t launch_rmsnorm_gather(const float* x, const int32_t* rows, int n, int D,
                                  const __bf16* w, float eps, __bf16* out, hipStream_t st);
 hipError_t launch_gemm(int epi, const GemmParams& G, hipStream_t st);
+// output columns per workgroup launch_gemm uses for G (64 or 128)
+int gemm_tile_n(const GemmParams& G);
 hipError_t launch_rope_split(const __bf16* qkv, const int32_t* rows, int n, int H, int d,
                              float theta, __bf16* q, __bf16* k, __bf16* v, hipStream_t st);
 hipError_t launch_scatter_rows_bf16(const __bf16* src, const int32_t* rows, long n, int D,

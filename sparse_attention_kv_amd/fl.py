@@ -28,7 +28,8 @@ MAX_LEVELS = 32
 EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
            "fl_decode_append", "fl_sq_err", "fl_kv_dequant", "fl_workspace_size",
-           "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report"]
+           "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report",
+           "fl_check_indices", "fl_check_finite", "fl_set_checks"]
 FL_WS_BLOCK_STEP = 5
 FL_WS_SQ_ERR = 6
 
@@ -96,7 +97,7 @@ class FlLayerState(ctypes.Structure):
     _fields_ = [("cache", FlKvCache), ("q_state", c_void_p), ("out", c_void_p), ("lse", c_void_p),
                 ("mass_u", c_void_p), ("out_u", c_void_p), ("sel", c_void_p * MAX_LEVELS),
                 ("sel_used", c_void_p * MAX_LEVELS), ("k_cur", c_int * MAX_LEVELS),
-                ("col_stat", c_void_p * MAX_LEVELS)]
+                ("col_stat", c_void_p * MAX_LEVELS), ("k_in", c_void_p), ("v_in", c_void_p)]
 
 
 class FlBlockState(ctypes.Structure):
@@ -163,6 +164,9 @@ def lib():
         L.fl_kv_dequant.argtypes = [POINTER(FlKvCache), c_int, c_int, c_void_p, c_void_p]
         L.fl_timing_enable.argtypes = [c_int]
         L.fl_timing_report.argtypes = [ctypes.c_char_p, c_size_t]
+        L.fl_check_indices.argtypes = [c_void_p, c_long, c_long, c_long]
+        L.fl_check_finite.argtypes = [c_void_p, c_long]
+        L.fl_set_checks.argtypes = [c_int]
         for name in EXPORTS:
             if name not in ("fl_last_error", "fl_version", "fl_workspace_size"):
                 getattr(L, name).restype = c_int
@@ -202,8 +206,10 @@ def fl_workspace_size(op, a, b=0, c=0, e=0):
     return int(lib().fl_workspace_size(op, a, b, c, e))
 
 
-def fl_timing_enable(on=True):
-    _check("fl_timing_enable", lib().fl_timing_enable(int(bool(on))))
+def fl_timing_enable(level=1):
+    """0 off; 1 per-kernel and per-phase events; 2 per-phase events only
+    (see the header).  True / False mean 1 / 0."""
+    _check("fl_timing_enable", lib().fl_timing_enable(int(level)))
 
 
 def fl_timing_report():
@@ -293,6 +299,30 @@ def fl_kv_dequant(cache: FlKvCache, level, which, out, stream=None):
     values (1) at loop level+1."""
     _check("fl_kv_dequant", lib().fl_kv_dequant(ctypes.byref(cache), level, which, _p(out),
                                                 _stream(stream)))
+
+
+def fl_check_indices(idx, lo, hi):
+    """Host-side validation of an index list (numpy int32): strictly
+    ascending, every element in [lo, hi); returns (status, message)."""
+    import numpy as np
+    a = np.ascontiguousarray(idx, dtype=np.int32)
+    rc = lib().fl_check_indices(a.ctypes.data_as(c_void_p), a.size, int(lo), int(hi))
+    return rc, lib().fl_last_error().decode() if rc else ""
+
+
+def fl_check_finite(x):
+    """Host-side validation of fp32 values (numpy): all finite; returns
+    (status, message)."""
+    import numpy as np
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    rc = lib().fl_check_finite(a.ctypes.data_as(c_void_p), a.size)
+    return rc, lib().fl_last_error().decode() if rc else ""
+
+
+def fl_set_checks(on=True):
+    """Check mode: entry points validate their device index lists and
+    statistics on the host before enqueuing anything (see the header)."""
+    _check("fl_set_checks", lib().fl_set_checks(int(bool(on))))
 
 
 def fl_sq_err(x, ref, out, ws=None, stream=None):
@@ -408,6 +438,61 @@ class LoopRunner:
     def k_used(self, r):
         return self.state.k_cur[r - 1]
 
+    # ---- checkpoint / resume of the loop state ----
+    def _state_tensors(self):
+        """Every device buffer that carries state from one loop to the next
+        (the workspace is scratch and carries none)."""
+        named = {}
+        for r, lev in enumerate(self.codes):
+            for key, t in lev.items():
+                named[f"level{r}.{key}"] = t
+        for r in range(self.R):
+            for key in ("active", "slot", "sel", "col_stat"):
+                t = getattr(self, key)[r]
+                if t is not None:
+                    named[f"{key}{r}"] = t
+        for key in ("stat", "out", "lse", "mass_u", "out_u"):
+            named[key] = getattr(self, key)
+        return named
+
+    def snapshot(self):
+        """Host copy of the whole loop state after some loop: the device
+        buffers of the cache levels and per-loop state, and the host-side
+        bookkeeping of fl_loop_state (column counts, which selection each loop
+        used, the cache levels' row counts and widths).  ``restore`` on a
+        runner of the same configuration (this one or a fresh one) resumes
+        from it."""
+        torch.cuda.synchronize()
+        st = self.state
+        sel_idx = []
+        for r in range(self.R):
+            p = st.sel_used[r]
+            sel_idx.append(None if not p else
+                           next(i for i, t in enumerate(self.sel) if t is not None and t.data_ptr() == p))
+        levels = [(st.cache.level[r].bits, st.cache.level[r].n_rows, bool(st.cache.level[r].rows))
+                  for r in range(self.R)]
+        return dict(tensors={k: t.cpu().clone() for k, t in self._state_tensors().items()},
+                    k_cur=[st.k_cur[r] for r in range(self.R)], sel_used=sel_idx, levels=levels,
+                    n_levels=st.cache.n_levels)
+
+    def restore(self, snap):
+        mine = self._state_tensors()
+        assert set(mine) == set(snap["tensors"]), "snapshot of another configuration"
+        for k, t in mine.items():
+            t.copy_(snap["tensors"][k])
+        st = self.state
+        for r in range(self.R):
+            st.k_cur[r] = snap["k_cur"][r]
+            i = snap["sel_used"][r]
+            st.sel_used[r] = None if i is None else self.sel[i].data_ptr()
+            bits, n_rows, has_rows = snap["levels"][r]
+            L = st.cache.level[r]
+            L.bits, L.n_rows = bits, n_rows
+            L.rows = st.active[r] if has_rows else None
+            L.slot = st.slot[r] if has_rows else None
+        st.cache.n_levels = snap["n_levels"]
+        torch.cuda.synchronize()
+
 
 class BlockRunner:
     """Allocates per-layer caches and state for the looped block and runs
@@ -418,9 +503,12 @@ class BlockRunner:
     def __init__(self, N, H, d, g, R, n_sink, n_active, k_cols, bits, weights, ffn,
                  rope_theta=10000.0, norm_eps=1e-6, mode=FL_DEQ_AUTO,
                  token_stat=FL_TOKEN_STAT_ABS, col_stat=FL_COL_STAT_MASS, row_capacity=None,
-                 quant=FL_QUANT_ABSMAX, device="cuda"):
+                 quant=FL_QUANT_ABSMAX, capture_kv=False, device="cuda"):
         """row_capacity: per-loop row counts to allocate (default n_active),
-        so that ``set_active_counts`` can later run other schedules."""
+        so that ``set_active_counts`` can later run other schedules.
+        capture_kv: also keep each layer's latest pre-quantisation keys (after
+        RoPE) and values of the active rows (``layer_bufs[l]["k_in"]``,
+        ``["v_in"]``, bf16 [N][H][d], first n_active rows valid)."""
         dev = torch.device(device)
         self.N, self.H, self.d, self.R, self.g = N, H, d, R, g
         cap = list(row_capacity) if row_capacity is not None else list(n_active)
@@ -465,6 +553,10 @@ class BlockRunner:
             lb["out_u"] = buf((N, H, d), torch.float32)
             Ls.q_state, Ls.out, Ls.lse = _p(lb["q_state"]), _p(lb["out"]), _p(lb["lse"])
             Ls.mass_u, Ls.out_u = _p(lb["mass_u"]), _p(lb["out_u"])
+            if capture_kv:
+                lb["k_in"] = buf((N, H, d), torch.bfloat16)
+                lb["v_in"] = buf((N, H, d), torch.bfloat16)
+                Ls.k_in, Ls.v_in = _p(lb["k_in"]), _p(lb["v_in"])
             lb["sel"], lb["col_stat"] = [], []
             for r in range(R):
                 sl = buf((H, k_cols[r]), torch.int32) if r > 0 and k_cols[r] < N else None

@@ -122,6 +122,59 @@ def assert_close_scaled(got, want, what, rel=1e-2, mabs=3e-2):
     return e, worst
 
 
+def assert_close_bf16(got, want, what, rel=1e-2, mabs=3e-2):
+    """Activations of the looped block stored as bf16 by two implementations
+    (keys and values before quantisation: a bf16 projection of the RMSNorm'd
+    hidden state, RoPE, a second bf16 rounding), rows [n][...] per token.
+    Two parts make their difference:
+      * bf16 keeps 8 significant bits, so values summed in different orders
+        round to neighbours one ulp (2^-8 to 2^-7 of the value) apart at each
+        rounding -- a value in [4, 8) already has an ulp of 2^-5 > 3e-2;
+      * the hidden state's own difference (bounded in units of its row's
+        RMS, see assert_close_state), carried through RMSNorm and the
+        projection, is spread over the whole row of the token.
+    Elementwise |got - want| <= mabs * max(1, |want|, rms(want row)) (about
+    four ulps of the value, or 3e-2 of the row's scale), rel-L2 <= rel."""
+    got = np.asarray(got, np.float64); want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    e = rel_l2(got, want)
+    w2 = want.reshape(want.shape[0], -1)
+    rms = np.sqrt(np.mean(w2 * w2, axis=1)).reshape((-1,) + (1,) * (want.ndim - 1))
+    lim = mabs * np.maximum(np.maximum(1.0, np.abs(want)), rms)
+    worst = float(np.max(np.abs(got - want) / lim)) if got.size else 0.0
+    if not (e <= rel and worst <= 1.0):
+        idx = np.unravel_index(np.argmax(np.abs(got - want) / lim), got.shape)
+        print(f"  {what}: worst at {idx}: got {got[idx]:.5f} want {want[idx]:.5f}", flush=True)
+    assert e <= rel and worst <= 1.0, f"{what}: rel-L2 {e:.3e} (<= {rel}), scaled max {worst:.3f} (<= 1)"
+    return e, worst
+
+
+def assert_close_state(got, want, what, rel=1e-2, mabs=3e-2):
+    """The looped block's fp32 residual stream h [N][D].  Its bounds follow
+    from how the block reads it: every layer sees h only through RMSNorm,
+    i.e. relative to each row's RMS, so an elementwise difference counts in
+    units of its row's RMS: |got - want| <= mabs * max(1, rms(want row)),
+    with rel-L2 <= rel over the whole state.  (An attention output that
+    differs within the attention bound moves every later row of h through
+    the output projection, and rows updated in more loops carry larger
+    states and larger absolute differences.)"""
+    got = np.asarray(got, np.float64); want = np.asarray(want, np.float64)
+    assert got.shape == want.shape and got.ndim == 2, (what, got.shape, want.shape)
+    e = rel_l2(got, want)
+    rms = np.sqrt(np.mean(want * want, axis=1, keepdims=True))
+    lim = mabs * np.maximum(1.0, rms)
+    ratio = np.abs(got - want) / lim
+    worst = float(ratio.max()) if got.size else 0.0
+    m = float(np.max(np.abs(got - want))) if got.size else 0.0
+    if not (e <= rel and worst <= 1.0):
+        idx = np.unravel_index(np.argmax(ratio), got.shape)
+        print(f"  {what}: worst at {idx}: got {got[idx]:.5f} want {want[idx]:.5f} "
+              f"(row rms {rms[idx[0], 0]:.3f})", flush=True)
+    assert e <= rel and worst <= 1.0, (f"{what}: rel-L2 {e:.3e} (<= {rel}), max-abs {m:.3e}, "
+                                       f"row-scaled max {worst:.3f} (<= 1)")
+    return e, m, worst
+
+
 def compare_chain(w, gres, ores, bits=None, check_codes=True, quant=fl.FL_QUANT_ABSMAX):
     bits = bits or w.bits
     report = []

@@ -212,3 +212,39 @@ def test_decode_append_rejects(L):
     # absmax: the base must be int8
     st.cache.scheme = fl.FL_QUANT_ABSMAX
     assert app(0, 1) == -2 and "base level bits 4" in _err(L)
+
+
+def test_check_indices_host(L):
+    import numpy as np
+    ok = np.array([0, 3, 4, 9], np.int32)
+    assert fl.fl_check_indices(ok, 0, 10) == (0, "")
+    assert fl.fl_check_indices(np.zeros(0, np.int32), 0, 10)[0] == 0
+    rc, msg = fl.fl_check_indices(np.array([0, 4, 3], np.int32), 0, 10)
+    assert rc == -1 and "element 2 = 3" in msg and "ascending" in msg
+    rc, msg = fl.fl_check_indices(np.array([1, 1], np.int32), 0, 10)
+    assert rc == -1 and "element 1 = 1" in msg                    # duplicate
+    rc, msg = fl.fl_check_indices(np.array([2, 10], np.int32), 0, 10)
+    assert rc == -1 and "outside [0, 10)" in msg
+    rc, msg = fl.fl_check_indices(np.array([-1, 2], np.int32), 0, 10)
+    assert rc == -1 and "element 0 = -1" in msg
+
+
+def test_check_finite_host(L):
+    import numpy as np
+    assert fl.fl_check_finite(np.array([0.0, -1.5, 3e38], np.float32)) == (0, "")
+    for bad in (np.nan, np.inf, -np.inf):
+        rc, msg = fl.fl_check_finite(np.array([1.0, bad], np.float32))
+        assert rc == -1 and "element 1" in msg and "finite" in msg
+    assert L.fl_check_finite(None, 3) == -1
+    assert L.fl_check_indices(None, 3, 0, 1) == -1
+
+
+def test_check_mode_toggles(L):
+    fl.fl_set_checks(True)
+    try:
+        # host-side argument validation still comes first (nothing is copied)
+        rc = L.fl_select_active(1, 0, FAKE, FAKE, 100, 64, None, 100, 0, None, FAKE, FAKE, None,
+                                None, 0, None)
+        assert rc == -1 and "n_select" in _err(L)
+    finally:
+        fl.fl_set_checks(False)

@@ -64,7 +64,7 @@ def test_calibration_decisions_match_oracle():
     wdev = [{k: to_dev(v, "bf16") for k, v in lw.items()} for lw in inp["layers"]]
     run = fl.BlockRunner(N, w.H, w.d, w.g, R, w.n_sink, [N] * R, w.kcols, w.bits, wdev,
                          w.extra["ffn"], rope_theta=w.extra["theta"], norm_eps=w.extra["eps"],
-                         row_capacity=[N] * R)
+                         row_capacity=[N] * R, capture_kv=True)
     h1 = torch.from_numpy(inp["h1"]).cuda()
     grid = [0.1 * i for i in range(1, 11)]
     tol = 0.05          # the paper's bound on the relative reconstruction error

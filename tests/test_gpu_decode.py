@@ -36,6 +36,12 @@ CASES = {
                            quant="asym"),
     "asym_d64_g32_mixed": _w(2, 515, 3, 64, 32, (515, 128, 128, 60), bits=(8, 4, 2, 2), seed=16,
                              quant="asym"),
+    # a 2-bit asymmetric base: the dense loop's kernel specialised on that
+    # width (16 column loads in flight per lane), d = 128 and d = 64
+    "asym_base2": _w(2, 433, 2, 128, 64, (433, 96, 64, 40), bits=(2, 4, 4, 2), seed=17,
+                     quant="asym"),
+    "asym_base2_d64_g32": _w(2, 301, 3, 64, 32, (301, 96, 96), bits=(2, 2, 4), seed=18,
+                             quant="asym"),
 }
 
 

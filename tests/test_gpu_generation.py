@@ -175,6 +175,8 @@ def _check_block(w, b, o, i, app, run, n_act):
      132, 64),
     ("asym_d64_g32", 3, 411, 3, 64, 32, (411, 128, 128), (8, 2, 4), (1.0, 0.3, 0.3), 72, 6),
     ("asym_no_window", 2, 200, 2, 64, 32, (200, 80, 48), (4, 4, 2), (1.0, 0.4, 0.2), 66, 0),
+    # a 2-bit asymmetric base (the dense loop's width-specialised kernel)
+    ("asym_base2", 2, 213, 2, 64, 32, (213, 80, 48), (2, 4, 2), (1.0, 0.4, 0.2), 72, 6),
 ])
 def test_generation_matches_oracle(name, B, N, H, d, g, kcols, bits, rho, n_gen, window):
     w = _w(B, N, H, d, g, kcols, bits, rho, seed=21, quant="asym" if name.startswith("asym") else "absmax")
