@@ -279,6 +279,29 @@ typedef struct fl_attn_args {
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void* ws,
                         size_t ws_bytes, fl_stream_t stream);
 
+/* fl_sparse_loop_attn_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): fl_sparse_loop_attn with its workspace taken from a
+ * scratch area the library keeps in every GPU's memory for the life of the
+ * process (FL_NOALLOC_SCRATCH_BYTES per GPU), instead of a caller workspace.
+ * The caller still passes the cache, inputs and outputs.  The call makes no
+ * device allocation (no hipMalloc / hipFree; with the timing aid on, no
+ * events are recorded for it) and needs no zeroed memory: every part of the
+ * scratch it reads it has written in the same call.  Its first call on a
+ * device looks up that device's scratch address (the device must be
+ * current).  All calls on one GPU share its scratch, so calls that overlap
+ * on one GPU (on different streams, or from several threads without stream
+ * ordering between them) race; calls ordered on one stream do not.
+ * Limit: the workspace the call needs (fl_workspace_size(FL_WS_SPARSE_ATTN,
+ * H, k, d, level + 1) for FL_DEQ_IN_TILE, less for the other modes) must fit
+ * FL_NOALLOC_SCRATCH_BYTES -- e.g. 16 heads x 128 with up to 2048 selected
+ * columns in the default mode.  Errors: as fl_sparse_loop_attn;
+ * FL_ERR_WORKSPACE (before anything is enqueued) when the call needs more,
+ * FL_ERR_HIP when the scratch address cannot be looked up. */
+#define FL_NOALLOC_SCRATCH_BYTES (72L << 20)
+int fl_sparse_loop_attn_noalloc(const fl_kv_cache* cache, const fl_attn_args* args,
+                                fl_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * fl_loop_step -- one whole loop r >= 1 of the lazy-update attention step
  * (paper Sec. 4.1-4.3) in attention-only form: the loop's hidden states and

@@ -105,9 +105,12 @@ hipEvent_t ev_get() {
     return e;
 }
 
+// set while an allocation-free call runs on this thread: no events
+thread_local bool g_no_events = false;
+
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& f) {
-    if (!g_timing) return f();
+    if (!g_timing || g_no_events) return f();
     std::lock_guard<std::mutex> lk(g_tmu);
     hipEvent_t a = ev_get(), b = ev_get();
     if (a) (void)hipEventRecord(a, st);
@@ -120,7 +123,7 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
 // An event recorded on the stream when phase timing is on (else NULL);
 // phase_end records the closing event and keeps the pair under `name`.
 hipEvent_t phase_begin(hipStream_t st) {
-    if (!g_phases) return nullptr;
+    if (!g_phases || g_no_events) return nullptr;
     std::lock_guard<std::mutex> lk(g_tmu);
     hipEvent_t a = ev_get();
     if (a && hipEventRecord(a, st) != hipSuccess) {
@@ -596,6 +599,50 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, void* ws,
                         size_t ws_bytes, fl_stream_t stream) {
     return sparse_loop_attn(cache, a, ws, ws_bytes, stream, nullptr);
+}
+
+} // extern "C"
+
+// Scratch of fl_sparse_loop_attn_noalloc: one copy per GPU the library runs
+// on, for the life of the process.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[FL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address (looked up once per device)
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    FL_HIP(hipGetDevice(&dev), "hipGetDevice");
+    FL_REQUIRE(dev >= 0 && dev < kMaxDevices, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        FL_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        FL_REQUIRE(p != nullptr, "scratch address of device %d is NULL", dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FL_OK;
+}
+
+struct NoEvents {
+    NoEvents() { g_no_events = true; }
+    ~NoEvents() { g_no_events = false; }
+};
+} // namespace
+
+extern "C" {
+
+int fl_sparse_loop_attn_noalloc(const fl_kv_cache* cache, const fl_attn_args* a, fl_stream_t stream) {
+    void* ws = nullptr;
+    const int rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    NoEvents guard;
+    return sparse_loop_attn(cache, a, ws, (size_t)FL_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 // Phase events of fl_loop_step: e0 opens steps a1-a4 at the call's start;

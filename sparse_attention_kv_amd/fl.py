@@ -29,7 +29,7 @@ EXPORTS = ["fl_select_active", "fl_select_columns", "fl_kv_residual_quant",
            "fl_sparse_loop_attn", "fl_loop_step", "fl_block_step", "fl_decode_step",
            "fl_decode_append", "fl_sq_err", "fl_kv_dequant", "fl_workspace_size",
            "fl_last_error", "fl_version", "fl_timing_enable", "fl_timing_report",
-           "fl_check_indices", "fl_check_finite", "fl_set_checks"]
+           "fl_check_indices", "fl_check_finite", "fl_set_checks", "fl_sparse_loop_attn_noalloc"]
 FL_WS_BLOCK_STEP = 5
 FL_WS_SQ_ERR = 6
 
@@ -152,6 +152,7 @@ def lib():
                                            c_int, c_void_p]
         L.fl_sparse_loop_attn.argtypes = [POINTER(FlKvCache), POINTER(FlAttnArgs), c_void_p,
                                           c_size_t, c_void_p]
+        L.fl_sparse_loop_attn_noalloc.argtypes = [POINTER(FlKvCache), POINTER(FlAttnArgs), c_void_p]
         L.fl_loop_step.argtypes = [POINTER(FlLoopCfg), POINTER(FlLoopState), POINTER(FlLoopInputs),
                                    c_int, c_void_p, c_size_t, c_void_p]
         L.fl_block_step.argtypes = [POINTER(FlBlockCfg), POINTER(FlLayerWeights),
@@ -262,6 +263,16 @@ def fl_sparse_loop_attn(cache: FlKvCache, args: FlAttnArgs, ws, stream=None):
     rc = lib().fl_sparse_loop_attn(ctypes.byref(cache), ctypes.byref(args), _p(ws),
                                    ws.numel() * ws.element_size(), _stream(stream))
     _check("fl_sparse_loop_attn", rc)
+
+
+def fl_sparse_loop_attn_noalloc(cache: FlKvCache, args: FlAttnArgs, stream=None):
+    """fl_sparse_loop_attn with the library's per-GPU scratch as workspace
+    (allocates nothing; see the header for the size limit and sharing)."""
+    rc = lib().fl_sparse_loop_attn_noalloc(ctypes.byref(cache), ctypes.byref(args), _stream(stream))
+    _check("fl_sparse_loop_attn_noalloc", rc)
+
+
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 
 def fl_loop_step(cfg: FlLoopCfg, state: FlLoopState, inputs: FlLoopInputs, r, ws, stream=None):
