@@ -117,8 +117,10 @@ typedef struct fl_kv_cache {
 enum fl_ws_op {
     FL_WS_SELECT_ACTIVE = 1,  /* a = n_cand                                    */
     FL_WS_SELECT_COLUMNS = 2, /* a = H, b = n_cand                             */
-    FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k, c = d, e = cache levels used (level+1; <= 0: max) */
-    FL_WS_LOOP_STEP = 4,      /* a = H, b = N (largest k), c = d, e = R        */
+    FL_WS_SPARSE_ATTN = 3,    /* a = H, b = k (k_prev for a rebuild with sel_prev),
+                                 c = d, e = n (active rows of the call);
+                                 FL_DEQ_IN_TILE calls need FL_WS_LOOP_STEP's size */
+    FL_WS_LOOP_STEP = 4,      /* a = H, b = N (largest k and n), c = d, e = R  */
     FL_WS_BLOCK_STEP = 5,     /* a = N, b = H, c = d, e = ffn width            */
     FL_WS_SQ_ERR = 6          /* a = n                                         */
 };
@@ -274,6 +276,14 @@ typedef struct fl_attn_args {
     const void* q_prev;
     int q_prev_gathered;
     int col_stat_kind;         /* fl_col_stat (used when col_stat != NULL)      */
+    /* rebuild after a sparse loop: that loop's column set [H][k_prev]
+     * (ascending, sel a subset of it per head).  Given, the rebuild adds the
+     * pruned columns' share to the carried caches (additive form,
+     * M_U += sum P_prev, O_U += sum P_prev V^_prev over S_prev \ sel) and
+     * does not read o_prev; NULL, it subtracts the selected columns' share
+     * from o_prev (after the dense first loop, where S_prev is every column). */
+    const int32_t* sel_prev;
+    int k_prev;
 } fl_attn_args;
 
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void* ws,
@@ -293,12 +303,12 @@ int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void
  * on one GPU (on different streams, or from several threads without stream
  * ordering between them) race; calls ordered on one stream do not.
  * Limit: the workspace the call needs (fl_workspace_size(FL_WS_SPARSE_ATTN,
- * H, k, d, level + 1) for FL_DEQ_IN_TILE, less for the other modes) must fit
+ * H, k, d, n) in the default mode; more for FL_DEQ_IN_TILE) must fit
  * FL_NOALLOC_SCRATCH_BYTES -- e.g. 16 heads x 128 with up to 2048 selected
- * columns in the default mode.  Errors: as fl_sparse_loop_attn;
+ * columns and 32768 active rows.  Errors: as fl_sparse_loop_attn;
  * FL_ERR_WORKSPACE (before anything is enqueued) when the call needs more,
  * FL_ERR_HIP when the scratch address cannot be looked up. */
-#define FL_NOALLOC_SCRATCH_BYTES (72L << 20)
+#define FL_NOALLOC_SCRATCH_BYTES (80L << 20)
 int fl_sparse_loop_attn_noalloc(const fl_kv_cache* cache, const fl_attn_args* args,
                                 fl_stream_t stream);
 

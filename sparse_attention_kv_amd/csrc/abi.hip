@@ -45,25 +45,29 @@ constexpr long kAlign = 256;
 long align_up(long x) { return (x + kAlign - 1) / kAlign * kAlign; }
 long kpad(long k) { return (k + 63) / 64 * 64; }
 
-// workspace of fl_sparse_loop_attn: two compact bf16 copies (K, V^T) for the
-// current loop and, for a cache rebuild, two for the previous loop, each with
-// a "lo" copy (used when the cache has residual levels or inputs are fp32),
-// plus the column positions and the fp32 value norms of the selected columns.
-// The in-tile path adds per-level quantised planes (codes <= 8 bits, fp32
-// scales per group of >= 32 channels) for K and V.
+// Workspace of fl_sparse_loop_attn (k selected columns, n active rows):
+//  * compact bf16 copies of the selected columns, K and V^T, each with a "lo"
+//    copy (the residual x - bf16(x)), for the current loop and, for a cache
+//    rebuild, the previous one: 8 buffers of H x kp x d bf16, kp = the padded
+//    column count plus room for the [normal | pad | outlier] slot order;
+//  * per side: column positions and slot order [H][kp], the parts' sizes
+//    [H][2], the row order [H][n] and normal-row count [H]; one [H][n] byte
+//    plane of row flags; the value norms [H][kp];
+//  * the in-tile path adds per-level quantised planes (codes <= 8 bits, fp32
+//    scales per group of >= 32 channels) for K and V.
+long kslots(long k) { return kpad(k) + 128; }
 long quant_plane_bytes(long H, long kp, long d) {
     return 2 * (align_up(H * kp * d) + align_up(H * kp * (d / 32) * 4));
 }
-long attn_ws_bytes(long H, long k, long d, long levels) {
-    const long kp = kpad(k);
-    if (levels <= 0 || levels > FL_MAX_LEVELS) levels = FL_MAX_LEVELS;
-    return 8 * align_up(H * kp * d * 2) + 2 * align_up(H * kp * 4) +
-           levels * quant_plane_bytes(H, kp, d) + kAlign;
+long attn_ws_bytes_once(long H, long k, long d, long n) {
+    const long kp = kslots(k);
+    return 8 * align_up(H * kp * d * 2) + 5 * align_up(H * kp * 4) + align_up(H * kp) +
+           2 * align_up(H * 2 * 4) + align_up(H * n) + 2 * align_up(H * n * 4) + 2 * align_up(H * 4) +
+           kAlign;
 }
-// the compact-gather (FL_DEQ_ONCE) path alone: no per-level code planes
-long attn_ws_bytes_once(long H, long k, long d) {
-    const long kp = kpad(k);
-    return 8 * align_up(H * kp * d * 2) + 2 * align_up(H * kp * 4) + kAlign;
+long attn_ws_bytes(long H, long k, long d, long n, long levels) {
+    if (levels <= 0 || levels > FL_MAX_LEVELS) levels = FL_MAX_LEVELS;
+    return attn_ws_bytes_once(H, k, d, n) + levels * quant_plane_bytes(H, kslots(k), d);
 }
 
 // workspace of fl_block_step: compact bf16 activations of the active rows
@@ -72,7 +76,7 @@ long attn_ws_bytes_once(long H, long k, long d) {
 long block_ws_bytes(long N, long H, long d, long F) {
     const long D = H * d;
     return align_up(N * D * 2) * 5 + align_up(N * 3 * D * 2) + align_up(N * F * 2) +
-           attn_ws_bytes_once(H, N, d) + kAlign;
+           attn_ws_bytes_once(H, N, d, N) + kAlign;
 }
 
 // Operand precision of the attention products: residual levels hold the
@@ -309,9 +313,11 @@ size_t fl_workspace_size(int op, long a, long b, long c, long e) {
     case FL_WS_SQ_ERR:
         return a > 0 ? (size_t)(align_up(16L * fl::sq_err_blocks(a)) + kAlign) : 0;
     case FL_WS_SPARSE_ATTN:
+        if (a <= 0 || b <= 0 || !(c == 64 || c == 128) || e <= 0) return 0;
+        return (size_t)attn_ws_bytes_once(a, b, c, e);
     case FL_WS_LOOP_STEP:
         if (a <= 0 || b <= 0 || !(c == 64 || c == 128)) return 0;
-        return (size_t)attn_ws_bytes(a, b, c, e);
+        return (size_t)attn_ws_bytes(a, b, c, b, e);
     default: return 0;
     }
 }
@@ -480,6 +486,9 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     if (a->cache_op == FL_CACHE_REBUILD) {
         FL_REQUIRE(a->level >= 1, "cache rebuild needs a previous loop (level >= 1)");
         FL_REQUIRE(a->q_prev != nullptr, "q_prev NULL");
+        if (a->sel_prev)
+            FL_REQUIRE(a->k_prev >= a->k && a->k_prev <= N, "k_prev %d not in [k=%d, N=%d]", a->k_prev,
+                       a->k, N);
     }
     FL_REQUIRE(a->mode >= FL_DEQ_AUTO && a->mode <= FL_DEQ_IN_TILE, "mode %d", a->mode);
     FL_REQUIRE(a->col_stat_kind == FL_COL_STAT_MASS || a->col_stat_kind == FL_COL_STAT_VNORM,
@@ -488,6 +497,8 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
         hipStream_t st0 = (hipStream_t)stream;
         rc = check_idx_dev(a->active, 1, a->n, 0, N, "active", st0);
         if (!rc) rc = check_idx_dev(a->sel, H, a->k, 0, N, "sel", st0);
+        if (!rc && a->cache_op == FL_CACHE_REBUILD)
+            rc = check_idx_dev(a->sel_prev, H, a->k_prev, 0, N, "sel_prev", st0);
         if (!rc) rc = check_levels_dev(*cache, a->level, st0);
         if (rc) return rc;
     }
@@ -504,18 +515,40 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
         for (int l = 0; l <= a->level; ++l)
             if (cache->level[l].bits == 32)
                 return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE needs quantised levels (level %d is raw)", l);
-    const long need = in_tile ? attn_ws_bytes(H, a->k, d, a->level + 1) : attn_ws_bytes_once(H, a->k, d);
+    // Precision-adaptive operands (bf16 queries over a cache with residual
+    // levels): columns and rows are classed per head, and only outlier rows
+    // or columns take hi + lo operand pairs.  A rebuild after a sparse loop
+    // takes the additive form over the pruned columns (it does not inherit
+    // the previous loop's output error).
+    const bool adapt = !in_tile && a->dtype == FL_BF16 && a->level >= 1;
+    const bool adapt_old = !in_tile && a->dtype == FL_BF16 && a->level - 1 >= 1;
+    const bool rebuild_add = a->cache_op == FL_CACHE_REBUILD && adapt_old && a->sel_prev;
+    const int kcols = rebuild_add ? a->k_prev : a->k;
+    const long need = in_tile ? attn_ws_bytes(H, kcols, d, a->n, a->level + 1)
+                              : attn_ws_bytes_once(H, kcols, d, a->n);
     if (!ws || (long)ws_bytes < need)
         return fail(FL_ERR_WORKSPACE, "workspace %zu < %ld bytes", ws_bytes, need);
     hipStream_t st = (hipStream_t)stream;
-    const int kp = (int)kpad(a->k);
-    char* base = (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
-    const long kvb = align_up((long)H * kp * d * 2);
+    const int kp = (int)kslots(kcols);
+    char* p = (char*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+    auto take = [&](long bytes) { char* q = p; p += align_up(bytes); return q; };
     __bf16* buf[8];
-    for (int i = 0; i < 8; ++i) buf[i] = (__bf16*)(base + i * kvb);
-    int32_t* cpos = (int32_t*)(base + 8 * kvb);
-    float* vnorm_buf = (float*)(base + 8 * kvb + align_up((long)H * kp * 4));
-    char* qbase = base + 8 * kvb + 2 * align_up((long)H * kp * 4);
+    for (int i = 0; i < 8; ++i) buf[i] = (__bf16*)take((long)H * kp * d * 2);
+    int32_t* cpos = (int32_t*)take((long)H * kp * 4);
+    int32_t* cpos_old = (int32_t*)take((long)H * kp * 4);
+    float* vnorm_buf = (float*)take((long)H * kp * 4);
+    int32_t* perm = (int32_t*)take((long)H * kp * 4);
+    int32_t* perm_old = (int32_t*)take((long)H * kp * 4);
+    uint8_t* colflags = (uint8_t*)take((long)H * kp);
+    int32_t* pruned = (int32_t*)take((long)H * kp * 4);
+    int32_t* colseg = (int32_t*)take((long)H * 2 * 4);
+    int32_t* colseg_old = (int32_t*)take((long)H * 2 * 4);
+    uint8_t* rowflags = (uint8_t*)take((long)H * a->n);
+    int32_t* rowperm = (int32_t*)take((long)H * a->n * 4);
+    int32_t* rowperm_old = (int32_t*)take((long)H * a->n * 4);
+    int32_t* rowseg = (int32_t*)take((long)H * 4);
+    int32_t* rowseg_old = (int32_t*)take((long)H * 4);
+    char* qbase = p;
     // value norms of the current loop's columns, written by its gather
     float* vn = (a->col_stat && a->col_stat_kind == FL_COL_STAT_VNORM) ? vnorm_buf : nullptr;
     // new side: K, V^T (+ lo parts); previous-loop side for a rebuild
@@ -527,6 +560,24 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     P.H = H; P.n = a->n; P.k = a->k; P.kp = kp; P.dtype = a->dtype; P.cache_op = a->cache_op;
     P.c2 = c2; P.active = a->active; P.cpos = cpos;
     P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u; P.out_bf = out_bf;
+    // one side's compact columns (and, adaptive, its column and row orders)
+    auto prepare = [&](const int32_t* sel, int k, int upto, bool ad, int pr, const void* q, int q_gathered,
+                       int32_t* cp, int32_t* pm, int32_t* cs, int32_t* rp, int32_t* rs, __bf16* K_, __bf16* V_,
+                       __bf16* Kl_, __bf16* Vl_, float* vnorm) -> int {
+        if (ad)
+            FL_HIP(timed("classify", st, [&] {
+                       return fl::launch_classify(*cache, upto, sel, k, kp, q, a->dtype, q_gathered,
+                                                  a->active, a->n, fl::kTauCol, fl::kTauRow, colflags, pm,
+                                                  cs, rowflags, rp, rs, st);
+                   }),
+                   "classify");
+        FL_HIP(timed("gather", st, [&] {
+                   return fl::launch_gather_bf16(*cache, upto, sel, k, kp, ad || pr >= 1, K_, V_, Kl_,
+                                                 Vl_, cp, vnorm, ad ? pm : nullptr, st);
+               }),
+               "gather");
+        return FL_OK;
+    };
     if (in_tile) {
         fl::QTiles& qt = P.qt;
         qt.n_levels = a->level + 1;
@@ -546,42 +597,66 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
                }),
                "gather_q");
     } else {
-        FL_HIP(timed("gather", st, [&] {
-                   return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc, Vt,
-                                                 Kl, Vl, cpos, vn, st);
-               }),
-               "gather");
+        rc = prepare(a->sel, a->k, a->level, adapt, prec, a->q, a->q_gathered, cpos, perm, colseg, rowperm,
+                     rowseg, Kc, Vt, Kl, Vl, vn);
+        if (rc) return rc;
     }
     if (a->cache_op == FL_CACHE_REBUILD) {
         fl::AttnParams R = P;
         if (in_tile) {
             R.deq_levels = a->level; // the previous loop's cache: levels 0..level-1
         } else {
-            FL_HIP(timed("gather", st, [&] {
-                       return fl::launch_gather_bf16(*cache, a->level - 1, a->sel, a->k, kp,
-                                                     prec_old >= 1, Kc_old, Vt_old, Kl_old, Vl_old,
-                                                     cpos, nullptr, st);
-                   }),
-                   "gather(prev)");
-            R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old;
+            // additive form: the previous loop's side over the pruned columns
+            const int32_t* osel = a->sel;
+            int ok = a->k;
+            if (rebuild_add) {
+                FL_HIP(timed("prune_list", st, [&] {
+                           return fl::launch_set_diff(a->sel_prev, a->k_prev, a->sel, a->k, H, pruned, st);
+                       }),
+                       "set_diff");
+                osel = pruned;
+                ok = a->k_prev - a->k;
+            }
+            if (ok > 0) {
+                rc = prepare(osel, ok, a->level - 1, adapt_old, prec_old, a->q_prev, a->q_prev_gathered, cpos_old,
+                             perm_old, colseg_old, rowperm_old, rowseg_old, Kc_old, Vt_old, Kl_old, Vl_old,
+                             nullptr);
+                if (rc) return rc;
+            }
+            R.k = ok;
+            R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old; R.cpos = cpos_old;
         }
         R.q = a->q_prev; R.q_gathered = a->q_prev_gathered;
-        FL_HIP(timed(prec_old ? "attn_rebuild_split" : "attn_rebuild", st,
-                     [&] { return fl::launch_attn(d, fl::MODE_REBUILD, prec_old, in_tile, R, st); }),
-               "attn(rebuild)");
+        if (adapt_old) {
+            R.rowperm = rowperm_old; R.rowseg = rowseg_old; R.colseg = colseg_old;
+            if (R.k > 0 || !rebuild_add)
+                FL_HIP(timed(rebuild_add ? "attn_ad_rebuild_add" : "attn_ad_rebuild", st, [&] {
+                           return fl::launch_attn_ad(d, rebuild_add ? fl::MODE_REBUILD_ADD : fl::MODE_REBUILD, R, st);
+                       }),
+                       "attn(rebuild)");
+        } else {
+            FL_HIP(timed(prec_old ? "attn_rebuild_split" : "attn_rebuild", st,
+                         [&] { return fl::launch_attn(d, fl::MODE_REBUILD, prec_old, in_tile, R, st); }),
+                   "attn(rebuild)");
+        }
     }
     P.q = a->q; P.q_gathered = a->q_gathered; P.Kc = Kc; P.Vt = Vt; P.Kc_lo = Kl; P.Vt_lo = Vl;
     P.deq_levels = a->level + 1;
-    // timing names follow the kernel instantiation: bf16 operands ("attn",
-    // the dense first loop) and hi/lo split operands ("attn_split")
-    FL_HIP(timed(prec ? "attn_split" : "attn", st,
-                 [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),
-           "attn");
+    // timing names follow the kernel: bf16 operands ("attn", the dense first
+    // loop), precision-adaptive ("attn_ad"), hi/lo split ("attn_split")
+    if (adapt) {
+        P.rowperm = rowperm; P.rowseg = rowseg; P.colseg = colseg;
+        FL_HIP(timed("attn_ad", st, [&] { return fl::launch_attn_ad(d, fl::MODE_ATTN, P, st); }), "attn");
+    } else {
+        FL_HIP(timed(prec ? "attn_split" : "attn", st,
+                     [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),
+               "attn");
+    }
     if (a->col_stat) {
         if (in_tile) // the statistics sweep reads the keys as compact bf16
             FL_HIP(timed("gather", st, [&] {
                        return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc,
-                                                     Vt, Kl, Vl, cpos, vn, st);
+                                                     Vt, Kl, Vl, cpos, vn, nullptr, st);
                    }),
                    "gather");
         fl::ColParams C{};
@@ -589,8 +664,10 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
         C.cache_op = a->cache_op == FL_CACHE_ZERO ? FL_CACHE_ZERO : FL_CACHE_CARRY;
         C.c2 = c2; C.q = a->q; C.active = a->active; C.Kc = Kc; C.Kc_lo = Kl; C.cpos = cpos;
         C.lse = a->lse; C.mass_u = a->mass_u; C.col_stat = a->col_stat; C.vnorm = vn;
-        FL_HIP(timed(prec ? "colstat_split" : "colstat", st,
-                     [&] { return fl::launch_colstat(d, prec, C, st); }),
+        C.perm = adapt ? perm : nullptr;
+        const int cprec = adapt ? 1 : prec;
+        FL_HIP(timed(cprec ? "colstat_split" : "colstat", st,
+                     [&] { return fl::launch_colstat(d, cprec, C, st); }),
                "colstat");
     }
     return FL_OK;
@@ -764,6 +841,7 @@ static int loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inp
     A.sel = S->sel_used[r - 1]; A.k = S->k_cur[r - 1]; A.level = r - 1;
     A.cache_op = changed ? FL_CACHE_REBUILD : FL_CACHE_CARRY;
     A.q_prev = in->q_prev; A.q_prev_gathered = 0;
+    A.sel_prev = S->sel_used[r - 2]; A.k_prev = k_prev;
     const bool need_c = r < cfg->R && cfg->k_cols[r] < S->k_cur[r - 1];
     A.col_stat = need_c ? S->col_stat[r - 1] : nullptr;
     FL_REQUIRE(!need_c || A.col_stat, "col_stat[%d] buffer NULL", r - 1);
@@ -799,7 +877,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
     __bf16* qkv = (__bf16*)take((long)N * 3 * D * 2);
     __bf16* act_buf = (__bf16*)take((long)N * F * 2);
     void* aws = p;
-    const size_t aws_bytes = (size_t)attn_ws_bytes_once(H, N, d);
+    const size_t aws_bytes = (size_t)attn_ws_bytes_once(H, N, d, N);
 
     // ---- the loop's active tokens (Sec. 4.1) ----
     int n;
@@ -893,6 +971,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
             }
             A.sel = Ls.sel_used[r - 1]; A.k = Ls.k_cur[r - 1];
             A.cache_op = changed ? FL_CACHE_REBUILD : FL_CACHE_CARRY;
+            A.sel_prev = Ls.sel_used[r - 2]; A.k_prev = k_prev;
             const bool need_c = r < cfg->R && cfg->k_cols[r] < Ls.k_cur[r - 1];
             A.col_stat = need_c ? Ls.col_stat[r - 1] : nullptr;
             FL_REQUIRE(!need_c || A.col_stat, "layer %d col_stat[%d] NULL", l, r - 1);

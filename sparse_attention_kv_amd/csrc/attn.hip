@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      __bf16* __restrict__ Kc_lo,
                                                      __bf16* __restrict__ Vt_lo,
                                                      int32_t* __restrict__ cpos,
-                                                     float* __restrict__ vnorm) {
+                                                     float* __restrict__ vnorm,
+                                                     const int32_t* __restrict__ perm) {
     constexpr int TPC = D / 8;            // threads per column
     constexpr int GC = gather_cols<D>();  // columns per workgroup (16 or 32)
     __shared__ __bf16 sV[X3 ? 2 : 1][GC][D + 8];
@@ -73,9 +74,10 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
     const int tid = threadIdx.x;
     const int col = tid / TPC;
     const int c0 = (tid % TPC) * 8;
-    const int p = p0 + col;
-    const bool live = p < k;
-    const long j = live ? (sel ? (long)sel[(long)h * k + p] : (long)p) : 0;
+    const int p = p0 + col;  // compact slot
+    const int src = perm ? perm[(long)h * kp + p] : (p < k ? p : -1);  // selection index
+    const bool live = src >= 0;
+    const long j = live ? (sel ? (long)sel[(long)h * k + src] : (long)src) : 0;
     if (c0 == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
     const int HD = c.H * D;
     const int ch = h * D + c0;
@@ -84,49 +86,7 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-        if (live && c.scheme == FL_QUANT_ASYM) {
-            // asymmetric levels: code*s + z per element, summed in level order
-            deq8_asym(c.level[0], which, j, HD, ch, c.g, x);
-            for (int l = 1; l <= upto; ++l) {
-                const int sl = c.level[l].slot[j];
-                if (sl < 0) break;
-                float t[8];
-                deq8_asym(c.level[l], which, sl, HD, ch, c.g, t);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] += t[i];
-            }
-        } else if (live) {
-            const fl_kv_level& L0 = c.level[0];
-            const long e0 = j * HD + ch;
-            const void* codes = which ? L0.v_codes : L0.k_codes;
-            if (L0.bits == 32) {
-                const float* src = reinterpret_cast<const float*>(codes) + e0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = src[e];
-            } else {
-                const float s = (which ? L0.v_scale : L0.k_scale)[e0 / c.g];
-                const uint64_t w = load_codes8(codes, e0, 8);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = (float)code_at(w, 8, i) * s;
-            }
-            for (int l = 1; l <= upto; ++l) {
-                const fl_kv_level& L = c.level[l];
-                const int sl = L.slot[j];
-                if (sl < 0) break;
-                const long el = (long)sl * HD + ch;
-                const void* cl = which ? L.v_codes : L.k_codes;
-                if (L.bits == 32) {
-                    const float* src = reinterpret_cast<const float*>(cl) + el;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] += src[e];
-                } else {
-                    const float s = (which ? L.v_scale : L.k_scale)[el / c.g];
-                    const uint64_t w = load_codes8(cl, el, L.bits);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] += (float)code_at(w, L.bits, i) * s;
-                }
-            }
-        }
+        if (live) deq_col8(c, upto, which, j, HD, ch, x);
         if (which == 0) {
             bf16x8 v, vl;
 #pragma unroll
@@ -981,9 +941,12 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
-    const int p = pc0 + w * 32 + r;
+    const int p = pc0 + w * 32 + r;  // compact slot
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    const bool colv = p < P.k;
+    // selection index of the slot (a slot order from k_classify_cols puts
+    // pads between and after its two ascending parts)
+    const int src = P.perm ? (p < P.kp ? P.perm[(long)h * P.kp + p] : -1) : (p < P.k ? p : -1);
+    const bool colv = src >= 0;
     const int cp = colv ? cpos_h[p] : 0x7fffffff;
     bf16x8 kf[D / 16], kl[X3 ? D / 16 : 1];
     {
@@ -994,10 +957,12 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
             if (X3) kl[X3 ? kk : 0] = *reinterpret_cast<const bf16x8*>(P.Kc_lo + ko + 16 * kk);
         }
     }
-    if (tid == 0) {
-        s_start = lower_bound_i32(P.active, P.n, cpos_h[pc0]);
-        s_cmax = cpos_h[min(pc0 + CTW, P.k) - 1];
-    }
+    // the block's first and last column positions
+    if (tid == 0) { s_start = 0x7fffffff; s_cmax = -1; }
+    __syncthreads();
+    if (colv) { atomicMin(&s_start, cp); atomicMax(&s_cmax, cp); }
+    __syncthreads();
+    if (tid == 0) s_start = lower_bound_i32(P.active, P.n, s_start);
     __syncthreads();
     const int t_start = __builtin_amdgcn_readfirstlane(s_start);
     const int cmax = __builtin_amdgcn_readfirstlane(s_cmax);
@@ -1127,18 +1092,18 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
     }
     csum += __shfl_xor(csum, 32);
     if (colv && half == 0)
-        P.col_stat[(long)h * P.k + p] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
+        P.col_stat[(long)h * P.k + src] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, float* vnorm, hipStream_t st) {
+                              int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st) {
     dim3 grid(kp / (c.d == 128 ? gather_cols<128>() : gather_cols<64>()), c.H);
 #define FL_GATHER(D_, X_)                                                                       \
     hipLaunchKernelGGL((k_gather_bf16<D_, X_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
-                       Vt, Kc_lo, Vt_lo, cpos, vnorm)
+                       Vt, Kc_lo, Vt_lo, cpos, vnorm, perm)
     if (c.d == 128) { if (x3) FL_GATHER(128, true); else FL_GATHER(128, false); }
     else { if (x3) FL_GATHER(64, true); else FL_GATHER(64, false); }
 #undef FL_GATHER
@@ -1193,12 +1158,14 @@ template <int PREC>
 constexpr int colstat_waves() { return PREC == 0 ? 8 : 4; }
 
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
-    // one-dimensional grids of column blocks x heads (see col_coords)
-    const dim3 grid(((P.k + CT - 1) / CT) * P.H);
+    // one-dimensional grids of column blocks x heads (see col_coords); with a
+    // slot order every compact slot is covered
+    const int ncol = P.perm ? P.kp : P.k;
+    const dim3 grid(((ncol + CT - 1) / CT) * P.H);
 #define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
 #define FL_COLL(D_, P_)                                                                        \
     hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>()>),                           \
-                       dim3(((P.k + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>())) * P.H), \
+                       dim3(((ncol + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>())) * P.H), \
                        dim3(64 * colstat_waves<P_>()), 0, st, P)
 #define FL_COL_D(D_) \
     if (prec == 0) FL_COLL(D_, 0); else if (prec == 1) FL_COLL(D_, 1); else FL_COL(D_, 2);

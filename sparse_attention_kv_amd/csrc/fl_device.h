@@ -105,6 +105,57 @@ __device__ __forceinline__ void deq8_asym(const fl_kv_level& L, int which, long 
     }
 }
 
+// 8 consecutive channels (offset ch, a multiple of 8, within a row of
+// HD = H*d) of token j's dequantised keys (which = 0) or values (1) at cache
+// levels 0..upto: the base row, then each residual level's row while the
+// token is present (the sets are nested, so presence stops at the first
+// absent level), summed in level order.  Raw (32-bit) levels hold fp32 values.
+__device__ __forceinline__ void deq_col8(const fl_kv_cache& c, int upto, int which, long j, int HD,
+                                         int ch, float* x) {
+    if (c.scheme == FL_QUANT_ASYM) {
+        deq8_asym(c.level[0], which, j, HD, ch, c.g, x);
+        for (int l = 1; l <= upto; ++l) {
+            const int sl = c.level[l].slot[j];
+            if (sl < 0) break;
+            float t[8];
+            deq8_asym(c.level[l], which, sl, HD, ch, c.g, t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] += t[i];
+        }
+        return;
+    }
+    const fl_kv_level& L0 = c.level[0];
+    const long e0 = j * HD + ch;
+    const void* codes = which ? L0.v_codes : L0.k_codes;
+    if (L0.bits == 32) {
+        const float* src = reinterpret_cast<const float*>(codes) + e0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = src[e];
+    } else {
+        const float s = (which ? L0.v_scale : L0.k_scale)[e0 / c.g];
+        const uint64_t w = load_codes8(codes, e0, 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)code_at(w, 8, i) * s;
+    }
+    for (int l = 1; l <= upto; ++l) {
+        const fl_kv_level& L = c.level[l];
+        const int sl = L.slot[j];
+        if (sl < 0) break;
+        const long el = (long)sl * HD + ch;
+        const void* cl = which ? L.v_codes : L.k_codes;
+        if (L.bits == 32) {
+            const float* src = reinterpret_cast<const float*>(cl) + el;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] += src[e];
+        } else {
+            const float s = (which ? L.v_scale : L.k_scale)[el / c.g];
+            const uint64_t w = load_codes8(cl, el, L.bits);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] += (float)code_at(w, L.bits, i) * s;
+        }
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -39,6 +39,13 @@ struct AttnParams {
     float* mass_u;
     float* out_u;
     __bf16* out_bf;        // optional: the output also as bf16 [n][H][d] by active index
+    // precision-adaptive kernel (k_attn_ad): per head, the row order
+    // [normal | outlier] (indices into `active`) and the normal row count,
+    // and the column parts (normal count, outlier count) of the compact
+    // buffers, laid out [normal | pad to 64 | outlier]
+    const int32_t* rowperm;  // [H][n]
+    const int32_t* rowseg;   // [H]
+    const int32_t* colseg;   // [H][2]
     int xcd_remap;
     int deq_levels;        // in-tile dequantisation: levels 0..deq_levels-1 of q
     QTiles qt;
@@ -55,10 +62,14 @@ struct ColParams {
     const float* lse;
     const float* mass_u;
     const float* vnorm;    // [H][kp] value norms (value-weighted statistic) or NULL
+    const int32_t* perm;   // [H][kp] selection index of each compact slot (-1: pad), or NULL
     float* col_stat;
 };
 
-enum { MODE_ATTN = 0, MODE_REBUILD = 1 };
+// MODE_REBUILD: pruned-column caches by subtraction from o_prev over the
+// selected columns; MODE_REBUILD_ADD: added to the carried caches over the
+// pruned columns (k_attn_ad only)
+enum { MODE_ATTN = 0, MODE_REBUILD = 1, MODE_REBUILD_ADD = 2 };
 
 // Batched decode: B sequences x H heads, one new query token each.
 struct DecodeParams {
@@ -135,14 +146,29 @@ hipError_t launch_decode_append(int d, int scheme, const AppendParams& P, hipStr
 hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const void* k_new,
                         const void* v_new, int gathered, hipStream_t st);
 // attn.hip
+// perm (NULL: slot p holds selection index p): [H][kp] selection index of
+// each compact slot, -1 for padding
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool split, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, float* vnorm, hipStream_t st);
+                              int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st);
 // prec: 0 bf16 operands, 1 K/V/P as hi+lo bf16 pairs, 2 also q (fp32 inputs)
 hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                            const QTiles& out, int32_t* cpos, hipStream_t st);
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st);
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st);
+// adaptive.hip: operand-precision classes of the selected columns and the
+// active rows (per head), and the precision-adaptive attention
+constexpr float kTauCol = 4.0f;  // |K^|, |V^| bound of a "normal" column
+constexpr float kTauRow = 6.0f;  // |q| bound of a "normal" query row
+hipError_t launch_classify(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
+                           const void* q, int dtype, int q_gathered, const int32_t* active, int n,
+                           float tau_col, float tau_row, uint8_t* colflags, int32_t* perm, int32_t* colseg,
+                           uint8_t* rowflags, int32_t* rowperm, int32_t* rowseg, hipStream_t st);
+hipError_t launch_attn_ad(int d, int mode, const AttnParams& P, hipStream_t st);
+// per head, the columns of sel_prev [H][k_prev] absent from sel [H][k]
+// (ascending; k_prev - k of them) -> pruned [H][k_prev - k]
+hipError_t launch_set_diff(const int32_t* sel_prev, int k_prev, const int32_t* sel, int k, int H,
+                           int32_t* pruned, hipStream_t st);
 // calib.hip
 int sq_err_blocks(long n);
 hipError_t launch_sq_err(const float* x, const float* ref, long n, double* part, double* out,

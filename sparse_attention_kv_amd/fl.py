@@ -57,7 +57,7 @@ class FlAttnArgs(ctypes.Structure):
                 ("level", c_int), ("mode", c_int), ("cache_op", c_int), ("out", c_void_p),
                 ("lse", c_void_p), ("mass_u", c_void_p), ("out_u", c_void_p),
                 ("col_stat", c_void_p), ("q_prev", c_void_p), ("q_prev_gathered", c_int),
-                ("col_stat_kind", c_int)]
+                ("col_stat_kind", c_int), ("sel_prev", c_void_p), ("k_prev", c_int)]
 
 
 class FlLoopCfg(ctypes.Structure):
@@ -272,7 +272,7 @@ def fl_sparse_loop_attn_noalloc(cache: FlKvCache, args: FlAttnArgs, stream=None)
     _check("fl_sparse_loop_attn_noalloc", rc)
 
 
-NOALLOC_SCRATCH_BYTES = 72 << 20
+NOALLOC_SCRATCH_BYTES = 80 << 20
 
 
 def fl_loop_step(cfg: FlLoopCfg, state: FlLoopState, inputs: FlLoopInputs, r, ws, stream=None):

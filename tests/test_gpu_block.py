@@ -33,9 +33,10 @@ pytestmark = pytest.mark.gpu
 def _workload(N=640, H=2, d=128, L=2, F=512, R=3):
     w = synth.WORKLOADS["block8k"].scaled(N=N, H=H, d=d, R=R, rho=[1.0, 0.5, 0.25][:R],
                                           kcols=[N, 256, 128][:R], bits=[8, 4, 2][:R])
-    # weight scale: the workload's 0.02 at its own width, larger for narrow
-    # blocks so that every layer still moves the states by O(1)
-    w.extra = dict(w.extra, layers=L, ffn=F, wstd=0.05 if H * d <= 512 else 0.02)
+    # weight scale: narrow blocks 0.05 (a projection gain of about 0.8), wide
+    # ones the 8K block's gain, 0.02 sqrt(2048 / D) (0.02 at its own width)
+    w.extra = dict(w.extra, layers=L, ffn=F,
+                   wstd=0.05 if H * d <= 512 else 0.02 * float(np.sqrt(2048 / (H * d))))
     return w
 
 

@@ -42,7 +42,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
 
 @pytest.mark.slow
 def test_abi_host_under_asan_ubsan(tmp_path):
-    objs = [os.path.join(BUILD, f"{s}.o") for s in ("select", "quant", "attn", "block", "decode", "calib")]
+    objs = [os.path.join(BUILD, f"{s}.o") for s in ("select", "quant", "attn", "adaptive", "block", "decode", "calib")]
     if not all(os.path.exists(o) for o in objs):
         from sparse_attention_kv_amd import build
         build.build()

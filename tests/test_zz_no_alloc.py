@@ -54,8 +54,8 @@ def test_noalloc_matches_workspace_entry():
     torch.cuda.synchronize()
     act3, sel3, k3 = run.active[2], run.sel_used(3), run.k_used(3)
     assert k3 == 600 and run.k_used(2) == 1024
-    ws = torch.empty(fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, w.H, k3, w.d, 3), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, w.H, k3, w.d, len(act3)),
+                     dtype=torch.uint8, device="cuda")
 
     def state_from(snap):
         return {key: snap["tensors"][key].cuda() for key in ("out", "lse", "mass_u", "out_u")}
@@ -92,8 +92,9 @@ def test_noalloc_matches_workspace_entry():
 
 
 def test_noalloc_rejects_oversize():
-    """A dense call over 3000 columns of 16 x 128 heads needs about 94 MB of
-    workspace, beyond the scratch: FL_ERR_WORKSPACE, nothing written."""
+    """A dense call over 3000 columns and rows of 16 x 128 heads needs about
+    104 MB of workspace, beyond the scratch: FL_ERR_WORKSPACE, nothing
+    written."""
     N, H, d = 3000, 16, 128
     w = synth.WORKLOADS["layer4k"].scaled(N=N, H=H, R=1, rho=[1.0], kcols=[N], bits=[8])
     inp = synth.generate(w)
@@ -101,7 +102,7 @@ def test_noalloc_rejects_oversize():
     run.step(1, to_dev(inp["h"][0], "bf16"), None, to_dev(inp["q"][0], "bf16"),
              to_dev(inp["k"][0], "bf16"), to_dev(inp["v"][0], "bf16"), None)
     torch.cuda.synchronize()
-    need = fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, H, N, d, 1)
+    need = fl.fl_workspace_size(fl.FL_WS_SPARSE_ATTN, H, N, d, N)
     assert need > fl.NOALLOC_SCRATCH_BYTES
     st = {key: torch.full_like(getattr(run, key), 7.0) for key in ("out", "lse", "mass_u", "out_u")}
     a = fl.FlAttnArgs()
