@@ -174,15 +174,6 @@ __global__ __launch_bounds__(1024) void k_class_scan(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int ubound_i32(const int32_t* a, int n, int v) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
 constexpr int kAdBM = 128;  // query rows per workgroup (4 waves x 32)
 
 // Attention of the loop's active rows over its selected columns with
@@ -205,24 +196,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     __shared__ __attribute__((aligned(256))) int sC0[64];
     __shared__ __attribute__((aligned(256))) int sC1[64];
     __shared__ int s_mm[2];
+    __shared__ int s_bd[4];
     const int n_tiles = (P.n + kAdBM - 1) / kAdBM;
     int tile, h;
-    {
-        const int b = blockIdx.x;
-        if (P.xcd_remap) {  // a head's workgroups on one XCD, costliest tiles first
-            const int x = b & 7, m = b >> 3;
-            h = x + 8 * (m / n_tiles);
-            tile = n_tiles - 1 - (m % n_tiles);
-        } else {
-            h = b / n_tiles;
-            tile = n_tiles - 1 - (b % n_tiles);
-        }
-    }
+    block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
     const int tt = tile * kAdBM + w * 32 + r;  // place in the head's row order
     const bool valid = tt < P.n;
+    // head-wide sizes first: their loads overlap the row-index chain
+    const int nn_l = P.colseg[2 * h], no_l = P.colseg[2 * h + 1];
+    const int rseg_l = P.rowseg ? P.rowseg[h] : 0;
     const int t = valid ? (P.rowperm ? P.rowperm[(long)h * P.n + tt] : tt) : 0;
     const int rowpos = valid ? P.active[t] : -1;
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
@@ -251,18 +236,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         wgt = 1.0f - mu_prev;
     }
     __syncthreads();
+    // the two column parts and their causal bounds for these rows: wave w
+    // finds bound w (columns <= the last / first row position, in the normal /
+    // outlier part) with two rounds of loads
+    const int nn = __builtin_amdgcn_readfirstlane(nn_l);
+    const int no = __builtin_amdgcn_readfirstlane(no_l);
+    const int seg1 = (nn + 63) / 64 * 64;
+    {
+        const int v = w & 1 ? s_mm[0] : s_mm[1];
+        const int b = w < 2 ? wave_ubound(cpos_h, nn, v) : wave_ubound(cpos_h + seg1, no, v);
+        if (lane == 0) s_bd[w] = b;
+    }
+    __syncthreads();
     const int minpos = __builtin_amdgcn_readfirstlane(s_mm[0]);
     const int maxpos = __builtin_amdgcn_readfirstlane(s_mm[1]);
-    // the two column parts and their causal bounds for these rows
-    const int nn = __builtin_amdgcn_readfirstlane(P.colseg[2 * h]);
-    const int no = __builtin_amdgcn_readfirstlane(P.colseg[2 * h + 1]);
-    const int seg1 = (nn + 63) / 64 * 64;
-    const int pe0 = __builtin_amdgcn_readfirstlane(ubound_i32(cpos_h, nn, maxpos));
-    const int pf0 = __builtin_amdgcn_readfirstlane(ubound_i32(cpos_h, nn, minpos));
-    const int pe1 = __builtin_amdgcn_readfirstlane(ubound_i32(cpos_h + seg1, no, maxpos));
-    const int pf1 = __builtin_amdgcn_readfirstlane(ubound_i32(cpos_h + seg1, no, minpos));
+    const int pe0 = __builtin_amdgcn_readfirstlane(s_bd[0]);
+    const int pf0 = __builtin_amdgcn_readfirstlane(s_bd[1]);
+    const int pe1 = __builtin_amdgcn_readfirstlane(s_bd[2]);
+    const int pf1 = __builtin_amdgcn_readfirstlane(s_bd[3]);
     const int tile_end = min(tile * kAdBM + kAdBM, P.n);
-    const bool rnorm = P.rowseg ? tile_end <= P.rowseg[h] : false;
+    const bool rnorm = P.rowseg ? tile_end <= __builtin_amdgcn_readfirstlane(rseg_l) : false;
     const int W0 = rnorm ? 64 : 32;
     const int T0 = (pe0 + W0 - 1) / W0;
     const int T = T0 + (pe1 + 31) / 32;
@@ -479,16 +472,32 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     if (!valid) return;
     float* orow = P.out + rh * D;
     if (MODE == MODE_ATTN) {
-        const float mu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
-        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
+        // every load of the caches before the first store (the stores could
+        // alias them for the compiler, which would then serialise each pair)
+        const bool cached = P.cache_op != FL_CACHE_ZERO;
         const float* ourow = P.out_u + rh * D;
+        float4 uc[D / 32][4];
+        float mu = 0.0f;
+        if (cached) {
+            mu = P.mass_u[rh];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    uc[dt][jq] = *reinterpret_cast<const float4*>(ourow + 32 * dt + jq * 8 + half * 4);
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq) uc[dt][jq] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (P.cache_op != FL_CACHE_ZERO) u = *reinterpret_cast<const float4*>(ourow + d0);
+                const float4 u = uc[dt][jq];
                 float4 v;
                 v.x = o[dt][4 * jq + 0] * scale + u.x;
                 v.y = o[dt][4 * jq + 1] * scale + u.y;
@@ -511,12 +520,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         float* ourow = P.out_u + rh * D;
         const float* base = MODE == MODE_REBUILD ? orow : ourow;
         const float sg = MODE == MODE_REBUILD ? -1.0f : 1.0f;
+        float4 bc[D / 32][4];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq)
+                bc[dt][jq] = *reinterpret_cast<const float4*>(base + 32 * dt + jq * 8 + half * 4);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                const float4 op = *reinterpret_cast<const float4*>(base + d0);
+                const float4 op = bc[dt][jq];
                 float4 v;
                 v.x = op.x + sg * o[dt][4 * jq + 0];
                 v.y = op.y + sg * o[dt][4 * jq + 1];

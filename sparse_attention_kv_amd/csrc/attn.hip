@@ -210,31 +210,6 @@ __global__ __launch_bounds__(256) void k_gather_q(fl_kv_cache c, int upto,
 }
 
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int v) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-__device__ __forceinline__ void block_coords(int xcd_remap, int n_tiles, int H, int& tile, int& h) {
-    const int b = blockIdx.x;
-    if (xcd_remap) {
-        // keep every head's workgroups on one XCD (blocks are dealt to the
-        // 8 XCDs round-robin), so the head's compact K/V stays in that L2;
-        // the costliest (latest-position) tiles start first.
-        const int x = b & 7, m = b >> 3;
-        h = x + 8 * (m / n_tiles);
-        tile = n_tiles - 1 - (m % n_tiles);
-    } else {
-        h = b / n_tiles;
-        tile = n_tiles - 1 - (b % n_tiles);
-    }
-}
-
 // PREC 0: bf16 operands (a cache without residual levels); 1: K, V and P as
 // hi + lo bf16 pairs (residual levels carry information below bf16's
 // resolution of the summed value); 2: q split as well (fp32 inputs).
@@ -264,10 +239,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
     const bool valid = t < P.n;
     const int rowpos = valid ? P.active[t] : -1;
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    if (tid == 0) {
-        const int tl = min(t0 + BM, P.n) - 1;
-        s_bounds[0] = upper_bound_i32(cpos_h, P.k, P.active[tl]); // p_end
-        s_bounds[1] = upper_bound_i32(cpos_h, P.k, P.active[t0]); // p_full
+    if (w < 2) {  // wave 0: p_end (columns <= the last row's position), wave 1: p_full (first row's)
+        const int b = wave_ubound(cpos_h, P.k, P.active[w == 0 ? min(t0 + BM, P.n) - 1 : t0]);
+        if (lane == 0) s_bounds[w] = b;
     }
     // query fragment: B operand of S^T = K Q^T (lane: row r, d = 16kk + 8half)
     bf16x8 qf[D / 16], ql[QS ? D / 16 : 1];
@@ -490,16 +464,32 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
     if (!valid) return;
     float* orow = P.out + rh * D;
     if (MODE == MODE_ATTN) {
-        const float mu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
-        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
+        // every load of the caches before the first store (the stores could
+        // alias them for the compiler, which would then serialise each pair)
+        const bool cached = P.cache_op != FL_CACHE_ZERO;
         const float* ourow = P.out_u + rh * D;
+        float4 uc[D / 32][4];
+        float mu = 0.0f;
+        if (cached) {
+            mu = P.mass_u[rh];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    uc[dt][jq] = *reinterpret_cast<const float4*>(ourow + 32 * dt + jq * 8 + half * 4);
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq) uc[dt][jq] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (P.cache_op != FL_CACHE_ZERO) u = *reinterpret_cast<const float4*>(ourow + d0);
+                const float4 u = uc[dt][jq];
                 float4 v;
                 v.x = o[dt][4 * jq + 0] * scale + u.x;
                 v.y = o[dt][4 * jq + 1] * scale + u.y;
@@ -512,12 +502,18 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
             P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     } else {
         float* ourow = P.out_u + rh * D;
+        float4 bc[D / 32][4];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq)
+                bc[dt][jq] = *reinterpret_cast<const float4*>(orow + 32 * dt + jq * 8 + half * 4);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                const float4 op = *reinterpret_cast<const float4*>(orow + d0);
+                const float4 op = bc[dt][jq];
                 float4 v;
                 v.x = op.x - o[dt][4 * jq + 0];
                 v.y = op.y - o[dt][4 * jq + 1];
@@ -573,10 +569,9 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
     const bool valid = t < P.n;
     const int rowpos = valid ? P.active[t] : -1;
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    if (tid == 0) {
-        const int tl = min(t0 + BM, P.n) - 1;
-        s_bounds[0] = upper_bound_i32(cpos_h, P.k, P.active[tl]); // p_end
-        s_bounds[1] = upper_bound_i32(cpos_h, P.k, P.active[t0]); // p_full
+    if (w < 2) {  // wave 0: p_end (columns <= the last row's position), wave 1: p_full (first row's)
+        const int b = wave_ubound(cpos_h, P.k, P.active[w == 0 ? min(t0 + BM, P.n) - 1 : t0]);
+        if (lane == 0) s_bounds[w] = b;
     }
     bf16x8 qf[D / 16];
     {
@@ -745,16 +740,32 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
     if (!valid) return;
     float* orow = P.out + rh * D;
     if (MODE == MODE_ATTN) {
-        const float mu = P.cache_op == FL_CACHE_ZERO ? 0.0f : P.mass_u[rh];
-        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
+        // every load of the caches before the first store (the stores could
+        // alias them for the compiler, which would then serialise each pair)
+        const bool cached = P.cache_op != FL_CACHE_ZERO;
         const float* ourow = P.out_u + rh * D;
+        float4 uc[D / 32][4];
+        float mu = 0.0f;
+        if (cached) {
+            mu = P.mass_u[rh];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    uc[dt][jq] = *reinterpret_cast<const float4*>(ourow + 32 * dt + jq * 8 + half * 4);
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq) uc[dt][jq] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const float scale = l_tot > 0.0f ? (1.0f - mu) / l_tot : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (P.cache_op != FL_CACHE_ZERO) u = *reinterpret_cast<const float4*>(ourow + d0);
+                const float4 u = uc[dt][jq];
                 float4 v;
                 v.x = o[dt][4 * jq + 0] * scale + u.x;
                 v.y = o[dt][4 * jq + 1] * scale + u.y;
@@ -767,12 +778,18 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
             P.lse[rh] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     } else {
         float* ourow = P.out_u + rh * D;
+        float4 bc[D / 32][4];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq)
+                bc[dt][jq] = *reinterpret_cast<const float4*>(orow + 32 * dt + jq * 8 + half * 4);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jq = 0; jq < 4; ++jq) {
                 const int d0 = 32 * dt + jq * 8 + half * 4;
-                const float4 op = *reinterpret_cast<const float4*>(orow + d0);
+                const float4 op = bc[dt][jq];
                 float4 v;
                 v.x = op.x - o[dt][4 * jq + 0];
                 v.y = op.y - o[dt][4 * jq + 1];

@@ -198,4 +198,41 @@ __device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, void* l, uint
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, voff, soff, 0, 0);
 }
 
+// ---- work mapping and position bounds ----
+
+// (row tile, head) of this workgroup, the costliest (latest-position) tiles
+// first.  With xcd_remap (H % 8 == 0) every head's workgroups stay on one
+// XCD (blocks are dealt to the 8 XCDs round-robin), so the head's compact
+// K / V stays in that L2, and the XCD's heads are interleaved so that each
+// one's costliest tiles start in the first wave of workgroups.
+__device__ __forceinline__ void block_coords(int xcd_remap, int n_tiles, int H, int& tile, int& h) {
+    const int b = blockIdx.x;
+    if (xcd_remap) {
+        const int hpx = H / 8;
+        const int x = b & 7, m = b >> 3;
+        h = x + 8 * (m % hpx);
+        tile = n_tiles - 1 - m / hpx;
+    } else {
+        h = b / n_tiles;
+        tile = n_tiles - 1 - (b % n_tiles);
+    }
+}
+
+// Number of elements <= v of the ascending a[0, n), found by one whole wave
+// (every lane calls it with the same arguments): the last element of each
+// of 64 equal blocks, then the block that holds the boundary -- two
+// dependent rounds of loads for n <= 4096.
+__device__ __forceinline__ int wave_ubound(const int32_t* a, int n, int v) {
+    const int lane = threadIdx.x & 63;
+    if (n <= 0) return 0;
+    const int S = (n + 63) >> 6;
+    const bool whole = lane * S < n && a[min((lane + 1) * S, n) - 1] <= v;
+    const int lo = __popcll(__ballot(whole)) * S;
+    if (lo >= n) return n;
+    const int hi = min(lo + S, n);
+    int cnt = lo;
+    for (int j = lo; j < hi; j += 64) cnt += __popcll(__ballot(j + lane < hi && a[j + lane] <= v));
+    return cnt;
+}
+
 } // namespace fl
