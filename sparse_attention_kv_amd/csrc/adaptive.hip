@@ -195,8 +195,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     __shared__ __attribute__((aligned(1024))) __bf16 sV1[KB / 2];
     __shared__ __attribute__((aligned(256))) int sC0[64];
     __shared__ __attribute__((aligned(256))) int sC1[64];
-    __shared__ int s_mm[2];
-    __shared__ int s_bd[4];
+    __shared__ int s_mn[4], s_mx[4], s_bd[4];
     const int n_tiles = (P.n + kAdBM - 1) / kAdBM;
     int tile, h;
     block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
@@ -205,15 +204,56 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     const int r = lane & 31, half = lane >> 5;
     const int tt = tile * kAdBM + w * 32 + r;  // place in the head's row order
     const bool valid = tt < P.n;
-    // head-wide sizes first: their loads overlap the row-index chain
+    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(cpos_h, (uint32_t)P.kp * 4);
+    // Prologue: the head's column positions are copied into the second tile
+    // buffer (idle until the first tile is computed) while the row indices
+    // are looked up; the causal bounds are then searched in LDS, and the
+    // query fragments are loaded together with the first tile.
+    const bool cpos_lds = P.kp * 4 <= KB;
+    if (cpos_lds)
+        for (int m = w; m * 1024 < P.kp * 4; m += 4)
+            buf_dma16(rC, reinterpret_cast<char*>(sK1) + m * 1024, lane * 16, m * 1024);
     const int nn_l = P.colseg[2 * h], no_l = P.colseg[2 * h + 1];
     const int rseg_l = P.rowseg ? P.rowseg[h] : 0;
     const int t = valid ? (P.rowperm ? P.rowperm[(long)h * P.n + tt] : tt) : 0;
     const int rowpos = valid ? P.active[t] : -1;
-    const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    if (tid == 0) { s_mm[0] = 0x7fffffff; s_mm[1] = -1; }
+    {
+        int mn = valid ? rowpos : 0x7fffffff, mx = rowpos;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            mn = min(mn, __shfl_xor(mn, o));
+            mx = max(mx, __shfl_xor(mx, o));
+        }
+        if (lane == 0) { s_mn[w] = mn; s_mx[w] = mx; }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this lane's position copies landed
     __syncthreads();
-    if (valid) { atomicMin(&s_mm[0], rowpos); atomicMax(&s_mm[1], rowpos); }
+    const int minpos = __builtin_amdgcn_readfirstlane(min(min(s_mn[0], s_mn[1]), min(s_mn[2], s_mn[3])));
+    const int maxpos = __builtin_amdgcn_readfirstlane(max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3])));
+    // the two column parts and their causal bounds for these rows: wave w
+    // finds bound w (columns <= the last / first row position, in the normal /
+    // outlier part)
+    const int nn = __builtin_amdgcn_readfirstlane(nn_l);
+    const int no = __builtin_amdgcn_readfirstlane(no_l);
+    const int seg1 = (nn + 63) / 64 * 64;
+    {
+        const int v = w & 1 ? minpos : maxpos;
+        const int off = w < 2 ? 0 : seg1, len = w < 2 ? nn : no;
+        const int b = cpos_lds ? wave_ubound(reinterpret_cast<const int32_t*>(sK1) + off, len, v)
+                               : wave_ubound(cpos_h + off, len, v);
+        if (lane == 0) s_bd[w] = b;
+    }
+    __syncthreads();
+    const int pe0 = __builtin_amdgcn_readfirstlane(s_bd[0]);
+    const int pf0 = __builtin_amdgcn_readfirstlane(s_bd[1]);
+    const int pe1 = __builtin_amdgcn_readfirstlane(s_bd[2]);
+    const int pf1 = __builtin_amdgcn_readfirstlane(s_bd[3]);
+    const int tile_end = min(tile * kAdBM + kAdBM, P.n);
+    const bool rnorm = P.rowseg ? tile_end <= __builtin_amdgcn_readfirstlane(rseg_l) : false;
+    const int W0 = rnorm ? 64 : 32;
+    const int T0 = (pe0 + W0 - 1) / W0;
+    const int T = T0 + (pe1 + 31) / 32;
     bf16x8 qf[D / 16];
     {
         const long qrow = P.q_gathered ? (long)t : (long)rowpos;
@@ -235,37 +275,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         mu_prev = P.mass_u[rh];
         wgt = 1.0f - mu_prev;
     }
-    __syncthreads();
-    // the two column parts and their causal bounds for these rows: wave w
-    // finds bound w (columns <= the last / first row position, in the normal /
-    // outlier part) with two rounds of loads
-    const int nn = __builtin_amdgcn_readfirstlane(nn_l);
-    const int no = __builtin_amdgcn_readfirstlane(no_l);
-    const int seg1 = (nn + 63) / 64 * 64;
-    {
-        const int v = w & 1 ? s_mm[0] : s_mm[1];
-        const int b = w < 2 ? wave_ubound(cpos_h, nn, v) : wave_ubound(cpos_h + seg1, no, v);
-        if (lane == 0) s_bd[w] = b;
-    }
-    __syncthreads();
-    const int minpos = __builtin_amdgcn_readfirstlane(s_mm[0]);
-    const int maxpos = __builtin_amdgcn_readfirstlane(s_mm[1]);
-    const int pe0 = __builtin_amdgcn_readfirstlane(s_bd[0]);
-    const int pf0 = __builtin_amdgcn_readfirstlane(s_bd[1]);
-    const int pe1 = __builtin_amdgcn_readfirstlane(s_bd[2]);
-    const int pf1 = __builtin_amdgcn_readfirstlane(s_bd[3]);
-    const int tile_end = min(tile * kAdBM + kAdBM, P.n);
-    const bool rnorm = P.rowseg ? tile_end <= __builtin_amdgcn_readfirstlane(rseg_l) : false;
-    const int W0 = rnorm ? 64 : 32;
-    const int T0 = (pe0 + W0 - 1) / W0;
-    const int T = T0 + (pe1 + 31) / 32;
 
     const long koff = (long)h * P.kp * D;
     const long voff = (long)h * (P.kp / 64) * D * 64;
     const uint32_t kbytes = (uint32_t)P.kp * D * 2;
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(P.Kc + koff, kbytes), rV = make_rsrc(P.Vt + voff, kbytes);
     const __amdgpu_buffer_rsrc_t rKl = make_rsrc(P.Kc_lo + koff, kbytes), rVl = make_rsrc(P.Vt_lo + voff, kbytes);
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(cpos_h, (uint32_t)P.kp * 4);
     // per-lane byte offsets: plain tiles (64 keys: K rows of D, V^T rows of 64
     // keys) and hi/lo tiles (32 keys: each part half a region, V^T rows of 32
     // keys inside the stored 64-key rows)
