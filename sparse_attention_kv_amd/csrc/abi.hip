@@ -52,7 +52,8 @@ long kpad(long k) { return (k + 63) / 64 * 64; }
 //    column count plus room for the [normal | pad | outlier] slot order;
 //  * per side: column positions and slot order [H][kp], the parts' sizes
 //    [H][2], the row order [H][n] and normal-row count [H]; one [H][n] byte
-//    plane of row flags; the value norms [H][kp];
+//    plane of row flags; the value norms [H][kp]; the pruned-column list of
+//    an additive rebuild [H][kp] (six [H][kp] int planes in all);
 //  * the in-tile path adds per-level quantised planes (codes <= 8 bits, fp32
 //    scales per group of >= 32 channels) for K and V.
 long kslots(long k) { return kpad(k) + 128; }
@@ -61,7 +62,7 @@ long quant_plane_bytes(long H, long kp, long d) {
 }
 long attn_ws_bytes_once(long H, long k, long d, long n) {
     const long kp = kslots(k);
-    return 8 * align_up(H * kp * d * 2) + 5 * align_up(H * kp * 4) + align_up(H * kp) +
+    return 8 * align_up(H * kp * d * 2) + 6 * align_up(H * kp * 4) + align_up(H * kp) +
            2 * align_up(H * 2 * 4) + align_up(H * n) + 2 * align_up(H * n * 4) + 2 * align_up(H * 4) +
            kAlign;
 }
