@@ -63,7 +63,8 @@ long quant_plane_bytes(long H, long kp, long d) {
 long attn_ws_bytes_once(long H, long k, long d, long n) {
     const long kp = kslots(k);
     return 8 * align_up(H * kp * d * 2) + 6 * align_up(H * kp * 4) + align_up(H * kp) +
-           2 * align_up(H * 2 * 4) + align_up(H * n) + 2 * align_up(H * n * 4) + 2 * align_up(H * 4) +
+           2 * align_up(H * 2 * 4) + align_up(H * fl::class_row_stride(n)) + 2 * align_up(H * n * 4) +
+           2 * align_up(H * 4) +
            kAlign;
 }
 long attn_ws_bytes(long H, long k, long d, long n, long levels) {
@@ -544,7 +545,7 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     int32_t* pruned = (int32_t*)take((long)H * kp * 4);
     int32_t* colseg = (int32_t*)take((long)H * 2 * 4);
     int32_t* colseg_old = (int32_t*)take((long)H * 2 * 4);
-    uint8_t* rowflags = (uint8_t*)take((long)H * a->n);
+    uint8_t* rowflags = (uint8_t*)take((long)H * fl::class_row_stride(a->n));
     int32_t* rowperm = (int32_t*)take((long)H * a->n * 4);
     int32_t* rowperm_old = (int32_t*)take((long)H * a->n * 4);
     int32_t* rowseg = (int32_t*)take((long)H * 4);

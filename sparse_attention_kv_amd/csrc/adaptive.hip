@@ -65,16 +65,21 @@ __device__ __forceinline__ int block_scan_1024(int v, int* sh, int* total) {
 //    the gather writes) exceeds tau_col or is not finite; D/8 threads per
 //    column, 8 channels each;
 //  * the rest: active row t of head h is an outlier when max |q| exceeds
-//    tau_row or is not finite; 16 lanes per (row, head).
+//    tau_row or is not finite; 16 lanes per (row, head), kRowItems of them
+//    per lane group (the items of one pass are consecutive (row, head)
+//    pairs, so the query reads coalesce).
+// The flag planes have 16-byte aligned rows (strides cstride, rstride).
+constexpr int kRowItems = 4;
 template <int D>
 __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, const int32_t* __restrict__ sel,
                                                      int k, int ncolblk, float tau_col,
-                                                     uint8_t* __restrict__ colflags,
+                                                     uint8_t* __restrict__ colflags, int cstride,
                                                      const void* __restrict__ q, int dtype, int q_gathered,
                                                      const int32_t* __restrict__ active, int n, float tau_row,
-                                                     uint8_t* __restrict__ rowflags) {
+                                                     uint8_t* __restrict__ rowflags, int rstride) {
     const int tid = threadIdx.x;
     const int H = c.H;
+    auto amax = [](float m, float a) { a = fabsf(a); return a <= m ? m : (a > m ? a : INFINITY); };
     if ((int)blockIdx.x < ncolblk) {
         constexpr int TPC = D / 8, CPB = 256 / TPC;
         const int per_head = (k + CPB - 1) / CPB;
@@ -92,41 +97,52 @@ __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, co
                 for (int e = 0; e < 8; ++e) x[e] = 0.0f;
                 deq_col8(c, upto, which, j, H * D, h * D + c0, x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) m = fabsf(x[e]) <= m ? m : (fabsf(x[e]) > m ? fabsf(x[e]) : INFINITY);
+                for (int e = 0; e < 8; ++e) m = amax(m, x[e]);
             }
         }
 #pragma unroll
         for (int o = 1; o < TPC; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        if (live && tid % TPC == 0) colflags[(long)h * k + p] = !(m <= tau_col);
+        if (live && tid % TPC == 0) colflags[(long)h * cstride + p] = !(m <= tau_col);
         return;
     }
     constexpr int CPL = D / 16;  // channels per lane (8 or 4)
-    const long item = (long)(blockIdx.x - ncolblk) * 16 + (tid >> 4);
+    const int nh = n * H;
+    const int ngroups = (gridDim.x - ncolblk) * 16;
+    const int g = (blockIdx.x - ncolblk) * 16 + (tid >> 4);
     const int sub = tid & 15;
-    const bool live = item < (long)n * H;
-    const long t = live ? item / H : 0;
-    const int h = live ? (int)(item % H) : 0;
-    float m = 0.0f;
-    if (live) {
-        const long row = q_gathered ? t : (long)active[t];
-        const long e = (row * H + h) * D + sub * CPL;
-        float x[8];
-        if (CPL == 8) {
-            load8_f32(q, e, dtype, x);
-        } else if (dtype == FL_BF16) {
-            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(q) + e);
-            x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
-            x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-            const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e);
-            x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-        }
+    float x[kRowItems][8];
+    int tt[kRowItems], hh[kRowItems];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) m = fabsf(x[i]) <= m ? m : (fabsf(x[i]) > m ? fabsf(x[i]) : INFINITY);
+    for (int u = 0; u < kRowItems; ++u) {
+        const int item = g + u * ngroups;
+        tt[u] = item / H;
+        hh[u] = item - tt[u] * H;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
+        if (item < nh) {
+            const long row = q_gathered ? (long)tt[u] : (long)active[tt[u]];
+            const long e = (row * H + hh[u]) * D + sub * CPL;
+            if (CPL == 8) {
+                load8_f32(q, e, dtype, x[u]);
+            } else if (dtype == FL_BF16) {
+                const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(q) + e);
+                x[u][0] = __uint_as_float(w.x << 16); x[u][1] = __uint_as_float(w.x & 0xffff0000u);
+                x[u][2] = __uint_as_float(w.y << 16); x[u][3] = __uint_as_float(w.y & 0xffff0000u);
+            } else {
+                const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + e);
+                x[u][0] = f.x; x[u][1] = f.y; x[u][2] = f.z; x[u][3] = f.w;
+            }
+        }
     }
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (live && sub == 0) rowflags[(long)h * n + t] = !(m <= tau_row);
+    for (int u = 0; u < kRowItems; ++u) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) m = amax(m, x[u][i]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if (g + u * ngroups < nh && sub == 0) rowflags[(long)hh[u] * rstride + tt[u]] = !(m <= tau_row);
+    }
 }
 
 // Orders from the flags, one workgroup per (kind, head):
@@ -135,38 +151,72 @@ __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, co
 //    order (perm[h][slot] = selection index, -1 for pads), colseg = sizes;
 //  * blocks [H, 2H): head h's row order [normal | outlier] (indices into
 //    the active list), rowseg = the normal count.
-__global__ __launch_bounds__(1024) void k_class_scan(const uint8_t* __restrict__ colflags, int k, int kp,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ colseg,
-                                                     const uint8_t* __restrict__ rowflags, int n, int H,
-                                                     int32_t* __restrict__ rowperm,
+// Each thread reads a run of 16 flags with one 16-byte load (the planes' rows
+// are 16-byte aligned), one pass per 16K flags.
+__global__ __launch_bounds__(1024) void k_class_scan(const uint8_t* __restrict__ colflags, int k, int cstride,
+                                                     int kp, int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ colseg,
+                                                     const uint8_t* __restrict__ rowflags, int n, int rstride,
+                                                     int H, int32_t* __restrict__ rowperm,
                                                      int32_t* __restrict__ rowseg) {
+    constexpr int E = 16, CH = 1024 * E;
     __shared__ int sh[32];
     const bool cols = (int)blockIdx.x < H;
     const int h = cols ? blockIdx.x : blockIdx.x - H;
     const int tid = threadIdx.x;
     const int len = cols ? k : n;
-    const uint8_t* f = cols ? colflags + (long)h * k : rowflags + (long)h * n;
+    const uint8_t* f = cols ? colflags + (long)h * cstride : rowflags + (long)h * rstride;
     int32_t* out = cols ? perm + (long)h * kp : rowperm + (long)h * n;
     if (cols)
         for (int p = tid; p < kp; p += 1024) out[p] = -1;
-    const int per = (len + 1023) / 1024;
-    const int t0 = tid * per, t1 = min(t0 + per, len);
-    int nn = 0;
-    for (int t = t0; t < t1; ++t) nn += f[t] ? 0 : 1;
-    int n_norm, n_out;
-    const int pre_n = block_scan_1024(nn, sh, &n_norm);
-    const int pre_o = block_scan_1024((t1 > t0 ? t1 - t0 : 0) - nn, sh, &n_out);
-    // (the scans' barriers order the -1 fill before these writes)
+    // flags of run base + 16 tid .. +15 as bits (bit i: entry i is an outlier,
+    // entries past len count as neither part)
+    auto run = [&](int base, uint32_t& outl, uint32_t& live) {
+        const int x0 = base + tid * E;
+        outl = 0;
+        live = 0;
+        if (x0 < len) {
+            const uint4 w = *reinterpret_cast<const uint4*>(f + x0);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                if (x0 + i < len) {
+                    live |= 1u << i;
+                    if ((ws[i >> 2] >> (8 * (i & 3))) & 255u) outl |= 1u << i;
+                }
+        }
+    };
+    int cnt = 0;
+    for (int base = 0; base < len; base += CH) {
+        uint32_t outl, live;
+        run(base, outl, live);
+        cnt += __popc(live & ~outl);
+    }
+    int n_norm;
+    block_scan_1024(cnt, sh, &n_norm);
     const int seg1 = cols ? (n_norm + 63) / 64 * 64 : n_norm;
-    int in_ = pre_n, io = seg1 + pre_o;
-    for (int t = t0; t < t1; ++t) {
-        if (f[t]) out[io++] = t;
-        else out[in_++] = t;
+    // (the scans' barriers order the -1 fill before these writes)
+    int done = 0;  // normal entries of the earlier passes
+    for (int base = 0; base < len; base += CH) {
+        uint32_t outl, live;
+        run(base, outl, live);
+        int pass_norm;
+        int in_ = done + block_scan_1024(__popc(live & ~outl), sh, &pass_norm);
+        // outlier entries before this run: all entries before it minus the normal ones
+        int io = seg1 + (min(base + tid * E, len) - in_);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            if (!((live >> i) & 1u)) continue;
+            const int x = base + tid * E + i;
+            if ((outl >> i) & 1u) out[io++] = x;
+            else out[in_++] = x;
+        }
+        done += pass_norm;
     }
     if (tid == 0) {
         if (cols) {
             colseg[2 * h] = n_norm;
-            colseg[2 * h + 1] = n_out;
+            colseg[2 * h + 1] = len - n_norm;
         } else {
             rowseg[h] = n_norm;
         }
@@ -306,10 +356,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     // (outlier rows, normal columns: only the scores need the keys' lo part,
     // P.V over values within the column bound keeps bf16), and 32-column
     // hi/lo tiles (outlier columns)
-    auto tile_p0 = [&](int i) { return i < T0 ? i * W0 : seg1 + (i - T0) * 32; };
-    auto tile_split = [&](int i) { return i >= T0 || !rnorm; };
-    auto tile_full = [&](int i) { return i >= T0; };
-    auto issue = [&](int i, __bf16* sK, __bf16* sV, int* sC) {
+    auto tile_p0 = [&](int i) __attribute__((always_inline)) { return i < T0 ? i * W0 : seg1 + (i - T0) * 32; };
+    auto tile_split = [&](int i) __attribute__((always_inline)) { return i >= T0 || !rnorm; };
+    auto tile_full = [&](int i) __attribute__((always_inline)) { return i >= T0; };
+    auto issue = [&](int i, __bf16* sK, __bf16* sV, int* sC) __attribute__((always_inline)) {
         const int p0 = tile_p0(i);
         if (!tile_split(i)) {
             const uint32_t ks = (uint32_t)p0 * D * 2, vs = (uint32_t)(p0 / 64) * D * 64 * 2;
@@ -344,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // online softmax over one 32-column block's scores (shared by both kinds)
-    auto softmax_ref = [&](f32x16* s, int KT) -> float {
+    auto softmax_ref = [&](f32x16* s, int KT) __attribute__((always_inline)) -> float {
         if (MODE != MODE_ATTN) return lse_prev2;
         float tmax = -INFINITY;
         for (int kt = 0; kt < KT; ++kt)
@@ -364,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         return m_run == -INFINITY ? 0.0f : m_run;
     };
 
-    auto compute_plain = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) {
+    auto compute_plain = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
         const int p0 = tile_p0(i);
         f32x16 s[2];
         __builtin_amdgcn_s_setprio(1);
@@ -412,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
     };
 
-    auto compute_split = [&](auto full, int i, const __bf16* sK, const __bf16* sV, const int* sC) {
+    auto compute_split = [&](auto full, int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
         const int p0 = tile_p0(i);
         const bool seg = i >= T0;
@@ -463,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
         }
     };
-    auto compute = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) {
+    auto compute = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
         if (tile_full(i)) compute_split(std::true_type{}, i, sK, sV, sC);
         else if (tile_split(i)) compute_split(std::false_type{}, i, sK, sV, sC);
         else compute_plain(i, sK, sV, sC);
@@ -601,15 +651,17 @@ hipError_t launch_classify(const fl_kv_cache& c, int upto, const int32_t* sel, i
     const int H = c.H;
     const int cpb = 256 / (c.d / 8);
     const int ncolblk = H * ((k + cpb - 1) / cpb);
-    const unsigned nblk = (unsigned)(ncolblk + ((long)n * H + 15) / 16);
+    const int nrowblk = (int)(((long)n * H + 16 * kRowItems - 1) / (16 * kRowItems));
+    const unsigned nblk = (unsigned)(ncolblk + nrowblk);
+    const int cstride = kp, rstride = (int)class_row_stride(n);
     if (c.d == 128)
         hipLaunchKernelGGL(k_class_flags<128>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           colflags, q, dtype, q_gathered, active, n, tau_row, rowflags);
+                           colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
     else
         hipLaunchKernelGGL(k_class_flags<64>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           colflags, q, dtype, q_gathered, active, n, tau_row, rowflags);
-    hipLaunchKernelGGL(k_class_scan, dim3(2 * H), dim3(1024), 0, st, colflags, k, kp, perm, colseg, rowflags, n,
-                       H, rowperm, rowseg);
+                           colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
+    hipLaunchKernelGGL(k_class_scan, dim3(2 * H), dim3(1024), 0, st, colflags, k, cstride, kp, perm, colseg,
+                       rowflags, n, rstride, H, rowperm, rowseg);
     return hipGetLastError();
 }
 
