@@ -108,6 +108,15 @@ typedef struct fl_kv_cache {
     int n_levels; /* levels 0..n_levels-1 hold data */
     int scheme;   /* fl_quant_scheme */
     fl_kv_level level[FL_MAX_LEVELS];
+    /* Optional (NULL: not kept): [2][N][H] bytes, keys then values.  Under
+     * FL_QUANT_ABSMAX, fl_kv_residual_quant(level) sets entry [w][i][h] of
+     * every token i it quantises to 1 when some channel of that token's
+     * dequantised value through `level` (head h, keys w = 0 / values w = 1)
+     * has magnitude above 4 or is not finite, else 0.  Tokens not quantised
+     * keep their entry, which is then their newest level's (the levels are
+     * nested).  fl_sparse_loop_attn reads it when args->cls_current is set:
+     * it is the operand class of a selected column (see fl_attn_args). */
+    uint8_t* cls;
 } fl_kv_cache;
 
 /* ------------------------------------------------------------------------
@@ -284,6 +293,13 @@ typedef struct fl_attn_args {
      * from o_prev (after the dense first loop, where S_prev is every column). */
     const int32_t* sel_prev;
     int k_prev;
+    /* 1: cache->cls holds the classes of this call's level (the newest
+     * level quantised into the cache, as right after fl_kv_residual_quant
+     * of `level`), so the operand classes of the selected columns are read
+     * from it instead of being recomputed from the cache.  Ignored when
+     * cache->cls is NULL or the scheme is not FL_QUANT_ABSMAX.  0: always
+     * recomputed (calls at an older level must pass 0). */
+    int cls_current;
 } fl_attn_args;
 
 int fl_sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* args, void* ws,

@@ -563,14 +563,17 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     P.c2 = c2; P.active = a->active; P.cpos = cpos;
     P.out = a->out; P.lse = a->lse; P.mass_u = a->mass_u; P.out_u = a->out_u; P.out_bf = out_bf;
     // one side's compact columns (and, adaptive, its column and row orders)
+    // the current side's operand classes come from the cache's per-token
+    // classes when the caller says they are those of this level
+    const uint8_t* cls_cur = a->cls_current && cache->cls && cache->scheme == FL_QUANT_ABSMAX ? cache->cls : nullptr;
     auto prepare = [&](const int32_t* sel, int k, int upto, bool ad, int pr, const void* q, int q_gathered,
                        int32_t* cp, int32_t* pm, int32_t* cs, int32_t* rp, int32_t* rs, __bf16* K_, __bf16* V_,
-                       __bf16* Kl_, __bf16* Vl_, float* vnorm) -> int {
+                       __bf16* Kl_, __bf16* Vl_, float* vnorm, const uint8_t* cls_side) -> int {
         if (ad)
             FL_HIP(timed("classify", st, [&] {
                        return fl::launch_classify(*cache, upto, sel, k, kp, q, a->dtype, q_gathered,
                                                   a->active, a->n, fl::kTauCol, fl::kTauRow, colflags, pm,
-                                                  cs, rowflags, rp, rs, st);
+                                                  cs, rowflags, rp, rs, cls_side, st);
                    }),
                    "classify");
         FL_HIP(timed("gather", st, [&] {
@@ -600,7 +603,7 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
                "gather_q");
     } else {
         rc = prepare(a->sel, a->k, a->level, adapt, prec, a->q, a->q_gathered, cpos, perm, colseg, rowperm,
-                     rowseg, Kc, Vt, Kl, Vl, vn);
+                     rowseg, Kc, Vt, Kl, Vl, vn, cls_cur);
         if (rc) return rc;
     }
     if (a->cache_op == FL_CACHE_REBUILD) {
@@ -622,7 +625,7 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
             if (ok > 0) {
                 rc = prepare(osel, ok, a->level - 1, adapt_old, prec_old, a->q_prev, a->q_prev_gathered, cpos_old,
                              perm_old, colseg_old, rowperm_old, rowseg_old, Kc_old, Vt_old, Kl_old, Vl_old,
-                             nullptr);
+                             nullptr, nullptr);
                 if (rc) return rc;
             }
             R.k = ok;
@@ -779,6 +782,7 @@ static int loop_step(const fl_loop_cfg* cfg, fl_loop_state* S, const fl_loop_inp
     hipStream_t st = (hipStream_t)stream;
     const float sm = 1.0f / sqrtf((float)d);
     fl_attn_args A{};
+    A.cls_current = 1;  // this loop's quantisation precedes its attention
     A.dtype = cfg->dtype; A.q = in->q; A.q_gathered = 0; A.sm = sm; A.mode = cfg->mode;
     A.col_stat_kind = cfg->col_stat;
     A.out = S->out; A.lse = S->lse; A.mass_u = S->mass_u; A.out_u = S->out_u;
@@ -945,6 +949,7 @@ int fl_block_step(const fl_block_cfg* cfg, const fl_layer_weights* W, fl_block_s
         int rc = fl_kv_residual_quant(&C, r - 1, FL_BF16, kc, vc, 1, stream);
         if (rc) return rc;
         fl_attn_args A{};
+        A.cls_current = 1;  // this loop's quantisation precedes its attention
         A.dtype = FL_BF16; A.q = qc; A.q_gathered = 1; A.active = act; A.n = n; A.sm = sm;
         A.level = r - 1; A.mode = cfg->mode; A.col_stat_kind = cfg->col_stat;
         A.out = Ls.out; A.lse = Ls.lse; A.mass_u = Ls.mass_u; A.out_u = Ls.out_u;

@@ -63,7 +63,8 @@ __device__ __forceinline__ int block_scan_1024(int v, int* sh, int* total) {
 //  * blocks [0, ncolblk): selected column p of head h is an outlier when
 //    some |K^| or |V^| of its dequantised row (levels 0..upto, the values
 //    the gather writes) exceeds tau_col or is not finite; D/8 threads per
-//    column, 8 channels each;
+//    column, 8 channels each; or, given the cache's per-token classes (kept
+//    by the quantiser with the same bound), one lookup per column;
 //  * the rest: active row t of head h is an outlier when max |q| exceeds
 //    tau_row or is not finite; 16 lanes per (row, head), kRowItems of them
 //    per lane group (the items of one pass are consecutive (row, head)
@@ -73,6 +74,7 @@ constexpr int kRowItems = 4;
 template <int D>
 __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, const int32_t* __restrict__ sel,
                                                      int k, int ncolblk, float tau_col,
+                                                     const uint8_t* __restrict__ cls,
                                                      uint8_t* __restrict__ colflags, int cstride,
                                                      const void* __restrict__ q, int dtype, int q_gathered,
                                                      const int32_t* __restrict__ active, int n, float tau_row,
@@ -80,6 +82,16 @@ __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, co
     const int tid = threadIdx.x;
     const int H = c.H;
     auto amax = [](float m, float a) { a = fabsf(a); return a <= m ? m : (a > m ? a : INFINITY); };
+    if ((int)blockIdx.x < ncolblk && cls) {  // classes kept by the quantiser: one column per thread
+        const int per_head = (k + 255) / 256;
+        const int h = blockIdx.x / per_head;
+        const int p = (blockIdx.x % per_head) * 256 + tid;
+        if (p < k) {
+            const long o = (sel ? (long)sel[(long)h * k + p] : (long)p) * H + h;
+            colflags[(long)h * cstride + p] = (cls[o] | cls[(long)c.N * H + o]) ? 1 : 0;
+        }
+        return;
+    }
     if ((int)blockIdx.x < ncolblk) {
         constexpr int TPC = D / 8, CPB = 256 / TPC;
         const int per_head = (k + CPB - 1) / CPB;
@@ -647,19 +659,20 @@ hipError_t launch_set_diff(const int32_t* sel_prev, int k_prev, const int32_t* s
 hipError_t launch_classify(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                            const void* q, int dtype, int q_gathered, const int32_t* active, int n,
                            float tau_col, float tau_row, uint8_t* colflags, int32_t* perm, int32_t* colseg,
-                           uint8_t* rowflags, int32_t* rowperm, int32_t* rowseg, hipStream_t st) {
+                           uint8_t* rowflags, int32_t* rowperm, int32_t* rowseg, const uint8_t* cls,
+                           hipStream_t st) {
     const int H = c.H;
-    const int cpb = 256 / (c.d / 8);
+    const int cpb = cls ? 256 : 256 / (c.d / 8);
     const int ncolblk = H * ((k + cpb - 1) / cpb);
     const int nrowblk = (int)(((long)n * H + 16 * kRowItems - 1) / (16 * kRowItems));
     const unsigned nblk = (unsigned)(ncolblk + nrowblk);
     const int cstride = kp, rstride = (int)class_row_stride(n);
     if (c.d == 128)
         hipLaunchKernelGGL(k_class_flags<128>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
+                           cls, colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
     else
         hipLaunchKernelGGL(k_class_flags<64>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
+                           cls, colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
     hipLaunchKernelGGL(k_class_scan, dim3(2 * H), dim3(1024), 0, st, colflags, k, cstride, kp, perm, colseg,
                        rowflags, n, rstride, H, rowperm, rowseg);
     return hipGetLastError();

@@ -160,12 +160,15 @@ hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st);
 // active rows (per head), and the precision-adaptive attention
 constexpr float kTauCol = 4.0f;  // |K^|, |V^| bound of a "normal" column
 constexpr float kTauRow = 6.0f;  // |q| bound of a "normal" query row
-// class flag planes: colflags [H][kp], rowflags [H][class_row_stride(n)] (rows 16-byte aligned)
+// class flag planes: colflags [H][kp], rowflags [H][class_row_stride(n)] (rows 16-byte aligned);
+// cls (or NULL): the cache's per-token classes [2][N][H], read instead of
+// dequantising the selected columns
 inline long class_row_stride(long n) { return (n + 15) / 16 * 16; }
 hipError_t launch_classify(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                            const void* q, int dtype, int q_gathered, const int32_t* active, int n,
                            float tau_col, float tau_row, uint8_t* colflags, int32_t* perm, int32_t* colseg,
-                           uint8_t* rowflags, int32_t* rowperm, int32_t* rowseg, hipStream_t st);
+                           uint8_t* rowflags, int32_t* rowperm, int32_t* rowseg, const uint8_t* cls,
+                           hipStream_t st);
 hipError_t launch_attn_ad(int d, int mode, const AttnParams& P, hipStream_t st);
 // per head, the columns of sel_prev [H][k_prev] absent from sel [H][k]
 // (ascending; k_prev - k of them) -> pruned [H][k_prev - k]

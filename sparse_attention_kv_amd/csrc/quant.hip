@@ -86,18 +86,37 @@ __device__ __forceinline__ void dequant8_chain(const fl_kv_cache& c, int which, 
 
 // The value to quantise for 8 channels of packed row t: the new value, minus
 // the token's previous dequantised value for a residual level.
+// xp: the previous dequantised value (zeros at level 0).
 __device__ __forceinline__ void quant_input8(const QuantArgs& a, int which, long t, long pos,
-                                             int ch, float* x) {
+                                             int ch, float* x, float* xp) {
     const int HD = a.H * a.d;
     const void* src = which ? a.v_new : a.k_new;
     const long row = a.gathered ? t : pos;
     load8_f32(src, row * HD + ch, a.dtype, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xp[i] = 0.0f;
     if (a.level > 0) {
-        float xp[8];
         dequant8_chain(a.cache, which, pos, ch, a.level - 1, xp);
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = x[i] - xp[i];
     }
+}
+
+// The token's operand class for one head (cache.cls): 1 when some channel
+// of its new dequantised value xh (8 per lane, d/8 adjacent lanes per head)
+// exceeds kTauCol in magnitude or is not finite.  Every lane of the head
+// group takes part; lane 0 of the group writes.
+__device__ __forceinline__ void store_class8(const QuantArgs& a, int which, long pos, int ch,
+                                             const float* xh) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = fabsf(xh[i]);
+        m = v <= m ? m : (v > m ? v : INFINITY);
+    }
+    for (int o = 1; o < a.d / 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (ch % a.d == 0)
+        a.cache.cls[((long)which * a.N + pos) * a.H + ch / a.d] = !(m <= kTauCol);
 }
 
 __device__ __forceinline__ void store_codes8(void* codes, long e, int bits, uint64_t packed) {
@@ -145,7 +164,8 @@ __global__ __launch_bounds__(256) void k_quant_kchan(QuantArgs a) {
         const long t = r0 + rl + 8 * j;
         if (live_ch && t < n_rows) {
             const long pos = a.level == 0 ? t : (long)L.rows[t];
-            quant_input8(a, 0, t, pos, ch, x[j]);
+            float xp[8];
+            quant_input8(a, 0, t, pos, ch, x[j], xp);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if (x[j][i] < mn[i]) mn[i] = x[j][i];
@@ -214,13 +234,15 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads, int 
     const fl_kv_level& L = a.cache.level[a.level];
     const long pos = live ? (a.level == 0 ? t : (long)L.rows[t]) : 0;
 
-    float x[8];
+    float x[8], xp[8];
     if (live) {
-        quant_input8(a, which, t, pos, ch, x);
+        quant_input8(a, which, t, pos, ch, x, xp);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+        for (int i = 0; i < 8; ++i) x[i] = xp[i] = 0.0f;
     }
+    // per-token classes kept for the attention (symmetric scheme)
+    const bool keep_cls = a.cache.cls != nullptr && a.cache.scheme == FL_QUANT_ABSMAX;
     void* codes = which ? L.v_codes : L.k_codes;
     const long e = t * HD + ch;
     if (a.bits == 32) {
@@ -228,6 +250,12 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads, int 
             float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(codes) + e);
             p[0] = make_float4(x[0], x[1], x[2], x[3]);
             p[1] = make_float4(x[4], x[5], x[6], x[7]);
+            if (keep_cls) {  // (live is uniform over a head's lanes)
+                float xh[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xh[i] = a.level > 0 ? xp[i] + x[i] : x[i];
+                store_class8(a, which, pos, ch, xh);
+            }
         }
         return;
     }
@@ -268,6 +296,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads, int 
     const int qmax = (1 << (a.bits - 1)) - 1;
     const float s = amax / (float)qmax;
     uint64_t packed = 0;
+    float xh[8];  // the new dequantised value, in the readers' order: previous + code * s
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         int q = 0;
@@ -277,9 +306,12 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, long n_threads, int 
             q = (int)r;
         }
         packed |= (uint64_t)((uint32_t)q & ((1u << a.bits) - 1u)) << (a.bits * i);
+        const float dq = (float)q * s;
+        xh[i] = a.level > 0 ? xp[i] + dq : dq;
     }
     store_codes8(codes, e, a.bits, packed);
     if ((ch % a.g) == 0) (which ? L.v_scale : L.k_scale)[e / a.g] = s;
+    if (keep_cls) store_class8(a, which, pos, ch, xh);
 }
 
 // Reconstruction of every token's K or V at loop level+1 (levels 0..level in

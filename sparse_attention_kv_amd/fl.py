@@ -48,7 +48,7 @@ class FlKvLevel(ctypes.Structure):
 
 class FlKvCache(ctypes.Structure):
     _fields_ = [("N", c_int), ("H", c_int), ("d", c_int), ("g", c_int), ("n_levels", c_int),
-                ("scheme", c_int), ("level", FlKvLevel * MAX_LEVELS)]
+                ("scheme", c_int), ("level", FlKvLevel * MAX_LEVELS), ("cls", c_void_p)]
 
 
 class FlAttnArgs(ctypes.Structure):
@@ -57,7 +57,8 @@ class FlAttnArgs(ctypes.Structure):
                 ("level", c_int), ("mode", c_int), ("cache_op", c_int), ("out", c_void_p),
                 ("lse", c_void_p), ("mass_u", c_void_p), ("out_u", c_void_p),
                 ("col_stat", c_void_p), ("q_prev", c_void_p), ("q_prev_gathered", c_int),
-                ("col_stat_kind", c_int), ("sel_prev", c_void_p), ("k_prev", c_int)]
+                ("col_stat_kind", c_int), ("sel_prev", c_void_p), ("k_prev", c_int),
+                ("cls_current", c_int)]
 
 
 class FlLoopCfg(ctypes.Structure):
@@ -402,6 +403,9 @@ class LoopRunner:
 
         st.cache.N, st.cache.H, st.cache.d, st.cache.g = N, H, d, g
         st.cache.scheme = quant
+        # per-token operand classes (written by the quantiser, read by the attention)
+        self.cls = buf((2, N, H), torch.uint8)
+        st.cache.cls = _p(self.cls)
         self.codes = []
         for r in range(R):
             rows = N if r == 0 else n_active[r]
@@ -462,7 +466,7 @@ class LoopRunner:
                 t = getattr(self, key)[r]
                 if t is not None:
                     named[f"{key}{r}"] = t
-        for key in ("stat", "out", "lse", "mass_u", "out_u"):
+        for key in ("stat", "out", "lse", "mass_u", "out_u", "cls"):
             named[key] = getattr(self, key)
         return named
 
@@ -553,6 +557,8 @@ class BlockRunner:
             Ls.cache.N, Ls.cache.H, Ls.cache.d, Ls.cache.g = N, H, d, g
             Ls.cache.scheme = quant
             lb = dict(codes=[])
+            lb["cls"] = buf((2, N, H), torch.uint8)
+            Ls.cache.cls = _p(lb["cls"])
             for r in range(R):
                 rows = N if r == 0 else cap[r]
                 lb["codes"].append(alloc_level(Ls.cache.level[r], rows, H, d, g, bits[r], quant,
