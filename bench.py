@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # library timing names -> kernel symbols as rocprofv3 reports them (d = 128)
 KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn_lds<128, 0, 1, 32>",
                  "attn_ad": "k_attn_ad<128, 0>", "attn_ad_rebuild": "k_attn_ad<128, 1>",
-                 "attn_ad_rebuild_add": "k_attn_ad<128, 2>",
+                 "attn_ad_rebuild_add": "k_attn_ad<128, 2>", "attn_ad_rb": "k_attn_ad<128, 3>",
                  "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 8>",
                  "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true, false, 0>",
                  "decode": "k_decode<128, 0, true, false, false, 0>",
@@ -297,16 +297,16 @@ def bench_prefill(args, w, np, torch, fl, synth, cpu=True, steps=None):
                        frac=round(ach_m / PEAK_BF16_TFLOPS, 4) if ach_m else None)
 
     def kernel_flops(kname):
-        """Algorithmic flops of one lazy-loop kernel over its launches."""
+        """Algorithmic flops of one lazy-loop kernel per step, over the loops
+        it ran in (attn_ad_rb: the cache rebuild and the attention of the
+        same pairs, one launch)."""
         per_pair = {"attn_split": 4.0, "attn": 4.0, "attn_ad": 4.0, "attn_rebuild": 4.0,
-                    "attn_rebuild_split": 4.0, "attn_ad_rebuild": 4.0,
+                    "attn_rebuild_split": 4.0, "attn_ad_rebuild": 4.0, "attn_ad_rb": 8.0,
                     "colstat": 2.0, "colstat_split": 2.0}.get(kname)
-        if per_pair is None:
+        if per_pair is None or kname not in lazy_k:
             return None     # (the additive rebuild's pairs are the pruned ones, not counted here)
-        rebuild = "rebuild" in kname
-        stat = kname.startswith("colstat")
-        return sum(per_pair * d * L["pairs"] for L in loops
-                   if L["r"] > 1 and (not rebuild or L["rebuilt"]) and (not stat or L["colstat"]))
+        ran = set(lazy_k[kname][2])
+        return sum(per_pair * d * L["pairs"] for L in loops if L["r"] in ran)
 
     roofline = None
     if lazy_k:

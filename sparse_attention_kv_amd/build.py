@@ -20,6 +20,11 @@ LIB = os.path.join(PKG, "libflashloop.so")
 SOURCES = ["abi.hip", "select.hip", "quant.hip", "attn.hip", "adaptive.hip", "block.hip", "decode.hip",
            "calib.hip"]
 NO_CONTRACT = {"select.hip", "quant.hip"}
+# the precision-adaptive attention's fused rebuild + attention instantiation
+# exceeds the default inlining budget (its per-tile lambdas would become
+# device-function calls with a stack frame); the other instantiations
+# compile to the same code with or without this
+EXTRA = {"adaptive.hip": ["-mllvm", "-inline-threshold=5000"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
@@ -34,6 +39,7 @@ def _compile(src: str) -> str:
     flags = list(COMMON)
     if src in NO_CONTRACT:
         flags.append("-ffp-contract=off")
+    flags += EXTRA.get(src, [])
     cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -606,6 +606,11 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
                      rowseg, Kc, Vt, Kl, Vl, vn, cls_cur);
         if (rc) return rc;
     }
+    // After the dense first loop (previous side plain bf16, subtract form)
+    // the rebuild runs inside the attention's workgroups, before their
+    // attention pass (MODE_ATTN_RB): one launch, one prologue per row tile.
+    const bool fuse_rb = a->cache_op == FL_CACHE_REBUILD && adapt && !adapt_old && !rebuild_add && !in_tile &&
+                         prec_old == 0;
     if (a->cache_op == FL_CACHE_REBUILD) {
         fl::AttnParams R = P;
         if (in_tile) {
@@ -632,7 +637,10 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
             R.Kc = Kc_old; R.Vt = Vt_old; R.Kc_lo = Kl_old; R.Vt_lo = Vl_old; R.cpos = cpos_old;
         }
         R.q = a->q_prev; R.q_gathered = a->q_prev_gathered;
-        if (adapt_old) {
+        if (fuse_rb) {
+            P.Kc_old = R.Kc; P.Vt_old = R.Vt; P.cpos_old = R.cpos; P.k_old = R.k;
+            P.q_old = a->q_prev; P.q_old_gathered = a->q_prev_gathered;
+        } else if (adapt_old) {
             R.rowperm = rowperm_old; R.rowseg = rowseg_old; R.colseg = colseg_old;
             if (R.k > 0 || !rebuild_add)
                 FL_HIP(timed(rebuild_add ? "attn_ad_rebuild_add" : "attn_ad_rebuild", st, [&] {
@@ -651,7 +659,11 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     // loop), precision-adaptive ("attn_ad"), hi/lo split ("attn_split")
     if (adapt) {
         P.rowperm = rowperm; P.rowseg = rowseg; P.colseg = colseg;
-        FL_HIP(timed("attn_ad", st, [&] { return fl::launch_attn_ad(d, fl::MODE_ATTN, P, st); }), "attn");
+        if (fuse_rb)
+            FL_HIP(timed("attn_ad_rb", st, [&] { return fl::launch_attn_ad(d, fl::MODE_ATTN_RB, P, st); }),
+                   "attn");
+        else
+            FL_HIP(timed("attn_ad", st, [&] { return fl::launch_attn_ad(d, fl::MODE_ATTN, P, st); }), "attn");
     } else {
         FL_HIP(timed(prec ? "attn_split" : "attn", st,
                      [&] { return fl::launch_attn(d, fl::MODE_ATTN, prec, in_tile, P, st); }),

@@ -257,7 +257,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     __shared__ __attribute__((aligned(1024))) __bf16 sV1[KB / 2];
     __shared__ __attribute__((aligned(256))) int sC0[64];
     __shared__ __attribute__((aligned(256))) int sC1[64];
-    __shared__ int s_mn[4], s_mx[4], s_bd[4];
+    __shared__ int s_mn[4], s_mx[4], s_bd[6];
+    constexpr bool RB = MODE == MODE_ATTN_RB;  // rebuild pass first (see the pass below)
     const int n_tiles = (P.n + kAdBM - 1) / kAdBM;
     int tile, h;
     block_coords(P.xcd_remap, n_tiles, P.H, tile, h);
@@ -273,9 +274,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     // are looked up; the causal bounds are then searched in LDS, and the
     // query fragments are loaded together with the first tile.
     const bool cpos_lds = P.kp * 4 <= KB;
+    const int32_t* cpos_old_h = RB ? P.cpos_old + (long)h * P.kp : nullptr;
+    const __amdgpu_buffer_rsrc_t rC_old = make_rsrc(RB ? cpos_old_h : cpos_h, (uint32_t)P.kp * 4);
     if (cpos_lds)
-        for (int m = w; m * 1024 < P.kp * 4; m += 4)
+        for (int m = w; m * 1024 < P.kp * 4; m += 4) {
             buf_dma16(rC, reinterpret_cast<char*>(sK1) + m * 1024, lane * 16, m * 1024);
+            if (RB) buf_dma16(rC_old, reinterpret_cast<char*>(sV1) + m * 1024, lane * 16, m * 1024);
+        }
     const int nn_l = P.colseg[2 * h], no_l = P.colseg[2 * h + 1];
     const int rseg_l = P.rowseg ? P.rowseg[h] : 0;
     const int t = valid ? (P.rowperm ? P.rowperm[(long)h * P.n + tt] : tt) : 0;
@@ -305,6 +310,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         const int b = cpos_lds ? wave_ubound(reinterpret_cast<const int32_t*>(sK1) + off, len, v)
                                : wave_ubound(cpos_h + off, len, v);
         if (lane == 0) s_bd[w] = b;
+        if (RB && w < 2) {  // the previous side's bounds (all its columns plain)
+            const int b2 = cpos_lds ? wave_ubound(reinterpret_cast<const int32_t*>(sV1), P.k_old, v)
+                                    : wave_ubound(cpos_old_h, P.k_old, v);
+            if (lane == 0) s_bd[4 + w] = b2;
+        }
     }
     __syncthreads();
     const int pe0 = __builtin_amdgcn_readfirstlane(s_bd[0]);
@@ -317,22 +327,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     const int T0 = (pe0 + W0 - 1) / W0;
     const int T = T0 + (pe1 + 31) / 32;
     bf16x8 qf[D / 16];
-    {
-        const long qrow = P.q_gathered ? (long)t : (long)rowpos;
+    auto load_q = [&](const void* qsrc, int gathered) {
+        const long qrow = gathered ? (long)t : (long)rowpos;
         const long qoff = (qrow * P.H + h) * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            if (valid) qf[kk] = load8_bf16(P.q, qoff + 16 * kk, P.dtype);
+            if (valid) qf[kk] = load8_bf16(qsrc, qoff + 16 * kk, P.dtype);
             else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)0.0f;
             }
         }
-    }
+    };
+    if (RB) load_q(P.q_old, P.q_old_gathered);
+    else load_q(P.q, P.q_gathered);
     const long rh = valid ? (long)rowpos * P.H + h : 0;
-    constexpr bool REB = MODE != MODE_ATTN;
+    // reb: the pass in progress is a cache rebuild (fixed exponent reference
+    // lse_prev, probabilities weighted by 1 - M_U_prev)
+    bool reb = MODE != MODE_ATTN;
     float lse_prev2 = 0.0f, wgt = 1.0f, mu_prev = 0.0f;
-    if (REB && valid) {
+    if (reb && valid) {
         lse_prev2 = P.lse[rh] * 1.4426950408889634f;
         mu_prev = P.mass_u[rh];
         wgt = 1.0f - mu_prev;
@@ -368,10 +382,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     // (outlier rows, normal columns: only the scores need the keys' lo part,
     // P.V over values within the column bound keeps bf16), and 32-column
     // hi/lo tiles (outlier columns)
-    auto tile_p0 = [&](int i) __attribute__((always_inline)) { return i < T0 ? i * W0 : seg1 + (i - T0) * 32; };
-    auto tile_split = [&](int i) __attribute__((always_inline)) { return i >= T0 || !rnorm; };
-    auto tile_full = [&](int i) __attribute__((always_inline)) { return i >= T0; };
-    auto issue = [&](int i, __bf16* sK, __bf16* sV, int* sC) __attribute__((always_inline)) {
+    auto tile_p0 = [&](int i) { return i < T0 ? i * W0 : seg1 + (i - T0) * 32; };
+    auto tile_split = [&](int i) { return i >= T0 || !rnorm; };
+    auto tile_full = [&](int i) { return i >= T0; };
+    auto issue = [&](int i, __bf16* sK, __bf16* sV, int* sC) {
         const int p0 = tile_p0(i);
         if (!tile_split(i)) {
             const uint32_t ks = (uint32_t)p0 * D * 2, vs = (uint32_t)(p0 / 64) * D * 64 * 2;
@@ -406,8 +420,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // online softmax over one 32-column block's scores (shared by both kinds)
-    auto softmax_ref = [&](f32x16* s, int KT) __attribute__((always_inline)) -> float {
-        if (MODE != MODE_ATTN) return lse_prev2;
+    auto softmax_ref = [&](f32x16* s, int KT) -> float {
+        if (reb) return lse_prev2;
         float tmax = -INFINITY;
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -426,8 +440,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         return m_run == -INFINITY ? 0.0f : m_run;
     };
 
-    auto compute_plain = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
-        const int p0 = tile_p0(i);
+    // a plain tile at column slot p0; columns from slot pf on may lie past the first row
+    auto compute_plain = [&](int p0, int pf, const __bf16* sK, const __bf16* sV, const int* sC)
+        {
         f32x16 s[2];
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -441,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (p0 + 64 > pf0) {
+        if (p0 + 64 > pf) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -457,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
-                if (REB) pj *= wgt;
+                if (reb) pj *= wgt;
                 pb[kt][j >> 3][j & 7] = (__bf16)pj;
                 l_run += pj;
             }
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
     };
 
-    auto compute_split = [&](auto full, int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
+    auto compute_split = [&](auto full, int i, const __bf16* sK, const __bf16* sV, const int* sC) {
         constexpr bool FULL = decltype(full)::value;
         const int p0 = tile_p0(i);
         const bool seg = i >= T0;
@@ -503,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             float pj = __builtin_amdgcn_exp2f(fmaf(s[0][j], P.c2, -m_use));
-            if (REB) pj *= wgt;
+            if (reb) pj *= wgt;
             const __bf16 hi = (__bf16)pj;
             pb[j >> 3][j & 7] = hi;
             if (FULL) pl[j >> 3][j & 7] = (__bf16)(pj - (float)hi);
@@ -525,11 +540,76 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
         }
     };
-    auto compute = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) __attribute__((always_inline)) {
+    auto compute = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) {
         if (tile_full(i)) compute_split(std::true_type{}, i, sK, sV, sC);
         else if (tile_split(i)) compute_split(std::false_type{}, i, sK, sV, sC);
-        else compute_plain(i, sK, sV, sC);
+        else compute_plain(tile_p0(i), pf0, sK, sV, sC);
     };
+
+    float mu_rb = 0.0f;  // RB: M_U of these rows after the rebuild pass
+    if constexpr (RB) {
+        // Rebuild pass (subtract form, as MODE_REBUILD): the previous loop's
+        // probabilities over its columns S (all plain tiles), weighted by
+        // 1 - M_U_prev; O_U = o_prev - sum_S P V^, M_U = 1 - sum_S P are
+        // written for these rows, then the attention pass starts afresh.
+        const int peA = __builtin_amdgcn_readfirstlane(s_bd[4]);
+        const int pfA = __builtin_amdgcn_readfirstlane(s_bd[5]);
+        const int TA = (peA + 63) / 64;
+        const __amdgpu_buffer_rsrc_t rKo = make_rsrc(P.Kc_old + koff, kbytes), rVo = make_rsrc(P.Vt_old + voff, kbytes);
+        auto issue_old = [&](int i, __bf16* sK, __bf16* sV, int* sC) {
+            const uint32_t ks = (uint32_t)(64 * i) * D * 2, vs = (uint32_t)i * D * 64 * 2;
+#pragma unroll
+            for (int j = 0; j < MPW; ++j) {
+                const int m = w * MPW + j;
+                buf_dma16(rKo, reinterpret_cast<char*>(sK) + m * 1024, kvo[j], ks);
+                buf_dma16(rVo, reinterpret_cast<char*>(sV) + m * 1024, vvo[j], vs);
+            }
+            if (w == 0) buf_dma4(rC_old, sC, lane * 4, 64 * i * 4);
+        };
+        if (TA > 0) issue_old(0, sK0, sV0, sC0);
+        for (int i = 0; i < TA;) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (i + 1 < TA) issue_old(i + 1, sK1, sV1, sC1);
+            compute_plain(64 * i, pfA, sK0, sV0, sC0);
+            if (++i >= TA) break;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (i + 1 < TA) issue_old(i + 1, sK0, sV0, sC0);
+            compute_plain(64 * i, pfA, sK1, sV1, sC1);
+            ++i;
+        }
+        const float l_a = l_run + __shfl_xor(l_run, 32);
+        mu_rb = 1.0f - l_a;
+        if (valid) {
+            const float* orow_prev = P.out + rh * D;
+            float* ourow = P.out_u + rh * D;
+            float4 bc[D / 32][4];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    bc[dt][jq] = *reinterpret_cast<const float4*>(orow_prev + 32 * dt + jq * 8 + half * 4);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq) {
+                    const float4 op = bc[dt][jq];
+                    *reinterpret_cast<float4*>(ourow + 32 * dt + jq * 8 + half * 4) =
+                        make_float4(op.x - o[dt][4 * jq + 0], op.y - o[dt][4 * jq + 1],
+                                    op.z - o[dt][4 * jq + 2], op.w - o[dt][4 * jq + 3]);
+                }
+            if (half == 0) P.mass_u[rh] = mu_rb;
+        }
+        // the attention pass: its own queries, fresh accumulators
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+        l_run = 0.0f;
+        m_run = -INFINITY;
+        reb = false;
+        load_q(P.q, P.q_gathered);
+        __syncthreads();  // every wave is done with the tile buffers
+    }
 
     if (T > 0) issue(0, sK0, sV0, sC0);
     for (int i = 0; i < T;) {
@@ -548,15 +628,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!valid) return;
     float* orow = P.out + rh * D;
-    if (MODE == MODE_ATTN) {
+    if (MODE == MODE_ATTN || RB) {
         // every load of the caches before the first store (the stores could
         // alias them for the compiler, which would then serialise each pair)
-        const bool cached = P.cache_op != FL_CACHE_ZERO;
+        const bool cached = RB || P.cache_op != FL_CACHE_ZERO;
         const float* ourow = P.out_u + rh * D;
         float4 uc[D / 32][4];
         float mu = 0.0f;
         if (cached) {
-            mu = P.mass_u[rh];
+            mu = RB ? mu_rb : P.mass_u[rh];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -686,6 +766,7 @@ hipError_t launch_attn_ad(int d, int mode, const AttnParams& P, hipStream_t st) 
 #define FL_AD(D_)                                                                                        \
     if (mode == MODE_ATTN) hipLaunchKernelGGL((k_attn_ad<D_, MODE_ATTN>), grid, dim3(256), 0, st, Q);        \
     else if (mode == MODE_REBUILD) hipLaunchKernelGGL((k_attn_ad<D_, MODE_REBUILD>), grid, dim3(256), 0, st, Q); \
+    else if (mode == MODE_ATTN_RB) hipLaunchKernelGGL((k_attn_ad<D_, MODE_ATTN_RB>), grid, dim3(256), 0, st, Q); \
     else hipLaunchKernelGGL((k_attn_ad<D_, MODE_REBUILD_ADD>), grid, dim3(256), 0, st, Q);
     if (d == 128) { FL_AD(128) } else { FL_AD(64) }
 #undef FL_AD

@@ -47,6 +47,16 @@ struct AttnParams {
     const int32_t* rowseg;   // [H]
     const int32_t* colseg;   // [H][2]
     int xcd_remap;
+    // MODE_ATTN_RB (k_attn_ad): the previous loop's side of a subtract-form
+    // cache rebuild, run by the same workgroups before the attention: its
+    // compact bf16 K / V^T (plain layout, k_old selected columns in
+    // selection order, kp slots), positions, and queries
+    const __bf16* Kc_old;
+    const __bf16* Vt_old;
+    const int32_t* cpos_old;
+    int k_old;
+    const void* q_old;
+    int q_old_gathered;
     int deq_levels;        // in-tile dequantisation: levels 0..deq_levels-1 of q
     QTiles qt;
 };
@@ -68,8 +78,10 @@ struct ColParams {
 
 // MODE_REBUILD: pruned-column caches by subtraction from o_prev over the
 // selected columns; MODE_REBUILD_ADD: added to the carried caches over the
-// pruned columns (k_attn_ad only)
-enum { MODE_ATTN = 0, MODE_REBUILD = 1, MODE_REBUILD_ADD = 2 };
+// pruned columns (k_attn_ad only); MODE_ATTN_RB: the subtract-form rebuild
+// over the previous loop's side, then the attention, in one launch
+// (k_attn_ad only)
+enum { MODE_ATTN = 0, MODE_REBUILD = 1, MODE_REBUILD_ADD = 2, MODE_ATTN_RB = 3 };
 
 // Batched decode: B sequences x H heads, one new query token each.
 struct DecodeParams {
