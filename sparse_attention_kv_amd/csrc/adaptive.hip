@@ -540,11 +540,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             }
         }
     };
-    auto compute = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) {
-        if (tile_full(i)) compute_split(std::true_type{}, i, sK, sV, sC);
-        else if (tile_split(i)) compute_split(std::false_type{}, i, sK, sV, sC);
-        else compute_plain(tile_p0(i), pf0, sK, sV, sC);
-    };
 
     float mu_rb = 0.0f;  // RB: M_U of these rows after the rebuild pass
     if constexpr (RB) {
@@ -611,19 +606,45 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         __syncthreads();  // every wave is done with the tile buffers
     }
 
+    // Tile i sits in buffer i & 1.  The tile kinds occupy consecutive ranges
+    // ([0, T0) plain or hi/lo-key tiles, [T0, T) full hi/lo tiles), and each
+    // range runs in a loop of its own: with one kind per loop body the
+    // accumulators keep their registers from tile to tile (a loop that
+    // branches between kinds gets them copied at every join).
+    auto run = [&](auto kind, auto odd, int ib, int ie) {
+        constexpr int KIND = decltype(kind)::value;
+        constexpr bool ODD = decltype(odd)::value;
+        __bf16* const kA = ODD ? sK1 : sK0;
+        __bf16* const vA = ODD ? sV1 : sV0;
+        int* const cA = ODD ? sC1 : sC0;
+        __bf16* const kB = ODD ? sK0 : sK1;
+        __bf16* const vB = ODD ? sV0 : sV1;
+        int* const cB = ODD ? sC0 : sC1;
+        auto step = [&](int i, const __bf16* sK, const __bf16* sV, const int* sC) {
+            if constexpr (KIND == 0) compute_plain(tile_p0(i), pf0, sK, sV, sC);
+            else compute_split(std::integral_constant<bool, KIND == 2>{}, i, sK, sV, sC);
+        };
+        for (int i = ib; i < ie;) {
+            __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the current tile landed
+            __syncthreads();               // ... every lane's; the other buffer is free
+            if (i + 1 < T) issue(i + 1, kB, vB, cB);
+            step(i, kA, vA, cA);
+            if (++i >= ie) break;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (i + 1 < T) issue(i + 1, kA, vA, cA);
+            step(i, kB, vB, cB);
+            ++i;
+        }
+    };
+    using plain_k = std::integral_constant<int, 0>;
+    using split_k = std::integral_constant<int, 1>;
+    using full_k = std::integral_constant<int, 2>;
     if (T > 0) issue(0, sK0, sV0, sC0);
-    for (int i = 0; i < T;) {
-        __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the current tile landed
-        __syncthreads();               // ... every lane's; the other buffer is free
-        if (i + 1 < T) issue(i + 1, sK1, sV1, sC1);
-        compute(i, sK0, sV0, sC0);
-        if (++i >= T) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (i + 1 < T) issue(i + 1, sK0, sV0, sC0);
-        compute(i, sK1, sV1, sC1);
-        ++i;
-    }
+    if (rnorm) run(plain_k{}, std::false_type{}, 0, T0);
+    else run(split_k{}, std::false_type{}, 0, T0);
+    if (T0 & 1) run(full_k{}, std::true_type{}, T0, T);
+    else run(full_k{}, std::false_type{}, T0, T);
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!valid) return;
