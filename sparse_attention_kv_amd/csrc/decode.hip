@@ -30,6 +30,7 @@
 namespace fl {
 
 constexpr int DT = 256;      // threads per workgroup (512 measured slower)
+constexpr size_t kDecodePairLds = 48 * 1024;  // dynamic LDS bound for the pair lists
 constexpr int DNW = DT / 64; // waves
 
 struct SeqLevel {
@@ -190,10 +191,18 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     // passes in flight: 4 for 16-byte code rows (8 measured no faster); a
     // narrower fixed base keeps the bytes in flight per lane the same
     constexpr int U = (ASYM && L0 && B0 == 4) ? 8 : (ASYM && L0 && B0 == 2) ? 16 : 4;
+    // the selected columns' level-by-level passes (absmax): 8 columns per
+    // lane, so that k = 256 takes one pass per level
+    constexpr int US = 8;
     extern __shared__ float dyn[];  // sc[k + T], then (sparse) rows[level + 1][k]
     __shared__ float qs[D];
     __shared__ float red[DNW];
     __shared__ float ored[DNW][D];
+    // (sparse absmax) per level and side: code and scale bases, code width
+    __shared__ const uint8_t* lv_codes[2][FL_MAX_LEVELS];
+    __shared__ const float* lv_scales[2][FL_MAX_LEVELS];
+    __shared__ int lv_bits[FL_MAX_LEVELS];
+    __shared__ int s_cnt[DNW];
     // blocks are dealt to the 8 XCDs round-robin; with B a multiple of 8 all
     // heads of a sequence run on one XCD, so a token's scale line (all heads'
     // group scales are adjacent) is fetched into one L2 only
@@ -226,6 +235,25 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
     };
     for (int c = tid; c < D; c += DT)
         qs[c] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P.q)[qo + c]);
+    // (sparse absmax, levels beyond the base) the selected columns' present
+    // cache rows as (column, level) pairs, level-major with the columns in
+    // selection order inside a level (a wave's loads then share one code
+    // width, and a pass walks one level's rows in order; column-major pairs
+    // measured 1.5x slower); ppart[l * k + c] receives pair (c, l)'s partial
+    // score
+    constexpr bool PAIRS_OK = SPARSE && !ASYM;
+    const bool use_pairs = PAIRS_OK && P.pairs;
+    int* pairs = rowtab + (P.level + 1) * k;
+    float* ppart = reinterpret_cast<float*>(pairs + (P.level + 1) * k);
+    if (use_pairs && tid < nlev) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const SeqLevel L = seq_level<D, ASYM>(P, tid, b, which);
+            lv_codes[which][tid] = L.codes;
+            lv_scales[which][tid] = L.scales;
+        }
+        lv_bits[tid] = L0 ? 8 : P.cache.level[tid].bits;
+    }
     if (SPARSE) {
         const int32_t* sel = P.sel + (long)bh * k;
         for (int c = tid; c < k; c += DT) {
@@ -235,6 +263,26 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
         }
     }
     __syncthreads();
+    int npairs = 0;
+    if (use_pairs) {
+        for (int l = 0; l < nlev; ++l)
+            for (int c0 = 0; c0 < k; c0 += DT) {
+                const int c = c0 + tid;
+                const bool f = c < k && rowtab[l * k + c] >= 0;
+                const unsigned long long bal = __ballot(f);
+                if (lane == 0) s_cnt[w] = __popcll(bal);
+                __syncthreads();
+                int base = npairs, tot = 0;
+#pragma unroll
+                for (int i = 0; i < DNW; ++i) {
+                    if (i < w) base += s_cnt[i];
+                    tot += s_cnt[i];
+                }
+                if (f) pairs[base + __popcll(bal & ((1ull << lane) - 1))] = (l << 26) | c;
+                npairs += tot;
+                __syncthreads();
+            }
+    }
     float qv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) qv[i] = qs[cs * 16 + i];
@@ -310,23 +358,68 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 if (cs == 0 && c < k) sc[c] = v * c2;
             }
         }
+    } else if (PAIRS_OK && use_pairs) {
+        // selected columns' present rows as (column, level) pairs: each pass
+        // issues its US pairs' code and scale loads before using any; a pair's
+        // partial score goes to LDS, and a column sums its levels in level
+        // order afterwards
+        for (int p0 = 0; p0 < npairs; p0 += CPI * US) {
+            uint4 raw[US];
+            float sv[US];
+            int pk[US];
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int pi = p0 + u * CPI + w * CPW + cl;
+                pk[u] = pi < npairs ? pairs[pi] : -1;
+                raw[u] = make_uint4(0u, 0u, 0u, 0u);
+                sv[u] = 0.0f;
+                if (pk[u] >= 0) {
+                    const int l = pk[u] >> 26, c = pk[u] & 0x3ffffff;
+                    const long rr = (long)rowtab[l * k + c] * H + h;
+                    raw[u] = load_raw16_rt(lv_codes[0][l], rr * D + cs * 16, lv_bits[l]);
+                    sv[u] = lv_scales[0][l][rr * G + grp];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                float v = 0.0f;
+                if (pk[u] >= 0) {
+                    float x[16];
+                    decode_s16_rt(raw[u], lv_bits[pk[u] >> 26], x);
+                    float dot = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) dot = fmaf(qv[i], x[i], dot);
+                    v = dot * sv[u];
+                }
+#pragma unroll
+                for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
+                if (cs == 0 && pk[u] >= 0) ppart[(pk[u] >> 26) * k + (pk[u] & 0x3ffffff)] = v;
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < k; c += DT) {
+            float v = 0.0f;
+            for (int l = 0; l < nlev; ++l)
+                if (rowtab[l * k + c] >= 0) v += ppart[l * k + c];
+            sc[c] = v * c2;
+        }
     } else if (!ASYM && SPARSE) {
-        // selected columns: level by level, each pass issues its U columns'
+        // selected columns: level by level, each pass issues its US columns'
         // code and scale loads before using any (an absent level's row is
         // -1 and its column is skipped); a column still sums its levels in
         // level order
-        for (int c0 = 0; c0 < k; c0 += CPI * U) {
-            float part[U];
+        for (int c0 = 0; c0 < k; c0 += CPI * US) {
+            float part[US];
 #pragma unroll
-            for (int u = 0; u < U; ++u) part[u] = 0.0f;
+            for (int u = 0; u < US; ++u) part[u] = 0.0f;
             for (int l = 0; l < nlev; ++l) {
                 const SeqLevel L = seq_level<D, ASYM>(P, l, b, 0);
                 const int bits = bits_of(L, l);
-                uint4 raw[U];
-                float sv[U];
-                int rowv[U];
+                uint4 raw[US];
+                float sv[US];
+                int rowv[US];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < US; ++u) {
                     const int c = c0 + u * CPI + w * CPW + cl;
                     rowv[u] = c < k ? row_of(l, c) : -1;
                     raw[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -338,7 +431,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < US; ++u) {
                     if (rowv[u] >= 0) {
                         float x[16];
                         decode_s16_rt(raw[u], bits, x);
@@ -350,7 +443,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < US; ++u) {
                 float v = part[u];
 #pragma unroll
                 for (int o = 1; o < LPC; o <<= 1) v += __shfl_xor(v, o);
@@ -492,23 +585,55 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 }
             }
         }
+    } else if (PAIRS_OK && use_pairs) {
+        // as in phase 1: (column, level) pairs, a pass's loads issued together
+        for (int p0 = 0; p0 < npairs; p0 += CPI * US) {
+            uint4 raw[US];
+            float sv[US], pu[US];
+            int pk[US];
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                const int pi = p0 + u * CPI + w * CPW + cl;
+                pk[u] = pi < npairs ? pairs[pi] : -1;
+                raw[u] = make_uint4(0u, 0u, 0u, 0u);
+                sv[u] = 0.0f;
+                pu[u] = 0.0f;
+                if (pk[u] >= 0) {
+                    const int l = pk[u] >> 26, c = pk[u] & 0x3ffffff;
+                    const long rr = (long)rowtab[l * k + c] * H + h;
+                    raw[u] = load_raw16_rt(lv_codes[1][l], rr * D + cs * 16, lv_bits[l]);
+                    sv[u] = lv_scales[1][l][rr * G + grp];
+                    pu[u] = sc[c];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < US; ++u) {
+                if (pk[u] >= 0) {
+                    const float ps = pu[u] * sv[u];
+                    float x[16];
+                    decode_s16_rt(raw[u], lv_bits[pk[u] >> 26], x);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[i] = fmaf(x[i], ps, acc[i]);
+                }
+            }
+        }
     } else if (!ASYM && SPARSE) {
         // as in phase 1: level by level, a pass's loads issued together
-        for (int c0 = 0; c0 < k; c0 += CPI * U) {
-            float pu[U];
+        for (int c0 = 0; c0 < k; c0 += CPI * US) {
+            float pu[US];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < US; ++u) {
                 const int c = c0 + u * CPI + w * CPW + cl;
                 pu[u] = c < k ? sc[c] : 0.0f;
             }
             for (int l = 0; l < nlev; ++l) {
                 const SeqLevel L = seq_level<D, ASYM>(P, l, b, 1);
                 const int bits = bits_of(L, l);
-                uint4 raw[U];
-                float sv[U];
-                int rowv[U];
+                uint4 raw[US];
+                float sv[US];
+                int rowv[US];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < US; ++u) {
                     const int c = c0 + u * CPI + w * CPW + cl;
                     rowv[u] = c < k ? row_of(l, c) : -1;
                     raw[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -520,7 +645,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < US; ++u) {
                     if (rowv[u] >= 0) {
                         const float ps = pu[u] * sv[u];
                         float x[16];
@@ -644,14 +769,21 @@ void launch_decode_d(int mode, bool sp, bool l0, bool asym, int b0, dim3 grid, s
 
 hipError_t launch_decode(int d, int mode, const DecodeParams& P, hipStream_t st) {
     const bool sp = P.sel != nullptr;
-    const size_t shm = (size_t)(P.k + P.n_tail) * sizeof(float) +
-                       (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
+    size_t shm = (size_t)(P.k + P.n_tail) * sizeof(float) + (sp ? (size_t)(P.level + 1) * P.k * 4 : 0);
+    // the (column, level) pair list and partial scores of the sparse absmax
+    // passes over more than the base level, when they fit the workgroup's LDS
+    // share (else level by level; a base-level-only pass gains nothing)
+    DecodeParams Q = P;
+    const size_t pair_shm = (size_t)2 * (P.level + 1) * P.k * 4;
+    Q.pairs = sp && P.level >= 1 && P.cache.scheme != FL_QUANT_ASYM && P.k < (1 << 26) &&
+              shm + pair_shm <= kDecodePairLds;
+    if (Q.pairs) shm += pair_shm;
     const dim3 grid(P.B * P.H);
     const bool l0 = P.level == 0;
     const bool asym = P.cache.scheme == FL_QUANT_ASYM;
     const int b0 = P.cache.level[0].bits;
-    if (d == 128) launch_decode_d<128>(mode, sp, l0, asym, b0, grid, shm, P, st);
-    else launch_decode_d<64>(mode, sp, l0, asym, b0, grid, shm, P, st);
+    if (d == 128) launch_decode_d<128>(mode, sp, l0, asym, b0, grid, shm, Q, st);
+    else launch_decode_d<64>(mode, sp, l0, asym, b0, grid, shm, Q, st);
     return hipGetLastError();
 }
 

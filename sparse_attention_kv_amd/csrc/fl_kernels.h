@@ -102,6 +102,7 @@ struct DecodeParams {
     int kg_pad[FL_MAX_LEVELS];
     int kg_count[FL_MAX_LEVELS];
     float* out; float* lse; float* mass_u; float* out_u; float* col_stat;
+    int pairs;              // set by the launcher: sparse absmax passes over (column, level) pairs
 };
 
 struct AppendParams {
