@@ -122,6 +122,27 @@ __device__ __forceinline__ uint4 load_raw16_rt(const uint8_t* base, long e, int 
     }
     return make_uint4(*reinterpret_cast<const uint32_t*>(base + e / 4), 0u, 0u, 0u);
 }
+// load_raw16_rt through a global-address-space pointer: the pair passes
+// take the level bases from LDS, where the compiler cannot tell them from
+// flat addresses (a flat load also holds up every LDS wait of the wave)
+#define FL_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ uint4 load_raw16_g(const uint8_t* base, long e, int bits) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const FL_GLOBAL uint8_t* g = (const FL_GLOBAL uint8_t*)base;
+    if (bits == 8) {
+        const u32x4 v = *(const FL_GLOBAL u32x4*)(g + e);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    if (bits == 4) {
+        const u32x2 v = *(const FL_GLOBAL u32x2*)(g + e / 2);
+        return make_uint4(v.x, v.y, 0u, 0u);
+    }
+    return make_uint4(*(const FL_GLOBAL uint32_t*)(g + e / 4), 0u, 0u, 0u);
+}
+__device__ __forceinline__ float load_f32_global(const float* base, long i) {
+    return ((const FL_GLOBAL float*)base)[i];
+}
 __device__ __forceinline__ void decode_s16_rt(const uint4 r, int bits, float (&x)[16]) {
     if (bits == 8) {
         const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
@@ -376,8 +397,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 if (pk[u] >= 0) {
                     const int l = pk[u] >> 26, c = pk[u] & 0x3ffffff;
                     const long rr = (long)rowtab[l * k + c] * H + h;
-                    raw[u] = load_raw16_rt(lv_codes[0][l], rr * D + cs * 16, lv_bits[l]);
-                    sv[u] = lv_scales[0][l][rr * G + grp];
+                    raw[u] = load_raw16_g(lv_codes[0][l], rr * D + cs * 16, lv_bits[l]);
+                    sv[u] = load_f32_global(lv_scales[0][l], rr * G + grp);
                 }
             }
 #pragma unroll
@@ -601,8 +622,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecodeParams P) {
                 if (pk[u] >= 0) {
                     const int l = pk[u] >> 26, c = pk[u] & 0x3ffffff;
                     const long rr = (long)rowtab[l * k + c] * H + h;
-                    raw[u] = load_raw16_rt(lv_codes[1][l], rr * D + cs * 16, lv_bits[l]);
-                    sv[u] = lv_scales[1][l][rr * G + grp];
+                    raw[u] = load_raw16_g(lv_codes[1][l], rr * D + cs * 16, lv_bits[l]);
+                    sv[u] = load_f32_global(lv_scales[1][l], rr * G + grp);
                     pu[u] = sc[c];
                 }
             }
