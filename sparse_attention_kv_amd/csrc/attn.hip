@@ -56,7 +56,7 @@ __device__ __forceinline__ int vt_key_of_slot(int so) {
 template <int D>
 constexpr int gather_cols() { return 256 / (D / 8); }
 
-template <int D, bool X3>
+template <int D, bool X3, bool BATCH>
 __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      const int32_t* __restrict__ sel, int k,
                                                      int kp, __bf16* __restrict__ Kc,
@@ -81,12 +81,21 @@ __global__ __launch_bounds__(256) void k_gather_bf16(fl_kv_cache c, int upto,
     if (c0 == 0) cpos[(long)h * kp + p] = live ? (int32_t)j : 0x7fffffff;
     const int HD = c.H * D;
     const int ch = h * D + c0;
+    float xkv[2][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        xkv[0][e] = 0.0f;
+        xkv[1][e] = 0.0f;
+    }
+    if constexpr (BATCH) {
+        if (live) deq_col8_kv(c, upto, j, HD, ch, xkv[0], xkv[1]);
+    }
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-        if (live) deq_col8(c, upto, which, j, HD, ch, x);
+        float* x = xkv[which];
+        if constexpr (!BATCH) {
+            if (live) deq_col8(c, upto, which, j, HD, ch, x);
+        }
         if (which == 0) {
             bf16x8 v, vl;
 #pragma unroll
@@ -1118,11 +1127,15 @@ hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel
                               bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
                               int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st) {
     dim3 grid(kp / (c.d == 128 ? gather_cols<128>() : gather_cols<64>()), c.H);
-#define FL_GATHER(D_, X_)                                                                       \
-    hipLaunchKernelGGL((k_gather_bf16<D_, X_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
+    // the keys' and values' level rows loaded together where the cache allows
+    const bool batch = deq_batch_ok(c, upto);
+#define FL_GATHER(D_, X_, B_)                                                                       \
+    hipLaunchKernelGGL((k_gather_bf16<D_, X_, B_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
                        Vt, Kc_lo, Vt_lo, cpos, vnorm, perm)
-    if (c.d == 128) { if (x3) FL_GATHER(128, true); else FL_GATHER(128, false); }
-    else { if (x3) FL_GATHER(64, true); else FL_GATHER(64, false); }
+#define FL_GATHER_B(D_, X_) { if (batch) FL_GATHER(D_, X_, true); else FL_GATHER(D_, X_, false); }
+    if (c.d == 128) { if (x3) FL_GATHER_B(128, true) else FL_GATHER_B(128, false) }
+    else { if (x3) FL_GATHER_B(64, true) else FL_GATHER_B(64, false) }
+#undef FL_GATHER_B
 #undef FL_GATHER
     return hipGetLastError();
 }

@@ -156,6 +156,65 @@ __device__ __forceinline__ void deq_col8(const fl_kv_cache& c, int upto, int whi
     }
 }
 
+// deq_col8 for the key and the value of one column together, for absmax
+// caches of at most kDeqBatch levels with an int8 base and no fp32 levels
+// (deq_batch_ok): every level's slot in one round of loads, then every
+// present level's K and V codes and scales in one more, instead of a
+// slot-then-codes round trip per level and side.  The sums keep deq_col8's
+// level order and its stop at the first absent level.
+constexpr int kDeqBatch = 8;
+inline bool deq_batch_ok(const fl_kv_cache& c, int upto) {
+    if (c.scheme == FL_QUANT_ASYM || upto >= kDeqBatch) return false;
+    for (int l = 0; l <= upto; ++l)
+        if (c.level[l].bits == 32 || (l == 0 && c.level[l].bits != 8)) return false;
+    return true;
+}
+// requires deq_batch_ok(c, upto)
+__device__ __forceinline__ void deq_col8_kv(const fl_kv_cache& c, int upto, long j, int HD, int ch,
+                                            float* xk, float* xv) {
+    long row[kDeqBatch];
+    row[0] = j;
+#pragma unroll
+    for (int l = 1; l < kDeqBatch; ++l) row[l] = l <= upto ? (long)c.level[l].slot[j] : -1;
+#pragma unroll
+    for (int l = 1; l < kDeqBatch; ++l)
+        if (row[l - 1] < 0) row[l] = -1;
+    uint64_t wk[kDeqBatch], wv[kDeqBatch];
+    float sk[kDeqBatch], sv[kDeqBatch];
+#pragma unroll
+    for (int l = 0; l < kDeqBatch; ++l) {
+        wk[l] = 0;
+        wv[l] = 0;
+        sk[l] = 0.0f;
+        sv[l] = 0.0f;
+        if (row[l] >= 0) {
+            const fl_kv_level& L = c.level[l];
+            const int b = l == 0 ? 8 : L.bits;
+            const long e = row[l] * HD + ch;
+            wk[l] = load_codes8(L.k_codes, e, b);
+            wv[l] = load_codes8(L.v_codes, e, b);
+            sk[l] = L.k_scale[e / c.g];
+            sv[l] = L.v_scale[e / c.g];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        xk[i] = (float)code_at(wk[0], 8, i) * sk[0];
+        xv[i] = (float)code_at(wv[0], 8, i) * sv[0];
+    }
+#pragma unroll
+    for (int l = 1; l < kDeqBatch; ++l) {
+        if (row[l] >= 0) {
+            const int b = c.level[l].bits;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xk[i] += (float)code_at(wk[l], b, i) * sk[l];
+                xv[i] += (float)code_at(wv[l], b, i) * sv[l];
+            }
+        }
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
