@@ -59,6 +59,8 @@ def parse():
                     help="query rows per loop in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="prefill32k: skip the batched-decode measurement attached to the line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -151,11 +153,36 @@ def main():
     if w.kind == "decode":
         if args.generate:
             return bench_generate(args, w, np, torch, fl, synth)
-        return bench_decode(args, w, np, torch, fl, synth)
+        print(json.dumps(bench_decode(args, w, np, torch, fl, synth)), flush=True)
+        return
     if args.sweep:
         return bench_sweep(args, w, np, torch, fl, synth)
     out = bench_prefill(args, w, np, torch, fl, synth, cpu=not args.no_cpu_baseline)
+    if w.name == "prefill32k" and not args.no_decode and args.quant == "absmax":
+        out["decode64x8k"] = decode_summary(args, np, torch, fl, synth)
     print(json.dumps(out), flush=True)
+
+
+def decode_summary(args, np, torch, fl, synth):
+    """The batched-decode workload (64 sequences x 8192 cached tokens, R=4,
+    one new token per sequence through all loops) timed after the prefill
+    measurement, 20 steps after 3 warm-up steps, no CPU baseline: its
+    throughput, per-loop times, the sparse and dense decode kernels' average
+    launch times and the dense kernel's HBM roofline."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    dargs = argparse.Namespace(**vars(args))
+    dargs.steps, dargs.warmup, dargs.no_cpu_baseline = 20, 3, True
+    d = bench_decode(dargs, synth.WORKLOADS["decode64x8k"], np, torch, fl, synth)
+    ks = d["kernels"]
+    return {
+        "metric": d["metric"], "value": d["value"], "unit": d["unit"], "steps": d["steps"],
+        "warmup": d["warmup"], "ms_per_step": d["ms_per_step"], "loops": d["loops"],
+        "sparse_decode_avg_launch_us": ks.get("decode", {}).get("avg_launch_us"),
+        "dense_decode_avg_launch_us": ks.get("decode_dense", {}).get("avg_launch_us"),
+        "kernels": ks, "roofline": d["roofline"],
+    }
 
 
 def lazy_flops(loops, d):
@@ -959,7 +986,7 @@ def bench_decode(args, w, np, torch, fl, synth):
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def bench_generate(args, w, np, torch, fl, synth):
