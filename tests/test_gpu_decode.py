@@ -30,6 +30,10 @@ CASES = {
     "d64_g32": _w(2, 515, 3, 64, 32, (515, 128, 128, 60), seed=12),
     "short37": _w(2, 37, 2, 128, 64, (37, 16, 8, 8), seed=13),
     "unpruned": _w(2, 300, 2, 128, 64, (300, 300, 300), bits=(8, 4, 4), seed=14),
+    # 1200 selected columns: loop 2's sparse pass lists its (column, level)
+    # pairs in LDS, loops 3-4 exceed the pair lists' LDS bound and walk the
+    # levels column by column
+    "wide_k_level_walk": _w(2, 1500, 2, 128, 64, (1500, 1200, 1200, 1200), seed=19),
     # the paper's quantiser (App. E): INT4 asymmetric at every level, keys
     # per channel over 64 (32) consecutive rows of a level (ragged last group)
     "asym_int4_ragged": _w(3, 700, 2, 128, 64, (700, 96, 64, 40), bits=(4, 4, 4, 4), seed=15,
