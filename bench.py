@@ -52,8 +52,8 @@ BLOCK_GEMM_SYMBOL = {"gemm_qkv": "k_gemm_lds<0, 128>", "gemm_gate_up": "k_gemm_l
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k")
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="query rows per loop in the CPU oracle sample")
@@ -265,26 +265,32 @@ def bench_prefill(args, w, np, torch, fl, synth, cpu=True, steps=None):
     fl.fl_timing_enable(2)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
+    # the phases of each step read back after it (GPU event times; the host
+    # waits between steps); figures are medians over the timed steps
     t_start = time.perf_counter()
+    per_step = []
     for s in range(steps):
         step(evs[s])
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        per_step.append(fl.fl_timing_report())
     wall = time.perf_counter() - t_start
     fl.fl_timing_enable(0)
-    ph = fl.fl_timing_report()
     loop_ms = np.array([[evs[s][r].elapsed_time(evs[s][r + 1]) for r in range(R)]
                         for s in range(steps)])
-    ms_per_step = float(np.mean(loop_ms.sum(axis=1)))
+    ms_per_step = float(np.median(loop_ms.sum(axis=1)))
 
-    def phase_ms(r, part):
+    def phase_ms(ph, r, part):
         c, ms = ph.get(f"loop{r}.{part}", (0, 0.0))
-        assert c == steps, f"phase loop{r}.{part}: {c} records for {steps} steps"
-        return ms / steps
+        assert c == 1, f"phase loop{r}.{part}: {c} records in one step"
+        return ms
 
-    a58 = {r: phase_ms(r, "a5-a8") for r in range(2, R + 1)}
-    a14 = {r: phase_ms(r, "a1-a4") for r in range(2, R + 1)}
+    a58_steps = np.array([[phase_ms(ph, r, "a5-a8") for r in range(2, R + 1)] for ph in per_step])
+    a14_steps = np.array([[phase_ms(ph, r, "a1-a4") for r in range(2, R + 1)] for ph in per_step])
+    a58 = {r: float(np.median(a58_steps[:, r - 2])) for r in range(2, R + 1)}
+    a14 = {r: float(np.median(a14_steps[:, r - 2])) for r in range(2, R + 1)}
     lazy_tokens = sum(n_act[1:])
-    a58_ms, a14_ms = sum(a58.values()), sum(a14.values())
+    a58_ms = float(np.median(a58_steps.sum(axis=1))) if R > 1 else 0.0
+    a14_ms = float(np.median(a14_steps.sum(axis=1))) if R > 1 else 0.0
     value = lazy_tokens / (a58_ms / 1e3) if R > 1 else None
 
     # ---- second run of the same steps: every kernel timed ----
@@ -396,13 +402,13 @@ def bench_prefill(args, w, np, torch, fl, synth, cpu=True, steps=None):
                    "bits_per_loop": w.bits, "n_sink": w.n_sink, "dequant": args.mode,
                    "token_stat": args.token_stat, "col_stat": args.col_stat,
                    "quant": args.quant},
-        "value_def": "sum_{r=2..R} n_r / time of steps a5-a8 of loops 2..R",
+        "value_def": "sum_{r=2..R} n_r / time of steps a5-a8 of loops 2..R (median over the timed steps)",
         "a5_a8_ms": {f"loop{r}": round(v, 4) for r, v in a58.items()},
         "a1_a4": dict(ms={f"loop{r}": round(v, 4) for r, v in a14.items()},
                       tokens_per_s=round(lazy_tokens / (a14_ms / 1e3), 1) if a14_ms else None),
         "lazy_loops_tokens_per_s": round(lazy_tokens / ((a14_ms + a58_ms) / 1e3), 1) if R > 1 else None,
         "step_tokens_per_s": round(sum(n_act) / (ms_per_step / 1e3), 1),
-        "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.mean(loop_ms[:, i])), 4),
+        "loops": [dict(r=L["r"], n=L["n"], k=L["k"], ms=round(float(np.median(loop_ms[:, i])), 4),
                        pairs=L["pairs"], rebuilt=L["rebuilt"], colstat=L["colstat"])
                   for i, L in enumerate(loops)],
         "wall_s_timed": round(wall, 4),
@@ -903,7 +909,7 @@ def bench_decode(args, w, np, torch, fl, synth):
     ktab = fl.fl_timing_report()
     loop_ms = np.array([[evs[s_][r].elapsed_time(evs[s_][r + 1]) for r in range(R)]
                         for s_ in range(args.steps)])
-    ms_per_step = float(np.mean(loop_ms.sum(axis=1)))
+    ms_per_step = float(np.median(loop_ms.sum(axis=1)))
 
     # algorithmic bytes per launch
     G = d // g
@@ -981,7 +987,7 @@ def bench_decode(args, w, np, torch, fl, synth):
         "config": {"workload": w.name, "B": B, "N": N, "H": H, "d": d, "R": R, "g": g,
                    "active_per_loop": n_act, "k_per_loop": w.kcols, "bits_per_loop": w.bits,
                    "quant": args.quant},
-        "loops": [dict(r=r + 1, ms=round(float(np.mean(loop_ms[:, r])), 4)) for r in range(R)],
+        "loops": [dict(r=r + 1, ms=round(float(np.median(loop_ms[:, r])), 4)) for r in range(R)],
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -283,6 +283,15 @@ def test_head_dim_64_group_32(mode):
     _chain(w, mode=mode)
 
 
+@pytest.mark.timeout(900)
+def test_layer4k_full_shape():
+    """The 4K layer workload at its own shape: N=4096, 16 x 128, R=4, 820
+    active rows in each later loop, 512 columns including 4 sinks, int8 base
+    and int4 residuals; every index set, code, output row and column
+    statistic against the oracle in lock step."""
+    _chain(synth.WORKLOADS["layer4k"])
+
+
 def test_tiny_in_tile():
     _chain(synth.WORKLOADS["tiny"], mode=fl.FL_DEQ_IN_TILE)
 
