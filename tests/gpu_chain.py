@@ -219,6 +219,14 @@ def compare_chain(w, gres, ores, bits=None, check_codes=True, quant=fl.FL_QUANT_
             # (max-abs, and L2 error relative to the output's norm)
             assert_close(g["out_u"], o["out_u"], f"loop {r} out_u",
                          ref_norm=float(np.linalg.norm(o["out"])))
+            # and relative to its own norm: the subtract form o_prev - sum_S P V
+            # loses digits when O_U is a small share of the output, so the
+            # bound is 5 %, or 3e-3 of the output's norm where O_U is smaller
+            # (measured: median 1 %, at most 8 % where |O_U| = 1.5 % of |out|)
+            own = rel_l2(g["out_u"], o["out_u"])
+            share = np.linalg.norm(o["out_u"]) / max(np.linalg.norm(o["out"]), 1e-30)
+            assert own <= max(5e-2, 3e-3 / max(share, 1e-30)), \
+                f"loop {r} out_u: rel-L2 to its own norm {own:.3e} at |O_U|/|out| = {share:.3e}"
         if o["cstat"] is not None:
             assert g["cstat"] is not None
             assert_close_scaled(g["cstat"], o["cstat"], f"loop {r} cstat")
