@@ -445,16 +445,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         {
         f32x16 s[2];
         __builtin_amdgcn_s_setprio(1);
+        // the two 32-key blocks' chains alternate (each keeps its own order)
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            s[kt] = f32x16{};
-            const int key = 32 * kt + r;
+        for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
+            for (int kt = 0; kt < 2; ++kt) {
+                const int key = 32 * kt + r;
                 const int e = key * D + (((2 * kk + half) ^ swz<KCPR>(key)) << 3);
                 s[kt] = mfma32(*reinterpret_cast<const bf16x8*>(&sK[e]), qf[kk], s[kt]);
             }
-        }
+        sched_reads_ahead16();
         __builtin_amdgcn_s_setprio(0);
         if (p0 + 64 > pf) {
 #pragma unroll
@@ -504,6 +506,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             s[0] = mfma32(*reinterpret_cast<const bf16x8*>(&sK[e]), qf[kk], s[0]);
             s[0] = mfma32(*reinterpret_cast<const bf16x8*>(&sKl[e]), qf[kk], s[0]);
         }
+        sched_reads_ahead16();
         __builtin_amdgcn_s_setprio(0);
         const bool mask = seg ? (p0 - seg1) + 32 > pf1 : p0 + 32 > pf0;
         if (mask) {

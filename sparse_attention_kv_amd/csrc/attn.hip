@@ -652,11 +652,13 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
         // cores while the other runs its softmax (measured 4.15 -> 3.98 ms)
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            s[kt] = f32x16{};
-            const int key = 32 * kt + r;
+        for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+        // the key blocks' chains alternate (each chain keeps its own order)
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int key = 32 * kt + r;
                 const int e = key * D + (((2 * kk + half) ^ swz<KCPR>(key)) << 3);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[0][e]);
                 s[kt] = mfma32(a, qf[kk], s[kt]);
@@ -665,7 +667,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
                     s[kt] = mfma32(al, qf[kk], s[kt]);
                 }
             }
-        }
+        if constexpr (KT == 2 && !X3) sched_reads_ahead16();
         __builtin_amdgcn_s_setprio(0);
         if (p0 + BT > p_full) {
 #pragma unroll

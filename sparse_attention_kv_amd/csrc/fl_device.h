@@ -232,6 +232,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Instruction-order hint for a score block of 16 LDS fragment reads feeding
+// 16 MFMAs (place it after the block, inside the same basic block): four
+// reads first, then one read behind each MFMA, so every read has about three
+// MFMAs' time to land instead of stalling the chain on its own latency.
+__device__ __forceinline__ void sched_reads_ahead16() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
 // ---- LDS-DMA tiles (gfx950) ----
 
 // 16-byte-chunk swizzle of a tile row with CPR chunks: the 16 lanes that one
