@@ -343,13 +343,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     else load_q(P.q, P.q_gathered);
     const long rh = valid ? (long)rowpos * P.H + h : 0;
     // reb: the pass in progress is a cache rebuild (fixed exponent reference
-    // lse_prev, probabilities weighted by 1 - M_U_prev)
+    // lse_prev, probabilities weighted by w = 1 - M_U_prev).  The weight
+    // folds into the reference, p w = 2^(s c2 - (lse_prev2 - log2 w)); a
+    // weight that rounding left at or below zero (M_U_prev >= 1) gives p = 0.
     bool reb = MODE != MODE_ATTN;
-    float lse_prev2 = 0.0f, wgt = 1.0f, mu_prev = 0.0f;
+    float lse_prev2 = 0.0f, mu_prev = 0.0f;
     if (reb && valid) {
-        lse_prev2 = P.lse[rh] * 1.4426950408889634f;
         mu_prev = P.mass_u[rh];
-        wgt = 1.0f - mu_prev;
+        const float wgt = 1.0f - mu_prev;
+        lse_prev2 = P.lse[rh] * 1.4426950408889634f - (wgt > 0.0f ? __log2f(wgt) : -INFINITY);
     }
 
     const long koff = (long)h * P.kp * D;
@@ -474,7 +476,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 float pj = __builtin_amdgcn_exp2f(fmaf(s[kt][j], P.c2, -m_use));
-                if (reb) pj *= wgt;
                 pb[kt][j >> 3][j & 7] = (__bf16)pj;
                 l_run += pj;
             }
@@ -521,7 +522,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             float pj = __builtin_amdgcn_exp2f(fmaf(s[0][j], P.c2, -m_use));
-            if (reb) pj *= wgt;
             const __bf16 hi = (__bf16)pj;
             pb[j >> 3][j & 7] = hi;
             if (FULL) pl[j >> 3][j & 7] = (__bf16)(pj - (float)hi);
