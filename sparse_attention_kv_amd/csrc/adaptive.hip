@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = max_xor32(tmax);
         const float m_new = fmaxf(m_run, tmax * P.c2);
         // lazy exponent reference: rescale only when some row's max passes
         // it by more than 8 (log2 units); the result does not depend on it

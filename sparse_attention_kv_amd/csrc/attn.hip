@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_xor32(tmax);
             const float m_new = fmaxf(m_run, tmax * P.c2);
             // The exponent reference m_run follows the running max lazily:
             // it moves (with a rescale of l and O) only when some row's max
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[kt][j]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_xor32(tmax);
             const float m_new = fmaxf(m_run, tmax * P.c2);
             // lazy exponent reference, as in k_attn
             if (__ballot(m_new > m_run + 8.0f)) {

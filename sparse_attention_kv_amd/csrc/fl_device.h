@@ -232,6 +232,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// max of a value over lanes l and l ^ 32: gfx950's cross-half lane swap
+// (no LDS round trip); the pair's two halves hold x_l and x_{l^32} as a set
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Instruction-order hint for a score block of 16 LDS fragment reads feeding
 // 16 MFMAs (place it after the block, inside the same basic block): four
 // reads first, then one read behind each MFMA, so every read has about three
