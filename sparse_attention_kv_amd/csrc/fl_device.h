@@ -169,20 +169,25 @@ inline bool deq_batch_ok(const fl_kv_cache& c, int upto) {
         if (c.level[l].bits == 32 || (l == 0 && c.level[l].bits != 8)) return false;
     return true;
 }
-// requires deq_batch_ok(c, upto)
+// register slots per side for deq_col8_kv over levels 0..upto
+inline int deq_batch_slots(int upto) { return upto < 4 ? upto + 1 : kDeqBatch; }
+// requires deq_batch_ok(c, upto) and upto < NB (NB <= kDeqBatch register
+// slots per side: the caller picks the smallest that holds its levels)
+template <int NB>
 __device__ __forceinline__ void deq_col8_kv(const fl_kv_cache& c, int upto, long j, int HD, int ch,
                                             float* xk, float* xv) {
-    long row[kDeqBatch];
+    static_assert(NB >= 1 && NB <= kDeqBatch, "level slots");
+    long row[NB];
     row[0] = j;
 #pragma unroll
-    for (int l = 1; l < kDeqBatch; ++l) row[l] = l <= upto ? (long)c.level[l].slot[j] : -1;
+    for (int l = 1; l < NB; ++l) row[l] = l <= upto ? (long)c.level[l].slot[j] : -1;
 #pragma unroll
-    for (int l = 1; l < kDeqBatch; ++l)
+    for (int l = 1; l < NB; ++l)
         if (row[l - 1] < 0) row[l] = -1;
-    uint64_t wk[kDeqBatch], wv[kDeqBatch];
-    float sk[kDeqBatch], sv[kDeqBatch];
+    uint64_t wk[NB], wv[NB];
+    float sk[NB], sv[NB];
 #pragma unroll
-    for (int l = 0; l < kDeqBatch; ++l) {
+    for (int l = 0; l < NB; ++l) {
         wk[l] = 0;
         wv[l] = 0;
         sk[l] = 0.0f;
@@ -203,7 +208,7 @@ __device__ __forceinline__ void deq_col8_kv(const fl_kv_cache& c, int upto, long
         xv[i] = (float)code_at(wv[0], 8, i) * sv[0];
     }
 #pragma unroll
-    for (int l = 1; l < kDeqBatch; ++l) {
+    for (int l = 1; l < NB; ++l) {
         if (row[l] >= 0) {
             const int b = c.level[l].bits;
 #pragma unroll
