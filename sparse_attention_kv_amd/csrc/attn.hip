@@ -52,15 +52,15 @@ __device__ __forceinline__ int vt_key_of_slot(int so) {
 // workgroup covers GC = 2048/D columns -- one or two of the 16-key groups of
 // the transposed V tile, which it writes on its own; a column's dequantisation
 // chain walks the levels in order, stopping at the first one the token is
-// absent from (the sets are nested).  NB > 0: every level's slot, then
-// every level's codes and scales, loaded together (deq_col8_kv with NB
-// register slots per side); small NB keeps the kernel at eight waves per
-// SIMD, so a whole gather's workgroups are resident at once.
+// absent from (the sets are nested).  NB > 0: the levels in chunks of NB,
+// each chunk's slots, then its codes and scales, loaded together
+// (deq_col8_kv); the kernel then stays at eight waves per SIMD, so a whole
+// gather's workgroups are resident at once.
 template <int D>
 constexpr int gather_cols() { return 256 / (D / 8); }
 
 template <int D, bool X3, int NB>
-__global__ __launch_bounds__(256, NB <= 4 ? 8 : 7) void k_gather_bf16(fl_kv_cache c, int upto,
+__global__ __launch_bounds__(256, 8) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      const int32_t* __restrict__ sel, int k,
                                                      int kp, __bf16* __restrict__ Kc,
                                                      __bf16* __restrict__ Vt,
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(256, NB <= 4 ? 8 : 7) void k_gather_bf16(fl_kv_cach
         xkv[0][e] = 0.0f;
         xkv[1][e] = 0.0f;
     }
-    if constexpr (NB > 0) {
-        if (live) deq_col8_kv<NB>(c, upto, j, HD, ch, xkv[0], xkv[1]);
+    if constexpr (NB > 0) {  // NB > kDeqBatch: chunks of kDeqBatch
+        if (live) deq_col8_kv<NB <= kDeqBatch ? NB : kDeqBatch, (NB > kDeqBatch)>(c, upto, j, HD, ch, xkv[0], xkv[1]);
     }
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
@@ -1133,7 +1133,8 @@ hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel
                               int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st) {
     dim3 grid(kp / (c.d == 128 ? gather_cols<128>() : gather_cols<64>()), c.H);
     // the keys' and values' level rows loaded together where the cache allows
-    const int nb = deq_batch_ok(c, upto) ? deq_batch_slots(upto) : 0;
+    // (kDeqBatch + 1: levels in several chunks)
+    const int nb = !deq_batch_ok(c, upto) ? 0 : upto < kDeqBatch ? upto + 1 : kDeqBatch + 1;
 #define FL_GATHER(D_, X_, B_)                                                                       \
     hipLaunchKernelGGL((k_gather_bf16<D_, X_, B_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
                        Vt, Kc_lo, Vt_lo, cpos, vnorm, perm)
@@ -1143,7 +1144,7 @@ hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel
         case 2: FL_GATHER(D_, X_, 2); break;                                    \
         case 3: FL_GATHER(D_, X_, 3); break;                                    \
         case 4: FL_GATHER(D_, X_, 4); break;                                    \
-        case kDeqBatch: FL_GATHER(D_, X_, kDeqBatch); break;                    \
+        case 5: FL_GATHER(D_, X_, 5); break;                                    \
         default: FL_GATHER(D_, X_, 0);                                          \
         } }
     if (c.d == 128) { if (x3) FL_GATHER_B(128, true) else FL_GATHER_B(128, false) }

@@ -157,67 +157,80 @@ __device__ __forceinline__ void deq_col8(const fl_kv_cache& c, int upto, int whi
 }
 
 // deq_col8 for the key and the value of one column together, for absmax
-// caches of at most kDeqBatch levels with an int8 base and no fp32 levels
-// (deq_batch_ok): every level's slot in one round of loads, then every
-// present level's K and V codes and scales in one more, instead of a
-// slot-then-codes round trip per level and side.  The sums keep deq_col8's
-// level order and its stop at the first absent level.
-constexpr int kDeqBatch = 8;
+// caches with an int8 base and no fp32 levels (deq_batch_ok): the levels go
+// in chunks of NB, each chunk's slots in one round of loads and its present
+// levels' K and V codes and scales in one more, instead of a slot-then-codes
+// round trip per level and side.  The sums keep deq_col8's level order and
+// its stop at the first absent level.
+constexpr int kDeqBatch = 4;
 inline bool deq_batch_ok(const fl_kv_cache& c, int upto) {
-    if (c.scheme == FL_QUANT_ASYM || upto >= kDeqBatch) return false;
+    if (c.scheme == FL_QUANT_ASYM) return false;
     for (int l = 0; l <= upto; ++l)
         if (c.level[l].bits == 32 || (l == 0 && c.level[l].bits != 8)) return false;
     return true;
 }
-// register slots per side for deq_col8_kv over levels 0..upto
-inline int deq_batch_slots(int upto) { return upto < 4 ? upto + 1 : kDeqBatch; }
-// requires deq_batch_ok(c, upto) and upto < NB (NB <= kDeqBatch register
-// slots per side: the caller picks the smallest that holds its levels)
-template <int NB>
-__device__ __forceinline__ void deq_col8_kv(const fl_kv_cache& c, int upto, long j, int HD, int ch,
-                                            float* xk, float* xv) {
-    static_assert(NB >= 1 && NB <= kDeqBatch, "level slots");
+
+// one chunk: levels l0..l0+NB-1 (those <= upto and present) added to x, or
+// with l0 == 0 the base level written first; returns false once a level of
+// the chunk is absent (all later ones are too)
+template <int NB, bool BASE>
+__device__ __forceinline__ bool deq_chunk_kv(const fl_kv_cache& c, int upto, int l0, long j, int HD, int ch,
+                                             float* xk, float* xv) {
     long row[NB];
-    row[0] = j;
 #pragma unroll
-    for (int l = 1; l < NB; ++l) row[l] = l <= upto ? (long)c.level[l].slot[j] : -1;
+    for (int u = 0; u < NB; ++u)
+        row[u] = (BASE && u == 0) ? j : (l0 + u <= upto ? (long)c.level[l0 + u].slot[j] : -1);
 #pragma unroll
-    for (int l = 1; l < NB; ++l)
-        if (row[l - 1] < 0) row[l] = -1;
+    for (int u = 1; u < NB; ++u)
+        if (row[u - 1] < 0) row[u] = -1;
     uint64_t wk[NB], wv[NB];
     float sk[NB], sv[NB];
 #pragma unroll
-    for (int l = 0; l < NB; ++l) {
-        wk[l] = 0;
-        wv[l] = 0;
-        sk[l] = 0.0f;
-        sv[l] = 0.0f;
-        if (row[l] >= 0) {
-            const fl_kv_level& L = c.level[l];
-            const int b = l == 0 ? 8 : L.bits;
-            const long e = row[l] * HD + ch;
-            wk[l] = load_codes8(L.k_codes, e, b);
-            wv[l] = load_codes8(L.v_codes, e, b);
-            sk[l] = L.k_scale[e / c.g];
-            sv[l] = L.v_scale[e / c.g];
+    for (int u = 0; u < NB; ++u) {
+        wk[u] = 0;
+        wv[u] = 0;
+        sk[u] = 0.0f;
+        sv[u] = 0.0f;
+        if (row[u] >= 0) {
+            const fl_kv_level& L = c.level[l0 + u];
+            const int b = (BASE && u == 0) ? 8 : L.bits;
+            const long e = row[u] * HD + ch;
+            wk[u] = load_codes8(L.k_codes, e, b);
+            wv[u] = load_codes8(L.v_codes, e, b);
+            sk[u] = L.k_scale[e / c.g];
+            sv[u] = L.v_scale[e / c.g];
+        }
+    }
+    if constexpr (BASE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            xk[i] = (float)code_at(wk[0], 8, i) * sk[0];
+            xv[i] = (float)code_at(wv[0], 8, i) * sv[0];
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        xk[i] = (float)code_at(wk[0], 8, i) * sk[0];
-        xv[i] = (float)code_at(wv[0], 8, i) * sv[0];
-    }
-#pragma unroll
-    for (int l = 1; l < NB; ++l) {
-        if (row[l] >= 0) {
-            const int b = c.level[l].bits;
+    for (int u = BASE ? 1 : 0; u < NB; ++u) {
+        if (row[u] >= 0) {
+            const int b = c.level[l0 + u].bits;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                xk[i] += (float)code_at(wk[l], b, i) * sk[l];
-                xv[i] += (float)code_at(wv[l], b, i) * sv[l];
+                xk[i] += (float)code_at(wk[u], b, i) * sk[u];
+                xv[i] += (float)code_at(wv[u], b, i) * sv[u];
             }
         }
     }
+    return row[NB - 1] >= 0;
+}
+
+// requires deq_batch_ok(c, upto); one chunk of NB = upto + 1 levels, or
+// (CHUNKS) chunks of NB = kDeqBatch
+template <int NB, bool CHUNKS>
+__device__ __forceinline__ void deq_col8_kv(const fl_kv_cache& c, int upto, long j, int HD, int ch,
+                                            float* xk, float* xv) {
+    static_assert(NB >= 1 && NB <= kDeqBatch, "levels per chunk");
+    bool more = deq_chunk_kv<NB, true>(c, upto, 0, j, HD, ch, xk, xv);
+    if constexpr (CHUNKS)
+        for (int l0 = NB; more && l0 <= upto; l0 += NB) more = deq_chunk_kv<NB, false>(c, upto, l0, j, HD, ch, xk, xv);
 }
 
 template <typename T>
