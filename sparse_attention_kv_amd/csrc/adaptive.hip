@@ -71,7 +71,7 @@ __device__ __forceinline__ int block_scan_1024(int v, int* sh, int* total) {
 //    pairs, so the query reads coalesce).
 // The flag planes have 16-byte aligned rows (strides cstride, rstride).
 constexpr int kRowItems = 4;
-template <int D>
+template <int D, int NB>
 __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, const int32_t* __restrict__ sel,
                                                      int k, int ncolblk, float tau_col,
                                                      const uint8_t* __restrict__ cls,
@@ -102,15 +102,19 @@ __global__ __launch_bounds__(256) void k_class_flags(fl_kv_cache c, int upto, co
         float m = 0.0f;
         if (live) {
             const long j = sel ? sel[(long)h * k + p] : p;
+            float x[2][8];
 #pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                float x[8];
+            for (int e = 0; e < 8; ++e) x[0][e] = x[1][e] = 0.0f;
+            if constexpr (NB > 0)  // the gather's batched level walk (NB > kDeqBatch: chunks)
+                deq_col8_kv<NB <= kDeqBatch ? NB : kDeqBatch, (NB > kDeqBatch)>(c, upto, j, H * D, h * D + c0,
+                                                                                 x[0], x[1]);
+            else
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-                deq_col8(c, upto, which, j, H * D, h * D + c0, x);
+                for (int which = 0; which < 2; ++which) deq_col8(c, upto, which, j, H * D, h * D + c0, x[which]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) m = amax(m, x[e]);
-            }
+            for (int which = 0; which < 2; ++which)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = amax(m, x[which][e]);
         }
 #pragma unroll
         for (int o = 1; o < TPC; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -771,12 +775,23 @@ hipError_t launch_classify(const fl_kv_cache& c, int upto, const int32_t* sel, i
     const int nrowblk = (int)(((long)n * H + 16 * kRowItems - 1) / (16 * kRowItems));
     const unsigned nblk = (unsigned)(ncolblk + nrowblk);
     const int cstride = kp, rstride = (int)class_row_stride(n);
-    if (c.d == 128)
-        hipLaunchKernelGGL(k_class_flags<128>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           cls, colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
-    else
-        hipLaunchKernelGGL(k_class_flags<64>, dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, tau_col,
-                           cls, colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride);
+    // the columns' level walk: batched as in the gather where the cache allows
+    const int nb = cls || !deq_batch_ok(c, upto) ? 0 : upto < kDeqBatch ? upto + 1 : kDeqBatch + 1;
+#define FL_FLAGS(D_, NB_)                                                                             \
+    hipLaunchKernelGGL((k_class_flags<D_, NB_>), dim3(nblk), dim3(256), 0, st, c, upto, sel, k, ncolblk, \
+                       tau_col, cls, colflags, cstride, q, dtype, q_gathered, active, n, tau_row, rowflags, rstride)
+#define FL_FLAGS_B(D_) {                                                       \
+        switch (nb) {                                                          \
+        case 1: FL_FLAGS(D_, 1); break;                                        \
+        case 2: FL_FLAGS(D_, 2); break;                                        \
+        case 3: FL_FLAGS(D_, 3); break;                                        \
+        case 4: FL_FLAGS(D_, 4); break;                                        \
+        case 5: FL_FLAGS(D_, 5); break;                                        \
+        default: FL_FLAGS(D_, 0);                                              \
+        } }
+    if (c.d == 128) FL_FLAGS_B(128) else FL_FLAGS_B(64)
+#undef FL_FLAGS_B
+#undef FL_FLAGS
     hipLaunchKernelGGL(k_class_scan, dim3(2 * H), dim3(1024), 0, st, colflags, k, cstride, kp, perm, colseg,
                        rowflags, n, rstride, H, rowperm, rowseg);
     return hipGetLastError();
