@@ -300,10 +300,22 @@ __global__ __launch_bounds__(NT) void k_topk_res(
             const int shift = 24 - 8 * pass;
             for (int b = tid; b < 256; b += NT) s_hist[b] = 0;
             __syncthreads();
+            // a run's keys mostly share their leading bytes: count equal
+            // consecutive bins in a register and add each count once (the
+            // LDS atomics on one bin from a whole wave serialise)
+            int cur = -1, cnt = 0;
 #pragma unroll
             for (int e = 0; e < kRes; ++e)
-                if (((ranked >> e) & 1u) && (u[e] & pmask) == prefix)
-                    atomicAdd(&s_hist[(u[e] >> shift) & 255], 1);
+                if (((ranked >> e) & 1u) && (u[e] & pmask) == prefix) {
+                    const int b = (u[e] >> shift) & 255;
+                    if (b != cur) {
+                        if (cnt) atomicAdd(&s_hist[cur], cnt);
+                        cur = b;
+                        cnt = 0;
+                    }
+                    ++cnt;
+                }
+            if (cnt) atomicAdd(&s_hist[cur], cnt);
             __syncthreads();
             if (tid < 64) {
                 int c[4], lsum = 0;
