@@ -202,6 +202,30 @@ __global__ __launch_bounds__(1024) void k_class_scan(const uint8_t* __restrict__
                 }
         }
     };
+    if (len <= CH) {  // one pass: one read of the flags, one scan
+        uint32_t outl, live;
+        run(0, outl, live);
+        int n_norm;
+        int in_ = block_scan_1024(__popc(live & ~outl), sh, &n_norm);
+        const int seg1 = cols ? (n_norm + 63) / 64 * 64 : n_norm;
+        // (the scan's barriers order the -1 fill before these writes)
+        int io = seg1 + (min(tid * E, len) - in_);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            if (!((live >> i) & 1u)) continue;
+            if ((outl >> i) & 1u) out[io++] = tid * E + i;
+            else out[in_++] = tid * E + i;
+        }
+        if (tid == 0) {
+            if (cols) {
+                colseg[2 * h] = n_norm;
+                colseg[2 * h + 1] = len - n_norm;
+            } else {
+                rowseg[h] = n_norm;
+            }
+        }
+        return;
+    }
     int cnt = 0;
     for (int base = 0; base < len; base += CH) {
         uint32_t outl, live;
