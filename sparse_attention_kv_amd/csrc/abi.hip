@@ -508,8 +508,9 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
     const int prec_old = attn_prec(a->dtype, a->level - 1);
     // FL_DEQ_AUTO resolves to FL_DEQ_ONCE: on the 32K, 4-loop workload the
     // in-tile placement repeats the dequantisation for every 128-row query
-    // tile and measured 1.6-2x slower on the sparse loops (20.9 vs 18.2 ms
-    // per step).
+    // tile and, with both on the LDS-DMA pipeline, measured 1.9x slower on
+    // the dense loop (7.67 vs 4.11 ms) and 3.1x on the sparse loops' steps
+    // a5-a8 (2.54 vs 0.82 ms).
     const bool in_tile = a->mode == FL_DEQ_IN_TILE;
     if (in_tile && cache->scheme != FL_QUANT_ABSMAX)
         return fail(FL_ERR_UNSUPPORTED, "FL_DEQ_IN_TILE needs a FL_QUANT_ABSMAX cache");

@@ -16,6 +16,12 @@
 //                   MODE_ATTN: online softmax, o = (1-M_U) o~ / l + O_U, lse.
 //                   MODE_REBUILD: the previous loop's probabilities with its
 //                   known lse: M_U = 1 - sum P_prev, O_U = o_prev - sum P_prev V.
+//   k_attn_lds      the same attention over compact bf16 tiles copied by
+//                   LDS-DMA into two buffers (the dequantise-once placement);
+//   k_attn_lds_dq   its in-tile variant: each tile's quantised planes are
+//                   copied into a staging buffer and expanded by the
+//                   workgroup into the operand tile (Sec. 4.4 fuses the cache
+//                   into the attention kernel).
 //   k_colstat       column statistics c(j) = sum_i (1-M_U(i)) exp(s - lse(i))
 //                   for the next loop's column ranking: one workgroup = 128
 //                   selected columns (a wave keeps its 32 columns' keys in
@@ -554,8 +560,17 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnParams P) {
 // copies into the other.  Arithmetic as k_attn (PREC 0/1, DEQ off).
 constexpr int kAttnLdsSplit = 1;  // PREC value routed to the LDS-DMA kernel besides 0
 
-template <int D, int MODE, int PREC, int BT>
-__global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2 : 1)) void k_attn_lds(AttnParams P) {
+// With DQ (the in-tile dequantisation placement) the tiles arrive as the
+// compact quantised planes of every level (codes and fp32 scales, as written
+// by k_gather_q): each tile's planes are copied by LDS-DMA into one staging
+// buffer while the previous tile is computed, and the workgroup then
+// dequantises them cooperatively (levels summed in order, rounded to bf16,
+// plus the lo part with PREC 1) into a single operand tile in the layout
+// the MFMA fragment reads expect; two barriers per tile.
+constexpr int kDqCap = 40960;  // staging bytes of one tile's planes (all levels, K and V)
+
+template <int D, int MODE, int PREC, int BT, bool DQ>
+__device__ __forceinline__ void attn_lds_body(AttnParams P) {
     static_assert(PREC == 0 || PREC == 1, "bf16 queries only");
     constexpr bool X3 = PREC >= 1;
     constexpr int NP = X3 ? 2 : 1;
@@ -565,8 +580,10 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
     constexpr int MPW = TB / 1024 / 4;      // LDS-DMA instructions per wave per operand tile
     __shared__ __attribute__((aligned(1024))) __bf16 sK0[NP][BT * D];
     __shared__ __attribute__((aligned(1024))) __bf16 sV0[NP][D * BT];
-    __shared__ __attribute__((aligned(1024))) __bf16 sK1[NP][BT * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV1[NP][D * BT];
+    // DQ: one operand tile; the second buffer is the planes' staging area
+    __shared__ __attribute__((aligned(1024))) __bf16 sK1[DQ ? 1 : NP][DQ ? 8 : BT * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[DQ ? 1 : NP][DQ ? 8 : D * BT];
+    __shared__ __attribute__((aligned(1024))) char sQ[DQ ? kDqCap : 16];
     __shared__ __attribute__((aligned(256))) int sC0[64];
     __shared__ __attribute__((aligned(256))) int sC1[64];
     __shared__ int s_bounds[2];
@@ -735,6 +752,130 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
         for (int kt = 0; kt < KT; ++kt) pvb(kt);
     };
 
+    if constexpr (DQ) {
+        // the staging buffer holds, level by level: K codes [BT][D] (b bits
+        // each), K scales [BT][G], V codes [D][BT] (key order of the V^T
+        // operand), V scales [G][BT]
+        const int nl = P.deq_levels, g = P.qt.g, G = D / g;
+        const int nt = P.kp / BN;
+        // copy `rows` rows of `rb` bytes (rb a power of two, a multiple of 4)
+        // found `stride` bytes apart into consecutive staging bytes; 16-byte
+        // copies where rows allow, else 4-byte ones; the waves take turns
+        auto stage_rows = [&](__amdgpu_buffer_rsrc_t rs, uint32_t soff, int rows, int rb, uint32_t stride,
+                              uint32_t dst) {
+            const int gs = rb % 16 == 0 ? 16 : 4;
+            const int lrg = __builtin_ctz(rb / gs);
+            const int total = rows << lrg;
+            for (int base = w * 64; base < total; base += 256) {
+                const int i = base + lane;
+                if (i < total) {
+                    const uint32_t src = (uint32_t)(i >> lrg) * stride + (uint32_t)(i & ((1 << lrg) - 1)) * gs;
+                    if (gs == 16) buf_dma16(rs, sQ + dst + base * 16, src, soff);
+                    else buf_dma4(rs, sQ + dst + base * 4, src, soff);
+                }
+            }
+        };
+        auto issue_q = [&](int p0, int* sC) {
+            uint32_t off = 0;
+            for (int l = 0; l < nl; ++l) {
+                const int b = P.qt.bits[l];
+                const int cb = BT * D * b / 8, sb = BT * G * 4;
+                const long hk = (long)h * P.kp;
+                const __amdgpu_buffer_rsrc_t rkq = make_rsrc(P.qt.kq[l] + hk * D * b / 8, (uint32_t)P.kp * D * b / 8);
+                const __amdgpu_buffer_rsrc_t rks = make_rsrc(P.qt.ks[l] + hk * G, (uint32_t)P.kp * G * 4);
+                const __amdgpu_buffer_rsrc_t rvq =
+                    make_rsrc(P.qt.vq[l] + (long)h * nt * D * BN * b / 8, (uint32_t)P.kp * D * b / 8);
+                const __amdgpu_buffer_rsrc_t rvs = make_rsrc(P.qt.vs[l] + (long)h * nt * G * BN, (uint32_t)P.kp * G * 4);
+                stage_rows(rkq, (uint32_t)p0 * D * b / 8, 1, cb, 0, off);
+                off += cb;
+                stage_rows(rks, (uint32_t)p0 * G * 4, 1, sb, 0, off);
+                off += sb;
+                stage_rows(rvq, ((uint32_t)(p0 / BN) * D * BN + p0 % BN) * b / 8, D, BT * b / 8, BN * b / 8, off);
+                off += cb;
+                stage_rows(rvs, ((uint32_t)(p0 / BN) * G * BN + p0 % BN) * 4, G, BT * 4, BN * 4, off);
+                off += sb;
+            }
+            if (w == 0 && lane < BT) buf_dma4(rC, sC, lane * 4, p0 * 4);
+        };
+        // the staged levels summed in order into the operand tile (bf16 hi,
+        // and the bf16 rounding of the remainder as lo with PREC 1)
+        auto dequant = [&]() {
+#pragma unroll
+            for (int it = tid; it < BT * (D / 8); it += 256) {
+                const int key = it / (D / 8), c8 = it % (D / 8);
+                float x[8];
+                uint32_t off = 0;
+                for (int l = 0; l < nl; ++l) {
+                    const int b = P.qt.bits[l];
+                    const int cb = BT * D * b / 8;
+                    const float sc = *reinterpret_cast<const float*>(sQ + off + cb + (key * G + c8 * 8 / g) * 4);
+                    const int e = key * D + c8 * 8;
+                    const uint64_t wd = b == 8 ? *reinterpret_cast<const uint64_t*>(sQ + off + e)
+                                      : b == 4 ? *reinterpret_cast<const uint32_t*>(sQ + off + e / 2)
+                                               : *reinterpret_cast<const uint16_t*>(sQ + off + e / 4);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float t = (float)code_at(wd, b, i) * sc;
+                        x[i] = l == 0 ? t : x[i] + t;
+                    }
+                    off += 2 * (cb + BT * G * 4);
+                }
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hi[i] = (__bf16)x[i];
+                    if (X3) lo[i] = (__bf16)(x[i] - (float)hi[i]);
+                }
+                const int ep = key * D + ((c8 ^ swz<KCPR>(key)) << 3);
+                *reinterpret_cast<bf16x8*>(&sK0[0][ep]) = hi;
+                if (X3) *reinterpret_cast<bf16x8*>(&sK0[NP - 1][ep]) = lo;
+            }
+#pragma unroll
+            for (int it = tid; it < D * (BT / 8); it += 256) {
+                const int dd = it / (BT / 8), oc = it % (BT / 8);
+                float y[8];
+                uint32_t off = 0;
+                for (int l = 0; l < nl; ++l) {
+                    const int b = P.qt.bits[l];
+                    const int cb = BT * D * b / 8, sb = BT * G * 4;
+                    const int e = dd * BT + oc * 8;
+                    const char* vc = sQ + off + cb + sb;
+                    const uint64_t wd = b == 8 ? *reinterpret_cast<const uint64_t*>(vc + e)
+                                      : b == 4 ? *reinterpret_cast<const uint32_t*>(vc + e / 2)
+                                               : *reinterpret_cast<const uint16_t*>(vc + e / 4);
+                    const float4* sp =
+                        reinterpret_cast<const float4*>(sQ + off + 2 * cb + sb + ((dd / g) * BT + oc * 8) * 4);
+                    const float4 s0 = sp[0], s1 = sp[1];
+                    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float t = (float)code_at(wd, b, i) * sc[i];
+                        y[i] = l == 0 ? t : y[i] + t;
+                    }
+                    off += 2 * (cb + sb);
+                }
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hi[i] = (__bf16)y[i];
+                    if (X3) lo[i] = (__bf16)(y[i] - (float)hi[i]);
+                }
+                const int ep = dd * BT + ((oc ^ swz<VCPR>(dd)) << 3);
+                *reinterpret_cast<bf16x8*>(&sV0[0][ep]) = hi;
+                if (X3) *reinterpret_cast<bf16x8*>(&sV0[NP - 1][ep]) = lo;
+            }
+        };
+        if (p_end > 0) issue_q(0, sC0);
+        for (int p0 = 0; p0 < p_end; p0 += BT) {
+            const bool odd = (p0 / BT) & 1;
+            __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the tile's planes landed
+            __syncthreads();               // ... every lane's; the operand tile is free
+            dequant();
+            __syncthreads();               // operand tile complete; the staging buffer is free
+            if (p0 + BT < p_end) issue_q(p0 + BT, odd ? sC0 : sC1);
+            compute(p0, sK0, sV0, odd ? sC1 : sC0);
+        }
+    } else {
     if (p_end > 0) issue(0, sK0, sV0, sC0);
     for (int p0 = 0; p0 < p_end;) {
         __builtin_amdgcn_s_waitcnt(0); // this lane's copies of the current tile landed
@@ -748,6 +889,7 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
         if (p0 + BT < p_end) issue(p0 + BT, sK0, sV0, sC0);
         compute(p0, sK1, sV1, sC1);
         p0 += BT;
+    }
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -813,6 +955,17 @@ __global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2
             }
         if (half == 0) P.mass_u[rh] = 1.0f - l_tot;
     }
+}
+
+template <int D, int MODE, int PREC, int BT>
+__global__ __launch_bounds__(256, PREC == 0 ? (BT == 32 ? 3 : 2) : (BT == 32 ? 2 : 1)) void k_attn_lds(AttnParams P) {
+    attn_lds_body<D, MODE, PREC, BT, false>(P);
+}
+
+// in-tile dequantisation over the same pipeline (see attn_lds_body)
+template <int D, int MODE, int PREC, int BT>
+__global__ __launch_bounds__(256, 2) void k_attn_lds_dq(AttnParams P) {
+    attn_lds_body<D, MODE, PREC, BT, true>(P);
 }
 
 // ---------------------------------------------------------------------------
@@ -1171,6 +1324,17 @@ hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, i
 // 0.87 ms for the 32K sparse loops)
 static bool lds_path(int prec) { return prec == 0 || prec == kAttnLdsSplit; }
 
+// in-tile placement: the LDS-DMA kernel takes bf16 queries (PREC 0 / 1) when
+// one tile's planes of every level fit its staging buffer; deeper caches and
+// fp32 queries use the register-staged kernel
+static bool dq_lds_fits(int d, int prec, const AttnParams& P) {
+    if (prec > 1) return false;
+    const int bt = prec == 0 ? 64 : 32, G = d / P.qt.g;
+    long bytes = 0;
+    for (int l = 0; l < P.deq_levels; ++l) bytes += 2L * ((long)bt * d * P.qt.bits[l] / 8 + (long)bt * G * 4);
+    return bytes <= kDqCap;
+}
+
 hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams& P, hipStream_t st) {
     const int n_tiles = (P.n + BM - 1) / BM;
     AttnParams Q = P;
@@ -1179,8 +1343,10 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
 #define FL_ATTN(D_, M_, P_, Q_) hipLaunchKernelGGL((k_attn<D_, M_, P_, Q_>), grid, dim3(256), 0, st, Q)
 #define FL_ATTN_LDS(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds<D_, M_, P_, P_ == 0 ? 64 : 32>), grid, dim3(256), 0, st, Q)
     // bf16 queries over compact bf16 tiles: the LDS-DMA pipelined kernel
+#define FL_ATTN_DQ(D_, M_, P_) hipLaunchKernelGGL((k_attn_lds_dq<D_, M_, P_, P_ == 0 ? 64 : 32>), grid, dim3(256), 0, st, Q)
 #define FL_ATTN_Q(D_, M_, P_)                                   \
-    if (in_tile) FL_ATTN(D_, M_, P_, true);                    \
+    if (in_tile && P_ <= 1 && dq_lds_fits(D_, P_, Q)) FL_ATTN_DQ(D_, M_, (P_ <= 1 ? P_ : 0)); \
+    else if (in_tile) FL_ATTN(D_, M_, P_, true);               \
     else if (P_ <= 1 && lds_path(P_)) FL_ATTN_LDS(D_, M_, (P_ <= 1 ? P_ : 0)); \
     else FL_ATTN(D_, M_, P_, false);
 #define FL_ATTN_M(D_, M_) \
@@ -1192,6 +1358,7 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
 #undef FL_ATTN_M
 #undef FL_ATTN_Q
 #undef FL_ATTN_LDS
+#undef FL_ATTN_DQ
 #undef FL_ATTN
     return hipGetLastError();
 }
