@@ -447,6 +447,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    if constexpr (RB) {
+        // the rebuild pass accumulates onto -o_prev (its exponent reference
+        // is fixed, so the accumulators are never rescaled): it ends holding
+        // -O_U, and the previous output's loads overlap the first tiles
+        if (valid) {
+            const float* orow_prev = P.out + rh * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq) {
+                    const float4 op = *reinterpret_cast<const float4*>(orow_prev + 32 * dt + jq * 8 + half * 4);
+                    o[dt][4 * jq + 0] = -op.x;
+                    o[dt][4 * jq + 1] = -op.y;
+                    o[dt][4 * jq + 2] = -op.z;
+                    o[dt][4 * jq + 3] = -op.w;
+                }
+        }
+    }
     float m_run = -INFINITY, l_run = 0.0f;
 
     // online softmax over one 32-column block's scores (shared by both kinds)
@@ -605,26 +623,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
             compute_plain(64 * i, pfA, sK1, sV1, sC1);
             ++i;
         }
+        // the attention pass's queries: loads in flight during the stores
+        load_q(P.q, P.q_gathered);
         const float l_a = l_run + __shfl_xor(l_run, 32);
         mu_rb = 1.0f - l_a;
         if (valid) {
-            const float* orow_prev = P.out + rh * D;
             float* ourow = P.out_u + rh * D;
-            float4 bc[D / 32][4];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                 for (int jq = 0; jq < 4; ++jq)
-                    bc[dt][jq] = *reinterpret_cast<const float4*>(orow_prev + 32 * dt + jq * 8 + half * 4);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int jq = 0; jq < 4; ++jq) {
-                    const float4 op = bc[dt][jq];
                     *reinterpret_cast<float4*>(ourow + 32 * dt + jq * 8 + half * 4) =
-                        make_float4(op.x - o[dt][4 * jq + 0], op.y - o[dt][4 * jq + 1],
-                                    op.z - o[dt][4 * jq + 2], op.w - o[dt][4 * jq + 3]);
-                }
+                        make_float4(-o[dt][4 * jq + 0], -o[dt][4 * jq + 1], -o[dt][4 * jq + 2],
+                                    -o[dt][4 * jq + 3]);
             if (half == 0) P.mass_u[rh] = mu_rb;
         }
         // the attention pass: its own queries, fresh accumulators
@@ -633,7 +644,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_ad(AttnParams P) {
         l_run = 0.0f;
         m_run = -INFINITY;
         reb = false;
-        load_q(P.q, P.q_gathered);
         __syncthreads();  // every wave is done with the tile buffers
     }
 
