@@ -33,14 +33,18 @@ def _say(*a):
 
 
 @pytest.mark.timeout(900)
-def test_prefill32k_sampled():
+@pytest.mark.parametrize("mode", [fl.FL_DEQ_AUTO, fl.FL_DEQ_IN_TILE], ids=["once", "in_tile"])
+def test_prefill32k_sampled(mode):
+    """Both dequantisation placements: the default (compact bf16 gather,
+    precision-adaptive operands) and in-tile (quantised planes expanded
+    inside the LDS-DMA attention kernel), each as bench.py runs it."""
     w = synth.WORKLOADS["prefill32k"]
-    _say("full-size", w.name, "N", w.N)
+    _say("full-size", w.name, "N", w.N, "mode", mode)
     inp = synth.generate(w)
     x = synth.as_f32_inputs(inp)
     dev = {k: [to_dev(a, "bf16") for a in inp[k]] for k in ("h", "q", "k", "v")}
     n_act = counts(w)
-    run = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, w.bits)
+    run = fl.LoopRunner(w.N, w.H, w.d, w.g, w.R, w.n_sink, n_act, w.kcols, w.bits, mode=mode)
     N, H, d, g = w.N, w.H, w.d, w.g
     sm = np.float32(1 / np.sqrt(d))
     G = {}
