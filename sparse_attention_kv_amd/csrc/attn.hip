@@ -803,7 +803,7 @@ __device__ __forceinline__ void attn_lds_body(AttnParams P) {
 #pragma unroll
             for (int it = tid; it < BT * (D / 8); it += 256) {
                 const int key = it / (D / 8), c8 = it % (D / 8);
-                float x[8];
+                float x[8] = {};
                 uint32_t off = 0;
                 for (int l = 0; l < nl; ++l) {
                     const int b = P.qt.bits[l];
@@ -833,7 +833,7 @@ __device__ __forceinline__ void attn_lds_body(AttnParams P) {
 #pragma unroll
             for (int it = tid; it < D * (BT / 8); it += 256) {
                 const int dd = it / (BT / 8), oc = it % (BT / 8);
-                float y[8];
+                float y[8] = {};
                 uint32_t off = 0;
                 for (int l = 0; l < nl; ++l) {
                     const int b = P.qt.bits[l];
