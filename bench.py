@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SYMBOL = {"attn": "k_attn_lds<128, 0, 0, 64>", "attn_split": "k_attn_lds<128, 0, 1, 32>",
                  "attn_ad": "k_attn_ad<128, 0>", "attn_ad_rebuild": "k_attn_ad<128, 1>",
                  "attn_ad_rebuild_add": "k_attn_ad<128, 2>", "attn_ad_rb": "k_attn_ad<128, 3>",
-                 "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 8>",
-                 "colstat_split": "k_colstat_lds<128, 1, 4>", "decode_dense": "k_decode<128, 0, false, true, false, 0>",
+                 "attn_rebuild": "k_attn_lds<128, 1, 0, 64>", "colstat": "k_colstat_lds<128, 0, 4, 2>",
+                 "colstat_split": "k_colstat_lds<128, 1, 4, 1>", "decode_dense": "k_decode<128, 0, false, true, false, 0>",
                  "decode": "k_decode<128, 0, true, false, false, 0>",
                  "decode_rebuild": "k_decode<128, 1, true, true, false, 0>"}
 # projections of the 2048-hidden block: epilogue (0 store, 1 residual, 2 SwiGLU)

@@ -1107,10 +1107,17 @@ constexpr int RT2 = 64;
 // NW waves per workgroup, 32 columns each: every query tile copied into LDS
 // feeds 32 * NW columns, so the queries are streamed from memory
 // k / (32 * NW) times per head.
-template <int D, int PREC, int NW>
-__global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
+// KB key blocks of 32 columns per wave: with KB = 2 every query fragment read
+// from LDS feeds two MFMAs (half the LDS operand traffic per MFMA, which
+// otherwise bounds the MFMA side of the sweep), at three workgroups per CU.
+template <int KB>
+constexpr int colstat_min_blocks() { return KB == 2 ? 3 : 1; }
+
+template <int D, int PREC, int NW, int KB>
+__global__ __launch_bounds__(64 * NW, colstat_min_blocks<KB>()) void k_colstat_lds(ColParams P) {
     constexpr bool X3 = PREC >= 1;
-    constexpr int CTW = 32 * NW;             // columns per workgroup
+    static_assert(KB == 1 || (KB == 2 && !X3), "two key blocks per wave with plain bf16 keys");
+    constexpr int CTW = 32 * NW * KB;        // columns per workgroup
     constexpr int QB = RT2 * D * 2;         // bytes of one step's query rows
     constexpr int MPW = QB / 1024 / NW;     // LDS-DMA instructions per wave per step
     static_assert(MPW >= 1 && QB % (1024 * NW) == 0, "step copy split over the waves");
@@ -1125,26 +1132,32 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, half = lane >> 5;
-    const int p = pc0 + w * 32 + r;  // compact slot
     const int32_t* cpos_h = P.cpos + (long)h * P.kp;
-    // selection index of the slot (a slot order from k_classify_cols puts
-    // pads between and after its two ascending parts)
-    const int src = P.perm ? (p < P.kp ? P.perm[(long)h * P.kp + p] : -1) : (p < P.k ? p : -1);
-    const bool colv = src >= 0;
-    const int cp = colv ? cpos_h[p] : 0x7fffffff;
-    bf16x8 kf[D / 16], kl[X3 ? D / 16 : 1];
-    {
-        const long ko = ((long)h * P.kp + (colv ? p : 0)) * D + 8 * half;
+    // this lane's columns (compact slots) and their selection indices (a
+    // slot order from k_classify_cols puts pads between and after its two
+    // ascending parts)
+    int p[KB], src[KB], cp[KB];
+    bool colv[KB];
+    bf16x8 kf[KB][D / 16], kl[X3 ? D / 16 : 1];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        p[kb] = pc0 + (w * KB + kb) * 32 + r;
+        src[kb] = P.perm ? (p[kb] < P.kp ? P.perm[(long)h * P.kp + p[kb]] : -1) : (p[kb] < P.k ? p[kb] : -1);
+        colv[kb] = src[kb] >= 0;
+        cp[kb] = colv[kb] ? cpos_h[p[kb]] : 0x7fffffff;
+        const long ko = ((long)h * P.kp + (colv[kb] ? p[kb] : 0)) * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(P.Kc + ko + 16 * kk);
+            kf[kb][kk] = *reinterpret_cast<const bf16x8*>(P.Kc + ko + 16 * kk);
             if (X3) kl[X3 ? kk : 0] = *reinterpret_cast<const bf16x8*>(P.Kc_lo + ko + 16 * kk);
         }
     }
     // the block's first and last column positions
     if (tid == 0) { s_start = 0x7fffffff; s_cmax = -1; }
     __syncthreads();
-    if (colv) { atomicMin(&s_start, cp); atomicMax(&s_cmax, cp); }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        if (colv[kb]) { atomicMin(&s_start, cp[kb]); atomicMax(&s_cmax, cp[kb]); }
     __syncthreads();
     if (tid == 0) s_start = lower_bound_i32(P.active, P.n, s_start);
     __syncthreads();
@@ -1205,7 +1218,9 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
         rp[lane] = mpos;
         ro[lane] = mpos >= 0 ? mlse * 1.4426950408889634f - __log2f(wgt) : INFINITY;
     };
-    float csum = 0.0f;
+    float csum[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) csum[kb] = 0.0f;
     auto compute = [&](int t0, const __bf16* sQ, const int* rpos, const float* roff) {
         const bool full = rpos[0] >= cmax && t0 + RT2 <= P.n;
         // (computing both halves' S^T before their exponentials, with or
@@ -1213,27 +1228,33 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
         // 3.01 ms at 32K)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            f32x16 s = f32x16{};
+            f32x16 s[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
             const int row = 32 * sub + r;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
                 const int e = row * D + (((2 * kk + half) ^ swz<D * 2 / 16>(row)) << 3);
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[e]);
-                s = mfma32(a, kf[kk], s);
-                if (X3) s = mfma32(a, kl[X3 ? kk : 0], s);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(a, kf[kb][kk], s[kb]);
+                if (X3) s[0] = mfma32(a, kl[X3 ? kk : 0], s[0]);
             }
-            if (full) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
-                    csum += __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[rw]));
-                }
-            } else {
+            for (int kb = 0; kb < KB; ++kb) {
+                if (full) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
-                    const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], P.c2, -roff[rw]));
-                    csum += (rpos[rw] >= cp) ? pj : 0.0f;
+                    for (int j = 0; j < 16; ++j) {
+                        const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
+                        csum[kb] += __builtin_amdgcn_exp2f(fmaf(s[kb][j], P.c2, -roff[rw]));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int rw = 32 * sub + (j >> 2) * 8 + half * 4 + (j & 3);
+                        const float pj = __builtin_amdgcn_exp2f(fmaf(s[kb][j], P.c2, -roff[rw]));
+                        csum[kb] += (rpos[rw] >= cp[kb]) ? pj : 0.0f;
+                    }
                 }
             }
         }
@@ -1274,9 +1295,12 @@ __global__ __launch_bounds__(64 * NW) void k_colstat_lds(ColParams P) {
             if (++it >= nsteps) break;
         }
     }
-    csum += __shfl_xor(csum, 32);
-    if (colv && half == 0)
-        P.col_stat[(long)h * P.k + src] = P.vnorm ? csum * P.vnorm[(long)h * P.kp + p] : csum;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const float cs = csum[kb] + __shfl_xor(csum[kb], 32);
+        if (colv[kb] && half == 0)
+            P.col_stat[(long)h * P.k + src[kb]] = P.vnorm ? cs * P.vnorm[(long)h * P.kp + p[kb]] : cs;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1366,7 +1390,10 @@ hipError_t launch_attn(int d, int mode, int prec, bool in_tile, const AttnParams
 // waves per workgroup of the LDS-DMA column statistics: 8 (256 columns) with
 // plain bf16 keys; hi/lo keys take more registers, so 4 keep 3 waves per SIMD
 template <int PREC>
-constexpr int colstat_waves() { return PREC == 0 ? 8 : 4; }
+constexpr int colstat_waves() { return PREC == 0 ? 4 : 4; }
+// key blocks per wave (two with plain bf16 keys, see k_colstat_lds)
+template <int PREC>
+constexpr int colstat_kb() { return PREC == 0 ? 2 : 1; }
 
 hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
     // one-dimensional grids of column blocks x heads (see col_coords); with a
@@ -1375,8 +1402,9 @@ hipError_t launch_colstat(int d, int prec, const ColParams& P, hipStream_t st) {
     const dim3 grid(((ncol + CT - 1) / CT) * P.H);
 #define FL_COL(D_, P_) hipLaunchKernelGGL((k_colstat<D_, P_>), grid, dim3(256), 0, st, P)
 #define FL_COLL(D_, P_)                                                                        \
-    hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>()>),                           \
-                       dim3(((ncol + 32 * colstat_waves<P_>() - 1) / (32 * colstat_waves<P_>())) * P.H), \
+    hipLaunchKernelGGL((k_colstat_lds<D_, P_, colstat_waves<P_>(), colstat_kb<P_>()>),        \
+                       dim3(((ncol + 32 * colstat_waves<P_>() * colstat_kb<P_>() - 1) /              \
+                             (32 * colstat_waves<P_>() * colstat_kb<P_>())) * P.H),                  \
                        dim3(64 * colstat_waves<P_>()), 0, st, P)
 #define FL_COL_D(D_) \
     if (prec == 0) FL_COLL(D_, 0); else if (prec == 1) FL_COLL(D_, 1); else FL_COL(D_, 2);
