@@ -14,11 +14,11 @@ from gpu_chain import compare_chain, run_gpu, run_oracle_lockstep
 pytestmark = pytest.mark.gpu
 
 
-def _chain(w, quant=fl.FL_QUANT_ABSMAX):
+def _chain(w, quant=fl.FL_QUANT_ABSMAX, mode=fl.FL_DEQ_AUTO):
     print("depth chain", w.N, w.H, w.R, "k", w.kcols[:4], "...", w.kcols[-1], "bits", w.bits[:3],
-          "quant", quant, flush=True)
+          "quant", quant, "mode", mode, flush=True)
     inp = synth.generate(w)
-    gres, _ = run_gpu(w, inp, quant=quant)
+    gres, _ = run_gpu(w, inp, quant=quant, mode=mode)
     ores = run_oracle_lockstep(w, inp, gres, quant=quant)
     rep = compare_chain(w, gres, ores, quant=quant)
     worst = max(rep, key=lambda t: t[1][0])
@@ -28,6 +28,13 @@ def _chain(w, quant=fl.FL_QUANT_ABSMAX):
 
 def test_depth32_small():
     _chain(synth.WORKLOADS["depth32x8k"].scaled(N=600, H=4))
+
+
+def test_depth32_small_in_tile():
+    """In-tile dequantisation through 32 levels: the LDS-DMA kernel while a
+    tile's planes fit its staging buffer (about the first 8 loops here),
+    then the register-staged kernel."""
+    _chain(synth.WORKLOADS["depth32x8k"].scaled(N=600, H=4), mode=fl.FL_DEQ_IN_TILE)
 
 
 @pytest.mark.timeout(600)
