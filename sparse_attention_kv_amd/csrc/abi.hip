@@ -579,7 +579,7 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
                    "classify");
         FL_HIP(timed("gather", st, [&] {
                    return fl::launch_gather_bf16(*cache, upto, sel, k, kp, ad || pr >= 1, K_, V_, Kl_,
-                                                 Vl_, cp, vnorm, ad ? pm : nullptr, st);
+                                                 Vl_, cp, vnorm, ad ? pm : nullptr, ad ? cs : nullptr, st);
                }),
                "gather");
         return FL_OK;
@@ -674,7 +674,7 @@ static int sparse_loop_attn(const fl_kv_cache* cache, const fl_attn_args* a, voi
         if (in_tile) // the statistics sweep reads the keys as compact bf16
             FL_HIP(timed("gather", st, [&] {
                        return fl::launch_gather_bf16(*cache, a->level, a->sel, a->k, kp, prec >= 1, Kc,
-                                                     Vt, Kl, Vl, cpos, vn, nullptr, st);
+                                                     Vt, Kl, Vl, cpos, vn, nullptr, nullptr, st);
                    }),
                    "gather");
         fl::ColParams C{};

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 8) void k_gather_bf16(fl_kv_cache c, int upto,
                                                      __bf16* __restrict__ Vt_lo,
                                                      int32_t* __restrict__ cpos,
                                                      float* __restrict__ vnorm,
-                                                     const int32_t* __restrict__ perm) {
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ colseg) {
     constexpr int TPC = D / 8;            // threads per column
     constexpr int GC = gather_cols<D>();  // columns per workgroup (16 or 32)
     __shared__ __bf16 sV[X3 ? 2 : 1][GC][D + 8];
@@ -135,8 +136,12 @@ __global__ __launch_bounds__(256, 8) void k_gather_bf16(fl_kv_cache c, int upto,
     // transpose this workgroup's columns of the V tile: rows d, its GC keys
     // (whole 16-key groups, key order permuted inside each group), 16-byte stores
     const int tile = p0 / BN, kbase = p0 % BN;
+    // with a slot order only the outlier part's tiles read the values' lo
+    // parts (normal columns enter P.V as bf16 in every tile kind)
+    const bool vlo = X3 && !(perm && colseg && p0 + GC <= (colseg[2 * h] + BN - 1) / BN * BN);
 #pragma unroll
     for (int part = 0; part < (X3 ? 2 : 1); ++part) {
+        if (part && !vlo) break;
         __bf16* vdst = (part ? Vt_lo : Vt) + ((long)h * (kp / BN) + tile) * D * BN + kbase;
         for (int idx = tid; idx < D * (GC / 8); idx += 256) {
             const int dd = idx / (GC / 8);
@@ -1307,14 +1312,15 @@ __global__ __launch_bounds__(64 * NW, colstat_min_blocks<KB>()) void k_colstat_l
 // launchers
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool x3, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st) {
+                              int32_t* cpos, float* vnorm, const int32_t* perm, const int32_t* colseg,
+                              hipStream_t st) {
     dim3 grid(kp / (c.d == 128 ? gather_cols<128>() : gather_cols<64>()), c.H);
     // the keys' and values' level rows loaded together where the cache allows
     // (kDeqBatch + 1: levels in several chunks)
     const int nb = !deq_batch_ok(c, upto) ? 0 : upto < kDeqBatch ? upto + 1 : kDeqBatch + 1;
 #define FL_GATHER(D_, X_, B_)                                                                       \
     hipLaunchKernelGGL((k_gather_bf16<D_, X_, B_>), grid, dim3(256), 0, st, c, upto, sel, k, kp, Kc, \
-                       Vt, Kc_lo, Vt_lo, cpos, vnorm, perm)
+                       Vt, Kc_lo, Vt_lo, cpos, vnorm, perm, colseg)
 #define FL_GATHER_B(D_, X_) {                                                   \
         switch (nb) {                                                           \
         case 1: FL_GATHER(D_, X_, 1); break;                                    \

@@ -163,7 +163,8 @@ hipError_t launch_quant(const fl_kv_cache& cache, int level, int dtype, const vo
 // each compact slot, -1 for padding
 hipError_t launch_gather_bf16(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                               bool split, __bf16* Kc, __bf16* Vt, __bf16* Kc_lo, __bf16* Vt_lo,
-                              int32_t* cpos, float* vnorm, const int32_t* perm, hipStream_t st);
+                              int32_t* cpos, float* vnorm, const int32_t* perm, const int32_t* colseg,
+                              hipStream_t st);
 // prec: 0 bf16 operands, 1 K/V/P as hi+lo bf16 pairs, 2 also q (fp32 inputs)
 hipError_t launch_gather_q(const fl_kv_cache& c, int upto, const int32_t* sel, int k, int kp,
                            const QTiles& out, int32_t* cpos, hipStream_t st);
