@@ -18,7 +18,9 @@ Prints ONE JSON line.  Extra fields: per-loop and per-phase times, per-kernel
 times, the roofline of the dominant kernel of the metric's work and of that
 work as a whole (algorithmic flops from the actual index sets), loop 1's
 dense attention roofline, KV bytes/token, and the CPU oracle timed on a
-bounded sample of the same work.
+bounded sample of the same work.  The default prefill line also carries the
+batched-decode workload (64 x 8K) under "decode64x8k" and the 24-layer
+looped block (8K) under "block8k" (--no-decode / --no-block skip them).
 """
 from __future__ import annotations
 
@@ -61,6 +63,8 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="prefill32k: skip the batched-decode measurement attached to the line")
+    ap.add_argument("--no-block", action="store_true",
+                    help="prefill32k: skip the 24-layer block measurement attached to the line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -160,7 +164,25 @@ def main():
     out = bench_prefill(args, w, np, torch, fl, synth, cpu=not args.no_cpu_baseline)
     if w.name == "prefill32k" and not args.no_decode and args.quant == "absmax":
         out["decode64x8k"] = decode_summary(args, np, torch, fl, synth)
+    if w.name == "prefill32k" and not args.no_block and args.quant == "absmax":
+        out["block8k"] = block_summary(args, np, torch, fl, synth)
     print(json.dumps(out), flush=True)
+
+
+def block_summary(args, np, torch, fl, synth):
+    """The 24-layer looped block (8K tokens, R=4, token-sparse projections,
+    sparse loop attention, residual KV store) timed after the prefill and
+    decode measurements, 5 steps after 2 warm-up steps, no CPU baseline: its
+    active tokens/s, per-loop times and the gate/up projection's roofline."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    bargs = argparse.Namespace(**vars(args))
+    bargs.steps, bargs.warmup, bargs.no_cpu_baseline = 5, 2, True
+    bargs.calibrate, bargs.return_record = False, True
+    b = bench_block(bargs, synth.WORKLOADS["block8k"], np, torch, fl, synth)
+    keep = ("metric", "value", "unit", "steps", "warmup", "ms_per_step", "loops", "roofline", "gemms_all")
+    return {k: b[k] for k in keep if k in b}
 
 
 def decode_summary(args, np, torch, fl, synth):
@@ -688,6 +710,8 @@ def bench_block(args, w, np, torch, fl, synth):
         out["cpu_baseline"] = cpu_baseline_block(w, inp, n_act, np, rel=args.token_stat == "rel",
                                                  vw=args.col_stat == "vnorm",
                                                  asym=args.quant == "asym")
+    if getattr(args, "return_record", False):
+        return out
     print(json.dumps(out), flush=True)
 
 
